@@ -1,0 +1,311 @@
+/*
+ * oracle.c -- plain CPU oracle for the DSA hot path (TEST INFRASTRUCTURE ONLY).
+ * Definitions and page citations are in oracle.h.  Everything is fp64 except the
+ * indexer dot products, which are exact int64 sums.  OpenMP parallelises over rows only;
+ * every row is an independent, straightforward loop.
+ */
+#include "oracle.h"
+
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* ---------------------------------------------------------------- decoders */
+
+/* OCP e4m3fn: sign | 4 exponent bits (bias 7) | 3 mantissa bits; E=15,M=7 is NaN,
+ * E=0 is subnormal M * 2^-9; there are no infinities. */
+double ora_e4m3fn_value(uint8_t code)
+{
+    int sign = code >> 7, E = (code >> 3) & 15, M = code & 7;
+    double mag;
+    if (E == 15 && M == 7) return NAN;
+    if (E == 0) mag = ldexp((double)M, -9);
+    else        mag = ldexp(1.0 + M / 8.0, E - 7);
+    return sign ? -mag : mag;
+}
+
+/* The same value times 2^9, which is always an integer of magnitude <= 448*512. */
+static int64_t e4m3fn_times_512(uint8_t code)
+{
+    int sign = code >> 7, E = (code >> 3) & 15, M = code & 7;
+    int64_t mag = (E == 0) ? (int64_t)M : ((int64_t)(8 + M) << (E - 1));
+    return sign ? -mag : mag;
+}
+
+static int e4m3fn_is_nan(uint8_t code) { return (code & 0x7F) == 0x7F; }
+
+/* bf16 is the top half of an IEEE binary32. */
+double ora_bf16_value(uint16_t bits)
+{
+    uint32_t u = (uint32_t)bits << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+int ora_num_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+/* ----------------------------------------------------------------- indexer */
+
+int ora_index_scores(const uint8_t* q8, const float* qs, const float* w,
+                     const uint8_t* k8, const float* ks, int64_t L, int H_I,
+                     int64_t q_pos0, double c, const int64_t* rows, int64_t n_rows,
+                     double* scores, double* bound)
+{
+    if (L <= 0 || H_I <= 0 || n_rows < 0 || q_pos0 < 0) return -1;
+    for (int64_t s = 0; s < L * 128; ++s)
+        if (e4m3fn_is_nan(k8[s])) return -1;
+
+    /* keys decoded once to integers (value * 2^9) */
+    int64_t* kint = (int64_t*)malloc(sizeof(int64_t) * (size_t)L * 128);
+    if (!kint) return -1;
+    for (int64_t s = 0; s < L * 128; ++s) kint[s] = e4m3fn_times_512(k8[s]);
+
+    int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : bad)
+    for (int64_t r = 0; r < n_rows; ++r) {
+        const int64_t t = rows[r];
+        const int64_t p = q_pos0 + t;          /* absolute position of the query */
+        int64_t qint[128 * 128];               /* H_I <= 128 */
+        double wprime[128];
+        if (t < 0 || H_I > 128) { bad = 1; continue; }
+        for (int h = 0; h < H_I; ++h) {
+            for (int d = 0; d < 128; ++d) {
+                uint8_t code = q8[(t * H_I + h) * 128 + d];
+                if (e4m3fn_is_nan(code)) bad = 1;
+                qint[h * 128 + d] = e4m3fn_times_512(code);
+            }
+            /* per-head weight a_h carries the query's dequantisation scale and c */
+            wprime[h] = (double)w[t * H_I + h] * (double)qs[t * H_I + h] * c;
+        }
+        for (int64_t s = 0; s < L; ++s) {
+            double* out = scores + r * L + s;
+            if (s > p) {                         /* future token: masked */
+                *out = -INFINITY;
+                if (bound) bound[r * L + s] = 0.0;
+                continue;
+            }
+            double acc = 0.0, acc_abs = 0.0;
+            for (int h = 0; h < H_I; ++h) {
+                int64_t dot = 0, dot_abs = 0;
+                for (int d = 0; d < 128; ++d) {
+                    int64_t prod = qint[h * 128 + d] * kint[s * 128 + d];
+                    dot += prod;
+                    dot_abs += prod < 0 ? -prod : prod;
+                }
+                /* |dot| < 128 * 2^36 = 2^43, so the scaling to fp64 is exact */
+                double D = ldexp((double)dot, -18);
+                double relu = D > 0.0 ? D : 0.0;
+                acc += wprime[h] * relu;
+                acc_abs += fabs(wprime[h]) * ldexp((double)dot_abs, -18);
+            }
+            *out = (double)ks[s] * acc;
+            if (bound) bound[r * L + s] = (double)ks[s] * acc_abs;
+        }
+    }
+    free(kint);
+    return bad ? -1 : 0;
+}
+
+/* ------------------------------------------------------------------- top-k */
+
+typedef struct { double v; int64_t pos; } item_t;
+
+/* (score descending, position ascending): a total order, so any sort is deterministic */
+static int cmp_item(const void* a, const void* b)
+{
+    const item_t* x = (const item_t*)a;
+    const item_t* y = (const item_t*)b;
+    if (x->v > y->v) return -1;
+    if (x->v < y->v) return 1;
+    return (x->pos > y->pos) - (x->pos < y->pos);
+}
+
+static int cmp_i32(const void* a, const void* b)
+{
+    int32_t x = *(const int32_t*)a, y = *(const int32_t*)b;
+    return (x > y) - (x < y);
+}
+
+static int fill_all_visible(int64_t n, int k, int32_t* out)
+{
+    for (int j = 0; j < k; ++j) out[j] = (j < n) ? (int32_t)j : -1;
+    return 0;
+}
+
+int ora_topk_sort(const double* scores, int64_t ld, int64_t n_rows, const int64_t* n_vis,
+                  int k, int32_t* idx)
+{
+    if (k <= 0 || n_rows < 0) return -1;
+    int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : bad)
+    for (int64_t r = 0; r < n_rows; ++r) {
+        const int64_t n = n_vis[r];
+        int32_t* out = idx + r * k;
+        if (n < 0 || n > ld) { bad = 1; continue; }
+        if (n <= k) { fill_all_visible(n, k, out); continue; }
+        item_t* it = (item_t*)malloc(sizeof(item_t) * (size_t)n);
+        if (!it) { bad = 1; continue; }
+        for (int64_t s = 0; s < n; ++s) { it[s].v = scores[r * ld + s]; it[s].pos = s; }
+        qsort(it, (size_t)n, sizeof(item_t), cmp_item);
+        for (int j = 0; j < k; ++j) out[j] = (int32_t)it[j].pos;
+        qsort(out, (size_t)k, sizeof(int32_t), cmp_i32);
+        free(it);
+    }
+    return bad ? -1 : 0;
+}
+
+/* k-th largest (1-based) of v[0..n) by Hoare-style quickselect; reorders v. */
+static double kth_largest(double* v, int64_t n, int64_t kth)
+{
+    int64_t lo = 0, hi = n - 1, want = kth - 1;   /* index in descending order */
+    while (lo < hi) {
+        double pivot = v[lo + (hi - lo) / 2];
+        int64_t i = lo, j = hi;
+        while (i <= j) {
+            while (v[i] > pivot) ++i;
+            while (v[j] < pivot) --j;
+            if (i <= j) { double tmp = v[i]; v[i] = v[j]; v[j] = tmp; ++i; --j; }
+        }
+        if (want <= j) hi = j;
+        else if (want >= i) lo = i;
+        else return v[want];
+    }
+    return v[want];
+}
+
+int ora_topk_select(const double* scores, int64_t ld, int64_t n_rows, const int64_t* n_vis,
+                    int k, int32_t* idx)
+{
+    if (k <= 0 || n_rows < 0) return -1;
+    int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : bad)
+    for (int64_t r = 0; r < n_rows; ++r) {
+        const int64_t n = n_vis[r];
+        int32_t* out = idx + r * k;
+        if (n < 0 || n > ld) { bad = 1; continue; }
+        if (n <= k) { fill_all_visible(n, k, out); continue; }
+        const double* row = scores + r * ld;
+        double* tmp = (double*)malloc(sizeof(double) * (size_t)n);
+        if (!tmp) { bad = 1; continue; }
+        memcpy(tmp, row, sizeof(double) * (size_t)n);
+        const double tau = kth_largest(tmp, n, k);      /* the k-th best score */
+        free(tmp);
+        int64_t above = 0;
+        for (int64_t s = 0; s < n; ++s) above += row[s] > tau;
+        int64_t ties_left = k - above;                   /* >= 1 */
+        int j = 0;
+        for (int64_t s = 0; s < n && j < k; ++s) {
+            if (row[s] > tau) out[j++] = (int32_t)s;
+            else if (row[s] == tau && ties_left > 0) { out[j++] = (int32_t)s; --ties_left; }
+        }
+        if (j != k) bad = 1;
+    }
+    return bad ? -1 : 0;
+}
+
+/* --------------------------------------------------------------------- MLA */
+
+/* softmax attention of one query head over a list of cache rows */
+static void attend(const uint16_t* qrow, const uint16_t* kv, const int64_t* sel, int64_t m,
+                   double sm_scale, double* logit, double* out, double* lse)
+{
+    double qv[576];
+    for (int d = 0; d < 576; ++d) qv[d] = ora_bf16_value(qrow[d]);
+    for (int d = 0; d < 512; ++d) out[d] = 0.0;
+    if (m == 0) { *lse = -INFINITY; return; }
+    double mx = -INFINITY;
+    for (int64_t j = 0; j < m; ++j) {
+        const uint16_t* row = kv + sel[j] * 576;
+        double dot = 0.0;
+        for (int d = 0; d < 576; ++d) dot += qv[d] * ora_bf16_value(row[d]);
+        logit[j] = sm_scale * dot;
+        if (logit[j] > mx) mx = logit[j];
+    }
+    double Z = 0.0;
+    for (int64_t j = 0; j < m; ++j) Z += exp(logit[j] - mx);
+    for (int64_t j = 0; j < m; ++j) {
+        const double pj = exp(logit[j] - mx) / Z;
+        const uint16_t* row = kv + sel[j] * 576;
+        for (int d = 0; d < 512; ++d) out[d] += pj * ora_bf16_value(row[d]);
+    }
+    *lse = mx + log(Z);
+}
+
+int ora_sparse_mla(const uint16_t* q, const uint16_t* kv, const int32_t* idx, int64_t L,
+                   int H, int k, double sm_scale, const int64_t* rows, int64_t n_rows,
+                   double* out, double* lse)
+{
+    if (L <= 0 || H <= 0 || k <= 0 || n_rows < 0) return -1;
+    int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : bad)
+    for (int64_t r = 0; r < n_rows; ++r) {
+        const int64_t t = rows[r];
+        int64_t* sel = (int64_t*)malloc(sizeof(int64_t) * (size_t)k);
+        double* logit = (double*)malloc(sizeof(double) * (size_t)k);
+        int64_t m = 0;
+        for (int j = 0; j < k; ++j) {
+            int32_t s = idx[t * k + j];
+            if (s < 0) continue;                  /* padding */
+            if (s >= L) { bad = 1; continue; }
+            sel[m++] = s;
+        }
+        for (int h = 0; h < H; ++h)
+            attend(q + (t * H + h) * 576, kv, sel, m, sm_scale, logit,
+                   out + (r * H + h) * 512, lse + r * H + h);
+        free(sel);
+        free(logit);
+    }
+    return bad ? -1 : 0;
+}
+
+int ora_dense_mla(const uint16_t* q, const uint16_t* kv, int64_t L, int H, int64_t q_pos0,
+                  double sm_scale, const int64_t* rows, int64_t n_rows, double* out,
+                  double* lse)
+{
+    /* Written independently of attend(): a streaming (running-max) softmax over every
+     * visible position, no index list involved. */
+    if (L <= 0 || H <= 0 || n_rows < 0 || q_pos0 < 0) return -1;
+    int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : bad)
+    for (int64_t r = 0; r < n_rows; ++r) {
+        const int64_t t = rows[r];
+        const int64_t p = q_pos0 + t;
+        if (t < 0 || p >= L) { bad = 1; continue; }
+        for (int h = 0; h < H; ++h) {
+            const uint16_t* qrow = q + (t * H + h) * 576;
+            double* o = out + (r * H + h) * 512;
+            double run_max = -INFINITY, run_sum = 0.0;
+            for (int d = 0; d < 512; ++d) o[d] = 0.0;
+            for (int64_t s = 0; s <= p; ++s) {
+                const uint16_t* row = kv + s * 576;
+                double dot = 0.0;
+                for (int d = 0; d < 576; ++d)
+                    dot += ora_bf16_value(qrow[d]) * ora_bf16_value(row[d]);
+                const double logit = sm_scale * dot;
+                if (logit > run_max) {                 /* rescale what was summed so far */
+                    const double f = exp(run_max - logit);
+                    run_sum *= f;
+                    for (int d = 0; d < 512; ++d) o[d] *= f;
+                    run_max = logit;
+                }
+                const double e = exp(logit - run_max);
+                run_sum += e;
+                for (int d = 0; d < 512; ++d) o[d] += e * ora_bf16_value(row[d]);
+            }
+            for (int d = 0; d < 512; ++d) o[d] /= run_sum;
+            lse[r * H + h] = run_max + log(run_sum);
+        }
+    }
+    return bad ? -1 : 0;
+}

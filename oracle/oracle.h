@@ -1,0 +1,79 @@
+/*
+ * oracle.h -- plain CPU oracle for the DeepSeek Sparse Attention (DSA) hot path.
+ *
+ * TEST INFRASTRUCTURE ONLY.  The tests, the package's smoke check and the benchmark's
+ * CPU-baseline leg are the only callers.  It shares no code, header, table or constant
+ * with the HIP library: its own e4m3fn/bf16 decoders, its own loops, fp64 arithmetic.
+ *
+ * Pages cited (by title; section names as printed on each page):
+ *   [csdn-workflow] 《DeepSeek-V3.2-Exp模型优势与 DSA 工作原理,token降价性能不减的背后》
+ *                   (agent.csdn.net) -- §2 风险边界明确, §3 两大核心组件, §4 四步工作流程.
+ *   [devpress-dsa]  《狂降75%！大模型DeepSeek-V3.2 API杀疯了：性能零衰减的秘密，藏在DSA这两大
+ *                   “黑科技”里》 (devpress.csdn.net) -- §二 两大核心武器, §三 四步工作流.
+ *   [gxzdkb-dsa]    gxzdkb.com explainer of DSA -- sections 原始 Attention 的计算逻辑,
+ *                   秘密武器：DSA, 实测效果.
+ *   [yufo-notes]    ele-yufo.com notes "DeepSeek V3.2-Exp" -- §三 两步跑通稀疏路由.
+ *
+ * Conventions shared by every function:
+ *   fp8 operands are OCP e4m3fn bytes; bf16 operands are raw uint16 bits.
+ *   Query row t sits at absolute position p_t = q_pos0 + t and sees keys s <= p_t
+ *   (the causal mask of [csdn-workflow] §4 步骤二; "update the cache first, then
+ *   compute" in [gxzdkb-dsa] makes the query see itself).
+ *   `rows` lists which query rows to compute (n_rows of them); outputs are packed
+ *   in that order.  All functions return 0, or -1 on invalid input.
+ */
+#ifndef DSA_ORACLE_H
+#define DSA_ORACLE_H
+#include <stdint.h>
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Value of one e4m3fn code (NaN for 0x7F / 0xFF) and of one bf16 bit pattern. */
+double ora_e4m3fn_value(uint8_t code);
+double ora_bf16_value(uint16_t bits);
+
+/* Lightning-indexer scores, [csdn-workflow] §4 步骤二 and [devpress-dsa] §三 第二步:
+ *   D[t,h,s]    = sum_d q8[t,h,d] * k8[s,d]          (exact, int64 at scale 2^18)
+ *   score[t,s]  = ks[s] * sum_h (w[t,h]*qs[t,h]*c) * max(D[t,h,s], 0)   for s <= p_t
+ *               = -inf                                                  for s >  p_t
+ *   bound[t,s]  = ks[s] * sum_h |w*qs*c| * sum_d |q8*k8|   (conditioning bound, nullable)
+ * q8[T,H_I,128], qs[T,H_I], w[T,H_I], k8[L,128], ks[L]; scores/bound [n_rows, L]. */
+int ora_index_scores(const uint8_t* q8, const float* qs, const float* w,
+                     const uint8_t* k8, const float* ks, int64_t L, int H_I,
+                     int64_t q_pos0, double c, const int64_t* rows, int64_t n_rows,
+                     double* scores, double* bound);
+
+/* Top-k, [csdn-workflow] §4 步骤三: the k visible positions with the largest score,
+ * ties to the lower position, -0 == +0; all n visible positions when n <= k.
+ * scores [n_rows, ld] (entries s < n_vis[r] are read), idx [n_rows, k] int32,
+ * ascending positions then -1 padding.  Two independent selectors:
+ *   _sort   : full sort of (score desc, position asc), keep the first k;
+ *   _select : k-th largest value by quickselect, then a position-ordered sweep. */
+int ora_topk_sort(const double* scores, int64_t ld, int64_t n_rows, const int64_t* n_vis,
+                  int k, int32_t* idx);
+int ora_topk_select(const double* scores, int64_t ld, int64_t n_rows, const int64_t* n_vis,
+                    int k, int32_t* idx);
+
+/* Sparse MLA, [csdn-workflow] §4 步骤四 and [devpress-dsa] §三 第四步: for each row t
+ * and head h, logits l_j = sm_scale * <q[t,h,0:576], kv[I_j,0:576]> over the selected
+ * rows I_j = idx[t,j] (-1 entries skipped), out = softmax(l) . kv[I,0:512],
+ * lse = log sum exp l.  A row with no valid index gives out = 0, lse = -inf.
+ * q[T,H,576] bf16, kv[L,576] bf16, idx[T,k]; out [n_rows,H,512], lse [n_rows,H]. */
+int ora_sparse_mla(const uint16_t* q, const uint16_t* kv, const int32_t* idx, int64_t L,
+                   int H, int k, double sm_scale, const int64_t* rows, int64_t n_rows,
+                   double* out, double* lse);
+
+/* Dense causal MLA over every s <= p_t, no index list: the full attention that DSA
+ * equals when a query sees at most k tokens ([csdn-workflow] §2 风险边界明确, §4 步骤三). */
+int ora_dense_mla(const uint16_t* q, const uint16_t* kv, int64_t L, int H, int64_t q_pos0,
+                  double sm_scale, const int64_t* rows, int64_t n_rows, double* out,
+                  double* lse);
+
+/* Threads the OpenMP loops use. */
+int ora_num_threads(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

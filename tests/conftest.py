@@ -1,0 +1,30 @@
+import os
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+
+def pytest_configure(config):
+    config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU")
+
+
+def gpu_available() -> bool:
+    try:
+        import torch
+        return torch.cuda.is_available()
+    except Exception:
+        return False
+
+
+@pytest.fixture(scope="session")
+def dsa():
+    """The HIP library binding; GPU tests fail loudly if it cannot be loaded."""
+    if not gpu_available():
+        pytest.skip("no GPU")
+    import sparse_attention_05_amd as dsa_mod
+    dsa_mod.load()
+    return dsa_mod

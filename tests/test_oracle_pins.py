@@ -1,0 +1,342 @@
+"""Pins of the CPU oracle against things other than itself (CPU only).
+
+Each test ties one oracle function to a library routine, a closed form, a hand-computed
+example, brute force, or an invariant, so that a dropped term, a wrong sign or index, or a
+transposed operand in the oracle fails at least one of them.
+"""
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from synth import PrefillCfg, host_arrays, make_prefill
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ----------------------------------------------------------------------------- codecs
+
+def test_e4m3fn_decoder_all_codes_match_torch():
+    codes = np.arange(256, dtype=np.uint8)
+    mine = oracle.e4m3fn_values(codes)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(mine), nan)
+    assert nan.sum() == 2                      # 0x7F and 0xFF
+    assert np.array_equal(mine[~nan], ref[~nan])
+    assert np.array_equal(np.signbit(mine[~nan]), np.signbit(ref[~nan]))   # -0 is 0x80
+
+
+def test_bf16_decoder_all_codes_match_torch():
+    bits = np.arange(65536, dtype=np.uint16)
+    mine = oracle.bf16_values(bits)
+    ref = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(mine), nan)
+    assert np.array_equal(mine[~nan], ref[~nan])
+
+
+# ---------------------------------------------------------------------------- indexer
+
+def _e4m3_deq(codes):
+    return torch.from_numpy(np.ascontiguousarray(codes)).view(torch.float8_e4m3fn).to(torch.float64)
+
+
+def _small_prefill(L=48, H_I=1, H=2, k=8, seed=5, q_pos0=0, T=None):
+    cfg = PrefillCfg("t", L=L, k=k, H_I=H_I, H=H, w_std=1.0, seed=seed, q_pos0=q_pos0, T=T)
+    return host_arrays(make_prefill(cfg))
+
+
+def test_indexer_single_head_is_relu_of_matmul():
+    """H_I = 1, unit weights/scales: scores are ReLU(deq(q) @ deq(k)^T) under the causal
+    mask.  fp64 matmul is exact here (products of e4m3 values span < 53 bits)."""
+    a = _small_prefill(L=40, H_I=1, q_pos0=3, T=30)
+    T, L = a["T"], a["L"]
+    ones_t = np.ones((T, 1), np.float32)
+    s = oracle.index_scores(a["q8"], ones_t, ones_t, a["k8"], np.ones(L, np.float32),
+                            a["q_pos0"], 1.0)
+    D = _e4m3_deq(a["q8"][:, 0, :]) @ _e4m3_deq(a["k8"]).T
+    ref = torch.clamp(D, min=0).numpy()
+    mask = np.arange(L)[None, :] > (a["q_pos0"] + np.arange(T))[:, None]
+    ref[mask] = -np.inf
+    assert np.array_equal(s, ref)
+
+
+def test_indexer_single_head_scales_multiply():
+    a = _small_prefill(L=33, H_I=1)
+    c = 0.0883883
+    s = oracle.index_scores(a["q8"], a["qs"], a["w"], a["k8"], a["ks"], 0, c)
+    D = (_e4m3_deq(a["q8"][:, 0, :]) @ _e4m3_deq(a["k8"]).T).numpy()
+    wp = a["w"][:, 0].astype(np.float64) * a["qs"][:, 0].astype(np.float64) * c
+    ref = np.maximum(D, 0) * wp[:, None] * a["ks"].astype(np.float64)[None, :]
+    vis = np.tril(np.ones_like(ref, dtype=bool))
+    assert np.allclose(s[vis], ref[vis], rtol=1e-14, atol=0)
+    assert np.all(np.isneginf(s[~vis]))
+
+
+def test_indexer_hand_example():
+    g = json.load(open(os.path.join(GOLDEN, "indexer_hand.json")))
+    enc = {float(v): c for v, c in g["e4m3fn_codes"].items()}
+    enc[0.0] = 0
+    T, H_I, L = g["T"], g["H_I"], g["L"]
+    q8 = np.zeros((T, H_I, 128), np.uint8)
+    k8 = np.zeros((L, 128), np.uint8)
+    for t in range(T):
+        for h in range(H_I):
+            for d, v in enumerate(g["q_values"][t][h]):
+                q8[t, h, d] = enc[v]
+    for s in range(L):
+        for d, v in enumerate(g["k_values"][s]):
+            k8[s, d] = enc[v]
+    got, bound = oracle.index_scores(q8, np.array(g["qs"], np.float32), np.array(g["w"], np.float32),
+                                     k8, np.array(g["ks"], np.float32), g["q_pos0"], g["c"],
+                                     with_bound=True)
+    exp = np.array([[float(x) for x in row] for row in g["expected_scores"]])
+    assert np.array_equal(got, exp)
+    vis = np.isfinite(exp)
+    assert np.all(bound[vis] >= np.abs(got[vis]))
+    n_vis = g["q_pos0"] + np.arange(T) + 1
+    assert oracle.topk(got, n_vis, 1).tolist() == g["expected_top1"]
+    assert oracle.topk(got, n_vis, 2).tolist() == g["expected_top2"]
+
+
+def test_indexer_power_of_two_scaling_is_exact():
+    a = _small_prefill(L=40, H_I=4, seed=9)
+    c = 0.125
+    base = oracle.index_scores(a["q8"], a["qs"], a["w"], a["k8"], a["ks"], 0, c)
+    s2 = oracle.index_scores(a["q8"], a["qs"], a["w"] * 2, a["k8"], a["ks"] * 4, 0, c / 8)
+    assert np.array_equal(base, s2)          # 2 * 4 / 8 = 1, all exact in binary fp
+
+
+def test_indexer_joint_head_permutation_invariance():
+    a = _small_prefill(L=40, H_I=8, seed=11)
+    perm = np.array([3, 7, 0, 5, 1, 6, 2, 4])
+    c = 0.1
+    base = oracle.index_scores(a["q8"], a["qs"], a["w"], a["k8"], a["ks"], 0, c)
+    p = oracle.index_scores(a["q8"][:, perm], a["qs"][:, perm], a["w"][:, perm], a["k8"],
+                            a["ks"], 0, c)
+    vis = np.isfinite(base)
+    assert np.allclose(p[vis], base[vis], rtol=1e-13, atol=1e-13)
+    # and a single-head split: score(heads) == sum over one-head calls
+    acc = np.zeros_like(base)
+    for h in range(8):
+        acc += np.where(vis, oracle.index_scores(a["q8"][:, h:h + 1], a["qs"][:, h:h + 1],
+                                                 a["w"][:, h:h + 1], a["k8"], a["ks"], 0, c), 0)
+    assert np.allclose(acc[vis], base[vis], rtol=1e-12, atol=1e-12)
+
+
+def test_indexer_bound_single_head_is_abs_matmul():
+    a = _small_prefill(L=20, H_I=1, seed=4)
+    c = 0.3
+    _, bound = oracle.index_scores(a["q8"], a["qs"], a["w"], a["k8"], a["ks"], 0, c, with_bound=True)
+    absdot = (torch.abs(_e4m3_deq(a["q8"][:, 0, :])) @ torch.abs(_e4m3_deq(a["k8"])).T).numpy()
+    wp = np.abs(a["w"][:, 0].astype(np.float64) * a["qs"][:, 0].astype(np.float64) * c)
+    ref = absdot * wp[:, None] * a["ks"].astype(np.float64)[None, :]
+    vis = np.tril(np.ones_like(ref, dtype=bool))
+    assert np.allclose(bound[vis], ref[vis], rtol=1e-14, atol=0)
+
+
+# ------------------------------------------------------------------------------ top-k
+
+def _brute_topk(row, k):
+    """The unique k-subset whose every member beats every non-member under
+    (score descending, position ascending), found by enumeration."""
+    n = len(row)
+    if n <= k:
+        return list(range(n))
+    key = lambda s: (-row[s], s)
+    found = []
+    for sub in itertools.combinations(range(n), k):
+        worst_in = max(key(s) for s in sub)
+        rest = set(range(n)) - set(sub)
+        if all(key(s) > worst_in for s in rest):
+            found.append(list(sub))
+    assert len(found) == 1
+    return found[0]
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_topk_brute_force_with_ties_and_signed_zeros(seed):
+    rng = np.random.default_rng(seed)
+    n = int(rng.integers(1, 11))
+    vals = np.array([0.0, -0.0, 1.0, -1.0, 2.5, 2.5, 0.0])
+    row = rng.choice(vals, size=n) if seed % 2 == 0 else rng.standard_normal(n)
+    for k in range(1, n + 2):
+        want = _brute_topk(list(row), k)
+        want = want + [-1] * (k - len(want))
+        for m in ("sort", "select"):
+            got = oracle.topk(row[None, :], [n], k, method=m)[0].tolist()
+            assert got == want, (m, row, k)
+
+
+def test_topk_matches_torch_stable_sort_and_both_selectors_agree():
+    rng = np.random.default_rng(3)
+    rows = 40
+    L = 600
+    s = rng.standard_normal((rows, L))
+    s[::3] = np.round(s[::3] * 4) / 4          # heavy ties on some rows
+    s[1, :] = 0.0
+    s[1, ::2] = -0.0                           # -0 and +0 must tie
+    n_vis = rng.integers(1, L + 1, rows)
+    k = 64
+    a = oracle.topk(s, n_vis, k, "sort")
+    b = oracle.topk(s, n_vis, k, "select")
+    assert np.array_equal(a, b)
+    for r in range(rows):
+        n = n_vis[r]
+        if n <= k:
+            assert a[r].tolist() == list(range(n)) + [-1] * (k - n)
+            continue
+        order = torch.sort(torch.from_numpy(-s[r, :n]), stable=True).indices[:k]
+        assert a[r].tolist() == sorted(order.tolist())
+
+
+def test_topk_invariants():
+    rng = np.random.default_rng(7)
+    L, k = 3000, 100
+    s = rng.standard_normal((8, L))
+    n_vis = np.array([1, 50, 100, 101, 2000, 2999, 3000, 700])
+    idx = oracle.topk(s, n_vis, k)
+    for r in range(8):
+        n = n_vis[r]
+        sel = idx[r][idx[r] >= 0]
+        assert len(sel) == min(n, k)
+        assert len(set(sel.tolist())) == len(sel)
+        assert np.all(sel < n)
+        assert np.argmax(s[r, :n]) in sel
+        if n > k:
+            rest = np.setdiff1d(np.arange(n), sel)
+            assert s[r, sel].min() >= s[r, rest].max()
+
+
+# -------------------------------------------------------------------------------- MLA
+
+def _bf16(x):
+    return torch.as_tensor(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def _deq16(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(torch.float64)
+
+
+def test_mla_first_row_closed_form():
+    """Row at position 0 selects only token 0: out is kv[0, :512] exactly and
+    lse = sm_scale * <q, kv[0]>."""
+    a = _small_prefill(L=16, H=4, k=4, seed=2)
+    idx = np.full((a["T"], 4), -1, np.int32)
+    idx[0, 2] = 0
+    out, lse = oracle.sparse_mla(a["q"], a["kv"], idx, 0.05, rows=[0])
+    kv0 = _deq16(a["kv"][0]).numpy()
+    assert np.array_equal(out[0], np.broadcast_to(kv0[:512], (4, 512)))
+    qd = _deq16(a["q"][0]).numpy()
+    assert np.allclose(lse[0], 0.05 * (qd @ kv0), rtol=1e-14)
+
+
+def test_mla_zero_query_is_mean_of_selected_rows():
+    a = _small_prefill(L=30, H=2, k=6, seed=3)
+    q = np.zeros_like(a["q"])
+    idx = np.array([[3, 17, -1, 0, 29, 8]], np.int32).repeat(a["T"], 0)
+    out, lse = oracle.sparse_mla(q, a["kv"], idx, 0.1, rows=[5])
+    sel = [3, 17, 0, 29, 8]
+    mean = _deq16(a["kv"][sel]).numpy()[:, :512].mean(0)
+    assert np.allclose(out[0], mean[None, :], rtol=1e-13, atol=1e-15)
+    assert np.allclose(lse[0], math.log(5), rtol=1e-14)
+
+
+def _sdpa_ref(q_bits, kv_bits, q_pos0, sm_scale):
+    q = _deq16(q_bits).permute(1, 0, 2).unsqueeze(0)          # [1, H, T, 576]
+    kv = _deq16(kv_bits)
+    T, L = q.shape[2], kv.shape[0]
+    mask = torch.arange(L)[None, :] <= (q_pos0 + torch.arange(T))[:, None]
+    K = kv.unsqueeze(0).unsqueeze(0).expand(1, q.shape[1], L, 576).contiguous()
+    V = kv[:, :512].unsqueeze(0).unsqueeze(0).expand(1, q.shape[1], L, 512).contiguous()
+    o = torch.nn.functional.scaled_dot_product_attention(q, K, V, attn_mask=mask, scale=sm_scale)
+    logits = (q @ K.transpose(-1, -2)) * sm_scale
+    lse = torch.logsumexp(logits.masked_fill(~mask, -math.inf), dim=-1)
+    return o[0].permute(1, 0, 2).numpy(), lse[0].permute(1, 0).numpy()
+
+
+def test_dense_mla_matches_torch_sdpa():
+    a = _small_prefill(L=70, H=4, k=8, seed=8, q_pos0=20, T=50)
+    out, lse = oracle.dense_mla(a["q"], a["kv"], a["q_pos0"], a["sm_scale"])
+    ro, rl = _sdpa_ref(a["q"], a["kv"], a["q_pos0"], a["sm_scale"])
+    assert np.allclose(out, ro, rtol=1e-10, atol=1e-12)
+    assert np.allclose(lse, rl, rtol=1e-12, atol=1e-12)
+
+
+def test_sparse_mla_with_all_visible_equals_dense_and_sdpa():
+    a = _small_prefill(L=40, H=2, k=64, seed=12)
+    T = a["T"]
+    idx = np.full((T, 64), -1, np.int32)
+    rng = np.random.default_rng(0)
+    for t in range(T):
+        perm = rng.permutation(t + 1)                 # order within a row must not matter
+        slots = rng.choice(64, size=t + 1, replace=False)
+        idx[t, slots] = perm
+    so, sl = oracle.sparse_mla(a["q"], a["kv"], idx, a["sm_scale"])
+    do, dl = oracle.dense_mla(a["q"], a["kv"], 0, a["sm_scale"])
+    assert np.allclose(so, do, rtol=1e-12, atol=1e-13)
+    assert np.allclose(sl, dl, rtol=1e-13, atol=1e-13)
+    ro, rl = _sdpa_ref(a["q"], a["kv"], 0, a["sm_scale"])
+    assert np.allclose(so, ro, rtol=1e-10, atol=1e-12)
+
+
+def test_sparse_mla_subset_matches_masked_sdpa():
+    """An arbitrary index set is attention with every other key masked out."""
+    a = _small_prefill(L=50, H=3, k=10, seed=13)
+    rng = np.random.default_rng(1)
+    T = a["T"]
+    idx = np.full((T, 10), -1, np.int32)
+    mask = np.zeros((T, 50), bool)
+    for t in range(T):
+        m = min(10, t + 1)
+        sel = rng.choice(t + 1, size=m, replace=False)
+        idx[t, :m] = sel
+        mask[t, sel] = True
+    out, lse = oracle.sparse_mla(a["q"], a["kv"], idx, 0.07)
+    q = _deq16(a["q"]).permute(1, 0, 2).unsqueeze(0)
+    kv = _deq16(a["kv"])
+    K = kv.expand(3, 50, 576).unsqueeze(0).contiguous()
+    V = kv[:, :512].expand(3, 50, 512).unsqueeze(0).contiguous()
+    ro = torch.nn.functional.scaled_dot_product_attention(q, K, V, attn_mask=torch.from_numpy(mask), scale=0.07)
+    assert np.allclose(out, ro[0].permute(1, 0, 2).numpy(), rtol=1e-10, atol=1e-12)
+
+
+# ------------------------------------------------------------------- composed paths
+
+def test_prefill_short_context_equals_dense_attention():
+    """Every row sees <= k tokens: DSA selects everything and equals full attention."""
+    cfg = PrefillCfg("t", L=24, k=32, H_I=4, H=2, w_std=0.5, seed=21)
+    a = host_arrays(make_prefill(cfg))
+    res = oracle.prefill(a)
+    for t in range(a["T"]):
+        assert res["idx"][t].tolist() == list(range(t + 1)) + [-1] * (32 - t - 1)
+    do, dl = oracle.dense_mla(a["q"], a["kv"], 0, a["sm_scale"])
+    assert np.allclose(res["out"], do, rtol=1e-12, atol=1e-13)
+    assert np.allclose(res["lse"], dl, rtol=1e-13, atol=1e-13)
+
+
+def test_decode_matches_prefill_last_row_and_dense_when_short():
+    from synth import DecodeCfg, make_decode
+    cfg = DecodeCfg("t", B=3, len_lo=5, len_hi=40, k=16, H_I=4, H=2, w_std=0.5, seed=4)
+    a = host_arrays(make_decode(cfg))
+    res = oracle.decode(a)
+    st = a["seq_start"]
+    for r in res:
+        b, Lb = r["seq"], r["L"]
+        sl = slice(st[b], st[b + 1])
+        if Lb <= 16:
+            assert r["idx"].tolist() == list(range(Lb)) + [-1] * (16 - Lb)
+        do, dl = oracle.dense_mla(a["q"][b:b + 1], a["kv"][sl], Lb - 1, a["sm_scale"])
+        if Lb <= 16:
+            assert np.allclose(r["out"], do[0], rtol=1e-12, atol=1e-13)
+        # the decode query is the last row of a one-row prefill over its own cache
+        sc = oracle.index_scores(a["q8"][b:b + 1], a["qs"][b:b + 1], a["w"][b:b + 1],
+                                 a["k8"][sl], a["ks"][sl], Lb - 1, a["score_scale"])
+        assert np.array_equal(sc[0], r["scores"])
+        assert np.all(np.isfinite(r["scores"]))
