@@ -1,0 +1,285 @@
+#!/usr/bin/env python3
+"""Benchmark of the DSA hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+One step = one dsa_prefill call over the whole prefill workload (lightning indexer ->
+top-k -> sparse MLA for every query row), inputs resident in HBM.  Prints ONE JSON line:
+value = prefill tokens/s; `roofline` = the dominant kernel's algorithmic throughput against
+MI355X's published peak, its average launch duration taken from HIP events in a per-kernel
+pass that replays the fused call's chunks in the same launch configuration; `decode` = the
+decode step (B sequences, one token each); `cpu_baseline` = the CPU oracle timed on a
+bounded, uniformly sampled set of query rows of the same workload.  Progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK = {"fp8": 5000.0, "bf16": 2500.0}      # dense MFMA TFLOP/s, MI355X published
+HBM_PEAK_GBS = 8000.0                       # GB/s
+D_QK, D_V, D_I = 576, 512, 128
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="prefill-L131072-k2048")
+    ap.add_argument("--decode-workload", default="decode-B64-L4096-131072-k2048")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="target CPU time of the oracle baseline sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def prefill_units(L, T, q_pos0, k, t_lo, t_hi):
+    """(visible pairs of rows that need scores, selected (row, index) pairs) over rows
+    [t_lo, t_hi)."""
+    pairs = sel = 0
+    for t in range(t_lo, t_hi):
+        n = min(L, q_pos0 + t + 1)
+        if n > k:
+            pairs += n
+        sel += min(n, k)
+    return pairs, sel
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import sparse_attention_05_amd as dsa
+    from synth import WORKLOADS, make_decode, make_prefill
+
+    dsa.load()
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+    cfg = WORKLOADS[args.workload]
+    L, T, k, H_I, H = cfg.L, cfg.rows, cfg.k, cfg.H_I, cfg.H
+    log("generating", cfg.name)
+    inp = make_prefill(cfg, device=dev)
+    out = torch.empty((T, H, D_V), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((T, H), dtype=torch.float32, device=dev)
+    ws = torch.empty((dsa.dsa_prefill_workspace_bytes(T, L, H_I, H, k),), dtype=torch.uint8,
+                     device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        dsa.dsa_prefill(inp["q8"], inp["qs"], inp["w"], inp["k8"], inp["ks"], inp["q"],
+                        inp["kv"], k, cfg.q_pos0, cfg.score_scale, cfg.sm_scale, out=out,
+                        lse=lse, workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log("warmup done; timing %d steps" % args.steps)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    tok_s = T / (ms / 1e3)
+    log("prefill %.3f ms/step, %.0f tokens/s" % (ms, tok_s))
+
+    # ---- per-kernel pass: the fused call's chunks replayed through the single-kernel
+    # entry points, HIP events around each launch on the same stream
+    chunk = dsa.dsa_prefill_chunk_rows(T, L)
+    sc = ws[: chunk * L * 4].view(torch.float32).view(chunk, L)
+    idx = torch.empty((chunk, k), dtype=torch.int32, device=dev)
+    t_sel = max(0, k - cfg.q_pos0)
+    ktime = {"indexer": 0.0, "topk": 0.0, "sparse_mla": 0.0}
+    kcount = {"indexer": 0, "topk": 0, "sparse_mla": 0}
+    kunits = {"indexer": 0, "topk": 0, "sparse_mla": 0}
+    events = []
+    for r0 in range(0, T, chunk):
+        rows = min(chunk, T - r0)
+        s0 = max(r0, t_sel)
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        evs[0].record(stream)
+        if s0 < r0 + rows:
+            sl = slice(s0, r0 + rows)
+            dsa.dsa_index_scores(inp["q8"][sl], inp["qs"][sl], inp["w"][sl], inp["k8"],
+                                 inp["ks"], cfg.q_pos0 + s0, cfg.score_scale,
+                                 scores=sc[s0 - r0:rows], write_masked=False)
+        evs[1].record(stream)
+        dsa.dsa_topk(sc[:rows], L, cfg.q_pos0 + r0, k, idx=idx[:rows])
+        evs[2].record(stream)
+        dsa.dsa_sparse_mla(inp["q"][r0:r0 + rows], inp["kv"], idx[:rows], cfg.sm_scale,
+                           out=out[r0:r0 + rows], lse=lse[r0:r0 + rows])
+        evs[3].record(stream)
+        pairs, sel = prefill_units(L, T, cfg.q_pos0, k, r0, r0 + rows)
+        events.append((evs, s0 < r0 + rows, pairs, sel, rows))
+    torch.cuda.synchronize()
+    for evs, has_idx, pairs, sel, rows in events:
+        if has_idx:
+            ktime["indexer"] += evs[0].elapsed_time(evs[1])
+            kcount["indexer"] += 1
+            kunits["indexer"] += pairs
+        ktime["topk"] += evs[1].elapsed_time(evs[2])
+        kcount["topk"] += 1
+        kunits["topk"] += pairs
+        ktime["sparse_mla"] += evs[2].elapsed_time(evs[3])
+        kcount["sparse_mla"] += 1
+        kunits["sparse_mla"] += sel
+    idx_flop = 2.0 * H_I * D_I                     # per visible pair
+    mla_flop = 2.0 * H * (D_QK + D_V)              # per selected (row, index)
+    kern = {}
+    for name in ktime:
+        if kcount[name] == 0:
+            continue
+        sec = ktime[name] / 1e3
+        if name == "indexer":
+            ach, unit, peak, bound = kunits[name] * idx_flop / sec / 1e12, "TFLOP/s", PEAK["fp8"], "mfma"
+        elif name == "sparse_mla":
+            ach, unit, peak, bound = kunits[name] * mla_flop / sec / 1e12, "TFLOP/s", PEAK["bf16"], "mfma"
+        else:
+            ach, unit, peak, bound = kunits[name] * 4.0 / sec / 1e9, "GB/s", HBM_PEAK_GBS, "hbm"
+        kern[name] = dict(total_ms=round(ktime[name], 3), launches=kcount[name],
+                          avg_launch_ms=round(ktime[name] / kcount[name], 4),
+                          achieved=round(ach, 2), unit=unit, peak=peak,
+                          frac=round(ach / peak, 4), bound=bound)
+    dom = max(kern, key=lambda n: kern[n]["total_ms"])
+    log("kernels:", json.dumps(kern))
+    roofline = dict(bound=kern[dom]["bound"], achieved=kern[dom]["achieved"],
+                    peak=kern[dom]["peak"], unit=kern[dom]["unit"], frac=kern[dom]["frac"],
+                    traffic=None, kernel=dom, avg_launch_ms=kern[dom]["avg_launch_ms"])
+    sum_pairs, sum_sel = prefill_units(L, T, cfg.q_pos0, k, 0, T)
+    prefill_flops = sum_pairs * idx_flop + sum_sel * mla_flop
+    del sc, idx
+
+    # ---- decode
+    decode = None
+    if not args.no_decode:
+        dcfg = WORKLOADS[args.decode_workload]
+        log("generating", dcfg.name)
+        dinp = make_decode(dcfg, device=dev)
+        B, N = dcfg.B, dinp["N"]
+        dout = torch.empty((B, dcfg.H, D_V), dtype=torch.bfloat16, device=dev)
+        dlse = torch.empty((B, dcfg.H), dtype=torch.float32, device=dev)
+        dws = torch.empty((dsa.dsa_decode_workspace_bytes(B, dinp["max_len"], N, dcfg.H_I,
+                                                          dcfg.H, dcfg.k),), dtype=torch.uint8,
+                          device=dev)
+
+        def dstep():
+            dsa.dsa_decode(dinp["seq_start"], dinp["max_len"], dinp["q8"], dinp["qs"],
+                           dinp["w"], dinp["k8"], dinp["ks"], dinp["q"], dinp["kv"], dcfg.k,
+                           dcfg.score_scale, dcfg.sm_scale, out=dout, lse=dlse, workspace=dws)
+
+        for _ in range(args.warmup):
+            dstep()
+        torch.cuda.synchronize()
+        d0, d1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        dsteps = max(args.steps, 20)
+        d0.record(stream)
+        for _ in range(dsteps):
+            dstep()
+        d1.record(stream)
+        torch.cuda.synchronize()
+        dms = d0.elapsed_time(d1) / dsteps
+        lens = dinp["lens"].cpu().numpy()
+        hbm = (lens.sum() * (D_I + 4) + np.minimum(lens, dcfg.k).sum() * D_QK * 2
+               + B * dcfg.H_I * (D_I + 8) + B * dcfg.H * (D_QK * 2 + D_V * 2 + 4))
+        gbs = hbm / (dms / 1e3) / 1e9
+        decode = dict(workload=dcfg.name, ms_per_step=round(dms, 4),
+                      tokens_per_s=round(B / (dms / 1e3), 1), sequences=B,
+                      context_tokens=int(N),
+                      roofline=dict(bound="hbm", achieved=round(gbs, 1), peak=HBM_PEAK_GBS,
+                                    unit="GB/s", frac=round(gbs / HBM_PEAK_GBS, 4),
+                                    algorithmic_bytes=int(hbm)))
+        log("decode %.4f ms/step, %.0f tokens/s, %.0f GB/s" % (dms, B / (dms / 1e3), gbs))
+        del dinp, dws
+
+    # ---- CPU oracle baseline on sampled rows of the same prefill workload
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(inp, cfg, args.cpu_seconds)
+
+    res = {
+        "metric": "DSA prefill tokens/s at L=128K (k=2048); decode tokens/s; % MFMA/HBM peak",
+        "value": round(tok_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8-e4m3 indexer / bf16 MLA, fp32 accumulate",
+        "data": "synthetic (seeded N(0,1), fp8 per-vector scales, 1% planted indexer keys)",
+        "config": {"workload": cfg.name, "L": L, "query_rows": T, "k": k, "H_I": H_I, "H": H,
+                   "batch": 1, "chunk_rows": chunk,
+                   "algorithmic_tflop_per_step": round(prefill_flops / 1e12, 3)},
+        "roofline": roofline,
+        "kernels": kern,
+        "decode": decode,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(res), flush=True)
+
+
+def cpu_baseline(inp, cfg, seconds):
+    """The oracle, as it is, on uniformly sampled query rows (indexer scores, top-k and
+    sparse MLA of each row).  Rows are sampled uniformly over the workload, so rows/s is an
+    unbiased estimate of the oracle's tokens/s on the whole workload."""
+    import numpy as np
+    import torch
+
+    import oracle
+
+    k8 = inp["k8"].cpu().numpy()
+    ks = inp["ks"].cpu().numpy()
+    kv = inp["kv"].cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+    rng = np.random.default_rng(cfg.seed)
+
+    def run(rows):
+        t0 = time.perf_counter()
+        for t in rows:
+            t = int(t)
+            p = cfg.q_pos0 + t
+            sc = oracle.index_scores(inp["q8"][t:t + 1].cpu().numpy(),
+                                     inp["qs"][t:t + 1].cpu().numpy(),
+                                     inp["w"][t:t + 1].cpu().numpy(), k8, ks, p,
+                                     cfg.score_scale)
+            idx = oracle.topk(sc, [p + 1], cfg.k)
+            q = inp["q"][t:t + 1].cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+            oracle.sparse_mla(q, kv, idx, cfg.sm_scale)
+        return time.perf_counter() - t0
+
+    oracle.num_threads()
+    probe = rng.integers(0, cfg.rows, 4)
+    tp = run(probe)
+    n = int(min(4096, max(8, seconds / max(tp / len(probe), 1e-6))))
+    rows = rng.integers(0, cfg.rows, n)
+    log("cpu oracle: %d sampled rows (probe %.2f s for 4)" % (n, tp))
+    sec = run(rows)
+    return dict(value=round(n / sec, 3), unit="tokens/s", cores=oracle.num_threads(),
+                kind="oracle", seconds=round(sec, 2),
+                sample="%d query rows drawn uniformly from the %d rows of %s "
+                       "(indexer scores + top-k + sparse MLA per row)" % (n, cfg.rows, cfg.name))
+
+
+if __name__ == "__main__":
+    main()

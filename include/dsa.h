@@ -1,0 +1,138 @@
+/*
+ * dsa.h -- C ABI of the DeepSeek Sparse Attention (DSA) hot path on AMD MI355X (gfx950).
+ *
+ * The method (pages cited by title and section):
+ *   [csdn-workflow] 《DeepSeek-V3.2-Exp模型优势与 DSA 工作原理,token降价性能不减的背后》
+ *                   (agent.csdn.net): §3 两大核心组件 (a 128-d indexer key per token, a
+ *                   512-d latent cache for the sparse MLA), §4 四步工作流程 (步骤二 indexer
+ *                   score with mask and scale and per-head weights a_h, 步骤三 top-k with
+ *                   k = 2048 and select-all for short contexts, 步骤四 sparse MLA).
+ *   [devpress-dsa]  《狂降75%！大模型DeepSeek-V3.2 API杀疯了…》 (devpress.csdn.net):
+ *                   §三 第二步–第四步 (the same four steps).
+ *   [gxzdkb-dsa]    gxzdkb.com DSA explainer: 秘密武器：DSA (fp8 indexer, ReLU),
+ *                   原始 Attention 的计算逻辑 (decode appends to the cache first).
+ *
+ * Conventions for every entry point
+ *   - All tensor pointers are DEVICE pointers owned by the caller.  Tensors are row-major
+ *     and contiguous unless a leading dimension is given.  fp8 = OCP e4m3fn bytes,
+ *     bf16 = raw uint16 bits, scales fp32.
+ *   - Indexer: one shared 128-byte fp8 key per token (k8[L,128]) with a per-token fp32
+ *     scale ks[L]; query row t has H_I fp8 heads q8[t,h,128] with per-(token,head) scales
+ *     qs[t,h] and per-head weights w[t,h] (the pages' a_h).
+ *   - MLA: one 576-wide bf16 cache row per token, kv[L,576] = 512 latent (also the value)
+ *     + 64 rope dims; queries q[T,H,576]; outputs out[T,H,512] bf16 and lse[T,H] fp32
+ *     (natural log of the softmax denominator).
+ *   - Query row t sits at absolute position p_t = q_pos0 + t and sees keys 0..p_t, itself
+ *     included.  Requires q_pos0 >= 0 and q_pos0 + T <= L.
+ *   - Every call only enqueues work on `stream` (a hipStream_t; NULL = the default stream)
+ *     and returns.  Arguments are validated before any HIP call: an invalid call returns
+ *     its status and launches nothing.  Launch failures return DSA_ERR_HIP.  The library
+ *     allocates no memory and keeps no global state; calls are thread-safe.  The caller
+ *     keeps every buffer alive until the stream has reached the call.
+ *   - Not checked on the device (the caller's contract): scales positive and finite, no
+ *     NaN fp8 codes (0x7F/0xFF), finite bf16 values, index lists without duplicates.
+ *   - Supported shapes: H_I in {1,2,4,8,16,32,64,128}; 1 <= H <= 128;
+ *     1 <= k <= 8192 (index lists of dsa_sparse_mla: any k >= 1); L < 2^31;
+ *     T * max(L, k) < 2^40.  Other shapes return DSA_ERR_UNSUPPORTED.
+ */
+#ifndef DSA_H
+#define DSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t* dsa_stream_t;   /* identical to hipStream_t */
+
+typedef enum {
+    DSA_OK = 0,
+    DSA_ERR_INVALID_ARGUMENT = 1,    /* null pointer, negative size, q_pos0 + T > L, ... */
+    DSA_ERR_UNSUPPORTED = 2,         /* a shape outside the supported set */
+    DSA_ERR_WORKSPACE_TOO_SMALL = 3, /* workspace_bytes below the matching *_workspace_bytes */
+    DSA_ERR_HIP = 4                  /* a HIP launch or runtime error */
+} dsa_status_t;
+
+/* Static, human-readable name of a status code. */
+const char* dsa_status_string(dsa_status_t status);
+
+/* ABI version: major * 100 + minor. */
+int dsa_version(void);
+
+/* Lightning-indexer scores ([csdn-workflow] §4 步骤二, [devpress-dsa] §三 第二步):
+ *   score[t,s] = ks[s] * sum_h (w[t,h] * qs[t,h] * score_scale) * ReLU(sum_d q8[t,h,d] k8[s,d])
+ * for s <= q_pos0 + t.  The masked entries q_pos0 + t < s < L receive -inf when write_masked
+ * is non-zero and are left untouched otherwise (for callers that only read visible
+ * entries, as dsa_topk does).  fp8 products are exact, accumulation and the epilogue fp32.
+ *   q8 [T,H_I,128] u8; q_scale [T,H_I] f32; w [T,H_I] f32; k8 [L,128] u8; k_scale [L] f32;
+ *   scores [T, ld_scores] f32 with ld_scores >= L (columns >= L are not written). */
+dsa_status_t dsa_index_scores(const uint8_t* q8, const float* q_scale, const float* w,
+                              const uint8_t* k8, const float* k_scale, int T, int L, int H_I,
+                              int q_pos0, float score_scale, float* scores, int64_t ld_scores,
+                              int write_masked, dsa_stream_t stream);
+
+/* Per-row top-k ([csdn-workflow] §4 步骤三): row t keeps the k largest of its n_t =
+ * q_pos0 + t + 1 visible scores, ties to the lower position, -0 equal to +0; a row with
+ * n_t <= k keeps all of 0..n_t-1 without reading its scores.  idx [T,k] int32 receives
+ * the positions in ascending order, then -1 padding.  Scores must not be NaN.
+ * Uses no workspace (workspace may be NULL when dsa_topk_workspace_bytes returns 0). */
+dsa_status_t dsa_topk(const float* scores, int64_t ld_scores, int T, int L, int q_pos0, int k,
+                      int32_t* idx, void* workspace, size_t workspace_bytes,
+                      dsa_stream_t stream);
+size_t dsa_topk_workspace_bytes(int T, int L, int k);
+
+/* Sparse MLA ([csdn-workflow] §4 步骤四, [devpress-dsa] §三 第四步): for each row t, head h
+ *   l_j = sm_scale * <q[t,h,0:576], kv[idx[t,j],0:576]>,   out[t,h] = softmax(l) . kv[idx,0:512],
+ *   lse[t,h] = log sum_j exp(l_j).
+ * Entries of idx outside [0, L) are padding and skipped; a row with no valid entry gives
+ * out = 0 and lse = -inf.  q [T,H,576] bf16; kv [L,576] bf16; idx [T,k] int32;
+ * out [T,H,512] bf16 (rounded to nearest even); lse [T,H] f32 or NULL. */
+dsa_status_t dsa_sparse_mla(const uint16_t* q, const uint16_t* kv, const int32_t* idx, int T,
+                            int L, int H, int k, float sm_scale, uint16_t* out, float* lse,
+                            dsa_stream_t stream);
+
+/* The whole prefill path for T query rows (indexer -> top-k -> sparse MLA), processed in
+ * query chunks so the fp32 score rows of one chunk live in the workspace.  Arguments are
+ * those of the three calls above; idx_out [T,k] (nullable) receives the selected indices.
+ * workspace must be at least dsa_prefill_workspace_bytes(T, L, H_I, H, k) bytes,
+ * 256-byte aligned. */
+dsa_status_t dsa_prefill(const uint8_t* q8, const float* q_scale, const float* w,
+                         const uint8_t* k8, const float* k_scale, const uint16_t* q,
+                         const uint16_t* kv, int T, int L, int H_I, int H, int k, int q_pos0,
+                         float score_scale, float sm_scale, uint16_t* out, float* lse,
+                         int32_t* idx_out, void* workspace, size_t workspace_bytes,
+                         dsa_stream_t stream);
+size_t dsa_prefill_workspace_bytes(int T, int L, int H_I, int H, int k);
+
+/* Query rows per chunk that dsa_prefill uses for (T, L): chunk c covers rows
+ * [c * rows, min(T, (c + 1) * rows)), and within a chunk the path is exactly
+ * dsa_index_scores (write_masked = 0, rows that see more than k tokens only) ->
+ * dsa_topk -> dsa_sparse_mla on that chunk.  Returns 0 for invalid sizes. */
+int dsa_prefill_chunk_rows(int T, int L);
+
+/* One decode step for B sequences ([gxzdkb-dsa] 原始 Attention 的计算逻辑: the new token's
+ * cache entries are appended before attending).  Sequence b owns the packed cache rows
+ * [seq_start[b], seq_start[b+1]) of k8_cache [N,128], k_scale_cache [N] and kv_cache
+ * [N,576], N = total_tokens; its one query sits at position L_b - 1 = seq_start[b+1] -
+ * seq_start[b] - 1 and sees its whole cache.
+ *   seq_start  DEVICE int64 [B+1], non-decreasing, seq_start[0] = 0, seq_start[B] = N,
+ *              every length in [1, max_len] (not checked: the host never reads it);
+ *   q8 [B,H_I,128]; q_scale, w [B,H_I]; q [B,H,576]; out [B,H,512]; lse [B,H] or NULL;
+ *   idx_out [B,k] or NULL (positions within the sequence, ascending, -1 padded).
+ * workspace >= dsa_decode_workspace_bytes(B, max_len, total_tokens, H_I, H, k) bytes. */
+dsa_status_t dsa_decode(int B, const int64_t* seq_start, int max_len, int64_t total_tokens,
+                        const uint8_t* q8, const float* q_scale, const float* w,
+                        const uint8_t* k8_cache, const float* k_scale_cache,
+                        const uint16_t* q, const uint16_t* kv_cache, int H_I, int H, int k,
+                        float score_scale, float sm_scale, uint16_t* out, float* lse,
+                        int32_t* idx_out, void* workspace, size_t workspace_bytes,
+                        dsa_stream_t stream);
+size_t dsa_decode_workspace_bytes(int B, int max_len, int64_t total_tokens, int H_I, int H,
+                                  int k);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DSA_H */

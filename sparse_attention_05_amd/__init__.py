@@ -1,0 +1,244 @@
+"""DeepSeek Sparse Attention (DSA) hot path on AMD MI355X -- Python binding of libdsa.so.
+
+Argument marshalling only: every step of the path runs in the HIP kernels of libdsa.so,
+reached through its C ABI (include/dsa.h).  PyTorch supplies device memory and the stream
+(``torch.cuda.current_stream()``).  There is no fallback: if the library cannot be loaded,
+every call raises.
+
+Tensor conventions (all on the GPU, contiguous):
+    q8 [T,H_I,128] uint8 (OCP e4m3fn codes), q_scale/w [T,H_I] float32,
+    k8 [L,128] uint8, k_scale [L] float32, q [T,H,576] bfloat16, kv [L,576] bfloat16,
+    scores [T,>=L] float32, idx [T,k] int32, out [T,H,512] bfloat16, lse [T,H] float32.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libdsa.so")
+_lock = threading.Lock()
+_lib = None
+
+DSA_OK, DSA_ERR_INVALID_ARGUMENT, DSA_ERR_UNSUPPORTED = 0, 1, 2
+DSA_ERR_WORKSPACE_TOO_SMALL, DSA_ERR_HIP = 3, 4
+
+EXPORTS = ("dsa_status_string", "dsa_version", "dsa_index_scores", "dsa_topk",
+           "dsa_topk_workspace_bytes", "dsa_sparse_mla", "dsa_prefill",
+           "dsa_prefill_workspace_bytes", "dsa_prefill_chunk_rows", "dsa_decode",
+           "dsa_decode_workspace_bytes")
+
+
+class DSAError(RuntimeError):
+    def __init__(self, status: int, name: str, where: str):
+        super().__init__("%s: %s (%d)" % (where, name, status))
+        self.status = status
+
+
+def load(path: str = LIB_PATH):
+    """Load libdsa.so (built in-tree by ``build.py``); raises if it is missing."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(path):
+                raise RuntimeError("libdsa.so not built: run python -m sparse_attention_05_amd.build")
+            lib = ctypes.CDLL(path)
+            P, i32, i64, f32, sz = (ctypes.c_void_p, ctypes.c_int, ctypes.c_int64,
+                                    ctypes.c_float, ctypes.c_size_t)
+            lib.dsa_status_string.restype = ctypes.c_char_p
+            lib.dsa_status_string.argtypes = [i32]
+            lib.dsa_version.restype = i32
+            lib.dsa_index_scores.argtypes = [P, P, P, P, P, i32, i32, i32, i32, f32, P, i64, i32, P]
+            lib.dsa_topk.argtypes = [P, i64, i32, i32, i32, i32, P, P, sz, P]
+            lib.dsa_topk_workspace_bytes.restype = sz
+            lib.dsa_topk_workspace_bytes.argtypes = [i32, i32, i32]
+            lib.dsa_sparse_mla.argtypes = [P, P, P, i32, i32, i32, i32, f32, P, P, P]
+            lib.dsa_prefill.argtypes = [P, P, P, P, P, P, P, i32, i32, i32, i32, i32, i32, f32,
+                                        f32, P, P, P, P, sz, P]
+            lib.dsa_prefill_workspace_bytes.restype = sz
+            lib.dsa_prefill_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
+            lib.dsa_prefill_chunk_rows.restype = i32
+            lib.dsa_prefill_chunk_rows.argtypes = [i32, i32]
+            lib.dsa_decode.argtypes = [i32, P, i32, i64, P, P, P, P, P, P, P, i32, i32, i32, f32,
+                                       f32, P, P, P, P, sz, P]
+            lib.dsa_decode_workspace_bytes.restype = sz
+            lib.dsa_decode_workspace_bytes.argtypes = [i32, i32, i64, i32, i32, i32]
+            for fn in ("dsa_index_scores", "dsa_topk", "dsa_sparse_mla", "dsa_prefill",
+                       "dsa_decode"):
+                getattr(lib, fn).restype = i32
+            _lib = lib
+    return _lib
+
+
+def _check(status: int, where: str):
+    if status != DSA_OK:
+        raise DSAError(status, load().dsa_status_string(status).decode(), where)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _req(t, dtype, shape, name):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError("%s must be a CUDA tensor" % name)
+    if t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError("%s must have shape %s, got %s" % (name, tuple(shape), tuple(t.shape)))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    return t
+
+
+def _u8(t):
+    return t.view(torch.uint8) if t.dtype == torch.float8_e4m3fn else t
+
+
+def dsa_topk_workspace_bytes(T: int, L: int, k: int) -> int:
+    return int(load().dsa_topk_workspace_bytes(T, L, k))
+
+
+def dsa_prefill_workspace_bytes(T: int, L: int, H_I: int, H: int, k: int) -> int:
+    return int(load().dsa_prefill_workspace_bytes(T, L, H_I, H, k))
+
+
+def dsa_decode_workspace_bytes(B: int, max_len: int, total_tokens: int, H_I: int, H: int,
+                               k: int) -> int:
+    return int(load().dsa_decode_workspace_bytes(B, max_len, total_tokens, H_I, H, k))
+
+
+def dsa_prefill_chunk_rows(T: int, L: int) -> int:
+    return int(load().dsa_prefill_chunk_rows(T, L))
+
+
+def dsa_index_scores(q8, q_scale, w, k8, k_scale, q_pos0: int, score_scale: float,
+                     scores=None, write_masked: bool = True):
+    """Lightning-indexer scores [T, L] (or into `scores` [T, ld >= L]); masked entries are
+    -inf when write_masked, untouched otherwise."""
+    lib = load()
+    q8, k8 = _u8(q8), _u8(k8)
+    T, H_I = q8.shape[0], q8.shape[1]
+    L = k8.shape[0]
+    _req(q8, torch.uint8, (T, H_I, 128), "q8")
+    _req(q_scale, torch.float32, (T, H_I), "q_scale")
+    _req(w, torch.float32, (T, H_I), "w")
+    _req(k8, torch.uint8, (L, 128), "k8")
+    _req(k_scale, torch.float32, (L,), "k_scale")
+    if scores is None:
+        scores = torch.empty((T, L), dtype=torch.float32, device=q8.device)
+    if scores.dtype != torch.float32 or scores.dim() != 2 or scores.shape[0] != T \
+            or scores.stride(1) != 1 or scores.shape[1] < L:
+        raise ValueError("scores must be float32 [T, >=L] with unit column stride")
+    _check(lib.dsa_index_scores(_ptr(q8), _ptr(q_scale), _ptr(w), _ptr(k8), _ptr(k_scale), T, L,
+                                H_I, q_pos0, score_scale, _ptr(scores), scores.stride(0),
+                                int(bool(write_masked)), _stream()), "dsa_index_scores")
+    return scores
+
+
+def dsa_topk(scores, L: int, q_pos0: int, k: int, idx=None):
+    """Per-row top-k of scores [T, >=L]: int32 [T, k], ascending positions, -1 padded."""
+    lib = load()
+    T = scores.shape[0]
+    if scores.dtype != torch.float32 or scores.dim() != 2 or scores.stride(1) != 1:
+        raise ValueError("scores must be float32 [T, >=L] with unit column stride")
+    if idx is None:
+        idx = torch.empty((T, k), dtype=torch.int32, device=scores.device)
+    _req(idx, torch.int32, (T, k), "idx")
+    _check(lib.dsa_topk(_ptr(scores), scores.stride(0), T, L, q_pos0, k, _ptr(idx), None, 0,
+                        _stream()), "dsa_topk")
+    return idx
+
+
+def dsa_sparse_mla(q, kv, idx, sm_scale: float, out=None, lse=None):
+    """Attention of q [T,H,576] over the kv rows listed in idx [T,k]: (out, lse)."""
+    lib = load()
+    T, H = q.shape[0], q.shape[1]
+    L, k = kv.shape[0], idx.shape[1]
+    _req(q, torch.bfloat16, (T, H, 576), "q")
+    _req(kv, torch.bfloat16, (L, 576), "kv")
+    _req(idx, torch.int32, (T, k), "idx")
+    if out is None:
+        out = torch.empty((T, H, 512), dtype=torch.bfloat16, device=q.device)
+    if lse is None:
+        lse = torch.empty((T, H), dtype=torch.float32, device=q.device)
+    _req(out, torch.bfloat16, (T, H, 512), "out")
+    _req(lse, torch.float32, (T, H), "lse")
+    _check(lib.dsa_sparse_mla(_ptr(q), _ptr(kv), _ptr(idx), T, L, H, k, sm_scale, _ptr(out),
+                              _ptr(lse), _stream()), "dsa_sparse_mla")
+    return out, lse
+
+
+def dsa_prefill(q8, q_scale, w, k8, k_scale, q, kv, k: int, q_pos0: int, score_scale: float,
+                sm_scale: float, out=None, lse=None, idx_out=None, workspace=None):
+    """Whole prefill path (indexer -> top-k -> sparse MLA): (out, lse, idx_out)."""
+    lib = load()
+    q8, k8 = _u8(q8), _u8(k8)
+    T, H_I = q8.shape[0], q8.shape[1]
+    L, H = k8.shape[0], q.shape[1]
+    _req(q8, torch.uint8, (T, H_I, 128), "q8")
+    _req(q_scale, torch.float32, (T, H_I), "q_scale")
+    _req(w, torch.float32, (T, H_I), "w")
+    _req(k8, torch.uint8, (L, 128), "k8")
+    _req(k_scale, torch.float32, (L,), "k_scale")
+    _req(q, torch.bfloat16, (T, H, 576), "q")
+    _req(kv, torch.bfloat16, (L, 576), "kv")
+    dev = q.device
+    if out is None:
+        out = torch.empty((T, H, 512), dtype=torch.bfloat16, device=dev)
+    if lse is None:
+        lse = torch.empty((T, H), dtype=torch.float32, device=dev)
+    _req(out, torch.bfloat16, (T, H, 512), "out")
+    _req(lse, torch.float32, (T, H), "lse")
+    if idx_out is not None:
+        _req(idx_out, torch.int32, (T, k), "idx_out")
+    need = dsa_prefill_workspace_bytes(T, L, H_I, H, k)
+    if workspace is None:
+        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=dev)
+    _check(lib.dsa_prefill(_ptr(q8), _ptr(q_scale), _ptr(w), _ptr(k8), _ptr(k_scale), _ptr(q),
+                           _ptr(kv), T, L, H_I, H, k, q_pos0, score_scale, sm_scale, _ptr(out),
+                           _ptr(lse), _ptr(idx_out), _ptr(workspace), workspace.numel(),
+                           _stream()), "dsa_prefill")
+    return out, lse, idx_out
+
+
+def dsa_decode(seq_start, max_len: int, q8, q_scale, w, k8, k_scale, q, kv, k: int,
+               score_scale: float, sm_scale: float, out=None, lse=None, idx_out=None,
+               workspace=None):
+    """One decode step over B packed sequences: (out [B,H,512], lse [B,H], idx_out)."""
+    lib = load()
+    q8, k8 = _u8(q8), _u8(k8)
+    B, H_I = q8.shape[0], q8.shape[1]
+    N, H = k8.shape[0], q.shape[1]
+    _req(seq_start, torch.int64, (B + 1,), "seq_start")
+    _req(q8, torch.uint8, (B, H_I, 128), "q8")
+    _req(q_scale, torch.float32, (B, H_I), "q_scale")
+    _req(w, torch.float32, (B, H_I), "w")
+    _req(k8, torch.uint8, (N, 128), "k8")
+    _req(k_scale, torch.float32, (N,), "k_scale")
+    _req(q, torch.bfloat16, (B, H, 576), "q")
+    _req(kv, torch.bfloat16, (N, 576), "kv")
+    dev = q.device
+    if out is None:
+        out = torch.empty((B, H, 512), dtype=torch.bfloat16, device=dev)
+    if lse is None:
+        lse = torch.empty((B, H), dtype=torch.float32, device=dev)
+    _req(out, torch.bfloat16, (B, H, 512), "out")
+    _req(lse, torch.float32, (B, H), "lse")
+    if idx_out is not None:
+        _req(idx_out, torch.int32, (B, k), "idx_out")
+    need = dsa_decode_workspace_bytes(B, max_len, N, H_I, H, k)
+    if workspace is None:
+        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=dev)
+    _check(lib.dsa_decode(B, _ptr(seq_start), max_len, N, _ptr(q8), _ptr(q_scale), _ptr(w),
+                          _ptr(k8), _ptr(k_scale), _ptr(q), _ptr(kv), H_I, H, k, score_scale,
+                          sm_scale, _ptr(out), _ptr(lse), _ptr(idx_out), _ptr(workspace),
+                          workspace.numel(), _stream()), "dsa_decode")
+    return out, lse, idx_out

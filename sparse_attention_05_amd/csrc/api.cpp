@@ -1,0 +1,271 @@
+// api.cpp -- the C ABI of libdsa.so (declared in include/dsa.h).
+//
+// Every entry point validates all of its arguments before touching the HIP runtime, so an
+// invalid call returns its status having launched nothing.  Valid calls only enqueue
+// kernels on the caller's stream.
+#include "dsa.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdint>
+
+#include "kernels.h"
+
+namespace {
+
+constexpr int64_t kMaxElems = int64_t(1) << 40;   // T * max(L, k) bound
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+hipStream_t as_hip(dsa_stream_t s) { return reinterpret_cast<hipStream_t>(s); }
+
+dsa_status_t from_hip(hipError_t e) { return e == hipSuccess ? DSA_OK : DSA_ERR_HIP; }
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+bool heads_ok(int H) { return H >= 1 && H <= 128; }
+bool k_ok(int k) { return k >= 1 && k <= 8192; }
+
+// rows of the causal triangle: (T, L, q_pos0) consistency shared by the prefill calls
+dsa_status_t check_rows(int T, int L, int q_pos0)
+{
+    if (T < 0 || L <= 0 || q_pos0 < 0) return DSA_ERR_INVALID_ARGUMENT;
+    if ((int64_t)q_pos0 + T > L) return DSA_ERR_INVALID_ARGUMENT;
+    return DSA_OK;
+}
+
+// ---- prefill chunking: rows per chunk so one chunk's fp32 score rows stay bounded
+constexpr int64_t kChunkScoreBytes = int64_t(512) << 20;
+
+int prefill_chunk_rows(int T, int L)
+{
+    int64_t rows = kChunkScoreBytes / (int64_t(L) * 4);
+    rows = std::max<int64_t>(64, rows / 64 * 64);
+    return (int)std::min<int64_t>(std::max(T, 1), rows);
+}
+
+struct PrefillWs {
+    int chunk;
+    size_t scores_off, idx_off, total;
+};
+
+PrefillWs prefill_ws(int T, int L, int k)
+{
+    PrefillWs w;
+    w.chunk = prefill_chunk_rows(T, L);
+    w.scores_off = 0;
+    w.idx_off = align_up(size_t(w.chunk) * size_t(L) * 4);
+    w.total = w.idx_off + align_up(size_t(w.chunk) * size_t(k) * 4);
+    return w;
+}
+
+// ---- decode workspace: packed scores, indices, split-K partials
+int decode_splits(int k) { return std::min(8, std::max(1, (k + 511) / 512)); }
+
+struct DecodeWs {
+    int splits;
+    size_t scores_off, idx_off, po_off, pl_off, total;
+};
+
+DecodeWs decode_ws(int B, int64_t N, int H, int k)
+{
+    DecodeWs w;
+    w.splits = decode_splits(k);
+    w.scores_off = 0;
+    w.idx_off = align_up(size_t(N) * 4);
+    w.po_off = w.idx_off + align_up(size_t(B) * size_t(k) * 4);
+    w.pl_off = w.po_off + align_up(size_t(B) * w.splits * H * 512 * 4);
+    w.total = w.pl_off + align_up(size_t(B) * w.splits * H * 4);
+    return w;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* dsa_status_string(dsa_status_t status)
+{
+    switch (status) {
+        case DSA_OK: return "DSA_OK";
+        case DSA_ERR_INVALID_ARGUMENT: return "DSA_ERR_INVALID_ARGUMENT";
+        case DSA_ERR_UNSUPPORTED: return "DSA_ERR_UNSUPPORTED";
+        case DSA_ERR_WORKSPACE_TOO_SMALL: return "DSA_ERR_WORKSPACE_TOO_SMALL";
+        case DSA_ERR_HIP: return "DSA_ERR_HIP";
+    }
+    return "DSA_ERR_UNKNOWN";
+}
+
+int dsa_version(void) { return 100; }
+
+dsa_status_t dsa_index_scores(const uint8_t* q8, const float* q_scale, const float* w,
+                              const uint8_t* k8, const float* k_scale, int T, int L, int H_I,
+                              int q_pos0, float score_scale, float* scores, int64_t ld_scores,
+                              int write_masked, dsa_stream_t stream)
+{
+    if (dsa_status_t st = check_rows(T, L, q_pos0)) return st;
+    if (T > 0 && (!q8 || !q_scale || !w || !k8 || !k_scale || !scores))
+        return DSA_ERR_INVALID_ARGUMENT;
+    if (ld_scores < L) return DSA_ERR_INVALID_ARGUMENT;
+    if (!(score_scale > 0.f)) return DSA_ERR_INVALID_ARGUMENT;
+    if (!dsa::indexer_supports(H_I)) return DSA_ERR_UNSUPPORTED;
+    if ((int64_t)T * ld_scores > kMaxElems) return DSA_ERR_UNSUPPORTED;
+    if (!aligned(q8, 16) || !aligned(k8, 16)) return DSA_ERR_INVALID_ARGUMENT;
+    if (T == 0) return DSA_OK;
+    hipStream_t s = as_hip(stream);
+    hipError_t e = dsa::launch_indexer_prefill(q8, q_scale, w, k8, k_scale, T, L, H_I, q_pos0,
+                                               score_scale, scores, ld_scores, s);
+    if (e == hipSuccess && write_masked)
+        e = dsa::launch_mask_fill(T, L, q_pos0, scores, ld_scores, s);
+    return from_hip(e);
+}
+
+size_t dsa_topk_workspace_bytes(int, int, int) { return 0; }
+
+dsa_status_t dsa_topk(const float* scores, int64_t ld_scores, int T, int L, int q_pos0, int k,
+                      int32_t* idx, void*, size_t, dsa_stream_t stream)
+{
+    if (dsa_status_t st = check_rows(T, L, q_pos0)) return st;
+    if (T > 0 && (!scores || !idx)) return DSA_ERR_INVALID_ARGUMENT;
+    if (ld_scores < L) return DSA_ERR_INVALID_ARGUMENT;
+    if (!k_ok(k)) return k < 1 ? DSA_ERR_INVALID_ARGUMENT : DSA_ERR_UNSUPPORTED;
+    if ((int64_t)T * std::max<int64_t>(ld_scores, k) > kMaxElems) return DSA_ERR_UNSUPPORTED;
+    if (T == 0) return DSA_OK;
+    return from_hip(dsa::launch_topk_prefill(scores, ld_scores, T, L, q_pos0, k, idx,
+                                             as_hip(stream)));
+}
+
+dsa_status_t dsa_sparse_mla(const uint16_t* q, const uint16_t* kv, const int32_t* idx, int T,
+                            int L, int H, int k, float sm_scale, uint16_t* out, float* lse,
+                            dsa_stream_t stream)
+{
+    if (T < 0 || L <= 0 || k < 1) return DSA_ERR_INVALID_ARGUMENT;
+    if (T > 0 && (!q || !kv || !idx || !out)) return DSA_ERR_INVALID_ARGUMENT;
+    if (!heads_ok(H)) return H < 1 ? DSA_ERR_INVALID_ARGUMENT : DSA_ERR_UNSUPPORTED;
+    if (!(sm_scale > 0.f)) return DSA_ERR_INVALID_ARGUMENT;
+    if ((int64_t)T * std::max(L, k) > kMaxElems) return DSA_ERR_UNSUPPORTED;
+    if (!aligned(q, 16) || !aligned(kv, 16) || !aligned(out, 4)) return DSA_ERR_INVALID_ARGUMENT;
+    if (T == 0) return DSA_OK;
+    return from_hip(dsa::launch_sparse_mla(q, kv, idx, nullptr, T, L, H, k, sm_scale, 1, out,
+                                           lse, nullptr, nullptr, as_hip(stream)));
+}
+
+int dsa_prefill_chunk_rows(int T, int L)
+{
+    if (T <= 0 || L <= 0) return 0;
+    return prefill_chunk_rows(T, L);
+}
+
+size_t dsa_prefill_workspace_bytes(int T, int L, int H_I, int H, int k)
+{
+    (void)H_I;
+    (void)H;
+    if (T <= 0 || L <= 0 || k < 1) return 0;
+    return prefill_ws(T, L, k).total;
+}
+
+dsa_status_t dsa_prefill(const uint8_t* q8, const float* q_scale, const float* w,
+                         const uint8_t* k8, const float* k_scale, const uint16_t* q,
+                         const uint16_t* kv, int T, int L, int H_I, int H, int k, int q_pos0,
+                         float score_scale, float sm_scale, uint16_t* out, float* lse,
+                         int32_t* idx_out, void* workspace, size_t workspace_bytes,
+                         dsa_stream_t stream)
+{
+    if (dsa_status_t st = check_rows(T, L, q_pos0)) return st;
+    if (T > 0 && (!q8 || !q_scale || !w || !k8 || !k_scale || !q || !kv || !out))
+        return DSA_ERR_INVALID_ARGUMENT;
+    if (k < 1 || H < 1) return DSA_ERR_INVALID_ARGUMENT;
+    if (!(score_scale > 0.f) || !(sm_scale > 0.f)) return DSA_ERR_INVALID_ARGUMENT;
+    if (!dsa::indexer_supports(H_I) || !heads_ok(H) || !k_ok(k)) return DSA_ERR_UNSUPPORTED;
+    if ((int64_t)T * std::max(L, k) > kMaxElems) return DSA_ERR_UNSUPPORTED;
+    if (!aligned(q8, 16) || !aligned(k8, 16) || !aligned(q, 16) || !aligned(kv, 16) ||
+        !aligned(out, 4))
+        return DSA_ERR_INVALID_ARGUMENT;
+    if (T == 0) return DSA_OK;
+    const PrefillWs ws = prefill_ws(T, L, k);
+    if (!workspace || workspace_bytes < ws.total) return DSA_ERR_WORKSPACE_TOO_SMALL;
+    if (!aligned(workspace, kAlign)) return DSA_ERR_INVALID_ARGUMENT;
+
+    hipStream_t s = as_hip(stream);
+    uint8_t* base = static_cast<uint8_t*>(workspace);
+    float* scores = reinterpret_cast<float*>(base + ws.scores_off);
+    int32_t* idx_ws = reinterpret_cast<int32_t*>(base + ws.idx_off);
+    // first row that sees more than k tokens (earlier rows select all without scores)
+    const int t_sel = std::max(0, k - q_pos0);
+    for (int r0 = 0; r0 < T; r0 += ws.chunk) {
+        const int rows = std::min(ws.chunk, T - r0);
+        const int qp = q_pos0 + r0;
+        int32_t* idx = idx_out ? idx_out + (int64_t)r0 * k : idx_ws;
+        const int s0 = std::max(r0, t_sel);           // rows needing scores in this chunk
+        hipError_t e = hipSuccess;
+        if (s0 < r0 + rows) {
+            const int off = s0 - r0;
+            e = dsa::launch_indexer_prefill(q8 + (int64_t)s0 * H_I * 128,
+                                            q_scale + (int64_t)s0 * H_I, w + (int64_t)s0 * H_I,
+                                            k8, k_scale, rows - off, L, H_I, q_pos0 + s0,
+                                            score_scale, scores + (int64_t)off * L, L, s);
+        }
+        if (e == hipSuccess) e = dsa::launch_topk_prefill(scores, L, rows, L, qp, k, idx, s);
+        if (e == hipSuccess)
+            e = dsa::launch_sparse_mla(q + (int64_t)r0 * H * 576, kv, idx, nullptr, rows, L, H,
+                                       k, sm_scale, 1, out + (int64_t)r0 * H * 512,
+                                       lse ? lse + (int64_t)r0 * H : nullptr, nullptr, nullptr,
+                                       s);
+        if (e != hipSuccess) return DSA_ERR_HIP;
+    }
+    return DSA_OK;
+}
+
+size_t dsa_decode_workspace_bytes(int B, int max_len, int64_t total_tokens, int H_I, int H,
+                                  int k)
+{
+    (void)H_I;
+    (void)max_len;
+    if (B <= 0 || total_tokens <= 0 || H < 1 || k < 1) return 0;
+    return decode_ws(B, total_tokens, H, k).total;
+}
+
+dsa_status_t dsa_decode(int B, const int64_t* seq_start, int max_len, int64_t total_tokens,
+                        const uint8_t* q8, const float* q_scale, const float* w,
+                        const uint8_t* k8_cache, const float* k_scale_cache,
+                        const uint16_t* q, const uint16_t* kv_cache, int H_I, int H, int k,
+                        float score_scale, float sm_scale, uint16_t* out, float* lse,
+                        int32_t* idx_out, void* workspace, size_t workspace_bytes,
+                        dsa_stream_t stream)
+{
+    if (B < 0) return DSA_ERR_INVALID_ARGUMENT;
+    if (B == 0) return DSA_OK;                       // nothing to decode
+    if (max_len < 1 || total_tokens < 1 || k < 1 || H < 1) return DSA_ERR_INVALID_ARGUMENT;
+    if ((int64_t)B * max_len < total_tokens) return DSA_ERR_INVALID_ARGUMENT;
+    if ((!seq_start || !q8 || !q_scale || !w || !k8_cache || !k_scale_cache || !q ||
+                  !kv_cache || !out))
+        return DSA_ERR_INVALID_ARGUMENT;
+    if (!(score_scale > 0.f) || !(sm_scale > 0.f)) return DSA_ERR_INVALID_ARGUMENT;
+    if (!dsa::indexer_supports(H_I) || !heads_ok(H) || !k_ok(k)) return DSA_ERR_UNSUPPORTED;
+    if (total_tokens >= (int64_t(1) << 31) || B > 65535) return DSA_ERR_UNSUPPORTED;
+    if (!aligned(q8, 16) || !aligned(k8_cache, 16) || !aligned(q, 16) ||
+        !aligned(kv_cache, 16) || !aligned(out, 8))
+        return DSA_ERR_INVALID_ARGUMENT;
+    const DecodeWs ws = decode_ws(B, total_tokens, H, k);
+    if (!workspace || workspace_bytes < ws.total) return DSA_ERR_WORKSPACE_TOO_SMALL;
+    if (!aligned(workspace, kAlign)) return DSA_ERR_INVALID_ARGUMENT;
+
+    hipStream_t s = as_hip(stream);
+    uint8_t* base = static_cast<uint8_t*>(workspace);
+    float* scores = reinterpret_cast<float*>(base + ws.scores_off);
+    int32_t* idx = idx_out ? idx_out : reinterpret_cast<int32_t*>(base + ws.idx_off);
+    float* po = reinterpret_cast<float*>(base + ws.po_off);
+    float* pl = reinterpret_cast<float*>(base + ws.pl_off);
+    hipError_t e = dsa::launch_indexer_decode(q8, q_scale, w, k8_cache, k_scale_cache,
+                                              seq_start, B, max_len, H_I, score_scale, scores, s);
+    if (e == hipSuccess) e = dsa::launch_topk_decode(scores, seq_start, B, k, idx, s);
+    if (e == hipSuccess)
+        e = dsa::launch_sparse_mla(q, kv_cache, idx, seq_start, B, max_len, H, k, sm_scale,
+                                   ws.splits, out, lse, po, pl, s);
+    if (e == hipSuccess && ws.splits > 1)
+        e = dsa::launch_mla_combine(po, pl, B, H, ws.splits, out, lse, s);
+    return from_hip(e);
+}
+
+}  // extern "C"

@@ -1,0 +1,68 @@
+// dsa_device.h -- device-side helpers shared by the DSA kernels (gfx950, wave64).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dsa {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+// 16x16x128 fp8 (OCP e4m3fn) x fp8 -> fp32 MFMA.  Zero scale operands select the unscaled
+// v_mfma_f32_16x16x128_f8f6f4.  Lane l supplies row (A) / column (B) l%16 and 32 bytes of
+// K; A and B use the same K assignment, so a kernel only has to load both operands with
+// one lane->K mapping.  Output: lane l holds C[4*(l/16) + i][l%16], i = 0..3.
+__device__ __forceinline__ v4f mfma_f8(const v8i& a, const v8i& b, const v4f& c)
+{
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+// 16x16x32 bf16 MFMA, fp32 accumulate.  Lane l supplies row/column l%16 and 8 elements
+// of K (K group l/16); same output layout as above.
+__device__ __forceinline__ v4f mfma_bf16(const v8bf& a, const v8bf& b, const v4f& c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ v8bf as_bf16x8(const u32x4& v) { return __builtin_bit_cast(v8bf, v); }
+
+__device__ __forceinline__ v8i as_i8(const u32x4& lo, const u32x4& hi)
+{
+    v8i r;
+    r[0] = lo[0]; r[1] = lo[1]; r[2] = lo[2]; r[3] = lo[3];
+    r[4] = hi[0]; r[5] = hi[1]; r[6] = hi[2]; r[7] = hi[3];
+    return r;
+}
+
+// fp32 -> bf16 bits, round to nearest even (inputs are finite).
+__device__ __forceinline__ uint32_t bf16_bits(float f)
+{
+    uint32_t u = __float_as_uint(f);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
+{
+    return bf16_bits(lo) | (bf16_bits(hi) << 16);
+}
+
+// Order-preserving image of an fp32 score: larger float -> larger uint32, -0 == +0.
+__device__ __forceinline__ uint32_t score_key(float f)
+{
+    uint32_t u = __float_as_uint(f);
+    if (u == 0x80000000u) u = 0u;
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ float shfl_xor_f(float v, int m) { return __shfl_xor(v, m, 64); }
+
+__device__ __forceinline__ unsigned long long lanemask_lt(int lane)
+{
+    return (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+}
+
+}  // namespace dsa

@@ -1,0 +1,395 @@
+// indexer.hip -- the lightning indexer on gfx950.
+//
+// score[t,s] = ks[s] * sum_h a'[t,h] * ReLU(q8[t,h,:] . k8[s,:]),  a' = w * qs * c,
+// for visible keys s <= q_pos0 + t (《DeepSeek-V3.2-Exp模型优势与 DSA 工作原理》 §4 步骤二:
+// dot-product score, mask and scale, then per-head weights; ReLU per the gxzdkb DSA
+// explainer, section 秘密武器：DSA).  The fp8 dot products run on
+// v_mfma_f32_16x16x128_f8f6f4: one instruction contracts all 128 dims of 16 (token, head)
+// rows against 16 keys.  ReLU, the a' weighting, the head sum and the key scale are fused
+// on the accumulators in registers; the head sum crosses lane groups with a reduce-scatter
+// so every lane ends up owning distinct (token, key) outputs.
+#include "dsa_device.h"
+#include "kernels.h"
+
+namespace dsa {
+namespace {
+
+// ---------------------------------------------------------------- prefill geometry
+constexpr int IP_WAVES = 8;                // waves per workgroup
+constexpr int IP_ROWS = 128;               // (token, head) rows per wave
+constexpr int IP_NT = IP_ROWS / 16;        // 16-row MFMA tiles per wave
+constexpr int IP_KT = 128;                 // keys per LDS tile
+constexpr int IP_KSPLIT = 4096;            // keys per workgroup (grid.y)
+
+// LDS key tile: 128 keys x 128 B.  16-byte chunk c of key r lives at chunk c ^ (r & 7), so
+// the 16 keys one MFMA reads at equal chunk index fall on distinct banks.
+__device__ __forceinline__ int ktile_off(int key, int chunk)
+{
+    return key * 128 + ((chunk ^ (key & 7)) << 4);
+}
+
+// Head reduction of one 32-key step.  acc[kb][j][r] holds D for tile row 4g + r of tile j
+// and key kb*16 + c16.  Calls emit(token_in_wave, kb, value) once per distinct output.
+template <int HI, typename Emit>
+__device__ __forceinline__ void reduce_heads(const v4f (&acc)[2][IP_NT],
+                                             const float (&wp)[IP_NT][4], int lane,
+                                             Emit&& emit)
+{
+    const int g = lane >> 4;
+    const bool upper = lane >= 32, odd = (g & 1) != 0;
+    if constexpr (HI >= 16) {
+        constexpr int TPW = IP_ROWS / HI;      // tokens per wave
+        constexpr int TPT = HI / 16;           // tiles per token
+        constexpr int NO = 2 * TPW;            // (token, key block) partials per lane
+        constexpr int N1 = NO / 2;
+        float P[NO];
+#pragma unroll
+        for (int tk = 0; tk < TPW; ++tk) {
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                float s = 0.f;
+#pragma unroll
+                for (int jj = 0; jj < TPT; ++jj) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        s = fmaf(wp[tk * TPT + jj][r], fmaxf(acc[kb][tk * TPT + jj][r], 0.f), s);
+                }
+                P[tk * 2 + kb] = s;
+            }
+        }
+        // step 1: lanes 0-31 keep partials [0, N1), lanes 32-63 keep [N1, NO)
+        float Q[N1];
+#pragma unroll
+        for (int i = 0; i < N1; ++i) {
+            const float keep = upper ? P[N1 + i] : P[i];
+            const float send = upper ? P[i] : P[N1 + i];
+            Q[i] = keep + shfl_xor_f(send, 32);
+        }
+        if constexpr (N1 >= 2) {
+            // step 2: even lane groups keep [0, N2), odd keep [N2, N1) -> group g owns
+            // outputs g*N2 .. g*N2 + N2 - 1, each now summed over all four groups
+            constexpr int N2 = N1 / 2;
+#pragma unroll
+            for (int i = 0; i < N2; ++i) {
+                const float keep = odd ? Q[N2 + i] : Q[i];
+                const float send = odd ? Q[i] : Q[N2 + i];
+                const float v = keep + shfl_xor_f(send, 16);
+                const int o = g * N2 + i;
+                emit(o >> 1, o & 1, v);
+            }
+        } else {
+            const float v = Q[0] + shfl_xor_f(Q[0], 16);
+            if (!odd) emit(0, g >> 1, v);
+        }
+    } else if constexpr (HI == 8) {
+        // tile j: rows 0-7 token 2j, rows 8-15 token 2j+1; group g: token 2j + g/2
+#pragma unroll
+        for (int j = 0; j < IP_NT; ++j) {
+            float p0 = 0.f, p1 = 0.f;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                p0 = fmaf(wp[j][r], fmaxf(acc[0][j][r], 0.f), p0);
+                p1 = fmaf(wp[j][r], fmaxf(acc[1][j][r], 0.f), p1);
+            }
+            const float keep = odd ? p1 : p0;
+            const float send = odd ? p0 : p1;
+            emit(2 * j + (g >> 1), g & 1, keep + shfl_xor_f(send, 16));
+        }
+    } else {
+        // HI in {1, 2, 4}: the lane's four rows hold 4/HI whole tokens
+        constexpr int UPL = 4 / HI;
+#pragma unroll
+        for (int j = 0; j < IP_NT; ++j) {
+#pragma unroll
+            for (int u = 0; u < UPL; ++u) {
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb) {
+                    float v = 0.f;
+#pragma unroll
+                    for (int r = u * HI; r < u * HI + HI; ++r)
+                        v = fmaf(wp[j][r], fmaxf(acc[kb][j][r], 0.f), v);
+                    emit((16 * j + 4 * g) / HI + u, kb, v);
+                }
+            }
+        }
+    }
+}
+
+// Grid: x = token blocks of IP_WAVES * 128/HI rows (heaviest, i.e. latest, first),
+//       y = key ranges of IP_KSPLIT keys.  Each wave keeps 128 (token, head) query rows
+// in registers as MFMA A operands; the workgroup streams 128-key tiles through a
+// double-buffered LDS ring that all eight waves read as B operands.
+template <int HI>
+__global__ __launch_bounds__(IP_WAVES * 64) void indexer_prefill_kernel(
+    const uint8_t* __restrict__ q8, const float* __restrict__ qs, const float* __restrict__ w,
+    const uint8_t* __restrict__ k8, const float* __restrict__ ks, int T, int q_pos0, float c,
+    float* __restrict__ scores, int64_t ld)
+{
+    constexpr int TPW = IP_ROWS / HI;
+    constexpr int TB = IP_WAVES * TPW;
+    __shared__ __attribute__((aligned(16))) uint8_t s_key[2][IP_KT * 128];
+    __shared__ float s_ks[2][IP_KT];
+
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int g = lane >> 4, c16 = lane & 15;
+    const int blk = gridDim.x - 1 - blockIdx.x;
+    const int t0 = blk * TB;
+    const int t_end = min(T, t0 + TB);
+    const int p_last = q_pos0 + t_end - 1;            // last key any row here sees
+    const int kbeg = blockIdx.y * IP_KSPLIT;
+    if (kbeg > p_last) return;                         // uniform over the workgroup
+    const int kend = min(kbeg + IP_KSPLIT, p_last + 1);
+
+    const int tw0 = t0 + wave * TPW;                   // first token row of this wave
+    const bool wave_active = tw0 < T;
+    const int pw_last = q_pos0 + min(T, tw0 + TPW) - 1;
+    const int64_t nrows = (int64_t)T * HI;
+
+    // A operands: row 16j + c16 of the wave's (token, head) rows, bytes [32g, 32g + 32)
+    v8i qa[IP_NT];
+    float wp[IP_NT][4];
+#pragma unroll
+    for (int j = 0; j < IP_NT; ++j) {
+        const int64_t R = (int64_t)tw0 * HI + 16 * j + c16;
+        u32x4 lo = {0u, 0u, 0u, 0u}, hi = {0u, 0u, 0u, 0u};
+        if (wave_active && R < nrows) {
+            const u32x4* src = reinterpret_cast<const u32x4*>(q8 + R * 128 + 32 * g);
+            lo = src[0];
+            hi = src[1];
+        }
+        qa[j] = as_i8(lo, hi);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int64_t R2 = (int64_t)tw0 * HI + 16 * j + 4 * g + r;
+            wp[j][r] = (wave_active && R2 < nrows) ? w[R2] * qs[R2] * c : 0.f;
+        }
+    }
+
+    // cooperative tile load: thread -> key tid/4, bytes [32*(tid%4), +32)
+    const int lkey = tid >> 2, lpart = tid & 3;
+    u32x4 pre0 = {0u, 0u, 0u, 0u}, pre1 = {0u, 0u, 0u, 0u};
+    float pre_s = 0.f;
+    auto gload = [&](int tile) {
+        const int s = kbeg + tile * IP_KT + lkey;
+        if (s < kend) {
+            const u32x4* src = reinterpret_cast<const u32x4*>(k8 + (int64_t)s * 128 + 32 * lpart);
+            pre0 = src[0];
+            pre1 = src[1];
+        } else {
+            pre0 = u32x4{0u, 0u, 0u, 0u};
+            pre1 = pre0;
+        }
+        if (tid < IP_KT) {
+            const int s2 = kbeg + tile * IP_KT + tid;
+            pre_s = s2 < kend ? ks[s2] : 0.f;
+        }
+    };
+    auto sstore = [&](int buf) {
+        *reinterpret_cast<u32x4*>(&s_key[buf][ktile_off(lkey, 2 * lpart)]) = pre0;
+        *reinterpret_cast<u32x4*>(&s_key[buf][ktile_off(lkey, 2 * lpart + 1)]) = pre1;
+        if (tid < IP_KT) s_ks[buf][tid] = pre_s;
+    };
+
+    const int ntiles = (kend - kbeg + IP_KT - 1) / IP_KT;
+    gload(0);
+    sstore(0);
+    __syncthreads();
+    for (int it = 0; it < ntiles; ++it) {
+        const int buf = it & 1;
+        if (it + 1 < ntiles) gload(it + 1);
+        const int tbase = kbeg + it * IP_KT;
+        if (wave_active && tbase <= pw_last) {
+#pragma unroll 1
+            for (int step = 0; step < IP_KT / 32; ++step) {
+                const int key0 = tbase + step * 32;
+                if (key0 > pw_last) break;
+                v4f acc[2][IP_NT];
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb) {
+                    const int kl = step * 32 + kb * 16 + c16;
+                    const u32x4 lo = *reinterpret_cast<const u32x4*>(&s_key[buf][ktile_off(kl, 2 * g)]);
+                    const u32x4 hi = *reinterpret_cast<const u32x4*>(&s_key[buf][ktile_off(kl, 2 * g + 1)]);
+                    const v8i bb = as_i8(lo, hi);
+#pragma unroll
+                    for (int j = 0; j < IP_NT; ++j)
+                        acc[kb][j] = mfma_f8(qa[j], bb, v4f{0.f, 0.f, 0.f, 0.f});
+                }
+                reduce_heads<HI>(acc, wp, lane, [&](int tok, int kb, float v) {
+                    const int t = tw0 + tok;
+                    const int s = key0 + kb * 16 + c16;
+                    if (t < T && s <= q_pos0 + t && s < kend)
+                        scores[(int64_t)t * ld + s] = v * s_ks[buf][s - tbase];
+                });
+            }
+        }
+        if (it + 1 < ntiles) sstore(buf ^ 1);
+        __syncthreads();
+    }
+}
+
+__global__ __launch_bounds__(256) void mask_fill_kernel(int L, int q_pos0, float* scores,
+                                                        int64_t ld)
+{
+    const int t = blockIdx.x;
+    const float ninf = -__builtin_huge_valf();
+    for (int s = q_pos0 + t + 1 + threadIdx.x; s < L; s += blockDim.x)
+        scores[(int64_t)t * ld + s] = ninf;
+}
+
+// ---------------------------------------------------------------- decode geometry
+constexpr int ID_WAVES = 4;
+constexpr int ID_KPW = 256;                      // keys per wave
+constexpr int ID_KPB = ID_WAVES * ID_KPW;        // keys per workgroup
+
+// Grid: x = key chunks of one sequence's cache, y = sequence.  One query token of HI
+// heads is the MFMA A operand (HI/16 tiles, zero-padded below 16 heads); every wave
+// streams its own keys straight from HBM as B operands, 64 keys per step.  This is the
+// bandwidth-bound shape: 132 bytes of key and scale per scored token.
+template <int HI>
+__global__ __launch_bounds__(ID_WAVES * 64) void indexer_decode_kernel(
+    const uint8_t* __restrict__ q8, const float* __restrict__ qs, const float* __restrict__ w,
+    const uint8_t* __restrict__ k8, const float* __restrict__ ks,
+    const int64_t* __restrict__ seq_start, float c, float* __restrict__ scores)
+{
+    constexpr int NTQ = HI >= 16 ? HI / 16 : 1;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int g = lane >> 4, c16 = lane & 15;
+    const bool upper = lane >= 32, odd = (g & 1) != 0;
+    const int b = blockIdx.y;
+    const int64_t a = seq_start[b];
+    const int Lb = (int)(seq_start[b + 1] - a);
+    const int sw0 = blockIdx.x * ID_KPB + wave * ID_KPW;
+    if (sw0 >= Lb) return;                            // no barriers in this kernel
+
+    // lane K assignment (A and B alike): 16-byte chunks g and g + 4 of the 128-byte row
+    v8i qa[NTQ];
+    float wp[NTQ][4];
+#pragma unroll
+    for (int j = 0; j < NTQ; ++j) {
+        const int h = 16 * j + c16;
+        u32x4 lo = {0u, 0u, 0u, 0u}, hi = {0u, 0u, 0u, 0u};
+        if (h < HI) {
+            const uint8_t* src = q8 + ((int64_t)b * HI + h) * 128;
+            lo = *reinterpret_cast<const u32x4*>(src + 16 * g);
+            hi = *reinterpret_cast<const u32x4*>(src + 64 + 16 * g);
+        }
+        qa[j] = as_i8(lo, hi);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int hh = 16 * j + 4 * g + r;
+            wp[j][r] = hh < HI ? w[b * HI + hh] * qs[b * HI + hh] * c : 0.f;
+        }
+    }
+
+#pragma unroll 1
+    for (int it = 0; it < ID_KPW / 64; ++it) {
+        const int s0 = sw0 + it * 64;
+        if (s0 >= Lb) break;
+        float P[4];
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+            const int key = s0 + kb * 16 + c16;
+            u32x4 lo = {0u, 0u, 0u, 0u}, hi = {0u, 0u, 0u, 0u};
+            if (key < Lb) {
+                const uint8_t* src = k8 + (a + key) * 128;
+                lo = *reinterpret_cast<const u32x4*>(src + 16 * g);
+                hi = *reinterpret_cast<const u32x4*>(src + 64 + 16 * g);
+            }
+            const v8i bb = as_i8(lo, hi);
+            float s = 0.f;
+#pragma unroll
+            for (int j = 0; j < NTQ; ++j) {
+                const v4f d = mfma_f8(qa[j], bb, v4f{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+                for (int r = 0; r < 4; ++r) s = fmaf(wp[j][r], fmaxf(d[r], 0.f), s);
+            }
+            P[kb] = s;
+        }
+        // reduce-scatter over the four lane groups: group g ends with key block g
+        float Q0, Q1;
+        {
+            const float k0 = upper ? P[2] : P[0], s0v = upper ? P[0] : P[2];
+            const float k1 = upper ? P[3] : P[1], s1v = upper ? P[1] : P[3];
+            Q0 = k0 + shfl_xor_f(s0v, 32);
+            Q1 = k1 + shfl_xor_f(s1v, 32);
+        }
+        const float keep = odd ? Q1 : Q0, send = odd ? Q0 : Q1;
+        const float v = keep + shfl_xor_f(send, 16);
+        const int key = s0 + g * 16 + c16;
+        if (key < Lb) scores[a + key] = v * ks[a + key];
+    }
+}
+
+template <int HI>
+hipError_t launch_prefill_hi(const uint8_t* q8, const float* qs, const float* w,
+                             const uint8_t* k8, const float* ks, int T, int L, int q_pos0,
+                             float c, float* scores, int64_t ld, hipStream_t stream)
+{
+    constexpr int TB = IP_WAVES * (IP_ROWS / HI);
+    const int keys = min(L, q_pos0 + T);               // keys any row can see
+    dim3 grid((T + TB - 1) / TB, (keys + IP_KSPLIT - 1) / IP_KSPLIT);
+    hipLaunchKernelGGL(indexer_prefill_kernel<HI>, grid, dim3(IP_WAVES * 64), 0, stream, q8,
+                       qs, w, k8, ks, T, q_pos0, c, scores, ld);
+    return hipGetLastError();
+}
+
+template <int HI>
+hipError_t launch_decode_hi(const uint8_t* q8, const float* qs, const float* w,
+                            const uint8_t* k8, const float* ks, const int64_t* seq_start, int B,
+                            int max_len, float c, float* scores, hipStream_t stream)
+{
+    dim3 grid((max_len + ID_KPB - 1) / ID_KPB, B);
+    hipLaunchKernelGGL(indexer_decode_kernel<HI>, grid, dim3(ID_WAVES * 64), 0, stream, q8, qs,
+                       w, k8, ks, seq_start, c, scores);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+bool indexer_supports(int H_I)
+{
+    return H_I == 1 || H_I == 2 || H_I == 4 || H_I == 8 || H_I == 16 || H_I == 32 ||
+           H_I == 64 || H_I == 128;
+}
+
+hipError_t launch_indexer_prefill(const uint8_t* q8, const float* qs, const float* w,
+                                  const uint8_t* k8, const float* ks, int T, int L, int H_I,
+                                  int q_pos0, float c, float* scores, int64_t ld,
+                                  hipStream_t stream)
+{
+    if (T <= 0) return hipSuccess;
+#define DSA_IDX_CASE(HI) \
+    case HI: return launch_prefill_hi<HI>(q8, qs, w, k8, ks, T, L, q_pos0, c, scores, ld, stream);
+    switch (H_I) {
+        DSA_IDX_CASE(1) DSA_IDX_CASE(2) DSA_IDX_CASE(4) DSA_IDX_CASE(8)
+        DSA_IDX_CASE(16) DSA_IDX_CASE(32) DSA_IDX_CASE(64) DSA_IDX_CASE(128)
+        default: return hipErrorInvalidValue;
+    }
+#undef DSA_IDX_CASE
+}
+
+hipError_t launch_mask_fill(int T, int L, int q_pos0, float* scores, int64_t ld,
+                            hipStream_t stream)
+{
+    if (T <= 0) return hipSuccess;
+    hipLaunchKernelGGL(mask_fill_kernel, dim3(T), dim3(256), 0, stream, L, q_pos0, scores, ld);
+    return hipGetLastError();
+}
+
+hipError_t launch_indexer_decode(const uint8_t* q8, const float* qs, const float* w,
+                                 const uint8_t* k8, const float* ks, const int64_t* seq_start,
+                                 int B, int max_len, int H_I, float c, float* scores,
+                                 hipStream_t stream)
+{
+    if (B <= 0) return hipSuccess;
+#define DSA_IDX_CASE(HI) \
+    case HI: return launch_decode_hi<HI>(q8, qs, w, k8, ks, seq_start, B, max_len, c, scores, stream);
+    switch (H_I) {
+        DSA_IDX_CASE(1) DSA_IDX_CASE(2) DSA_IDX_CASE(4) DSA_IDX_CASE(8)
+        DSA_IDX_CASE(16) DSA_IDX_CASE(32) DSA_IDX_CASE(64) DSA_IDX_CASE(128)
+        default: return hipErrorInvalidValue;
+    }
+#undef DSA_IDX_CASE
+}
+
+}  // namespace dsa

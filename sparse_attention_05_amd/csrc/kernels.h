@@ -1,0 +1,49 @@
+// kernels.h -- host-side launchers of the DSA kernels (internal to libdsa.so).
+// Every launcher assumes arguments already validated by the C ABI layer and only
+// enqueues work on `stream`.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dsa {
+
+// ---- lightning indexer --------------------------------------------------------------
+// Scores of T query rows (positions q_pos0 + t) against keys 0..L-1; writes only the
+// visible entries s <= q_pos0 + t of each row (row t at scores + t * ld).
+hipError_t launch_indexer_prefill(const uint8_t* q8, const float* qs, const float* w,
+                                  const uint8_t* k8, const float* ks, int T, int L, int H_I,
+                                  int q_pos0, float c, float* scores, int64_t ld,
+                                  hipStream_t stream);
+// Writes -inf to the masked entries q_pos0 + t < s < L of every row.
+hipError_t launch_mask_fill(int T, int L, int q_pos0, float* scores, int64_t ld,
+                            hipStream_t stream);
+// Decode: query b scores every key of its packed cache slice [seq_start[b], seq_start[b+1])
+// into scores[seq_start[b] + s].
+hipError_t launch_indexer_decode(const uint8_t* q8, const float* qs, const float* w,
+                                 const uint8_t* k8, const float* ks, const int64_t* seq_start,
+                                 int B, int max_len, int H_I, float c, float* scores,
+                                 hipStream_t stream);
+bool indexer_supports(int H_I);
+
+// ---- top-k ----------------------------------------------------------------------------
+// Prefill rows: row t at scores + t * ld with n_t = min(L, q_pos0 + t + 1) visible scores.
+hipError_t launch_topk_prefill(const float* scores, int64_t ld, int T, int L, int q_pos0,
+                               int k, int32_t* idx, hipStream_t stream);
+// Decode rows: row b at scores + seq_start[b] with seq_start[b+1] - seq_start[b] scores.
+hipError_t launch_topk_decode(const float* scores, const int64_t* seq_start, int B, int k,
+                              int32_t* idx, hipStream_t stream);
+
+// ---- sparse MLA -----------------------------------------------------------------------
+// Row t attends over kv rows idx[t, :] (entries outside [0, L) skipped).
+// seq_start (nullable, device int64 [T+1]): row t's cache is the packed slice
+// kv[seq_start[t] .. seq_start[t+1]) and its indices are relative to that slice.
+// splits > 1: each split covers a contiguous slice of the index list and writes fp32
+// partials (o normalised by its own denominator, lse) that launch_mla_combine merges.
+hipError_t launch_sparse_mla(const uint16_t* q, const uint16_t* kv, const int32_t* idx,
+                             const int64_t* seq_start, int T, int L, int H, int k,
+                             float sm_scale, int splits, uint16_t* out, float* lse,
+                             float* part_o, float* part_lse, hipStream_t stream);
+hipError_t launch_mla_combine(const float* part_o, const float* part_lse, int T, int H,
+                              int splits, uint16_t* out, float* lse, hipStream_t stream);
+
+}  // namespace dsa

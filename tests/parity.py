@@ -1,0 +1,92 @@
+"""Parity rules between the HIP path and the CPU oracle (test infrastructure).
+
+* indexer scores: |g - o| <= 1e-3 |o| + 2^-16 A[t,s], A the conditioning bound
+  ks * sum_h |a'_h| sum_d |q k| (covers fp32 cancellation between signed heads, about
+  1.3x the worst-case fp32 summation error (128 + 64) 2^-24); masked entries exactly -inf.
+* top-k on the GPU's own fp32 scores: exactly the oracle's selection of the same values.
+* end-to-end indices: same count min(k, n_t); every position in the symmetric difference
+  has an oracle score within tol(tau) of the oracle's k-th score tau (a near-tie).
+* sparse MLA, against the oracle run on the GPU's own indices: max |out_g - out_o| <= 1e-2,
+  per (row, head) ||delta||_2 / ||o||_2 <= 1e-2, |delta lse| <= 1e-3.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import oracle
+
+SCORE_RTOL = 1e-3
+SCORE_FLOOR = 2.0 ** -16
+OUT_ATOL = 1e-2
+OUT_REL_L2 = 1e-2
+LSE_ATOL = 1e-3
+
+
+def to_device(inp: dict, device="cuda") -> dict:
+    return {k: (v.to(device) if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+
+
+def bf16_to_f64(t: torch.Tensor) -> np.ndarray:
+    return t.detach().float().cpu().double().numpy()
+
+
+def check_scores(g: np.ndarray, o: np.ndarray, bound: np.ndarray, what=""):
+    g = np.asarray(g, np.float64)
+    masked = np.isneginf(o)
+    assert np.array_equal(np.isneginf(g), masked), "%s: mask pattern differs" % what
+    vis = ~masked
+    err = np.abs(g[vis] - o[vis])
+    tol = SCORE_RTOL * np.abs(o[vis]) + SCORE_FLOOR * bound[vis]
+    bad = err > tol
+    assert not bad.any(), "%s: %d scores out of tolerance, worst err %.3g (tol %.3g)" % (
+        what, bad.sum(), err[bad].max(), tol[bad][np.argmax(err[bad])])
+    return float(err.max(initial=0.0))
+
+
+def check_topk_exact(gpu_idx: np.ndarray, gpu_scores: np.ndarray, n_vis, k: int, what=""):
+    want = oracle.topk(np.asarray(gpu_scores, np.float64), n_vis, k)
+    got = np.asarray(gpu_idx)
+    if not np.array_equal(got, want):
+        r = np.nonzero((got != want).any(1))[0]
+        raise AssertionError("%s: top-k differs on %d rows, first %d: got %s want %s" % (
+            what, len(r), r[0], got[r[0]][:16], want[r[0]][:16]))
+
+
+def check_indices_near_ties(gpu_idx, ora_idx, ora_scores, bound, n_vis, k: int, what=""):
+    """Returns the number of near-tie swaps; fails on any other difference."""
+    swaps = 0
+    for r in range(len(n_vis)):
+        n = int(n_vis[r])
+        g = np.asarray(gpu_idx[r])
+        o = np.asarray(ora_idx[r])
+        gs, os_ = set(g[g >= 0].tolist()), set(o[o >= 0].tolist())
+        assert len(gs) == len(os_) == min(n, k), "%s row %d: wrong count" % (what, r)
+        assert len(set(g[g >= 0].tolist())) == (g >= 0).sum(), "%s row %d: duplicates" % (what, r)
+        assert all(0 <= s < n for s in gs), "%s row %d: index outside the visible range" % (what, r)
+        diff = gs ^ os_
+        if not diff:
+            continue
+        row = ora_scores[r, :n]
+        tau = np.sort(row)[::-1][k - 1]
+        tol = SCORE_RTOL * abs(tau) + SCORE_FLOOR * bound[r, :n].max()
+        for s in diff:
+            assert abs(row[s] - tau) <= tol, "%s row %d: position %d (score %.9g) is not a " \
+                "near-tie of tau %.9g (tol %.3g)" % (what, r, s, row[s], tau, tol)
+        swaps += len(diff) // 2
+    return swaps
+
+
+def check_mla(out_g: np.ndarray, lse_g: np.ndarray, out_o: np.ndarray, lse_o: np.ndarray,
+              what=""):
+    d = np.abs(out_g - out_o)
+    assert d.max(initial=0.0) <= OUT_ATOL, "%s: max |dout| %.3g" % (what, d.max())
+    num = np.sqrt(((out_g - out_o) ** 2).sum(-1))
+    den = np.sqrt((out_o ** 2).sum(-1))
+    rel = num / np.maximum(den, 1e-30)
+    assert rel.max(initial=0.0) <= OUT_REL_L2, "%s: rel L2 %.3g" % (what, rel.max())
+    fin = np.isfinite(lse_o)
+    assert np.array_equal(np.isfinite(lse_g), fin), "%s: lse finiteness differs" % what
+    dl = np.abs(lse_g[fin] - lse_o[fin])
+    assert dl.max(initial=0.0) <= LSE_ATOL, "%s: max |dlse| %.3g" % (what, dl.max())
+    return float(d.max(initial=0.0)), float(rel.max(initial=0.0)), float(dl.max(initial=0.0))

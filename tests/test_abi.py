@@ -1,0 +1,122 @@
+"""The C ABI without a GPU: the library loads, exports every declared entry point, and
+rejects invalid arguments before any HIP call (so these run on a CPU-only host)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import sparse_attention_05_amd as dsa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dsa.h")
+NULL = None
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(dsa.LIB_PATH):
+        from sparse_attention_05_amd import build
+        build.build()
+    return dsa.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dsa_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert set(names) == set(dsa.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings_and_version(lib):
+    assert lib.dsa_version() == 100
+    for code, name in [(0, b"DSA_OK"), (1, b"DSA_ERR_INVALID_ARGUMENT"),
+                       (2, b"DSA_ERR_UNSUPPORTED"), (3, b"DSA_ERR_WORKSPACE_TOO_SMALL"),
+                       (4, b"DSA_ERR_HIP")]:
+        assert lib.dsa_status_string(code) == name
+
+
+FAKE = ctypes.c_void_p(1 << 20)   # aligned, never dereferenced: validation fails first
+
+
+def idx_scores(lib, T=4, L=8, H_I=4, q_pos0=0, c=0.1, ld=8, ptr=FAKE, qp=FAKE):
+    return lib.dsa_index_scores(qp, ptr, ptr, ptr, ptr, T, L, H_I, q_pos0, c, ptr, ld, 1, NULL)
+
+
+def test_index_scores_validation(lib):
+    assert idx_scores(lib, ptr=NULL) == dsa.DSA_ERR_INVALID_ARGUMENT
+    assert idx_scores(lib, T=-1) == dsa.DSA_ERR_INVALID_ARGUMENT
+    assert idx_scores(lib, q_pos0=5) == dsa.DSA_ERR_INVALID_ARGUMENT      # q_pos0 + T > L
+    assert idx_scores(lib, ld=7) == dsa.DSA_ERR_INVALID_ARGUMENT          # ld < L
+    assert idx_scores(lib, c=0.0) == dsa.DSA_ERR_INVALID_ARGUMENT
+    assert idx_scores(lib, c=float("nan")) == dsa.DSA_ERR_INVALID_ARGUMENT
+    assert idx_scores(lib, H_I=3) == dsa.DSA_ERR_UNSUPPORTED
+    assert idx_scores(lib, H_I=256) == dsa.DSA_ERR_UNSUPPORTED
+    assert idx_scores(lib, qp=ctypes.c_void_p((1 << 20) + 4)) == dsa.DSA_ERR_INVALID_ARGUMENT
+    assert idx_scores(lib, T=0, ptr=NULL, qp=NULL) == dsa.DSA_OK           # empty: no launch
+
+
+def test_topk_validation(lib):
+    f = lambda T=4, L=8, q=0, k=2, ld=8, p=FAKE: lib.dsa_topk(p, ld, T, L, q, k, p, NULL, 0, NULL)
+    assert f(p=NULL) == dsa.DSA_ERR_INVALID_ARGUMENT
+    assert f(k=0) == dsa.DSA_ERR_INVALID_ARGUMENT
+    assert f(k=8193) == dsa.DSA_ERR_UNSUPPORTED
+    assert f(ld=4) == dsa.DSA_ERR_INVALID_ARGUMENT
+    assert f(q=6) == dsa.DSA_ERR_INVALID_ARGUMENT
+    assert f(T=0, p=NULL) == dsa.DSA_OK
+    assert lib.dsa_topk_workspace_bytes(100, 1000, 10) == 0
+
+
+def test_sparse_mla_validation(lib):
+    f = lambda T=4, L=8, H=16, k=4, s=0.05, p=FAKE: lib.dsa_sparse_mla(p, p, p, T, L, H, k, s, p, p, NULL)
+    assert f(p=NULL) == dsa.DSA_ERR_INVALID_ARGUMENT
+    assert f(H=0) == dsa.DSA_ERR_INVALID_ARGUMENT
+    assert f(H=129) == dsa.DSA_ERR_UNSUPPORTED
+    assert f(k=0) == dsa.DSA_ERR_INVALID_ARGUMENT
+    assert f(s=-1.0) == dsa.DSA_ERR_INVALID_ARGUMENT
+    assert f(L=0) == dsa.DSA_ERR_INVALID_ARGUMENT
+    assert f(T=0, p=NULL) == dsa.DSA_OK
+
+
+def test_prefill_validation_and_workspace(lib):
+    need = lib.dsa_prefill_workspace_bytes(1024, 1024, 4, 8, 256)
+    assert need > 1024 * 1024 * 4
+    assert lib.dsa_prefill_workspace_bytes(0, 1024, 4, 8, 256) == 0
+    assert lib.dsa_prefill_chunk_rows(131072, 131072) == 1024
+    assert lib.dsa_prefill_chunk_rows(2048, 2048) == 2048
+    assert lib.dsa_prefill_chunk_rows(0, 10) == 0
+
+    def f(T=16, L=16, H_I=4, H=16, k=4, q=0, ws=FAKE, wsb=None, p=FAKE):
+        wsb = need if wsb is None else wsb
+        return lib.dsa_prefill(p, p, p, p, p, p, p, T, L, H_I, H, k, q, 0.1, 0.05, p, p, NULL,
+                               ws, wsb, NULL)
+    assert f(p=NULL) == dsa.DSA_ERR_INVALID_ARGUMENT
+    assert f(q=1) == dsa.DSA_ERR_INVALID_ARGUMENT
+    assert f(H_I=5) == dsa.DSA_ERR_UNSUPPORTED
+    assert f(k=0) == dsa.DSA_ERR_INVALID_ARGUMENT
+    assert f(ws=NULL) == dsa.DSA_ERR_WORKSPACE_TOO_SMALL
+    assert f(wsb=1) == dsa.DSA_ERR_WORKSPACE_TOO_SMALL
+    assert f(ws=ctypes.c_void_p((1 << 20) + 128)) == dsa.DSA_ERR_INVALID_ARGUMENT  # alignment
+
+
+def test_decode_validation_and_workspace(lib):
+    need = lib.dsa_decode_workspace_bytes(4, 100, 300, 64, 128, 64)
+    assert need >= 300 * 4 + 4 * 64 * 4
+
+    def f(B=4, ml=100, N=300, H_I=64, H=128, k=64, ws=FAKE, wsb=None, p=FAKE):
+        wsb = need if wsb is None else wsb
+        return lib.dsa_decode(B, p, ml, N, p, p, p, p, p, p, p, H_I, H, k, 0.1, 0.05, p, p,
+                              NULL, ws, wsb, NULL)
+    assert f(p=NULL) == dsa.DSA_ERR_INVALID_ARGUMENT
+    assert f(N=401) == dsa.DSA_ERR_INVALID_ARGUMENT       # more tokens than B * max_len
+    assert f(ml=0) == dsa.DSA_ERR_INVALID_ARGUMENT
+    assert f(H_I=48) == dsa.DSA_ERR_UNSUPPORTED
+    assert f(ws=NULL) == dsa.DSA_ERR_WORKSPACE_TOO_SMALL
+    assert f(wsb=need - 1) == dsa.DSA_ERR_WORKSPACE_TOO_SMALL
+    assert f(B=0, p=NULL) == dsa.DSA_OK

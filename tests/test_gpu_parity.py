@@ -1,0 +1,343 @@
+"""HIP path vs the CPU oracle, element by element, through the C ABI (needs an MI355X).
+
+Small cases compare every row; the long workloads (32K and 128K prefill, 64-sequence decode)
+run in the benchmark's launch configuration and compare sampled rows the oracle computes one
+by one.  Tolerances: tests/parity.py.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from parity import (check_indices_near_ties, check_mla, check_scores, check_topk_exact,
+                    bf16_to_f64, to_device)
+from synth import WORKLOADS, DecodeCfg, PrefillCfg, host_arrays, make_decode, make_prefill
+
+pytestmark = pytest.mark.gpu
+
+
+def _cfg(L, k, H_I, H, seed, q_pos0=0, T=None, planted=0.0):
+    return PrefillCfg("case", L=L, k=k, H_I=H_I, H=H, w_std=H_I ** -0.5, seed=seed,
+                      q_pos0=q_pos0, T=T, planted_frac=planted)
+
+
+def _np(t):
+    return t.detach().cpu().numpy()
+
+
+def _u16(t):
+    return t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+@pytest.fixture(autouse=True)
+def _free_gpu_memory():
+    yield
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+# --------------------------------------------------------------------------- indexer
+
+@pytest.mark.parametrize("H_I,L,q_pos0,T", [
+    (4, 1024, 0, None), (1, 300, 0, None), (2, 257, 5, 200), (8, 300, 0, None),
+    (16, 200, 0, None), (32, 257, 10, 100), (64, 513, 0, None), (128, 130, 0, None),
+    (64, 1, 0, None), (4, 17, 16, 1)])
+def test_indexer_parity(dsa, H_I, L, q_pos0, T):
+    cfg = _cfg(L, 16, H_I, 16, seed=100 + H_I + L, q_pos0=q_pos0, T=T)
+    inp = make_prefill(cfg)
+    h, d = host_arrays(inp), to_device(inp)
+    g = dsa.dsa_index_scores(d["q8"], d["qs"], d["w"], d["k8"], d["ks"], q_pos0, cfg.score_scale)
+    torch.cuda.synchronize()
+    o, bound = oracle.index_scores(h["q8"], h["qs"], h["w"], h["k8"], h["ks"], q_pos0,
+                                   cfg.score_scale, with_bound=True)
+    check_scores(_np(g), o, bound, "indexer H_I=%d L=%d" % (H_I, L))
+
+
+def test_indexer_leading_dimension_leaves_padding_untouched(dsa):
+    cfg = _cfg(200, 16, 64, 16, seed=7)
+    inp = to_device(make_prefill(cfg))
+    buf = torch.full((200, 256), 12345.0, device="cuda")
+    dsa.dsa_index_scores(inp["q8"], inp["qs"], inp["w"], inp["k8"], inp["ks"], 0,
+                         cfg.score_scale, scores=buf)
+    torch.cuda.synchronize()
+    assert torch.all(buf[:, 200:] == 12345.0)
+    ref = dsa.dsa_index_scores(inp["q8"], inp["qs"], inp["w"], inp["k8"], inp["ks"], 0,
+                               cfg.score_scale)
+    assert torch.equal(buf[:, :200], ref)
+
+
+def test_indexer_dense_heads_sampled_rows(dsa):
+    """64 heads at L=2048: the shape of the dense-fallback workload."""
+    cfg = WORKLOADS["prefill-L2048-k2048-dense"]
+    inp = make_prefill(cfg)
+    h, d = host_arrays(inp), to_device(inp)
+    g = _np(dsa.dsa_index_scores(d["q8"], d["qs"], d["w"], d["k8"], d["ks"], 0, cfg.score_scale))
+    rows = np.array([0, 1, 15, 16, 17, 500, 1023, 1024, 2046, 2047])
+    o, bound = oracle.index_scores(h["q8"], h["qs"], h["w"], h["k8"], h["ks"], 0,
+                                   cfg.score_scale, rows=rows, with_bound=True)
+    check_scores(g[rows], o, bound, "indexer L=2048 H_I=64")
+
+
+# ----------------------------------------------------------------------------- top-k
+
+def test_topk_exact_on_gpu_scores(dsa):
+    cfg = WORKLOADS["prefill-L1024-k256"]
+    d = to_device(make_prefill(cfg))
+    s = dsa.dsa_index_scores(d["q8"], d["qs"], d["w"], d["k8"], d["ks"], 0, cfg.score_scale)
+    idx = dsa.dsa_topk(s, cfg.L, 0, cfg.k)
+    torch.cuda.synchronize()
+    check_topk_exact(_np(idx), _np(s), np.arange(cfg.L) + 1, cfg.k, "top-k L=1024")
+
+
+@pytest.mark.parametrize("k", [1, 7, 64, 299, 300, 301, 8192])
+def test_topk_ties_signed_zeros_and_k_edges(dsa, k):
+    rng = np.random.default_rng(k)
+    T, L, q_pos0 = 64, 300, 236
+    vals = np.array([0.0, -0.0, 1.0, 1.0, 2.0, -1.0, 0.5], np.float32)
+    s = rng.choice(vals, size=(T, L)).astype(np.float32)
+    s[1] = 0.0
+    s[2] = -0.0
+    s[3] = rng.standard_normal(L).astype(np.float32)
+    s[4, ::2] = -np.inf                                  # masked-looking values are still ranked
+    g = torch.from_numpy(s).cuda()
+    idx = dsa.dsa_topk(g, L, q_pos0, k)
+    torch.cuda.synchronize()
+    check_topk_exact(_np(idx), s, np.minimum(L, q_pos0 + np.arange(T) + 1), k, "ties k=%d" % k)
+
+
+def test_topk_long_rows(dsa):
+    rng = np.random.default_rng(5)
+    T, L, k = 6, 40000, 2048
+    s = rng.standard_normal((T, L)).astype(np.float32)
+    s[1] = np.round(s[1] * 8) / 8                      # coarse values: ties at the threshold
+    s[2] = 0.0
+    g = torch.from_numpy(s).cuda()
+    idx = dsa.dsa_topk(g, L, L - T, k)
+    torch.cuda.synchronize()
+    check_topk_exact(_np(idx), s, L - T + np.arange(T) + 1, k, "long rows")
+
+
+# -------------------------------------------------------------------------- sparse MLA
+
+def _random_idx(T, L, k, q_pos0, rng, holes=True):
+    idx = np.full((T, k), -1, np.int32)
+    for t in range(T):
+        n = min(L, q_pos0 + t + 1)
+        m = min(n, k)
+        sel = rng.choice(n, size=m, replace=False).astype(np.int32)
+        if holes and m < k:
+            slots = np.sort(rng.choice(k, size=m, replace=False))
+            idx[t, slots] = sel
+        else:
+            idx[t, :m] = sel
+    return idx
+
+
+@pytest.mark.parametrize("H,L,k", [(8, 1024, 256), (16, 300, 64), (128, 600, 100),
+                                   (40, 200, 33), (128, 3000, 2048)])
+def test_sparse_mla_parity(dsa, H, L, k):
+    cfg = _cfg(L, k, 4, H, seed=H * 7 + k, T=min(L, 160), q_pos0=L - min(L, 160))
+    inp = make_prefill(cfg)
+    h, d = host_arrays(inp), to_device(inp)
+    idx = _random_idx(cfg.rows, L, k, cfg.q_pos0, np.random.default_rng(H))
+    out, lse = dsa.dsa_sparse_mla(d["q"], d["kv"], torch.from_numpy(idx).cuda(), cfg.sm_scale)
+    torch.cuda.synchronize()
+    oo, ol = oracle.sparse_mla(h["q"], h["kv"], idx, cfg.sm_scale)
+    check_mla(bf16_to_f64(out), _np(lse), oo, ol, "mla H=%d L=%d k=%d" % (H, L, k))
+
+
+def test_sparse_mla_single_row_closed_form_and_empty_rows(dsa):
+    """A row selecting only token 0 returns kv[0, :512] exactly (softmax weight 1); a row
+    with no valid index (all -1 or out of range) returns zeros and lse = -inf."""
+    cfg = _cfg(64, 8, 4, 32, seed=3)
+    d = to_device(make_prefill(cfg))
+    idx = torch.full((64, 8), -1, dtype=torch.int32)
+    idx[0, 3] = 0
+    idx[2, :] = 64                                     # out of range -> padding
+    idx[3, 5] = 1000
+    idx[5, :] = torch.arange(8)
+    out, lse = dsa.dsa_sparse_mla(d["q"], d["kv"], idx.cuda(), cfg.sm_scale)
+    torch.cuda.synchronize()
+    assert torch.equal(out[0], d["kv"][0, :512].unsqueeze(0).expand(32, 512))
+    ref = (d["q"][0].double() @ d["kv"][0].double()) * cfg.sm_scale
+    assert torch.allclose(lse[0].double(), ref, atol=1e-4, rtol=1e-5)
+    for r in (1, 2, 3, 4):
+        assert torch.all(out[r].float() == 0) and torch.all(torch.isneginf(lse[r]))
+
+
+# ------------------------------------------------------------------- prefill, end to end
+
+def _oracle_rows_from_device(d: dict, rows, k):
+    """Oracle prefill of selected rows, one at a time (inputs copied from the device)."""
+    k8, ks, kv = _np(d["k8"]), _np(d["ks"]), _u16(d["kv"])
+    res = []
+    for t in rows:
+        t = int(t)
+        p = d["q_pos0"] + t
+        sc, bd = oracle.index_scores(_np(d["q8"][t:t + 1]), _np(d["qs"][t:t + 1]),
+                                     _np(d["w"][t:t + 1]), k8, ks, p, d["score_scale"],
+                                     with_bound=True)
+        idx = oracle.topk(sc, [p + 1], k)
+        res.append(dict(t=t, n=p + 1, scores=sc[0], bound=bd[0], idx=idx[0]))
+    return res
+
+
+def _check_prefill_rows(d, out, lse, gidx, rows, k, what):
+    ora = _oracle_rows_from_device(d, rows, k)
+    kv = _u16(d["kv"])
+    swaps = 0
+    for r in ora:
+        t = r["t"]
+        swaps += check_indices_near_ties(gidx[t:t + 1], r["idx"][None], r["scores"][None],
+                                         r["bound"][None], [r["n"]], k, "%s row %d" % (what, t))
+        oo, ol = oracle.sparse_mla(_u16(d["q"][t:t + 1]), kv, gidx[t:t + 1], d["sm_scale"])
+        check_mla(bf16_to_f64(out[t:t + 1]), _np(lse[t:t + 1]), oo, ol, "%s row %d" % (what, t))
+    return swaps
+
+
+def test_prefill_small_every_row(dsa):
+    cfg = WORKLOADS["prefill-L1024-k256"]
+    inp = make_prefill(cfg)
+    h, d = host_arrays(inp), to_device(inp)
+    idx = torch.empty((cfg.L, cfg.k), dtype=torch.int32, device="cuda")
+    out, lse, _ = dsa.dsa_prefill(d["q8"], d["qs"], d["w"], d["k8"], d["ks"], d["q"], d["kv"],
+                                  cfg.k, 0, cfg.score_scale, cfg.sm_scale, idx_out=idx)
+    torch.cuda.synchronize()
+    ref = oracle.prefill(h, with_bound=True)
+    gidx = _np(idx)
+    check_indices_near_ties(gidx, ref["idx"], ref["scores"], ref["bound"], ref["n_vis"], cfg.k,
+                            "prefill L=1024")
+    oo, ol = oracle.sparse_mla(h["q"], h["kv"], gidx, cfg.sm_scale)
+    check_mla(bf16_to_f64(out), _np(lse), oo, ol, "prefill L=1024")
+
+
+def test_prefill_dense_fallback_equals_dense_attention(dsa):
+    """Every row sees <= k = 2048 tokens: the selection is everything and the output is
+    exact causal attention (sampled rows against the dense oracle)."""
+    cfg = WORKLOADS["prefill-L2048-k2048-dense"]
+    inp = make_prefill(cfg)
+    h, d = host_arrays(inp), to_device(inp)
+    idx = torch.empty((cfg.L, cfg.k), dtype=torch.int32, device="cuda")
+    out, lse, _ = dsa.dsa_prefill(d["q8"], d["qs"], d["w"], d["k8"], d["ks"], d["q"], d["kv"],
+                                  cfg.k, 0, cfg.score_scale, cfg.sm_scale, idx_out=idx)
+    torch.cuda.synchronize()
+    gidx = _np(idx)
+    want = np.where(np.arange(cfg.k)[None, :] <= np.arange(cfg.L)[:, None],
+                    np.arange(cfg.k)[None, :], -1)
+    assert np.array_equal(gidx, want)
+    rows = np.array([0, 1, 2, 31, 32, 33, 777, 1500, 2046, 2047])
+    do, dl = oracle.dense_mla(h["q"], h["kv"], 0, cfg.sm_scale, rows=rows)
+    check_mla(bf16_to_f64(out[rows]), _np(lse[rows]), do, dl, "dense fallback")
+
+
+def test_prefill_chunk_with_q_pos0_matches_full(dsa):
+    cfg = _cfg(700, 96, 64, 32, seed=44)
+    d = to_device(make_prefill(cfg))
+    args = lambda sl: (d["q8"][sl], d["qs"][sl], d["w"][sl], d["k8"], d["ks"], d["q"][sl], d["kv"])
+    full_idx = torch.empty((700, 96), dtype=torch.int32, device="cuda")
+    fo, fl, _ = dsa.dsa_prefill(*args(slice(0, 700)), 96, 0, cfg.score_scale, cfg.sm_scale,
+                                idx_out=full_idx)
+    part_idx = torch.empty((450, 96), dtype=torch.int32, device="cuda")
+    po, pl, _ = dsa.dsa_prefill(*args(slice(250, 700)), 96, 250, cfg.score_scale, cfg.sm_scale,
+                                idx_out=part_idx)
+    torch.cuda.synchronize()
+    assert torch.equal(full_idx[250:], part_idx)
+    assert torch.equal(fo[250:], po) and torch.equal(fl[250:], pl)
+
+
+def test_prefill_bitwise_repeatable(dsa):
+    cfg = _cfg(1500, 256, 64, 64, seed=9)
+    d = to_device(make_prefill(cfg))
+    outs = []
+    for _ in range(2):
+        idx = torch.empty((1500, 256), dtype=torch.int32, device="cuda")
+        o, l, _ = dsa.dsa_prefill(d["q8"], d["qs"], d["w"], d["k8"], d["ks"], d["q"], d["kv"],
+                                  256, 0, cfg.score_scale, cfg.sm_scale, idx_out=idx)
+        outs.append((o.clone(), l.clone(), idx.clone()))
+    torch.cuda.synchronize()
+    for a, b in zip(outs[0], outs[1]):
+        assert torch.equal(a, b)
+
+
+def _sampled_rows(L, k, planted, extra, seed):
+    rng = np.random.default_rng(seed)
+    fixed = [0, 1, k - 2, k - 1, k, k + 1, L - 2, L - 1]
+    tgt = [int(t) for t in planted[:, 1][:8]] if len(planted) else []
+    rnd = rng.integers(k, L, extra).tolist()
+    return np.unique(np.array(fixed + tgt + rnd))
+
+
+@pytest.mark.parametrize("name,extra", [("prefill-L32768-k2048", 10),
+                                        ("prefill-L131072-k2048", 4)])
+def test_prefill_long_context_sampled_rows(dsa, name, extra):
+    cfg = WORKLOADS[name]
+    d = make_prefill(cfg, device="cuda")
+    idx = torch.empty((cfg.L, cfg.k), dtype=torch.int32, device="cuda")
+    out, lse, _ = dsa.dsa_prefill(d["q8"], d["qs"], d["w"], d["k8"], d["ks"], d["q"], d["kv"],
+                                  cfg.k, 0, cfg.score_scale, cfg.sm_scale, idx_out=idx)
+    torch.cuda.synchronize()
+    planted = _np(d["planted"])
+    rows = _sampled_rows(cfg.L, cfg.k, planted, extra, cfg.seed)
+    gidx = _np(idx[torch.from_numpy(rows).cuda()])
+    full = np.zeros((cfg.L, cfg.k), np.int32)
+    full[rows] = gidx
+    sub_out = out[torch.from_numpy(rows).cuda()]
+    sub_lse = lse[torch.from_numpy(rows).cuda()]
+    sub = dict(d)
+    ora = _oracle_rows_from_device(d, rows, cfg.k)
+    kv = _u16(d["kv"])
+    for i, r in enumerate(ora):
+        t = r["t"]
+        check_indices_near_ties(gidx[i:i + 1], r["idx"][None], r["scores"][None],
+                                r["bound"][None], [r["n"]], cfg.k, "%s row %d" % (name, t))
+        oo, ol = oracle.sparse_mla(_u16(d["q"][t:t + 1]), kv, gidx[i:i + 1], cfg.sm_scale)
+        check_mla(bf16_to_f64(sub_out[i:i + 1]), _np(sub_lse[i:i + 1]), oo, ol,
+                  "%s row %d" % (name, t))
+    # planted tokens are found by the rows they were aimed at
+    for s, t, _h in planted[:64]:
+        assert s in set(_np(idx[int(t)]).tolist()), "planted key %d missed by row %d" % (s, t)
+    del sub
+
+
+# ---------------------------------------------------------------------------- decode
+
+def _check_decode(dsa, inp, seqs, what):
+    d = inp if inp["q"].is_cuda else to_device(inp)
+    B, k = inp["B"], inp["k"]
+    idx = torch.empty((B, k), dtype=torch.int32, device="cuda")
+    out, lse, _ = dsa.dsa_decode(d["seq_start"], inp["max_len"], d["q8"], d["qs"], d["w"],
+                                 d["k8"], d["ks"], d["q"], d["kv"], k, inp["score_scale"],
+                                 inp["sm_scale"], idx_out=idx)
+    torch.cuda.synchronize()
+    st = _np(d["seq_start"])
+    gidx = _np(idx)
+    for b in seqs:
+        a, e = int(st[b]), int(st[b + 1])
+        Lb = e - a
+        sc, bd = oracle.index_scores(_np(d["q8"][b:b + 1]), _np(d["qs"][b:b + 1]),
+                                     _np(d["w"][b:b + 1]), _np(d["k8"][a:e]), _np(d["ks"][a:e]),
+                                     Lb - 1, inp["score_scale"], with_bound=True)
+        oidx = oracle.topk(sc, [Lb], k)
+        check_indices_near_ties(gidx[b:b + 1], oidx, sc, bd, [Lb], k, "%s seq %d" % (what, b))
+        oo, ol = oracle.sparse_mla(_u16(d["q"][b:b + 1]), _u16(d["kv"][a:e]), gidx[b:b + 1],
+                                   inp["sm_scale"])
+        check_mla(bf16_to_f64(out[b:b + 1]), _np(lse[b:b + 1]), oo, ol, "%s seq %d" % (what, b))
+
+
+@pytest.mark.parametrize("B,lo,hi,k,H_I,H", [(8, 1, 9000, 2048, 64, 128), (5, 3, 700, 64, 4, 16),
+                                             (3, 1, 40, 8, 128, 8)])
+def test_decode_every_sequence(dsa, B, lo, hi, k, H_I, H):
+    cfg = DecodeCfg("case", B=B, len_lo=lo, len_hi=hi, k=k, H_I=H_I, H=H, w_std=H_I ** -0.5,
+                    seed=B * 31 + k)
+    inp = make_decode(cfg)
+    _check_decode(dsa, inp, range(B), "decode B=%d k=%d" % (B, k))
+
+
+def test_decode_64_sequences_to_128k_sampled(dsa):
+    cfg = WORKLOADS["decode-B64-L4096-131072-k2048"]
+    inp = make_decode(cfg, device="cuda")
+    lens = _np(inp["lens"])
+    seqs = sorted({int(np.argmax(lens)), int(np.argmin(lens)), 0, 63, 17})
+    _check_decode(dsa, inp, seqs, "decode B=64")
