@@ -6,7 +6,10 @@
 * top-k on the GPU's own fp32 scores: exactly the oracle's selection of the same values.
 * end-to-end indices: same count min(k, n_t); every position in the symmetric difference
   has an oracle score within tol(tau) of the oracle's k-th score tau (a near-tie).
-* sparse MLA, against the oracle run on the GPU's own indices: max |out_g - out_o| <= 1e-2,
+* sparse MLA, against the oracle run on the GPU's own indices: |out_g - out_o| <= 1e-2 +
+  2^-8 |out_o| per element (1e-2 for O(1) outputs plus the round-to-nearest bf16 rounding of
+  the output itself: bf16 keeps 8 significant bits, so an output of magnitude 2..4, which
+  rows averaging only a few latent rows produce, cannot be stored closer than 2^-8 |o|),
   per (row, head) ||delta||_2 / ||o||_2 <= 1e-2, |delta lse| <= 1e-3.
 """
 from __future__ import annotations
@@ -19,6 +22,7 @@ import oracle
 SCORE_RTOL = 1e-3
 SCORE_FLOOR = 2.0 ** -16
 OUT_ATOL = 1e-2
+OUT_BF16_REL = 2.0 ** -8
 OUT_REL_L2 = 1e-2
 LSE_ATOL = 1e-3
 
@@ -80,7 +84,9 @@ def check_indices_near_ties(gpu_idx, ora_idx, ora_scores, bound, n_vis, k: int, 
 def check_mla(out_g: np.ndarray, lse_g: np.ndarray, out_o: np.ndarray, lse_o: np.ndarray,
               what=""):
     d = np.abs(out_g - out_o)
-    assert d.max(initial=0.0) <= OUT_ATOL, "%s: max |dout| %.3g" % (what, d.max())
+    lim = OUT_ATOL + OUT_BF16_REL * np.abs(out_o)
+    assert np.all(d <= lim), "%s: |dout| %.3g exceeds 1e-2 + 2^-8|o| (|o| = %.3g)" % (
+        what, d.max(), np.abs(out_o).ravel()[np.argmax((d - lim).ravel())])
     num = np.sqrt(((out_g - out_o) ** 2).sum(-1))
     den = np.sqrt((out_o ** 2).sum(-1))
     rel = num / np.maximum(den, 1e-30)
