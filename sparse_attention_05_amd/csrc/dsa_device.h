@@ -60,6 +60,22 @@ __device__ __forceinline__ uint32_t score_key(float f)
 
 __device__ __forceinline__ float shfl_xor_f(float v, int m) { return __shfl_xor(v, m, 64); }
 
+// Reduce-scatter helpers on gfx950's lane-swap instructions.
+// fold32(x, y): lanes 0-31 get x summed over lanes l and l+32, lanes 32-63 get y so summed.
+__device__ __forceinline__ float fold32(float x, float y)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(y),
+                                                    false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+// fold16(x, y): even 16-lane rows get x summed over the row pair (0,1) or (2,3), odd rows y.
+__device__ __forceinline__ float fold16(float x, float y)
+{
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(y),
+                                                    false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 __device__ __forceinline__ unsigned long long lanemask_lt(int lane)
 {
     return (lane == 0) ? 0ull : (~0ull >> (64 - lane));

@@ -36,7 +36,7 @@ __device__ __forceinline__ void reduce_heads(const v4f (&acc)[2][IP_NT],
                                              Emit&& emit)
 {
     const int g = lane >> 4;
-    const bool upper = lane >= 32, odd = (g & 1) != 0;
+    const bool odd = (g & 1) != 0;
     if constexpr (HI >= 16) {
         constexpr int TPW = IP_ROWS / HI;      // tokens per wave
         constexpr int TPT = HI / 16;           // tiles per token
@@ -60,25 +60,19 @@ __device__ __forceinline__ void reduce_heads(const v4f (&acc)[2][IP_NT],
         // step 1: lanes 0-31 keep partials [0, N1), lanes 32-63 keep [N1, NO)
         float Q[N1];
 #pragma unroll
-        for (int i = 0; i < N1; ++i) {
-            const float keep = upper ? P[N1 + i] : P[i];
-            const float send = upper ? P[i] : P[N1 + i];
-            Q[i] = keep + shfl_xor_f(send, 32);
-        }
+        for (int i = 0; i < N1; ++i) Q[i] = fold32(P[i], P[N1 + i]);
         if constexpr (N1 >= 2) {
             // step 2: even lane groups keep [0, N2), odd keep [N2, N1) -> group g owns
             // outputs g*N2 .. g*N2 + N2 - 1, each now summed over all four groups
             constexpr int N2 = N1 / 2;
 #pragma unroll
             for (int i = 0; i < N2; ++i) {
-                const float keep = odd ? Q[N2 + i] : Q[i];
-                const float send = odd ? Q[i] : Q[N2 + i];
-                const float v = keep + shfl_xor_f(send, 16);
+                const float v = fold16(Q[i], Q[N2 + i]);
                 const int o = g * N2 + i;
                 emit(o >> 1, o & 1, v);
             }
         } else {
-            const float v = Q[0] + shfl_xor_f(Q[0], 16);
+            const float v = fold16(Q[0], Q[0]);
             if (!odd) emit(0, g >> 1, v);
         }
     } else if constexpr (HI == 8) {
@@ -91,9 +85,7 @@ __device__ __forceinline__ void reduce_heads(const v4f (&acc)[2][IP_NT],
                 p0 = fmaf(wp[j][r], fmaxf(acc[0][j][r], 0.f), p0);
                 p1 = fmaf(wp[j][r], fmaxf(acc[1][j][r], 0.f), p1);
             }
-            const float keep = odd ? p1 : p0;
-            const float send = odd ? p0 : p1;
-            emit(2 * j + (g >> 1), g & 1, keep + shfl_xor_f(send, 16));
+            emit(2 * j + (g >> 1), g & 1, fold16(p0, p1));
         }
     } else {
         // HI in {1, 2, 4}: the lane's four rows hold 4/HI whole tokens
@@ -254,7 +246,6 @@ __global__ __launch_bounds__(ID_WAVES * 64) void indexer_decode_kernel(
     constexpr int NTQ = HI >= 16 ? HI / 16 : 1;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int g = lane >> 4, c16 = lane & 15;
-    const bool upper = lane >= 32, odd = (g & 1) != 0;
     const int b = blockIdx.y;
     const int64_t a = seq_start[b];
     const int Lb = (int)(seq_start[b + 1] - a);
@@ -306,15 +297,8 @@ __global__ __launch_bounds__(ID_WAVES * 64) void indexer_decode_kernel(
             P[kb] = s;
         }
         // reduce-scatter over the four lane groups: group g ends with key block g
-        float Q0, Q1;
-        {
-            const float k0 = upper ? P[2] : P[0], s0v = upper ? P[0] : P[2];
-            const float k1 = upper ? P[3] : P[1], s1v = upper ? P[1] : P[3];
-            Q0 = k0 + shfl_xor_f(s0v, 32);
-            Q1 = k1 + shfl_xor_f(s1v, 32);
-        }
-        const float keep = odd ? Q1 : Q0, send = odd ? Q0 : Q1;
-        const float v = keep + shfl_xor_f(send, 16);
+        const float Q0 = fold32(P[0], P[2]), Q1 = fold32(P[1], P[3]);
+        const float v = fold16(Q0, Q1);
         const int key = s0 + g * 16 + c16;
         if (key < Lb) scores[a + key] = v * ks[a + key];
     }

@@ -5,27 +5,49 @@
 // 512-d latent doubling as the value (《DeepSeek-V3.2-Exp模型优势与 DSA 工作原理》 §3 稀疏
 // MLA and §4 步骤四; 《狂降75%！…》 §三 第四步).
 //
-// One workgroup handles one query row for all heads (ceil(H/16) waves, 16 heads each)
-// over a contiguous slice of its index list.  Per 32-key tile the workgroup gathers the
-// selected 1152-byte rows into LDS twice: row-major (the K operand of S^T = K Q^T, whose
-// contraction runs along a row), and, for the 512 latent dims, transposed into 4-key
-// groups (the V operand of O = P V, whose contraction runs across rows).  Computing S^T
-// rather than S leaves P in registers exactly where the A operand of P V needs it.
-// Softmax is online in the exp2 domain with fp32 statistics; P is rounded to bf16.
+// One workgroup handles one query row for all heads (ceil(H/32) waves, 32 heads each) over
+// a contiguous slice of its index list.  The slice's indices are staged in LDS; the selected
+// 1152-byte rows are gathered 64 at a time by direct global->LDS loads into a double-buffered
+// tile (16-byte chunks XOR-swizzled by row), so the next tile streams in while the current
+// one is used.  Per 32-key half: S^T = K Q^T on bf16 MFMA (A = gathered rows, B = Q^T held in
+// registers), online softmax in the exp2 domain with fp32 statistics, then O += P V with P
+// already in the A-operand layout and V read from the same row-major tile through the LDS
+// transpose read (ds_read_b64_tr_b16), so no transposed copy of V is ever built.
 #include "dsa_device.h"
 #include "kernels.h"
 
 namespace dsa {
 namespace {
 
-constexpr int MT = 32;                       // keys per tile
-constexpr int KROW = 576 * 2 + 16;           // LDS bytes per gathered row (+16 B skew)
-constexpr int K_BYTES = MT * KROW;           // row-major tile
-constexpr int VT_BYTES = (MT / 4) * 512 * 8; // [key quad][dim][4 keys] bf16
+constexpr int MT = 64;                       // keys per tile
+constexpr int CH = 72;                       // 16-byte chunks per 1152-byte row
+constexpr int TILE_BYTES = MT * CH * 16;     // 73,728
+constexpr int IDX_SEG = 2048;                // indices staged in LDS at a time
+#ifndef MLA_NHG
+#define MLA_NHG 1                            // 16-head groups per wave
+#endif
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
 
-template <int NW>
+typedef short v4s __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) v4s lds_v4s_t;
+typedef __attribute__((address_space(1))) void gbl_void_t;
+
+__device__ __forceinline__ u32x2 ds_read_tr(const uint8_t* p)
+{
+    const v4s v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_t*)(p));
+    return __builtin_bit_cast(u32x2, v);
+}
+
+// tile byte offset of dims [8c, 8c + 8) of row r (chunk c of the 72 per row).  The XOR only
+// touches the low three chunk bits, so for c = 8a + b: offset = row_base(r) + 128 a +
+// 16 (b ^ (r & 7)) -- a per-lane base plus an immediate.
+__device__ __forceinline__ int row_base(int r) { return r * CH * 16; }
+__device__ __forceinline__ int sub_off(int r, int b) { return (b ^ (r & 7)) << 4; }
+
+// NW waves per workgroup, NHG groups of 16 heads per wave.
+template <int NW, int NHG>
 __global__ __launch_bounds__(NW * 64) void sparse_mla_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
     const int32_t* __restrict__ idx, const int64_t* __restrict__ seq_start, int L, int H, int k,
@@ -33,15 +55,13 @@ __global__ __launch_bounds__(NW * 64) void sparse_mla_kernel(
     float* __restrict__ part_o, float* __restrict__ part_lse)
 {
     constexpr int NT = NW * 64;
-    __shared__ __attribute__((aligned(16))) uint8_t s_k[K_BYTES];
-    __shared__ __attribute__((aligned(16))) uint8_t s_vt[VT_BYTES];
-    __shared__ int s_idx[MT];
+    __shared__ __attribute__((aligned(16))) uint8_t s_tile[2][TILE_BYTES];
+    __shared__ int s_idx[IDX_SEG];
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int g = lane >> 4, c16 = lane & 15;
     const int row = blockIdx.x, split = blockIdx.y;
-    const int h0 = wave * 16;
-    const int head = h0 + c16;                         // this lane's head in S^T / softmax
+    const int h0 = wave * 16 * NHG;                    // this wave: heads h0 .. h0 + 16 NHG - 1
 
     int64_t kv_base = 0;
     int Lr = L;
@@ -53,169 +73,208 @@ __global__ __launch_bounds__(NW * 64) void sparse_mla_kernel(
     const int per = (k + splits - 1) / splits;
     const int jbeg = split * per;
     const int jend = min(k, jbeg + per);
-    const int ntile = jend > jbeg ? (jend - jbeg + MT - 1) / MT : 0;
 
-    // B operand of S^T: Q^T, lane holds head c16, dims [32s + 8g, +8) for s = 0..17
-    u32x4 qreg[18];
-    {
+    // B operands of S^T: Q^T for head groups hg = 0, 1 (heads h0 + 16 hg + c16),
+    // dims [32s + 8g, +8) for s = 0..17
+    u32x4 qreg[NHG][18];
+#pragma unroll
+    for (int hg = 0; hg < NHG; ++hg) {
+        const int head = h0 + 16 * hg + c16;
         const bool hv = head < H;
         const uint16_t* qh = q + ((int64_t)row * H + (hv ? head : 0)) * 576;
 #pragma unroll
-        for (int s = 0; s < 18; ++s) {
-            qreg[s] = hv ? *reinterpret_cast<const u32x4*>(qh + 32 * s + 8 * g)
-                         : u32x4{0u, 0u, 0u, 0u};
-        }
+        for (int s = 0; s < 18; ++s)
+            qreg[hg][s] = hv ? *reinterpret_cast<const u32x4*>(qh + 32 * s + 8 * g)
+                             : u32x4{0u, 0u, 0u, 0u};
     }
 
-    v4f O[32];
+    v4f O[NHG][32];                                    // O[hg][n]: heads 16hg + 4g + r, dim 16n + c16
 #pragma unroll
-    for (int n = 0; n < 32; ++n) O[n] = v4f{0.f, 0.f, 0.f, 0.f};
-    float m_run = -__builtin_huge_valf(), l_run = 0.f;
+    for (int hg = 0; hg < NHG; ++hg)
+#pragma unroll
+        for (int n = 0; n < 32; ++n) O[hg][n] = v4f{0.f, 0.f, 0.f, 0.f};
+    float m_run[NHG], l_run[NHG];
+#pragma unroll
+    for (int hg = 0; hg < NHG; ++hg) {
+        m_run[hg] = -__builtin_huge_valf();
+        l_run[hg] = 0.f;
+    }
     const float scale2 = sm_scale * LOG2E;
 
-#pragma unroll 1
-    for (int tile = 0; tile < ntile; ++tile) {
-        const int j0 = jbeg + tile * MT;
-        if (tid < MT) {
-            int s = -1;
-            if (j0 + tid < jend) s = idx[(int64_t)row * k + j0 + tid];
-            s_idx[tid] = (s >= 0 && s < Lr) ? s : -1;
+    // gather of tile t: 72 wave-instructions of 64 x 16 B; instruction qi fills tile bytes
+    // [1024 qi, +1024), lane l the chunk slot 64 qi + l
+    auto issue = [&](int seg_n, int t, int buf) {
+        for (int qi = wave; qi < MT * CH / 64; qi += NW) {
+            const int slot = qi * 64 + lane;
+            const int r = slot / CH, cs = slot - r * CH;
+            const int c = cs ^ (r & 7);
+            const int j = t * MT + r;
+            const int s = j < seg_n ? s_idx[j] : -1;
+            const uint16_t* src = kvr + (int64_t)(s >= 0 ? s : 0) * 576 + c * 8;
+            __builtin_amdgcn_global_load_lds((gbl_void_t*)src,
+                                             (lds_void_t*)(&s_tile[buf][qi * 1024]), 16, 0, 0);
         }
-        __syncthreads();
-        // gather: item = (key quad, 16-byte chunk of the 512 latent dims) -> 4 rows' chunks,
-        // stored row-major and transposed; then the 64 rope dims row-major only.
-        for (int it = tid; it < (MT / 4) * 64; it += NT) {
-            const int quad = it >> 6, ch = it & 63;
-            u32x4 v[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int s = s_idx[quad * 4 + e];
-                v[e] = s >= 0 ? *reinterpret_cast<const u32x4*>(kvr + (int64_t)s * 576 + ch * 8)
-                              : u32x4{0u, 0u, 0u, 0u};
-                *reinterpret_cast<u32x4*>(&s_k[(quad * 4 + e) * KROW + ch * 16]) = v[e];
-            }
-            // transpose 4 keys x 8 dims -> 8 dims x 4 keys (one 8-byte word per dim)
-#pragma unroll
-            for (int dd = 0; dd < 8; ++dd) {
-                const int wsel = dd >> 1;
-                const bool hi = dd & 1;
-                auto pick = [&](const u32x4& x) -> uint32_t {
-                    return hi ? (x[wsel] >> 16) : (x[wsel] & 0xFFFFu);
-                };
-                u32x2 word;
-                word[0] = pick(v[0]) | (pick(v[1]) << 16);
-                word[1] = pick(v[2]) | (pick(v[3]) << 16);
-                *reinterpret_cast<u32x2*>(&s_vt[(quad * 512 + ch * 8 + dd) * 8]) = word;
-            }
-        }
-        for (int it = tid; it < MT * 8; it += NT) {
-            const int key = it >> 3, ch = 64 + (it & 7);
-            const int s = s_idx[key];
-            const u32x4 v = s >= 0 ? *reinterpret_cast<const u32x4*>(kvr + (int64_t)s * 576 + ch * 8)
-                                   : u32x4{0u, 0u, 0u, 0u};
-            *reinterpret_cast<u32x4*>(&s_k[key * KROW + ch * 16]) = v;
-        }
-        __syncthreads();
+    };
 
-        if (h0 < H) {
-            // S^T[key][head] for two 16-key halves: A = gathered rows, B = Q^T
-            v4f S[2];
-#pragma unroll
-            for (int kt = 0; kt < 2; ++kt) {
-                S[kt] = v4f{0.f, 0.f, 0.f, 0.f};
-                const uint8_t* krow = &s_k[(kt * 16 + c16) * KROW];
-#pragma unroll
-                for (int s = 0; s < 18; ++s) {
-                    const u32x4 a = *reinterpret_cast<const u32x4*>(krow + (32 * s + 8 * g) * 2);
-                    S[kt] = mfma_bf16(as_bf16x8(a), as_bf16x8(qreg[s]), S[kt]);
-                }
-            }
-            // lane: head c16, keys kt*16 + 4g + r
-            float x[2][4];
-            float mloc = -__builtin_huge_valf();
-#pragma unroll
-            for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const bool valid = s_idx[kt * 16 + 4 * g + r] >= 0;
-                    x[kt][r] = valid ? S[kt][r] * scale2 : -__builtin_huge_valf();
-                    mloc = fmaxf(mloc, x[kt][r]);
-                }
-            mloc = fmaxf(mloc, shfl_xor_f(mloc, 16));
-            mloc = fmaxf(mloc, shfl_xor_f(mloc, 32));
-            const float m_new = fmaxf(m_run, mloc);
-            const bool any = m_new != -__builtin_huge_valf();
-            const float alpha = any ? exp2f(m_run - m_new) : 1.f;
-            float p[2][4];
-            float psum = 0.f;
-#pragma unroll
-            for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    p[kt][r] = any ? exp2f(x[kt][r] - m_new) : 0.f;
-                    psum += p[kt][r];
-                }
-            l_run = l_run * alpha + psum;
-            m_run = m_new;
-            // O rows are heads 4g + r: fetch their rescale factors
-            float ar[4];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) ar[r] = __shfl(alpha, 4 * g + r, 64);
-#pragma unroll
-            for (int n = 0; n < 32; ++n)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) O[n][r] *= ar[r];
-            // A operand of P V: head c16, K = keys {4g..4g+3} of each half
-            u32x4 pa;
-            pa[0] = pack_bf16x2(p[0][0], p[0][1]);
-            pa[1] = pack_bf16x2(p[0][2], p[0][3]);
-            pa[2] = pack_bf16x2(p[1][0], p[1][1]);
-            pa[3] = pack_bf16x2(p[1][2], p[1][3]);
-            const v8bf pav = as_bf16x8(pa);
-#pragma unroll
-            for (int n = 0; n < 32; ++n) {
-                const int d = 16 * n + c16;
-                const u32x2 lo = *reinterpret_cast<const u32x2*>(&s_vt[(g * 512 + d) * 8]);
-                const u32x2 hi = *reinterpret_cast<const u32x2*>(&s_vt[((4 + g) * 512 + d) * 8]);
-                u32x4 vb;
-                vb[0] = lo[0]; vb[1] = lo[1]; vb[2] = hi[0]; vb[3] = hi[1];
-                O[n] = mfma_bf16(pav, as_bf16x8(vb), O[n]);
-            }
+#pragma unroll 1
+    for (int seg0 = jbeg; seg0 < jend; seg0 += IDX_SEG) {
+        const int seg_n = min(IDX_SEG, jend - seg0);
+        __syncthreads();                               // previous segment fully consumed
+        for (int j = tid; j < seg_n; j += NT) {
+            const int s = idx[(int64_t)row * k + seg0 + j];
+            s_idx[j] = (s >= 0 && s < Lr) ? s : -1;
         }
         __syncthreads();
+        const int ntile = (seg_n + MT - 1) / MT;
+        issue(seg_n, 0, 0);
+#pragma unroll 1
+        for (int t = 0; t < ntile; ++t) {
+            __builtin_amdgcn_s_waitcnt(0);             // this wave's part of tile t landed
+            __syncthreads();                           // everyone's part; tile t-1 consumed
+            if (t + 1 < ntile) issue(seg_n, t + 1, (t + 1) & 1);
+            const uint8_t* tb = s_tile[t & 1];
+#pragma unroll 1
+            for (int half = 0; half < 2; ++half) {
+                // S^T[key][head] for keys 32 half + 16 kt + (4g + r), both head groups;
+                // A = row 32 half + 16 kt + c16, dims [32s + 8g, +8): chunk 4s + g
+                v4f S[2][NHG];
+#pragma unroll
+                for (int kt = 0; kt < 2; ++kt) {
+                    const int r = half * 32 + kt * 16 + c16;
+                    const uint8_t* rb = tb + row_base(r);
+                    const int o0 = sub_off(r, g), o1 = sub_off(r, 4 + g);
+#pragma unroll
+                    for (int hg = 0; hg < NHG; ++hg) S[kt][hg] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int s = 0; s < 18; ++s) {
+                        const u32x4 a = *reinterpret_cast<const u32x4*>(
+                            rb + 128 * (s >> 1) + ((s & 1) ? o1 : o0));
+#pragma unroll
+                        for (int hg = 0; hg < NHG; ++hg)
+                            S[kt][hg] = mfma_bf16(as_bf16x8(a), as_bf16x8(qreg[hg][s]), S[kt][hg]);
+                    }
+                }
+                bool valid[2][4];
+#pragma unroll
+                for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int j = t * MT + half * 32 + kt * 16 + 4 * g + r;
+                        valid[kt][r] = j < seg_n && s_idx[j] >= 0;
+                    }
+                u32x4 pa[NHG];
+                bool rescale = false;
+                float alpha[NHG];
+#pragma unroll
+                for (int hg = 0; hg < NHG; ++hg) {
+                    float x[2][4];
+                    float mloc = -__builtin_huge_valf();
+#pragma unroll
+                    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            x[kt][r] = valid[kt][r] ? S[kt][hg][r] * scale2 : -__builtin_huge_valf();
+                            mloc = fmaxf(mloc, x[kt][r]);
+                        }
+                    mloc = fmaxf(mloc, shfl_xor_f(mloc, 16));
+                    mloc = fmaxf(mloc, shfl_xor_f(mloc, 32));
+                    const float m_new = fmaxf(m_run[hg], mloc);
+                    const bool any = m_new != -__builtin_huge_valf();
+                    alpha[hg] = any ? exp2f(m_run[hg] - m_new) : 1.f;
+                    rescale |= alpha[hg] != 1.f;
+                    float p[2][4];
+                    float psum = 0.f;
+#pragma unroll
+                    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            p[kt][r] = any ? exp2f(x[kt][r] - m_new) : 0.f;
+                            psum += p[kt][r];
+                        }
+                    l_run[hg] = l_run[hg] * alpha[hg] + psum;
+                    m_run[hg] = m_new;
+                    pa[hg][0] = pack_bf16x2(p[0][0], p[0][1]);
+                    pa[hg][1] = pack_bf16x2(p[0][2], p[0][3]);
+                    pa[hg][2] = pack_bf16x2(p[1][0], p[1][1]);
+                    pa[hg][3] = pack_bf16x2(p[1][2], p[1][3]);
+                }
+                if (__any(rescale)) {                  // running max moved for some head
+#pragma unroll
+                    for (int hg = 0; hg < NHG; ++hg) {
+                        float ar[4];
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) ar[r] = __shfl(alpha[hg], 4 * g + r, 64);
+#pragma unroll
+                        for (int n = 0; n < 32; ++n)
+#pragma unroll
+                            for (int r = 0; r < 4; ++r) O[hg][n][r] *= ar[r];
+                    }
+                }
+                v8bf pav[NHG];
+#pragma unroll
+                for (int hg = 0; hg < NHG; ++hg) pav[hg] = as_bf16x8(pa[hg]);
+                // V operand: column 16n + c16, keys 32 half + 16 kt + 4g + r, by transpose reads:
+                // lane (g, i) addresses row 32 half + 16 kt + 4g + i/4, dims 16n + 4(i%4) .. +3,
+                // i.e. chunk 2n + (i%4)/2 = 8(n/4) + (2(n%4) + (i%4)/2), byte 8 (i%2) within it
+                const int rv0 = half * 32 + 4 * g + (c16 >> 2), rv1 = rv0 + 16;
+                const int cpart = (c16 & 3) >> 1, boff = (c16 & 1) * 8;
+                const uint8_t* vb0 = tb + row_base(rv0) + boff;
+                const uint8_t* vb1 = tb + row_base(rv1) + boff;
+                int vo0[4], vo1[4];
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    vo0[m] = sub_off(rv0, 2 * m + cpart);
+                    vo1[m] = sub_off(rv1, 2 * m + cpart);
+                }
+#pragma unroll
+                for (int n = 0; n < 32; ++n) {
+                    const u32x2 lo = ds_read_tr(vb0 + 128 * (n >> 2) + vo0[n & 3]);
+                    const u32x2 hi = ds_read_tr(vb1 + 128 * (n >> 2) + vo1[n & 3]);
+                    u32x4 vb;
+                    vb[0] = lo[0]; vb[1] = lo[1]; vb[2] = hi[0]; vb[3] = hi[1];
+                    const v8bf vbv = as_bf16x8(vb);
+#pragma unroll
+                    for (int hg = 0; hg < NHG; ++hg) O[hg][n] = mfma_bf16(pav[hg], vbv, O[hg][n]);
+                }
+            }
+        }
     }
 
-    if (h0 >= H) return;
-    // totals per head c16, then per O row (head 4g + r)
-    float l_tot = l_run + shfl_xor_f(l_run, 16);
-    l_tot += shfl_xor_f(l_tot, 32);
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    const float my_lse = l_tot > 0.f ? m_run * LN2 + logf(l_tot) : -__builtin_huge_valf();
-    float ir[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) ir[r] = __shfl(inv, 4 * g + r, 64);
-
-    if (splits == 1) {
+    for (int hg = 0; hg < NHG; ++hg) {
+        const int hb = h0 + 16 * hg;                   // this head group's first head
+        if (hb >= H) break;
+        const int head = hb + c16;
+        float l_tot = l_run[hg] + shfl_xor_f(l_run[hg], 16);
+        l_tot += shfl_xor_f(l_tot, 32);
+        const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+        const float my_lse = l_tot > 0.f ? m_run[hg] * LN2 + logf(l_tot) : -__builtin_huge_valf();
+        float ir[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int hh = h0 + 4 * g + r;
-            if (hh >= H) continue;
-            uint16_t* orow = out + ((int64_t)row * H + hh) * 512;
+        for (int r = 0; r < 4; ++r) ir[r] = __shfl(inv, 4 * g + r, 64);
+        if (splits == 1) {
 #pragma unroll
-            for (int n = 0; n < 32; ++n) orow[16 * n + c16] = (uint16_t)bf16_bits(O[n][r] * ir[r]);
+            for (int r = 0; r < 4; ++r) {
+                const int hh = hb + 4 * g + r;
+                if (hh >= H) continue;
+                uint16_t* orow = out + ((int64_t)row * H + hh) * 512;
+#pragma unroll
+                for (int n = 0; n < 32; ++n)
+                    orow[16 * n + c16] = (uint16_t)bf16_bits(O[hg][n][r] * ir[r]);
+            }
+            if (lse && g == 0 && head < H) lse[(int64_t)row * H + head] = my_lse;
+        } else {
+            const int64_t pb = ((int64_t)row * splits + split) * H;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int hh = hb + 4 * g + r;
+                if (hh >= H) continue;
+                float* orow = part_o + (pb + hh) * 512;
+#pragma unroll
+                for (int n = 0; n < 32; ++n) orow[16 * n + c16] = O[hg][n][r] * ir[r];
+            }
+            if (g == 0 && head < H) part_lse[pb + head] = my_lse;
         }
-        if (lse && g == 0 && head < H) lse[(int64_t)row * H + head] = my_lse;
-    } else {
-        const int64_t pb = ((int64_t)row * splits + split) * H;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int hh = h0 + 4 * g + r;
-            if (hh >= H) continue;
-            float* orow = part_o + (pb + hh) * 512;
-#pragma unroll
-            for (int n = 0; n < 32; ++n) orow[16 * n + c16] = O[n][r] * ir[r];
-        }
-        if (g == 0 && head < H) part_lse[pb + head] = my_lse;
     }
 }
 
@@ -253,14 +312,15 @@ __global__ __launch_bounds__(128) void mla_combine_kernel(const float* __restric
         lse[(int64_t)row * H + hh] = den > 0.f ? mx + logf(den) : -__builtin_huge_valf();
 }
 
-template <int NW>
+template <int NW, int NHG>
 hipError_t launch_nw(const uint16_t* q, const uint16_t* kv, const int32_t* idx,
                      const int64_t* seq_start, int T, int L, int H, int k, float sm_scale,
                      int splits, uint16_t* out, float* lse, float* part_o, float* part_lse,
                      hipStream_t stream)
 {
-    hipLaunchKernelGGL(sparse_mla_kernel<NW>, dim3(T, splits), dim3(NW * 64), 0, stream, q, kv,
-                       idx, seq_start, L, H, k, sm_scale, splits, out, lse, part_o, part_lse);
+    auto kern = sparse_mla_kernel<NW, NHG>;
+    hipLaunchKernelGGL(kern, dim3(T, splits), dim3(NW * 64), 0, stream, q, kv, idx, seq_start, L,
+                       H, k, sm_scale, splits, out, lse, part_o, part_lse);
     return hipGetLastError();
 }
 
@@ -272,9 +332,9 @@ hipError_t launch_sparse_mla(const uint16_t* q, const uint16_t* kv, const int32_
                              float* part_o, float* part_lse, hipStream_t stream)
 {
     if (T <= 0) return hipSuccess;
-    const int nw = (H + 15) / 16;
+    const int nw = (H + 16 * MLA_NHG - 1) / (16 * MLA_NHG);
 #define DSA_MLA_CASE(NW) \
-    case NW: return launch_nw<NW>(q, kv, idx, seq_start, T, L, H, k, sm_scale, splits, out, lse, part_o, part_lse, stream);
+    case NW: return launch_nw<NW, MLA_NHG>(q, kv, idx, seq_start, T, L, H, k, sm_scale, splits, out, lse, part_o, part_lse, stream);
     switch (nw) {
         DSA_MLA_CASE(1) DSA_MLA_CASE(2) DSA_MLA_CASE(3) DSA_MLA_CASE(4)
         DSA_MLA_CASE(5) DSA_MLA_CASE(6) DSA_MLA_CASE(7) DSA_MLA_CASE(8)
