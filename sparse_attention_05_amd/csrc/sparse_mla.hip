@@ -5,12 +5,13 @@
 // 512-d latent doubling as the value (《DeepSeek-V3.2-Exp模型优势与 DSA 工作原理》 §3 稀疏
 // MLA and §4 步骤四; 《狂降75%！…》 §三 第四步).
 //
-// One workgroup handles one query row for all heads (ceil(H/32) waves, 32 heads each) over
+// One workgroup handles one query row for all heads (ceil(H/16) waves, 16 heads each) over
 // a contiguous slice of its index list.  The slice's indices are staged in LDS; the selected
 // 1152-byte rows are gathered 64 at a time by direct global->LDS loads into a double-buffered
 // tile (16-byte chunks XOR-swizzled by row), so the next tile streams in while the current
 // one is used.  Per 32-key half: S^T = K Q^T on bf16 MFMA (A = gathered rows, B = Q^T held in
-// registers), online softmax in the exp2 domain with fp32 statistics, then O += P V with P
+// registers), softmax in the exp2 domain with fp32 statistics against a per-head reference
+// max that moves only when exceeded by 2^8, then O += P V with P
 // already in the A-operand layout and V read from the same row-major tile through the LDS
 // transpose read (ds_read_b64_tr_b16), so no transposed copy of V is ever built.
 #include "dsa_device.h"
@@ -23,9 +24,6 @@ constexpr int MT = 64;                       // keys per tile
 constexpr int CH = 72;                       // 16-byte chunks per 1152-byte row
 constexpr int TILE_BYTES = MT * CH * 16;     // 73,728
 constexpr int IDX_SEG = 2048;                // indices staged in LDS at a time
-#ifndef MLA_NHG
-#define MLA_NHG 1                            // 16-head groups per wave
-#endif
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
 
@@ -46,8 +44,14 @@ __device__ __forceinline__ u32x2 ds_read_tr(const uint8_t* p)
 __device__ __forceinline__ int row_base(int r) { return r * CH * 16; }
 __device__ __forceinline__ int sub_off(int r, int b) { return (b ^ (r & 7)) << 4; }
 
-// NW waves per workgroup, NHG groups of 16 heads per wave.
-template <int NW, int NHG>
+// Headroom of the softmax reference: a head's reference max m moves (and O is rescaled)
+// only when a logit exceeds it by more than REF_SLACK in log2 units, so p = 2^(x - m) stays
+// below 2^REF_SLACK -- far inside bf16/fp32 range -- and O is rescaled a handful of times
+// per row instead of whenever some head's running max creeps up.
+constexpr float REF_SLACK = 8.f;
+
+// NW waves per workgroup, 16 heads per wave.
+template <int NW>
 __global__ __launch_bounds__(NW * 64) void sparse_mla_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
     const int32_t* __restrict__ idx, const int64_t* __restrict__ seq_start, int L, int H, int k,
@@ -61,7 +65,8 @@ __global__ __launch_bounds__(NW * 64) void sparse_mla_kernel(
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int g = lane >> 4, c16 = lane & 15;
     const int row = blockIdx.x, split = blockIdx.y;
-    const int h0 = wave * 16 * NHG;                    // this wave: heads h0 .. h0 + 16 NHG - 1
+    const int h0 = wave * 16;
+    const int head = h0 + c16;                         // this lane's head in S^T / softmax
 
     int64_t kv_base = 0;
     int Lr = L;
@@ -74,31 +79,21 @@ __global__ __launch_bounds__(NW * 64) void sparse_mla_kernel(
     const int jbeg = split * per;
     const int jend = min(k, jbeg + per);
 
-    // B operands of S^T: Q^T for head groups hg = 0, 1 (heads h0 + 16 hg + c16),
-    // dims [32s + 8g, +8) for s = 0..17
-    u32x4 qreg[NHG][18];
-#pragma unroll
-    for (int hg = 0; hg < NHG; ++hg) {
-        const int head = h0 + 16 * hg + c16;
+    // B operand of S^T: Q^T, lane holds head c16, dims [32s + 8g, +8) for s = 0..17
+    u32x4 qreg[18];
+    {
         const bool hv = head < H;
         const uint16_t* qh = q + ((int64_t)row * H + (hv ? head : 0)) * 576;
 #pragma unroll
         for (int s = 0; s < 18; ++s)
-            qreg[hg][s] = hv ? *reinterpret_cast<const u32x4*>(qh + 32 * s + 8 * g)
-                             : u32x4{0u, 0u, 0u, 0u};
+            qreg[s] = hv ? *reinterpret_cast<const u32x4*>(qh + 32 * s + 8 * g)
+                         : u32x4{0u, 0u, 0u, 0u};
     }
 
-    v4f O[NHG][32];                                    // O[hg][n]: heads 16hg + 4g + r, dim 16n + c16
+    v4f O[32];                                         // O[n]: heads 4g + r, dim 16n + c16
 #pragma unroll
-    for (int hg = 0; hg < NHG; ++hg)
-#pragma unroll
-        for (int n = 0; n < 32; ++n) O[hg][n] = v4f{0.f, 0.f, 0.f, 0.f};
-    float m_run[NHG], l_run[NHG];
-#pragma unroll
-    for (int hg = 0; hg < NHG; ++hg) {
-        m_run[hg] = -__builtin_huge_valf();
-        l_run[hg] = 0.f;
-    }
+    for (int n = 0; n < 32; ++n) O[n] = v4f{0.f, 0.f, 0.f, 0.f};
+    float m_ref = -__builtin_huge_valf(), l_run = 0.f;
     const float scale2 = sm_scale * LOG2E;
 
     // gather of tile t: 72 wave-instructions of 64 x 16 B; instruction qi fills tile bytes
@@ -133,86 +128,72 @@ __global__ __launch_bounds__(NW * 64) void sparse_mla_kernel(
             __syncthreads();                           // everyone's part; tile t-1 consumed
             if (t + 1 < ntile) issue(seg_n, t + 1, (t + 1) & 1);
             const uint8_t* tb = s_tile[t & 1];
+            // validity of the tile's 64 keys as one wave-uniform mask
+            const int jt = t * MT + lane;
+            const uint64_t vmask = __ballot(jt < seg_n && s_idx[jt] >= 0);
 #pragma unroll 1
             for (int half = 0; half < 2; ++half) {
-                // S^T[key][head] for keys 32 half + 16 kt + (4g + r), both head groups;
+                // S^T[key][head] for keys 32 half + 16 kt + (4g + r);
                 // A = row 32 half + 16 kt + c16, dims [32s + 8g, +8): chunk 4s + g
-                v4f S[2][NHG];
+                v4f S[2];
 #pragma unroll
                 for (int kt = 0; kt < 2; ++kt) {
                     const int r = half * 32 + kt * 16 + c16;
                     const uint8_t* rb = tb + row_base(r);
                     const int o0 = sub_off(r, g), o1 = sub_off(r, 4 + g);
-#pragma unroll
-                    for (int hg = 0; hg < NHG; ++hg) S[kt][hg] = v4f{0.f, 0.f, 0.f, 0.f};
+                    S[kt] = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                     for (int s = 0; s < 18; ++s) {
                         const u32x4 a = *reinterpret_cast<const u32x4*>(
                             rb + 128 * (s >> 1) + ((s & 1) ? o1 : o0));
-#pragma unroll
-                        for (int hg = 0; hg < NHG; ++hg)
-                            S[kt][hg] = mfma_bf16(as_bf16x8(a), as_bf16x8(qreg[hg][s]), S[kt][hg]);
+                        S[kt] = mfma_bf16(as_bf16x8(a), as_bf16x8(qreg[s]), S[kt]);
                     }
                 }
-                bool valid[2][4];
+                // softmax statistics for head c16 over this half's 32 keys
+                float x[2][4];
+                float mloc = -__builtin_huge_valf();
+#pragma unroll
+                for (int kt = 0; kt < 2; ++kt) {
+                    const uint32_t bits = (uint32_t)(vmask >> (half * 32 + kt * 16 + 4 * g));
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        x[kt][r] = ((bits >> r) & 1u) ? S[kt][r] * scale2 : -__builtin_huge_valf();
+                        mloc = fmaxf(mloc, x[kt][r]);
+                    }
+                }
+                mloc = fmaxf(mloc, shfl_xor_f(mloc, 16));
+                mloc = fmaxf(mloc, shfl_xor_f(mloc, 32));
+                // move the reference only when the new max clears the headroom
+                const bool move = mloc > m_ref + REF_SLACK;
+                const float m_new = move ? mloc : m_ref;
+                const float alpha = move ? __builtin_amdgcn_exp2f(m_ref - m_new) : 1.f;
+                const bool rescale = move && m_ref != -__builtin_huge_valf();
+                m_ref = m_new;
+                // no valid logit yet: keep exp2(-inf - m) = 0 rather than exp2(-inf + inf)
+                const float m_sub = m_new == -__builtin_huge_valf() ? 0.f : m_new;
+                float p[2][4];
+                float psum = 0.f;
 #pragma unroll
                 for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
-                        const int j = t * MT + half * 32 + kt * 16 + 4 * g + r;
-                        valid[kt][r] = j < seg_n && s_idx[j] >= 0;
+                        p[kt][r] = __builtin_amdgcn_exp2f(x[kt][r] - m_sub);
+                        psum += p[kt][r];
                     }
-                u32x4 pa[NHG];
-                bool rescale = false;
-                float alpha[NHG];
+                l_run = l_run * alpha + psum;
+                if (__any(rescale)) {                  // rare: some head's reference moved
+                    float ar[4];
 #pragma unroll
-                for (int hg = 0; hg < NHG; ++hg) {
-                    float x[2][4];
-                    float mloc = -__builtin_huge_valf();
+                    for (int r = 0; r < 4; ++r) ar[r] = __shfl(alpha, 4 * g + r, 64);
 #pragma unroll
-                    for (int kt = 0; kt < 2; ++kt)
+                    for (int n = 0; n < 32; ++n)
 #pragma unroll
-                        for (int r = 0; r < 4; ++r) {
-                            x[kt][r] = valid[kt][r] ? S[kt][hg][r] * scale2 : -__builtin_huge_valf();
-                            mloc = fmaxf(mloc, x[kt][r]);
-                        }
-                    mloc = fmaxf(mloc, shfl_xor_f(mloc, 16));
-                    mloc = fmaxf(mloc, shfl_xor_f(mloc, 32));
-                    const float m_new = fmaxf(m_run[hg], mloc);
-                    const bool any = m_new != -__builtin_huge_valf();
-                    alpha[hg] = any ? exp2f(m_run[hg] - m_new) : 1.f;
-                    rescale |= alpha[hg] != 1.f;
-                    float p[2][4];
-                    float psum = 0.f;
-#pragma unroll
-                    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) {
-                            p[kt][r] = any ? exp2f(x[kt][r] - m_new) : 0.f;
-                            psum += p[kt][r];
-                        }
-                    l_run[hg] = l_run[hg] * alpha[hg] + psum;
-                    m_run[hg] = m_new;
-                    pa[hg][0] = pack_bf16x2(p[0][0], p[0][1]);
-                    pa[hg][1] = pack_bf16x2(p[0][2], p[0][3]);
-                    pa[hg][2] = pack_bf16x2(p[1][0], p[1][1]);
-                    pa[hg][3] = pack_bf16x2(p[1][2], p[1][3]);
+                        for (int r = 0; r < 4; ++r) O[n][r] *= ar[r];
                 }
-                if (__any(rescale)) {                  // running max moved for some head
-#pragma unroll
-                    for (int hg = 0; hg < NHG; ++hg) {
-                        float ar[4];
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) ar[r] = __shfl(alpha[hg], 4 * g + r, 64);
-#pragma unroll
-                        for (int n = 0; n < 32; ++n)
-#pragma unroll
-                            for (int r = 0; r < 4; ++r) O[hg][n][r] *= ar[r];
-                    }
-                }
-                v8bf pav[NHG];
-#pragma unroll
-                for (int hg = 0; hg < NHG; ++hg) pav[hg] = as_bf16x8(pa[hg]);
+                // A operand of P V: head c16, K = keys {4g..4g+3} of each 16-key group
+                const v8bf pav = __builtin_convertvector(
+                    (v8f){p[0][0], p[0][1], p[0][2], p[0][3], p[1][0], p[1][1], p[1][2], p[1][3]},
+                    v8bf);
                 // V operand: column 16n + c16, keys 32 half + 16 kt + 4g + r, by transpose reads:
                 // lane (g, i) addresses row 32 half + 16 kt + 4g + i/4, dims 16n + 4(i%4) .. +3,
                 // i.e. chunk 2n + (i%4)/2 = 8(n/4) + (2(n%4) + (i%4)/2), byte 8 (i%2) within it
@@ -232,49 +213,42 @@ __global__ __launch_bounds__(NW * 64) void sparse_mla_kernel(
                     const u32x2 hi = ds_read_tr(vb1 + 128 * (n >> 2) + vo1[n & 3]);
                     u32x4 vb;
                     vb[0] = lo[0]; vb[1] = lo[1]; vb[2] = hi[0]; vb[3] = hi[1];
-                    const v8bf vbv = as_bf16x8(vb);
-#pragma unroll
-                    for (int hg = 0; hg < NHG; ++hg) O[hg][n] = mfma_bf16(pav[hg], vbv, O[hg][n]);
+                    O[n] = mfma_bf16(pav, as_bf16x8(vb), O[n]);
                 }
             }
         }
     }
 
+    // totals per head c16, then per O row (head 4g + r)
+    float l_tot = l_run + shfl_xor_f(l_run, 16);
+    l_tot += shfl_xor_f(l_tot, 32);
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    const float my_lse = l_tot > 0.f ? m_ref * LN2 + logf(l_tot) : -__builtin_huge_valf();
+    float ir[4];
 #pragma unroll
-    for (int hg = 0; hg < NHG; ++hg) {
-        const int hb = h0 + 16 * hg;                   // this head group's first head
-        if (hb >= H) break;
-        const int head = hb + c16;
-        float l_tot = l_run[hg] + shfl_xor_f(l_run[hg], 16);
-        l_tot += shfl_xor_f(l_tot, 32);
-        const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-        const float my_lse = l_tot > 0.f ? m_run[hg] * LN2 + logf(l_tot) : -__builtin_huge_valf();
-        float ir[4];
+    for (int r = 0; r < 4; ++r) ir[r] = __shfl(inv, 4 * g + r, 64);
+
+    if (splits == 1) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) ir[r] = __shfl(inv, 4 * g + r, 64);
-        if (splits == 1) {
+        for (int r = 0; r < 4; ++r) {
+            const int hh = h0 + 4 * g + r;
+            if (hh >= H) continue;
+            uint16_t* orow = out + ((int64_t)row * H + hh) * 512;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int hh = hb + 4 * g + r;
-                if (hh >= H) continue;
-                uint16_t* orow = out + ((int64_t)row * H + hh) * 512;
-#pragma unroll
-                for (int n = 0; n < 32; ++n)
-                    orow[16 * n + c16] = (uint16_t)bf16_bits(O[hg][n][r] * ir[r]);
-            }
-            if (lse && g == 0 && head < H) lse[(int64_t)row * H + head] = my_lse;
-        } else {
-            const int64_t pb = ((int64_t)row * splits + split) * H;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int hh = hb + 4 * g + r;
-                if (hh >= H) continue;
-                float* orow = part_o + (pb + hh) * 512;
-#pragma unroll
-                for (int n = 0; n < 32; ++n) orow[16 * n + c16] = O[hg][n][r] * ir[r];
-            }
-            if (g == 0 && head < H) part_lse[pb + head] = my_lse;
+            for (int n = 0; n < 32; ++n) orow[16 * n + c16] = (uint16_t)bf16_bits(O[n][r] * ir[r]);
         }
+        if (lse && g == 0 && head < H) lse[(int64_t)row * H + head] = my_lse;
+    } else {
+        const int64_t pb = ((int64_t)row * splits + split) * H;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int hh = h0 + 4 * g + r;
+            if (hh >= H) continue;
+            float* orow = part_o + (pb + hh) * 512;
+#pragma unroll
+            for (int n = 0; n < 32; ++n) orow[16 * n + c16] = O[n][r] * ir[r];
+        }
+        if (g == 0 && head < H) part_lse[pb + head] = my_lse;
     }
 }
 
@@ -312,13 +286,13 @@ __global__ __launch_bounds__(128) void mla_combine_kernel(const float* __restric
         lse[(int64_t)row * H + hh] = den > 0.f ? mx + logf(den) : -__builtin_huge_valf();
 }
 
-template <int NW, int NHG>
+template <int NW>
 hipError_t launch_nw(const uint16_t* q, const uint16_t* kv, const int32_t* idx,
                      const int64_t* seq_start, int T, int L, int H, int k, float sm_scale,
                      int splits, uint16_t* out, float* lse, float* part_o, float* part_lse,
                      hipStream_t stream)
 {
-    auto kern = sparse_mla_kernel<NW, NHG>;
+    auto kern = sparse_mla_kernel<NW>;
     hipLaunchKernelGGL(kern, dim3(T, splits), dim3(NW * 64), 0, stream, q, kv, idx, seq_start, L,
                        H, k, sm_scale, splits, out, lse, part_o, part_lse);
     return hipGetLastError();
@@ -332,9 +306,9 @@ hipError_t launch_sparse_mla(const uint16_t* q, const uint16_t* kv, const int32_
                              float* part_o, float* part_lse, hipStream_t stream)
 {
     if (T <= 0) return hipSuccess;
-    const int nw = (H + 16 * MLA_NHG - 1) / (16 * MLA_NHG);
+    const int nw = (H + 15) / 16;                       // 16 heads per wave
 #define DSA_MLA_CASE(NW) \
-    case NW: return launch_nw<NW, MLA_NHG>(q, kv, idx, seq_start, T, L, H, k, sm_scale, splits, out, lse, part_o, part_lse, stream);
+    case NW: return launch_nw<NW>(q, kv, idx, seq_start, T, L, H, k, sm_scale, splits, out, lse, part_o, part_lse, stream);
     switch (nw) {
         DSA_MLA_CASE(1) DSA_MLA_CASE(2) DSA_MLA_CASE(3) DSA_MLA_CASE(4)
         DSA_MLA_CASE(5) DSA_MLA_CASE(6) DSA_MLA_CASE(7) DSA_MLA_CASE(8)
