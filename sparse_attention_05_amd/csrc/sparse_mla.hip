@@ -13,7 +13,10 @@
 // registers), softmax in the exp2 domain with fp32 statistics against a per-head reference
 // max that moves only when exceeded by 2^8, then O += P V with P
 // already in the A-operand layout and V read from the same row-major tile through the LDS
-// transpose read (ds_read_b64_tr_b16), so no transposed copy of V is ever built.
+// transpose read (ds_read_b64_tr_b16), so no transposed copy of V is ever built.  Both
+// contractions are software-pipelined: LDS operands are read several MFMAs ahead and QK runs
+// as four independent accumulation chains, since two waves per SIMD alone cannot hide LDS
+// latency at this register budget (Q^T 72 + O 128 of 256 VGPRs).
 #include "dsa_device.h"
 #include "kernels.h"
 
@@ -135,20 +138,44 @@ __global__ __launch_bounds__(NW * 64) void sparse_mla_kernel(
             for (int half = 0; half < 2; ++half) {
                 // S^T[key][head] for keys 32 half + 16 kt + (4g + r);
                 // A = row 32 half + 16 kt + c16, dims [32s + 8g, +8): chunk 4s + g
-                v4f S[2];
+                // four independent accumulation chains (2 key groups x even/odd K steps),
+                // A operands read QD steps ahead
+                v4f S[2], S2[2];
+                const uint8_t* rb[2];
+                int oo[2][2];
 #pragma unroll
                 for (int kt = 0; kt < 2; ++kt) {
                     const int r = half * 32 + kt * 16 + c16;
-                    const uint8_t* rb = tb + row_base(r);
-                    const int o0 = sub_off(r, g), o1 = sub_off(r, 4 + g);
+                    rb[kt] = tb + row_base(r);
+                    oo[kt][0] = sub_off(r, g);
+                    oo[kt][1] = sub_off(r, 4 + g);
                     S[kt] = v4f{0.f, 0.f, 0.f, 0.f};
+                    S2[kt] = v4f{0.f, 0.f, 0.f, 0.f};
+                }
+                constexpr int QD = 3;
+                u32x4 abuf[QD][2];
 #pragma unroll
-                    for (int s = 0; s < 18; ++s) {
-                        const u32x4 a = *reinterpret_cast<const u32x4*>(
-                            rb + 128 * (s >> 1) + ((s & 1) ? o1 : o0));
-                        S[kt] = mfma_bf16(as_bf16x8(a), as_bf16x8(qreg[s]), S[kt]);
+                for (int s = 0; s < QD; ++s)
+#pragma unroll
+                    for (int kt = 0; kt < 2; ++kt)
+                        abuf[s][kt] = *reinterpret_cast<const u32x4*>(rb[kt] + 128 * (s >> 1) + oo[kt][s & 1]);
+#pragma unroll
+                for (int s = 0; s < 18; ++s) {
+                    u32x4 a[2] = {abuf[s % QD][0], abuf[s % QD][1]};
+                    if (s + QD < 18) {
+                        const int m = s + QD;
+#pragma unroll
+                        for (int kt = 0; kt < 2; ++kt)
+                            abuf[s % QD][kt] = *reinterpret_cast<const u32x4*>(rb[kt] + 128 * (m >> 1) + oo[kt][m & 1]);
+                    }
+#pragma unroll
+                    for (int kt = 0; kt < 2; ++kt) {
+                        if (s & 1) S2[kt] = mfma_bf16(as_bf16x8(a[kt]), as_bf16x8(qreg[s]), S2[kt]);
+                        else S[kt] = mfma_bf16(as_bf16x8(a[kt]), as_bf16x8(qreg[s]), S[kt]);
                     }
                 }
+#pragma unroll
+                for (int kt = 0; kt < 2; ++kt) S[kt] += S2[kt];
                 // softmax statistics for head c16 over this half's 32 keys
                 float x[2][4];
                 float mloc = -__builtin_huge_valf();
@@ -207,12 +234,24 @@ __global__ __launch_bounds__(NW * 64) void sparse_mla_kernel(
                     vo0[m] = sub_off(rv0, 2 * m + cpart);
                     vo1[m] = sub_off(rv1, 2 * m + cpart);
                 }
+                // software-pipelined: the V operand of MFMA n is read PD MFMAs ahead
+                constexpr int PD = 4;
+                u32x2 vlo[PD], vhi[PD];
+#pragma unroll
+                for (int n = 0; n < PD; ++n) {
+                    vlo[n] = ds_read_tr(vb0 + 128 * (n >> 2) + vo0[n & 3]);
+                    vhi[n] = ds_read_tr(vb1 + 128 * (n >> 2) + vo1[n & 3]);
+                }
 #pragma unroll
                 for (int n = 0; n < 32; ++n) {
-                    const u32x2 lo = ds_read_tr(vb0 + 128 * (n >> 2) + vo0[n & 3]);
-                    const u32x2 hi = ds_read_tr(vb1 + 128 * (n >> 2) + vo1[n & 3]);
                     u32x4 vb;
-                    vb[0] = lo[0]; vb[1] = lo[1]; vb[2] = hi[0]; vb[3] = hi[1];
+                    vb[0] = vlo[n % PD][0]; vb[1] = vlo[n % PD][1];
+                    vb[2] = vhi[n % PD][0]; vb[3] = vhi[n % PD][1];
+                    if (n + PD < 32) {
+                        const int m = n + PD;
+                        vlo[n % PD] = ds_read_tr(vb0 + 128 * (m >> 2) + vo0[m & 3]);
+                        vhi[n % PD] = ds_read_tr(vb1 + 128 * (m >> 2) + vo1[m & 3]);
+                    }
                     O[n] = mfma_bf16(pav, as_bf16x8(vb), O[n]);
                 }
             }
