@@ -206,6 +206,9 @@ __global__ __launch_bounds__(IP_WAVES * 64) void indexer_prefill_kernel(
                     for (int j = 0; j < IP_NT; ++j)
                         acc[kb][j] = mfma_f8(qa[j], bb, v4f{0.f, 0.f, 0.f, 0.f});
                 }
+                // issue the step's MFMAs as one burst; the epilogue then trails the matrix
+                // pipe instead of waiting on each result in turn
+                __builtin_amdgcn_sched_barrier(0);
                 reduce_heads<HI>(acc, wp, lane, [&](int tok, int kb, float v) {
                     const int t = tw0 + tok;
                     const int s = key0 + kb * 16 + c16;
