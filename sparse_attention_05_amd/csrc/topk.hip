@@ -4,19 +4,18 @@
 // 0..n_t-1 (《DeepSeek-V3.2-Exp模型优势与 DSA 工作原理》 §4 步骤三 and §2 风险边界明确).  Ties
 // go to the lower position and -0 equals +0, which makes the selected set unique.
 //
-// Scores map to order-preserving uint32 keys.  One workgroup per row:
-//   pass 1  streams the row once into a 4096-bin LDS histogram of the top 12 key bits and
-//           finds the boundary bin b holding the k-th largest key;
-//   pass 2  streams the row again; positions whose bin is above b are final (list S, kept
-//           in position order by ballot/scan compaction), and the boundary bin's entries
-//           become LDS candidates (key, position), also in position order;
-//   resolve two more radix levels (10 + 10 bits) over the candidates in LDS give the exact
-//           k-th key tau; the candidates above tau and the lowest-position ties at tau
-//           form list C;
-//   merge   S and C are both ascending, so each element's output slot is its index plus
-//           its rank in the other list (binary search): the output is in ascending order.
-// A row whose boundary bin holds more than TK_CAP keys falls back to radix levels over
-// the row in global memory and a position-ordered emission sweep.
+// Scores map to order-preserving uint32 keys; one 1024-thread workgroup per row.
+//   short rows (n <= CAND_CAP): the whole row is staged in LDS once;
+//   long rows: 64 contiguous blocks spread over the row (4096 keys, a few KB of reads) give
+//     an estimate tau_lo of the key with about 2k keys above it; one ordered pass over the
+//     row keeps every key >= tau_lo as an LDS candidate (key, position) in position order.
+//   In both cases an exact three-level radix select over the LDS candidates finds the k-th
+//   key tau, and an ordered sweep emits the keys above tau and the lowest-position ties, so
+//   the output is ascending.  Each long row is read from memory once (plus the sample).
+// If the estimate leaves fewer than k or more than CAND_CAP candidates, the row falls back
+// to the exact path: a 4096-bin histogram pass, an ordered pass keeping the positions above
+// the boundary bin and the boundary bin's candidates, an LDS radix resolve and a co-rank
+// merge (two reads of the row; a global multi-level pass if even that bin overflows).
 #include "dsa_device.h"
 #include "kernels.h"
 
@@ -25,9 +24,17 @@ namespace {
 
 constexpr int TK_THREADS = 1024;
 constexpr int TK_WAVES = TK_THREADS / 64;
-constexpr int TK_BINS = 4096;               // first digit: key bits 31..20
-constexpr int TK_CAP = 3072;                // boundary-bin candidates kept in LDS
+constexpr int CAND_CAP = 6144;              // candidates kept in LDS
+constexpr int SAMPLE = 4096;                // sampled keys (64 blocks of 64)
+constexpr int FB_BINS = 4096;               // fallback first digit: key bits 31..20
+constexpr int FB_CAP = 3072;                // fallback boundary-bin candidates
 constexpr int TK_KMAX = 8192;
+
+// LDS carve-up (bytes): the paths never coexist, so they share one buffer.
+constexpr int OFF_HIST = 0;                                    // up to 4096 ints
+constexpr int OFF_A = OFF_HIST + 4 * FB_BINS;                  // 16 KB
+constexpr int LDS_BYTES = OFF_A + 8 * CAND_CAP + 4 * SAMPLE;   // 80 KB
+static_assert(4 * TK_KMAX + 8 * FB_CAP <= 8 * CAND_CAP + 4 * SAMPLE, "fallback fits");
 
 struct RowRef {
     const float* p;
@@ -71,8 +78,8 @@ __device__ __forceinline__ int block_excl_scan(int v, int* s_wave, int* total)
 }
 
 // Boundary bin of a descending histogram: the bin B with count(bins > B) < need <=
-// count(bins >= B).  Returns B and stores need - count(bins > B) in *rem.  hist has
-// nb = per * TK_THREADS bins; thread i covers bins nb-1-i*per downwards.
+// count(bins >= B).  Returns B and stores need - count(bins > B) in *rem.  The histogram
+// has PER * TK_THREADS bins; thread i covers bins NB-1-i*PER downwards.
 template <int PER>
 __device__ __forceinline__ int boundary_bin(const int* hist, int need, int* s_wave, int* s_res,
                                             int* rem)
@@ -100,6 +107,38 @@ __device__ __forceinline__ int boundary_bin(const int* hist, int need, int* s_wa
     *rem = s_res[1];
     __syncthreads();
     return b;
+}
+
+// Exact kth-largest key among keys[0..nk) held in LDS (1 <= kth <= nk): three radix
+// levels of 11, 11 and 10 bits.  Returns the key and stores in *need_eq how many keys equal
+// to it belong to the top kth.
+__device__ __forceinline__ uint32_t lds_select(const uint32_t* keys, int nk, int kth, int* hist,
+                                               int* s_wave, int* s_res, int* need_eq)
+{
+    const int tid = threadIdx.x;
+    uint32_t prefix = 0;
+    int need = kth;
+#pragma unroll 1
+    for (int lvl = 0; lvl < 3; ++lvl) {
+        const int sh = lvl == 0 ? 21 : (lvl == 1 ? 10 : 0);
+        const int above = lvl == 0 ? 32 : (lvl == 1 ? 21 : 10);   // bits fixed so far start here
+        const int nb = lvl == 2 ? 1024 : 2048;
+        for (int i = tid; i < nb; i += TK_THREADS) hist[i] = 0;
+        __syncthreads();
+        for (int i = tid; i < nk; i += TK_THREADS) {
+            const uint32_t u = keys[i];
+            const bool match = lvl == 0 || (u >> above) == prefix;
+            if (match) atomicAdd(&hist[(u >> sh) & (nb - 1)], 1);
+        }
+        __syncthreads();
+        int rem;
+        const int d = lvl == 2 ? boundary_bin<1>(hist, need, s_wave, s_res, &rem)
+                               : boundary_bin<2>(hist, need, s_wave, s_res, &rem);
+        prefix = (prefix << (lvl == 2 ? 10 : 11)) | (uint32_t)d;
+        need = rem;
+    }
+    *need_eq = need;
+    return prefix;
 }
 
 // Visit the row in rounds of up to 4 * TK_THREADS consecutive positions; within a round,
@@ -146,20 +185,60 @@ __device__ __forceinline__ void for_row_rounds(const RowRef& rr, F&& f)
     }
 }
 
+// Ordered emission from a position-ordered candidate list (cpos null: position = index):
+// every key > tau, plus the first need_eq keys equal to tau, at
+// slot = #(> tau before) + min(#ties before, need_eq).
+__device__ __forceinline__ void emit_sorted(const uint32_t* ckey, const int* cpos, int nc,
+                                            uint32_t tau, int need_eq, int k, int32_t* out,
+                                            int* s_wave)
+{
+    const int tid = threadIdx.x;
+    int base_g = 0, base_e = 0;
+    for (int r0 = 0; r0 < nc; r0 += 4 * TK_THREADS) {
+        uint32_t ku[4];
+        int pp[4], ng = 0, ne = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int i = r0 + 4 * tid + j;
+            ku[j] = i < nc ? ckey[i] : 0u;
+            pp[j] = i < nc ? (cpos ? cpos[i] : i) : -1;
+            ng += (i < nc) && ku[j] > tau;
+            ne += (i < nc) && ku[j] == tau;
+        }
+        int tot;
+        const int off = block_excl_scan(ng | (ne << 16), s_wave, &tot);
+        int gt_before = base_g + (off & 0xFFFF);
+        int eq_before = base_e + (off >> 16);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int i = r0 + 4 * tid + j;
+            if (i >= nc) break;
+            if (ku[j] > tau) {
+                const int slot = gt_before + min(eq_before, need_eq);
+                if (slot < k) out[slot] = pp[j];
+                ++gt_before;
+            } else if (ku[j] == tau) {
+                if (eq_before < need_eq && gt_before + eq_before < k) out[gt_before + eq_before] = pp[j];
+                ++eq_before;
+            }
+        }
+        base_g += tot & 0xFFFF;
+        base_e += tot >> 16;
+    }
+}
+
 template <bool DECODE>
 __global__ __launch_bounds__(TK_THREADS) void topk_kernel(
     const float* __restrict__ scores, int64_t ld, const int64_t* __restrict__ seq_start, int L,
     int q_pos0, int k, int32_t* __restrict__ idx)
 {
-    __shared__ int s_hist[TK_BINS];
-    __shared__ int s_sel[TK_KMAX];            // S: final positions above the boundary bin
-    __shared__ uint32_t s_ckey[TK_CAP];       // boundary-bin candidates (key, position)
-    __shared__ int s_cpos[TK_CAP];
+    __shared__ __attribute__((aligned(16))) uint8_t s_buf[LDS_BYTES];
     __shared__ int s_wave[TK_WAVES];
     __shared__ int s_res[4];
+    int* hist = reinterpret_cast<int*>(s_buf + OFF_HIST);
 
     const int row = blockIdx.x;
-    const int tid = threadIdx.x, lane = tid & 63;
+    const int tid = threadIdx.x;
     const RowRef rr = row_of<DECODE>(row, scores, ld, seq_start, L, q_pos0);
     const int n = rr.n;
     int32_t* out = idx + (int64_t)row * k;
@@ -169,77 +248,111 @@ __global__ __launch_bounds__(TK_THREADS) void topk_kernel(
         return;
     }
 
-    // ---- pass 1: histogram of key bits 31..20
-    for (int i = tid; i < TK_BINS; i += TK_THREADS) s_hist[i] = 0;
+    uint32_t* ckey = reinterpret_cast<uint32_t*>(s_buf + OFF_A);
+    int* cpos = reinterpret_cast<int*>(s_buf + OFF_A + 4 * CAND_CAP);
+    if (n <= CAND_CAP) {
+        // ---- the whole row fits: stage it, select, emit
+        for (int i = tid; i < n; i += TK_THREADS) ckey[i] = score_key(rr.p[i]);
+        __syncthreads();
+        int need_eq;
+        const uint32_t tau = lds_select(ckey, n, k, hist, s_wave, s_res, &need_eq);
+        emit_sorted(ckey, nullptr, n, tau, need_eq, k, out, s_wave);
+        return;
+    }
+
+    // ---- threshold estimate from 64 contiguous 64-key blocks spread over the row
+    uint32_t* samp = reinterpret_cast<uint32_t*>(s_buf + OFF_A + 8 * CAND_CAP);
+    {
+        const int blk = tid >> 4, off = (tid & 15) * 4;
+        const int start = (int)(((int64_t)blk * (n - 64)) / 63);   // n > CAND_CAP > 4096
+#pragma unroll
+        for (int j = 0; j < 4; ++j) samp[tid * 4 + j] = score_key(rr.p[start + off + j]);
+    }
+    __syncthreads();
+    // sample rank with about 2k of the n keys above it
+    const int rs = (int)min<int64_t>(SAMPLE, ((int64_t)2 * k * SAMPLE + n - 1) / n);
+    int unused_eq;
+    const uint32_t tau_lo = lds_select(samp, SAMPLE, rs, hist, s_wave, s_res, &unused_eq);
+
+    // ---- one ordered pass: candidates are the keys >= tau_lo
+    int nc = 0;
+    for_row_rounds(rr, [&](const int* pos, const uint32_t* key, int c) {
+        int mine = 0;
+        for (int j = 0; j < c; ++j) mine += key[j] >= tau_lo;
+        int tot;
+        int o = nc + block_excl_scan(mine, s_wave, &tot);
+        for (int j = 0; j < c; ++j) {
+            if (key[j] >= tau_lo) {
+                if (o < CAND_CAP) {
+                    ckey[o] = key[j];
+                    cpos[o] = pos[j];
+                }
+                ++o;
+            }
+        }
+        nc += tot;
+    });
+    __syncthreads();
+    if (nc >= k && nc <= CAND_CAP) {
+        int need_eq;
+        const uint32_t tau = lds_select(ckey, nc, k, hist, s_wave, s_res, &need_eq);
+        emit_sorted(ckey, cpos, nc, tau, need_eq, k, out, s_wave);
+        return;
+    }
+
+    // ---- fallback: exact two-pass path
+    int* s_sel = reinterpret_cast<int*>(s_buf + OFF_A);                 // S: 8192 ints
+    uint32_t* fkey = reinterpret_cast<uint32_t*>(s_buf + OFF_A + 4 * TK_KMAX);
+    int* fpos = reinterpret_cast<int*>(s_buf + OFF_A + 4 * TK_KMAX + 4 * FB_CAP);
+    for (int i = tid; i < FB_BINS; i += TK_THREADS) hist[i] = 0;
     __syncthreads();
     for_row_rounds(rr, [&](const int*, const uint32_t* key, int c) {
-        for (int j = 0; j < c; ++j) atomicAdd(&s_hist[key[j] >> 20], 1);
+        for (int j = 0; j < c; ++j) atomicAdd(&hist[key[j] >> 20], 1);
     });
     __syncthreads();
     int need_b;                                   // keys still needed from the boundary bin
-    const uint32_t b = (uint32_t)boundary_bin<TK_BINS / TK_THREADS>(s_hist, k, s_wave, s_res,
+    const uint32_t b = (uint32_t)boundary_bin<FB_BINS / TK_THREADS>(hist, k, s_wave, s_res,
                                                                     &need_b);
     const int n_above = k - need_b;               // keys in bins above b (all selected)
-    const int n_cand = s_hist[b];
+    const int n_cand = hist[b];
     __syncthreads();
 
-    if (n_cand <= TK_CAP) {
-        // ---- pass 2: S (bins above b) and the boundary candidates, both position-ordered
+    if (n_cand <= FB_CAP) {
+        // S (bins above b) and the boundary candidates, both position-ordered
         int base_s = 0, base_c = 0;
         for_row_rounds(rr, [&](const int* pos, const uint32_t* key, int c) {
-            int ns = 0, nc = 0;
+            int ns = 0, ncb = 0;
             for (int j = 0; j < c; ++j) {
                 const uint32_t d = key[j] >> 20;
                 ns += d > b;
-                nc += d == b;
+                ncb += d == b;
             }
             int tot;
-            const int off = block_excl_scan(ns | (nc << 16), s_wave, &tot);
+            const int off = block_excl_scan(ns | (ncb << 16), s_wave, &tot);
             int os = base_s + (off & 0xFFFF), oc = base_c + (off >> 16);
             for (int j = 0; j < c; ++j) {
                 const uint32_t d = key[j] >> 20;
                 if (d > b) s_sel[os++] = pos[j];
                 else if (d == b) {
-                    s_ckey[oc] = key[j];
-                    s_cpos[oc++] = pos[j];
+                    fkey[oc] = key[j];
+                    fpos[oc++] = pos[j];
                 }
             }
             base_s += tot & 0xFFFF;
             base_c += tot >> 16;
         });
         __syncthreads();
-
-        // ---- resolve the candidates: key bits 19..10, then 9..0
-        uint32_t prefix = b;
-        int need = need_b;
-#pragma unroll 1
-        for (int lvl = 0; lvl < 2; ++lvl) {
-            const int sh = lvl == 0 ? 10 : 0;
-            for (int i = tid; i < 1024; i += TK_THREADS) s_hist[i] = 0;
-            __syncthreads();
-            for (int i = tid; i < n_cand; i += TK_THREADS) {
-                const uint32_t u = s_ckey[i];
-                if ((u >> (sh + 10)) == prefix) atomicAdd(&s_hist[(u >> sh) & 1023], 1);
-            }
-            __syncthreads();
-            int rem;
-            const int d = boundary_bin<1>(s_hist, need, s_wave, s_res, &rem);
-            prefix = (prefix << 10) | (uint32_t)d;
-            need = rem;
-        }
-        const uint32_t tau = prefix;              // exact k-th largest key
-        const int need_eq = need;                 // ties at tau to keep, lowest first
-
-        // chosen candidates (key > tau, or the first need_eq ties) -> list C in s_ckey
-        // (reused as int positions), position order kept by an ordered scan
+        int need_eq;
+        const uint32_t tau = lds_select(fkey, n_cand, need_b, hist, s_wave, s_res, &need_eq);
+        // chosen candidates -> C (in place over fkey, as positions), position order kept
         int base_g = 0, base_e = 0;
         for (int r0 = 0; r0 < n_cand; r0 += 4 * TK_THREADS) {
             uint32_t ku[4];
             int pp[4], ng = 0, ne = 0;
             for (int j = 0; j < 4; ++j) {
                 const int i = r0 + 4 * tid + j;
-                ku[j] = i < n_cand ? s_ckey[i] : 0u;
-                pp[j] = i < n_cand ? s_cpos[i] : -1;
+                ku[j] = i < n_cand ? fkey[i] : 0u;
+                pp[j] = i < n_cand ? fpos[i] : -1;
                 ng += (i < n_cand) && ku[j] > tau;
                 ne += (i < n_cand) && ku[j] == tau;
             }
@@ -247,14 +360,14 @@ __global__ __launch_bounds__(TK_THREADS) void topk_kernel(
             const int off = block_excl_scan(ng | (ne << 16), s_wave, &tot);
             int eq_before = base_e + (off >> 16);
             int slot = base_g + (off & 0xFFFF) + min(eq_before, need_eq);
-            __syncthreads();                      // all reads of s_ckey in this round done
+            __syncthreads();                      // all reads of fkey in this round done
             for (int j = 0; j < 4; ++j) {
                 const int i = r0 + 4 * tid + j;
                 if (i >= n_cand) break;
                 if (ku[j] > tau) {
-                    reinterpret_cast<int*>(s_ckey)[slot++] = pp[j];
+                    reinterpret_cast<int*>(fkey)[slot++] = pp[j];
                 } else if (ku[j] == tau) {
-                    if (eq_before < need_eq) reinterpret_cast<int*>(s_ckey)[slot++] = pp[j];
+                    if (eq_before < need_eq) reinterpret_cast<int*>(fkey)[slot++] = pp[j];
                     ++eq_before;
                 }
             }
@@ -262,11 +375,11 @@ __global__ __launch_bounds__(TK_THREADS) void topk_kernel(
             base_e += tot >> 16;
             __syncthreads();
         }
-        // C holds need_b positions, ascending; S holds n_above positions, ascending.
-        const int* C = reinterpret_cast<const int*>(s_ckey);
+        // C holds need_b positions, S holds n_above positions, both ascending: co-rank merge
+        const int* C = reinterpret_cast<const int*>(fkey);
         for (int i = tid; i < n_above; i += TK_THREADS) {
             const int p = s_sel[i];
-            int lo = 0, hi = need_b;              // count of C below p
+            int lo = 0, hi = need_b;
             while (lo < hi) {
                 const int m = (lo + hi) >> 1;
                 if (C[m] < p) lo = m + 1; else hi = m;
@@ -275,7 +388,7 @@ __global__ __launch_bounds__(TK_THREADS) void topk_kernel(
         }
         for (int i = tid; i < need_b; i += TK_THREADS) {
             const int p = C[i];
-            int lo = 0, hi = n_above;             // count of S below p
+            int lo = 0, hi = n_above;
             while (lo < hi) {
                 const int m = (lo + hi) >> 1;
                 if (s_sel[m] < p) lo = m + 1; else hi = m;
@@ -285,29 +398,27 @@ __global__ __launch_bounds__(TK_THREADS) void topk_kernel(
         return;
     }
 
-    // ---- fallback: two more radix levels over the row in global memory
+    // boundary bin too large for LDS: two more radix levels over the row in memory
     uint32_t prefix = b;
     int need = need_b;
 #pragma unroll 1
     for (int lvl = 0; lvl < 2; ++lvl) {
         const int sh = lvl == 0 ? 10 : 0;
-        for (int i = tid; i < 1024; i += TK_THREADS) s_hist[i] = 0;
+        for (int i = tid; i < 1024; i += TK_THREADS) hist[i] = 0;
         __syncthreads();
         for_row_rounds(rr, [&](const int*, const uint32_t* key, int c) {
             for (int j = 0; j < c; ++j)
-                if ((key[j] >> (sh + 10)) == prefix) atomicAdd(&s_hist[(key[j] >> sh) & 1023], 1);
+                if ((key[j] >> (sh + 10)) == prefix) atomicAdd(&hist[(key[j] >> sh) & 1023], 1);
         });
         __syncthreads();
         int rem;
-        const int d = boundary_bin<1>(s_hist, need, s_wave, s_res, &rem);
+        const int d = boundary_bin<1>(hist, need, s_wave, s_res, &rem);
         prefix = (prefix << 10) | (uint32_t)d;
         need = rem;
     }
     const uint32_t tau = prefix;
     const int need_eq = need;
-    // slot of a selected position = #(key > tau before it) + min(#ties before it, need_eq)
     int base_gt = 0, base_eq = 0;
-    (void)lane;
     for_row_rounds(rr, [&](const int* pos, const uint32_t* key, int c) {
         int ng = 0, ne = 0;
         for (int j = 0; j < c; ++j) {

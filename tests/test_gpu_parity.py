@@ -119,6 +119,27 @@ def test_topk_long_rows(dsa):
     check_topk_exact(_np(idx), s, L - T + np.arange(T) + 1, k, "long rows")
 
 
+def test_topk_threshold_estimate_misses_fall_back_exactly(dsa):
+    """Rows whose sampled blocks are unrepresentative: the estimated threshold keeps too
+    few (or too many) candidates and the row must take the exact path."""
+    T, L, k = 4, 40000, 2048
+    rng = np.random.default_rng(11)
+    s = np.empty((T, L), np.float32)
+    pos = np.arange(L)
+    s[0] = -pos * 1e-3                                    # decreasing ...
+    for blk in range(64):                                 # ... with the sampled blocks high
+        start = blk * (L - 64) // 63
+        s[0, start:start + 64] = 100.0 + rng.random(64)
+    s[1] = np.where(pos % 2 == 0, 1.0, 0.0)               # massive ties at the threshold
+    s[2] = rng.standard_normal(L)
+    s[2, rng.choice(L, 3000, replace=False)] = 50.0       # many equal top values
+    s[3] = -s[0]
+    g = torch.from_numpy(s).cuda()
+    idx = dsa.dsa_topk(g, L, L - T, k)
+    torch.cuda.synchronize()
+    check_topk_exact(_np(idx), s, L - T + np.arange(T) + 1, k, "estimate misses")
+
+
 # -------------------------------------------------------------------------- sparse MLA
 
 def _random_idx(T, L, k, q_pos0, rng, holes=True):
