@@ -5,7 +5,7 @@
 // go to the lower position and -0 equals +0, which makes the selected set unique.
 //
 // Scores map to order-preserving uint32 keys; one 1024-thread workgroup per row.
-//   short rows (n <= CAND_CAP): the whole row is staged in LDS once;
+//   short rows (n <= CAND_CAP = 5888): the whole row is staged in LDS once;
 //   long rows: 64 contiguous blocks spread over the row (4096 keys, a few KB of reads) give
 //     an estimate tau_lo of the key with about 2k keys above it; one ordered pass over the
 //     row keeps every key >= tau_lo as an LDS candidate (key, position) in position order.
@@ -24,7 +24,7 @@ namespace {
 
 constexpr int TK_THREADS = 1024;
 constexpr int TK_WAVES = TK_THREADS / 64;
-constexpr int CAND_CAP = 6144;              // candidates kept in LDS
+constexpr int CAND_CAP = 5888;              // candidates kept in LDS (two workgroups per CU)
 constexpr int SAMPLE = 4096;                // sampled keys (64 blocks of 64)
 constexpr int FB_BINS = 4096;               // fallback first digit: key bits 31..20
 constexpr int FB_CAP = 3072;                // fallback boundary-bin candidates
@@ -141,10 +141,16 @@ __device__ __forceinline__ uint32_t lds_select(const uint32_t* keys, int nk, int
     return prefix;
 }
 
-// Visit the row in rounds of up to 4 * TK_THREADS consecutive positions; within a round,
-// thread t owns positions [4t, 4t + 4) of the round (fewer in the unaligned head and the
-// tail), so thread order is position order.  f(pos[4], key[4], cnt) is called by every
-// thread in every round (cnt may be 0); rounds are uniform across the workgroup.
+// Visit the row in position order.  The 16-byte-aligned body goes in super-rounds of
+// RPT * 4 * TK_THREADS positions: thread t owns the RPT * 4 consecutive positions starting at
+// RPT * 4 * t of the round and issues all RPT 16-byte loads before using any, so a
+// workgroup keeps RPT * 16 KB in flight.  Thread order is position order within a round.
+// f(pos0, key[], cnt) is called by every thread in every round with the keys of positions
+// pos0 .. pos0 + cnt - 1 (cnt may be 0); rounds are uniform across the workgroup.  The
+// unaligned head and the tail (fewer than 4 positions each) come as one-key rounds.
+constexpr int RPT = 4;
+constexpr int KPT = 4 * RPT;                            // keys per thread per round
+
 template <typename F>
 __device__ __forceinline__ void for_row_rounds(const RowRef& rr, F&& f)
 {
@@ -152,36 +158,32 @@ __device__ __forceinline__ void for_row_rounds(const RowRef& rr, F&& f)
     const int n = rr.n;
     const int mis = (int)((reinterpret_cast<uintptr_t>(rr.p) >> 2) & 3);
     const int head = min(n, (4 - mis) & 3);            // scalars until 16-byte aligned
-    int pos[4];
-    uint32_t key[4];
+    uint32_t key[KPT] = {};
     if (head > 0) {                                     // uniform
         const int c = tid < head ? 1 : 0;
-        pos[0] = tid;
         key[0] = c ? score_key(rr.p[tid]) : 0u;
-        f(pos, key, c);
+        f(tid, key, c);
     }
     const int body = (n - head) & ~3;
     const v4f* p4 = reinterpret_cast<const v4f*>(rr.p + head);
-    for (int base = 0; base < body; base += 4 * TK_THREADS) {
-        const int e = base + 4 * tid;
-        int c = 0;
-        if (e < body) {
-            const v4f v = p4[e >> 2];
+    for (int base = 0; base < body; base += KPT * TK_THREADS) {
+        const int e = base + KPT * tid;                 // first position (in the body)
+        const int c = max(0, min(KPT, body - e));       // a multiple of 4
+        v4f v[RPT];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                pos[j] = head + e + j;
-                key[j] = score_key(v[j]);
-            }
-            c = 4;
-        }
-        f(pos, key, c);
+        for (int i = 0; i < RPT; ++i)
+            if (4 * i < c) v[i] = p4[(e >> 2) + i];
+#pragma unroll
+        for (int i = 0; i < RPT; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) key[4 * i + j] = 4 * i < c ? score_key(v[i][j]) : 0u;
+        f(head + e, key, c);
     }
     const int tail = n - head - body;                   // 0..3
     if (tail > 0) {
         const int c = tid < tail ? 1 : 0;
-        pos[0] = head + body + tid;
         key[0] = c ? score_key(rr.p[head + body + tid]) : 0u;
-        f(pos, key, c);
+        f(head + body + tid, key, c);
     }
 }
 
@@ -276,16 +278,18 @@ __global__ __launch_bounds__(TK_THREADS) void topk_kernel(
 
     // ---- one ordered pass: candidates are the keys >= tau_lo
     int nc = 0;
-    for_row_rounds(rr, [&](const int* pos, const uint32_t* key, int c) {
+    for_row_rounds(rr, [&](int pos0, const uint32_t* key, int c) {
         int mine = 0;
-        for (int j = 0; j < c; ++j) mine += key[j] >= tau_lo;
+#pragma unroll
+        for (int j = 0; j < KPT; ++j) mine += (j < c) && key[j] >= tau_lo;
         int tot;
         int o = nc + block_excl_scan(mine, s_wave, &tot);
-        for (int j = 0; j < c; ++j) {
-            if (key[j] >= tau_lo) {
+#pragma unroll
+        for (int j = 0; j < KPT; ++j) {
+            if (j < c && key[j] >= tau_lo) {
                 if (o < CAND_CAP) {
                     ckey[o] = key[j];
-                    cpos[o] = pos[j];
+                    cpos[o] = pos0 + j;
                 }
                 ++o;
             }
@@ -306,8 +310,10 @@ __global__ __launch_bounds__(TK_THREADS) void topk_kernel(
     int* fpos = reinterpret_cast<int*>(s_buf + OFF_A + 4 * TK_KMAX + 4 * FB_CAP);
     for (int i = tid; i < FB_BINS; i += TK_THREADS) hist[i] = 0;
     __syncthreads();
-    for_row_rounds(rr, [&](const int*, const uint32_t* key, int c) {
-        for (int j = 0; j < c; ++j) atomicAdd(&hist[key[j] >> 20], 1);
+    for_row_rounds(rr, [&](int, const uint32_t* key, int c) {
+#pragma unroll
+        for (int j = 0; j < KPT; ++j)
+            if (j < c) atomicAdd(&hist[key[j] >> 20], 1);
     });
     __syncthreads();
     int need_b;                                   // keys still needed from the boundary bin
@@ -320,22 +326,25 @@ __global__ __launch_bounds__(TK_THREADS) void topk_kernel(
     if (n_cand <= FB_CAP) {
         // S (bins above b) and the boundary candidates, both position-ordered
         int base_s = 0, base_c = 0;
-        for_row_rounds(rr, [&](const int* pos, const uint32_t* key, int c) {
+        for_row_rounds(rr, [&](int pos0, const uint32_t* key, int c) {
             int ns = 0, ncb = 0;
-            for (int j = 0; j < c; ++j) {
+#pragma unroll
+            for (int j = 0; j < KPT; ++j) {
                 const uint32_t d = key[j] >> 20;
-                ns += d > b;
-                ncb += d == b;
+                ns += (j < c) && d > b;
+                ncb += (j < c) && d == b;
             }
             int tot;
             const int off = block_excl_scan(ns | (ncb << 16), s_wave, &tot);
             int os = base_s + (off & 0xFFFF), oc = base_c + (off >> 16);
-            for (int j = 0; j < c; ++j) {
+#pragma unroll
+            for (int j = 0; j < KPT; ++j) {
+                if (j >= c) break;
                 const uint32_t d = key[j] >> 20;
-                if (d > b) s_sel[os++] = pos[j];
+                if (d > b) s_sel[os++] = pos0 + j;
                 else if (d == b) {
                     fkey[oc] = key[j];
-                    fpos[oc++] = pos[j];
+                    fpos[oc++] = pos0 + j;
                 }
             }
             base_s += tot & 0xFFFF;
@@ -406,9 +415,11 @@ __global__ __launch_bounds__(TK_THREADS) void topk_kernel(
         const int sh = lvl == 0 ? 10 : 0;
         for (int i = tid; i < 1024; i += TK_THREADS) hist[i] = 0;
         __syncthreads();
-        for_row_rounds(rr, [&](const int*, const uint32_t* key, int c) {
-            for (int j = 0; j < c; ++j)
-                if ((key[j] >> (sh + 10)) == prefix) atomicAdd(&hist[(key[j] >> sh) & 1023], 1);
+        for_row_rounds(rr, [&](int, const uint32_t* key, int c) {
+#pragma unroll
+            for (int j = 0; j < KPT; ++j)
+                if (j < c && (key[j] >> (sh + 10)) == prefix)
+                    atomicAdd(&hist[(key[j] >> sh) & 1023], 1);
         });
         __syncthreads();
         int rem;
@@ -419,24 +430,27 @@ __global__ __launch_bounds__(TK_THREADS) void topk_kernel(
     const uint32_t tau = prefix;
     const int need_eq = need;
     int base_gt = 0, base_eq = 0;
-    for_row_rounds(rr, [&](const int* pos, const uint32_t* key, int c) {
+    for_row_rounds(rr, [&](int pos0, const uint32_t* key, int c) {
         int ng = 0, ne = 0;
-        for (int j = 0; j < c; ++j) {
-            ng += key[j] > tau;
-            ne += key[j] == tau;
+#pragma unroll
+        for (int j = 0; j < KPT; ++j) {
+            ng += (j < c) && key[j] > tau;
+            ne += (j < c) && key[j] == tau;
         }
         int tot;
         const int off = block_excl_scan(ng | (ne << 16), s_wave, &tot);
         int gt_before = base_gt + (off & 0xFFFF);
         int eq_before = base_eq + (off >> 16);
-        for (int j = 0; j < c; ++j) {
+#pragma unroll
+        for (int j = 0; j < KPT; ++j) {
+            if (j >= c) break;
             if (key[j] > tau) {
                 const int slot = gt_before + min(eq_before, need_eq);
-                if (slot < k) out[slot] = pos[j];
+                if (slot < k) out[slot] = pos0 + j;
                 ++gt_before;
             } else if (key[j] == tau) {
                 if (eq_before < need_eq && gt_before + eq_before < k)
-                    out[gt_before + eq_before] = pos[j];
+                    out[gt_before + eq_before] = pos0 + j;
                 ++eq_before;
             }
         }
