@@ -4,7 +4,7 @@
 // 0..n_t-1 (《DeepSeek-V3.2-Exp模型优势与 DSA 工作原理》 §4 步骤三 and §2 风险边界明确).  Ties
 // go to the lower position and -0 equals +0, which makes the selected set unique.
 //
-// Scores map to order-preserving uint32 keys; one 1024-thread workgroup per row.
+// Scores map to order-preserving uint32 keys; one 512-thread workgroup per row.
 //   short rows (n <= CAND_CAP = 5888): the whole row is staged in LDS once;
 //   long rows: 64 contiguous blocks spread over the row (4096 keys, a few KB of reads) give
 //     an estimate tau_lo of the key with about 2k keys above it; one ordered pass over the
@@ -22,7 +22,7 @@
 namespace dsa {
 namespace {
 
-constexpr int TK_THREADS = 1024;
+constexpr int TK_THREADS = 512;
 constexpr int TK_WAVES = TK_THREADS / 64;
 constexpr int CAND_CAP = 5888;              // candidates kept in LDS (two workgroups per CU)
 constexpr int SAMPLE = 4096;                // sampled keys (64 blocks of 64)
@@ -77,14 +77,15 @@ __device__ __forceinline__ int block_excl_scan(int v, int* s_wave, int* total)
     return off + x - v;
 }
 
-// Boundary bin of a descending histogram: the bin B with count(bins > B) < need <=
-// count(bins >= B).  Returns B and stores need - count(bins > B) in *rem.  The histogram
-// has PER * TK_THREADS bins; thread i covers bins NB-1-i*PER downwards.
-template <int PER>
+// Boundary bin of a descending histogram of NB bins: the bin B with count(bins > B) < need
+// <= count(bins >= B).  Returns B and stores need - count(bins > B) in *rem.  Thread i
+// covers bins NB-1-i*PER downwards.
+template <int NB>
 __device__ __forceinline__ int boundary_bin(const int* hist, int need, int* s_wave, int* s_res,
                                             int* rem)
 {
-    constexpr int NB = PER * TK_THREADS;
+    constexpr int PER = NB / TK_THREADS;
+    static_assert(PER * TK_THREADS == NB, "bins per thread");
     const int tid = threadIdx.x;
     int cnt[PER], sum = 0;
 #pragma unroll
@@ -132,8 +133,8 @@ __device__ __forceinline__ uint32_t lds_select(const uint32_t* keys, int nk, int
         }
         __syncthreads();
         int rem;
-        const int d = lvl == 2 ? boundary_bin<1>(hist, need, s_wave, s_res, &rem)
-                               : boundary_bin<2>(hist, need, s_wave, s_res, &rem);
+        const int d = lvl == 2 ? boundary_bin<1024>(hist, need, s_wave, s_res, &rem)
+                               : boundary_bin<2048>(hist, need, s_wave, s_res, &rem);
         prefix = (prefix << (lvl == 2 ? 10 : 11)) | (uint32_t)d;
         need = rem;
     }
@@ -265,10 +266,11 @@ __global__ __launch_bounds__(TK_THREADS) void topk_kernel(
     // ---- threshold estimate from 64 contiguous 64-key blocks spread over the row
     uint32_t* samp = reinterpret_cast<uint32_t*>(s_buf + OFF_A + 8 * CAND_CAP);
     {
-        const int blk = tid >> 4, off = (tid & 15) * 4;
+        constexpr int SPT = SAMPLE / TK_THREADS;                  // sampled keys per thread
+        const int i0 = tid * SPT, blk = i0 >> 6, off = i0 & 63;
         const int start = (int)(((int64_t)blk * (n - 64)) / 63);   // n > CAND_CAP > 4096
 #pragma unroll
-        for (int j = 0; j < 4; ++j) samp[tid * 4 + j] = score_key(rr.p[start + off + j]);
+        for (int j = 0; j < SPT; ++j) samp[i0 + j] = score_key(rr.p[start + off + j]);
     }
     __syncthreads();
     // sample rank with about 2k of the n keys above it
@@ -317,8 +319,7 @@ __global__ __launch_bounds__(TK_THREADS) void topk_kernel(
     });
     __syncthreads();
     int need_b;                                   // keys still needed from the boundary bin
-    const uint32_t b = (uint32_t)boundary_bin<FB_BINS / TK_THREADS>(hist, k, s_wave, s_res,
-                                                                    &need_b);
+    const uint32_t b = (uint32_t)boundary_bin<FB_BINS>(hist, k, s_wave, s_res, &need_b);
     const int n_above = k - need_b;               // keys in bins above b (all selected)
     const int n_cand = hist[b];
     __syncthreads();
@@ -423,7 +424,7 @@ __global__ __launch_bounds__(TK_THREADS) void topk_kernel(
         });
         __syncthreads();
         int rem;
-        const int d = boundary_bin<1>(hist, need, s_wave, s_res, &rem);
+        const int d = boundary_bin<1024>(hist, need, s_wave, s_res, &rem);
         prefix = (prefix << 10) | (uint32_t)d;
         need = rem;
     }
