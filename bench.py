@@ -26,6 +26,34 @@ sys.path.insert(0, ROOT)
 PEAK = {"fp8": 5000.0, "bf16": 2500.0}      # dense MFMA TFLOP/s, MI355X published
 HBM_PEAK_GBS = 8000.0                       # GB/s
 D_QK, D_V, D_I = 576, 512, 128
+# HBM traffic per launch measured with rocprofv3 FETCH_SIZE / WRITE_SIZE counters (scaled by a
+# plain copy of known size), keyed by workload; valid only for the kernel source it was taken on.
+TRAFFIC_FILES = {"prefill-L131072-k2048": "profiles/prefill_L131072_k2048_hbm_traffic.txt"}
+KERNEL_SOURCES = {"indexer": ["indexer.hip", "dsa_device.h"],
+                  "topk": ["topk.hip", "dsa_device.h"],
+                  "sparse_mla": ["sparse_mla.hip", "dsa_device.h"]}
+
+
+def measured_traffic(workload, kernel):
+    """Counter-measured HBM bytes per launch (fetch + write) of `kernel` on `workload`, or None
+    when no measurement exists or the kernel source has changed since it was taken."""
+    import hashlib
+    path = TRAFFIC_FILES.get(workload)
+    if path is None or not os.path.exists(os.path.join(ROOT, path)):
+        return None
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(ROOT, "sparse_attention_05_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    digest = h.hexdigest()[:16]
+    with open(os.path.join(ROOT, path)) as fh:
+        for line in fh:
+            if not line.startswith("traffic "):
+                continue
+            kv = dict(item.split("=", 1) for item in line.split()[1:])
+            if kv.get("kernel") == kernel and kv.get("source") == digest:
+                return int(float(kv["fetch_bytes"]) + float(kv["write_bytes"]))
+    return None
 
 
 def log(*a):
@@ -43,6 +71,11 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true",
+                    help="decode only (for profiling runs; prints no prefill value)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="run a plain 1 GiB device copy 5 times and exit (the known-size "
+                         "reference for FETCH_SIZE / WRITE_SIZE counter scaling)")
     return ap.parse_args()
 
 
@@ -73,8 +106,22 @@ def main():
     dsa.load()
     torch.cuda.set_device(0)
     dev = torch.device("cuda:0")
+    if args.calibrate_copy:
+        nbytes = 1 << 30
+        src = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes_per_launch": nbytes, "launches": 5}), flush=True)
+        return
     cfg = WORKLOADS[args.workload]
     L, T, k, H_I, H = cfg.L, cfg.rows, cfg.k, cfg.H_I, cfg.H
+    if args.no_prefill:
+        decode = run_decode(args, WORKLOADS[args.decode_workload], dev)
+        print(json.dumps({"decode": decode}), flush=True)
+        return
     log("generating", cfg.name)
     inp = make_prefill(cfg, device=dev)
     out = torch.empty((T, H, D_V), dtype=torch.bfloat16, device=dev)
@@ -159,57 +206,19 @@ def main():
         kern[name] = dict(total_ms=round(ktime[name], 3), launches=kcount[name],
                           avg_launch_ms=round(ktime[name] / kcount[name], 4),
                           achieved=round(ach, 2), unit=unit, peak=peak,
-                          frac=round(ach / peak, 4), bound=bound)
+                          frac=round(ach / peak, 4), bound=bound,
+                          traffic=measured_traffic(cfg.name, name))
     dom = max(kern, key=lambda n: kern[n]["total_ms"])
     log("kernels:", json.dumps(kern))
     roofline = dict(bound=kern[dom]["bound"], achieved=kern[dom]["achieved"],
                     peak=kern[dom]["peak"], unit=kern[dom]["unit"], frac=kern[dom]["frac"],
-                    traffic=None, kernel=dom, avg_launch_ms=kern[dom]["avg_launch_ms"])
+                    traffic=kern[dom]["traffic"], kernel=dom, avg_launch_ms=kern[dom]["avg_launch_ms"])
     sum_pairs, sum_sel = prefill_units(L, T, cfg.q_pos0, k, 0, T)
     prefill_flops = sum_pairs * idx_flop + sum_sel * mla_flop
     del sc, idx
 
     # ---- decode
-    decode = None
-    if not args.no_decode:
-        dcfg = WORKLOADS[args.decode_workload]
-        log("generating", dcfg.name)
-        dinp = make_decode(dcfg, device=dev)
-        B, N = dcfg.B, dinp["N"]
-        dout = torch.empty((B, dcfg.H, D_V), dtype=torch.bfloat16, device=dev)
-        dlse = torch.empty((B, dcfg.H), dtype=torch.float32, device=dev)
-        dws = torch.empty((dsa.dsa_decode_workspace_bytes(B, dinp["max_len"], N, dcfg.H_I,
-                                                          dcfg.H, dcfg.k),), dtype=torch.uint8,
-                          device=dev)
-
-        def dstep():
-            dsa.dsa_decode(dinp["seq_start"], dinp["max_len"], dinp["q8"], dinp["qs"],
-                           dinp["w"], dinp["k8"], dinp["ks"], dinp["q"], dinp["kv"], dcfg.k,
-                           dcfg.score_scale, dcfg.sm_scale, out=dout, lse=dlse, workspace=dws)
-
-        for _ in range(args.warmup):
-            dstep()
-        torch.cuda.synchronize()
-        d0, d1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        dsteps = max(args.steps, 20)
-        d0.record(stream)
-        for _ in range(dsteps):
-            dstep()
-        d1.record(stream)
-        torch.cuda.synchronize()
-        dms = d0.elapsed_time(d1) / dsteps
-        lens = dinp["lens"].cpu().numpy()
-        hbm = (lens.sum() * (D_I + 4) + np.minimum(lens, dcfg.k).sum() * D_QK * 2
-               + B * dcfg.H_I * (D_I + 8) + B * dcfg.H * (D_QK * 2 + D_V * 2 + 4))
-        gbs = hbm / (dms / 1e3) / 1e9
-        decode = dict(workload=dcfg.name, ms_per_step=round(dms, 4),
-                      tokens_per_s=round(B / (dms / 1e3), 1), sequences=B,
-                      context_tokens=int(N),
-                      roofline=dict(bound="hbm", achieved=round(gbs, 1), peak=HBM_PEAK_GBS,
-                                    unit="GB/s", frac=round(gbs / HBM_PEAK_GBS, 4),
-                                    algorithmic_bytes=int(hbm)))
-        log("decode %.4f ms/step, %.0f tokens/s, %.0f GB/s" % (dms, B / (dms / 1e3), gbs))
-        del dinp, dws
+    decode = None if args.no_decode else run_decode(args, WORKLOADS[args.decode_workload], dev)
 
     # ---- CPU oracle baseline on sampled rows of the same prefill workload
     cpu = None
@@ -238,6 +247,52 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)
+
+
+def run_decode(args, dcfg, dev):
+    """Time dsa_decode on one batch of the decode workload; returns its result object."""
+    import numpy as np
+    import torch
+
+    import sparse_attention_05_amd as dsa
+    from synth import make_decode
+
+    log("generating", dcfg.name)
+    dinp = make_decode(dcfg, device=dev)
+    B, N = dcfg.B, dinp["N"]
+    dout = torch.empty((B, dcfg.H, D_V), dtype=torch.bfloat16, device=dev)
+    dlse = torch.empty((B, dcfg.H), dtype=torch.float32, device=dev)
+    dws = torch.empty((dsa.dsa_decode_workspace_bytes(B, dinp["max_len"], N, dcfg.H_I, dcfg.H,
+                                                      dcfg.k),), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def dstep():
+        dsa.dsa_decode(dinp["seq_start"], dinp["max_len"], dinp["q8"], dinp["qs"], dinp["w"],
+                       dinp["k8"], dinp["ks"], dinp["q"], dinp["kv"], dcfg.k, dcfg.score_scale,
+                       dcfg.sm_scale, out=dout, lse=dlse, workspace=dws)
+
+    for _ in range(args.warmup):
+        dstep()
+    torch.cuda.synchronize()
+    d0, d1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    dsteps = max(args.steps, 20)
+    d0.record(stream)
+    for _ in range(dsteps):
+        dstep()
+    d1.record(stream)
+    torch.cuda.synchronize()
+    dms = d0.elapsed_time(d1) / dsteps
+    lens = dinp["lens"].cpu().numpy()
+    hbm = (lens.sum() * (D_I + 4) + np.minimum(lens, dcfg.k).sum() * D_QK * 2
+           + B * dcfg.H_I * (D_I + 8) + B * dcfg.H * (D_QK * 2 + D_V * 2 + 4))
+    gbs = hbm / (dms / 1e3) / 1e9
+    log("decode %.4f ms/step, %.0f tokens/s, %.0f GB/s" % (dms, B / (dms / 1e3), gbs))
+    return dict(workload=dcfg.name, ms_per_step=round(dms, 4),
+                tokens_per_s=round(B / (dms / 1e3), 1), sequences=B, context_tokens=int(N),
+                steps=dsteps,
+                roofline=dict(bound="hbm", achieved=round(gbs, 1), peak=HBM_PEAK_GBS,
+                              unit="GB/s", frac=round(gbs / HBM_PEAK_GBS, 4),
+                              algorithmic_bytes=int(hbm)))
 
 
 def cpu_baseline(inp, cfg, seconds):
