@@ -61,6 +61,20 @@ __device__ __forceinline__ uint32_t score_key(float f)
 
 __device__ __forceinline__ float shfl_xor_f(float v, int m) { return __shfl_xor(v, m, 64); }
 
+// max over lanes {l, l ^ 32} / {l, l ^ 16} on the lane-swap instructions (VALU, no LDS)
+__device__ __forceinline__ float max_xor32(float v)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v),
+                                                    false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_xor16(float v)
+{
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v),
+                                                    false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 // Reduce-scatter helpers on gfx950's lane-swap instructions.
 // fold32(x, y): lanes 0-31 get x summed over lanes l and l+32, lanes 32-63 get y so summed.
 __device__ __forceinline__ float fold32(float x, float y)

@@ -5,18 +5,27 @@
 // 512-d latent doubling as the value (《DeepSeek-V3.2-Exp模型优势与 DSA 工作原理》 §3 稀疏
 // MLA and §4 步骤四; 《狂降75%！…》 §三 第四步).
 //
-// One workgroup handles one query row for all heads (ceil(H/16) waves, 16 heads each) over
-// a contiguous slice of its index list.  The slice's indices are staged in LDS; the selected
-// 1152-byte rows are gathered 64 at a time by direct global->LDS loads into a double-buffered
-// tile (16-byte chunks XOR-swizzled by row), so the next tile streams in while the current
-// one is used.  Per 32-key half: S^T = K Q^T on bf16 MFMA (A = gathered rows, B = Q^T held in
-// registers), softmax in the exp2 domain with fp32 statistics against a per-head reference
-// max that moves only when exceeded by 2^8, then O += P V with P
-// already in the A-operand layout and V read from the same row-major tile through the LDS
-// transpose read (ds_read_b64_tr_b16), so no transposed copy of V is ever built.  Both
-// contractions are software-pipelined: LDS operands are read several MFMAs ahead and QK runs
-// as four independent accumulation chains, since two waves per SIMD alone cannot hide LDS
-// latency at this register budget (Q^T 72 + O 128 of 256 VGPRs).
+// One workgroup handles one query row for all heads over a contiguous slice of its index
+// list: four waves (128 head slots), one wave per SIMD with the full 512-register file.  The
+// selected 1152-byte rows are gathered 64 at a time by direct global->LDS loads into a
+// double-buffered tile, so the next tile streams in while the current one is used.  A tile
+// holds the rows' 512 latent dims as [64 rows][1024 B] and their 64 rope dims as
+// [64 rows][128 B], 16-byte chunks XOR-swizzled by row: one gather instruction moves one
+// row's latent part (a wave-uniform scalar base address plus a fixed per-lane chunk offset)
+// or the rope parts of eight rows, so issuing the gather costs a few scalar instructions per
+// row.  LDS read bandwidth, not MFMA, bounds the arithmetic, so the two contractions split
+// the work to minimise LDS reads:
+//  * S^T = K Q^T: wave w owns 32 heads (A = gathered rows, each 16-byte operand read feeding
+//    two MFMAs; B = Q^T held in registers) and their softmax, and writes P (bf16, already
+//    in the A-operand layout of P V) to LDS;
+//  * O = P V: wave w owns 128 of the value dims for every head, so each V element is read
+//    (by the transposing read ds_read_b64_tr_b16, half the rate of a plain 16-byte read) by
+//    one wave only, and P by every wave (plain 16-byte reads).
+// Softmax runs in the exp2 domain with fp32 statistics against a per-head reference max
+// fixed by the first valid logits of the row; O is never rescaled, which is what lets other
+// waves accumulate a head's P V.  Should a later logit exceed the reference by more than
+// 2^OVF_SLACK (a logit spread no real attention row reaches), the row is recomputed once
+// with the exact per-head max as the reference.
 #include "dsa_device.h"
 #include "kernels.h"
 
@@ -26,9 +35,14 @@ namespace {
 constexpr int MT = 64;                       // keys per tile
 constexpr int CH = 72;                       // 16-byte chunks per 1152-byte row
 constexpr int TILE_BYTES = MT * CH * 16;     // 73,728
-constexpr int IDX_SEG = 2048;                // indices staged in LDS at a time
+constexpr int LROW = 1024;                   // latent bytes per row (dims 0..511)
+constexpr int ROPE_OFF = MT * LROW;          // rope part of a tile: [MT rows][128 B]
+constexpr int RROW = 128;                    // rope bytes per row (dims 512..575)
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
+// Headroom of the fixed softmax reference (log2 units): p = 2^(x - m_ref) <= 2^64, so the
+// row sum stays below 2^77 for k <= 8192 and fp32 keeps its relative precision throughout.
+constexpr float OVF_SLACK = 64.f;
 
 typedef short v4s __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void_t;
@@ -41,19 +55,40 @@ __device__ __forceinline__ u32x2 ds_read_tr(const uint8_t* p)
     return __builtin_bit_cast(u32x2, v);
 }
 
-// tile byte offset of dims [8c, 8c + 8) of row r (chunk c of the 72 per row).  The XOR only
-// touches the low three chunk bits, so for c = 8a + b: offset = row_base(r) + 128 a +
-// 16 (b ^ (r & 7)) -- a per-lane base plus an immediate.
-__device__ __forceinline__ int row_base(int r) { return r * CH * 16; }
+// Direct global->LDS load of 16 bytes per lane: lane l's bytes land at LDS byte address
+// lds_dst + 16 l (lds_dst wave-uniform, passed in M0).  Written as one asm statement because
+// the compiler cannot tell that the LDS reads which follow it (of the other tile buffer) do not
+// touch the bytes in flight, and would otherwise wait for the load before each of them.  The
+// statement has no register results; completion is awaited explicitly (s_waitcnt 0 and a
+// barrier) before the destination buffer is read.
+__device__ __forceinline__ void dma16(const void* src, uint32_t lds_dst)
+{
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                 :
+                 : "v"(src), "s"(lds_dst)
+                 : "memory", "m0");
+}
+// the same with a wave-uniform 64-bit base in SGPRs and a 32-bit per-lane byte offset
+__device__ __forceinline__ void dma16_s(uint32_t voff, const void* sbase, uint32_t lds_dst)
+{
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :
+                 : "v"(voff), "s"(sbase), "s"(lds_dst)
+                 : "memory", "m0");
+}
+__device__ __forceinline__ uint32_t lds_addr(const void* p)
+{
+    return (uint32_t)(uintptr_t)(const lds_void_t*)p;
+}
+
+// tile byte offset of latent dims [8c, 8c + 8) of row r (chunk c < 64).  The XOR only touches
+// the low three chunk bits, so for c = 8a + b: offset = row_base(r) + 128 a + 16 (b ^ (r & 7))
+// -- a per-lane base plus an immediate.  Rope chunk 64 + b: ROPE_OFF + RROW r + sub_off(r, b).
+__device__ __forceinline__ int row_base(int r) { return r * LROW; }
 __device__ __forceinline__ int sub_off(int r, int b) { return (b ^ (r & 7)) << 4; }
 
-// Headroom of the softmax reference: a head's reference max m moves (and O is rescaled)
-// only when a logit exceeds it by more than REF_SLACK in log2 units, so p = 2^(x - m) stays
-// below 2^REF_SLACK -- far inside bf16/fp32 range -- and O is rescaled a handful of times
-// per row instead of whenever some head's running max creeps up.
-constexpr float REF_SLACK = 8.f;
-
-// NW waves per workgroup, 16 heads per wave.
+// NW waves; wave w: heads [32w, 32w + 32) in S^T / softmax (two 16-head groups hq), 16-dim
+// blocks [DPW w, DPW w + DPW) of O for all 2 NW head groups in P V.
 template <int NW>
 __global__ __launch_bounds__(NW * 64) void sparse_mla_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
@@ -61,15 +96,17 @@ __global__ __launch_bounds__(NW * 64) void sparse_mla_kernel(
     float sm_scale, int splits, uint16_t* __restrict__ out, float* __restrict__ lse,
     float* __restrict__ part_o, float* __restrict__ part_lse)
 {
-    constexpr int NT = NW * 64;
+    constexpr int NG = 2 * NW;                         // 16-head groups
+    constexpr int DPW = 32 / NW;                       // 16-dim blocks of O per wave
+    // P of one tile: [head group][32-key step][lane][8 bf16], the PV A-operand layout
     __shared__ __attribute__((aligned(16))) uint8_t s_tile[2][TILE_BYTES];
-    __shared__ int s_idx[IDX_SEG];
+    __shared__ __attribute__((aligned(16))) uint8_t s_p[NG * 2 * 64 * 16];
 
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 4, c16 = lane & 15;
     const int row = blockIdx.x, split = blockIdx.y;
-    const int h0 = wave * 16;
-    const int head = h0 + c16;                         // this lane's head in S^T / softmax
+    const int n0 = wave * DPW;                         // first 16-dim block of O owned here
 
     int64_t kv_base = 0;
     int Lr = L;
@@ -80,214 +117,285 @@ __global__ __launch_bounds__(NW * 64) void sparse_mla_kernel(
     const uint16_t* kvr = kv + kv_base * 576;
     const int per = (k + splits - 1) / splits;
     const int jbeg = split * per;
-    const int jend = min(k, jbeg + per);
+    const int nkeys = max(0, min(k, jbeg + per) - jbeg);
+    const int ntile = (nkeys + MT - 1) / MT;
+    const int32_t* idxr = idx + (int64_t)row * k + jbeg;
 
-    // B operand of S^T: Q^T, lane holds head c16, dims [32s + 8g, +8) for s = 0..17
-    u32x4 qreg[18];
-    {
-        const bool hv = head < H;
-        const uint16_t* qh = q + ((int64_t)row * H + (hv ? head : 0)) * 576;
+    // B operand of S^T: Q^T, lane holds head 32 wave + 16 hq + c16, dims [32s + 8g, +8)
+    u32x4 qreg[2][18];
+#pragma unroll
+    for (int hq = 0; hq < 2; ++hq) {
+        const int hh = wave * 32 + hq * 16 + c16;
+        const bool hv = hh < H;
+        const uint16_t* qh = q + ((int64_t)row * H + (hv ? hh : 0)) * 576;
 #pragma unroll
         for (int s = 0; s < 18; ++s)
-            qreg[s] = hv ? *reinterpret_cast<const u32x4*>(qh + 32 * s + 8 * g)
-                         : u32x4{0u, 0u, 0u, 0u};
+            qreg[hq][s] = hv ? *reinterpret_cast<const u32x4*>(qh + 32 * s + 8 * g)
+                             : u32x4{0u, 0u, 0u, 0u};
     }
-
-    v4f O[32];                                         // O[n]: heads 4g + r, dim 16n + c16
-#pragma unroll
-    for (int n = 0; n < 32; ++n) O[n] = v4f{0.f, 0.f, 0.f, 0.f};
-    float m_ref = -__builtin_huge_valf(), l_run = 0.f;
+    // Q^T complete before the tile loop: the compiler would otherwise place its wait for these
+    // loads inside the loop, as a full vector-memory wait that also drains the gathers
+    __builtin_amdgcn_s_waitcnt(0);
     const float scale2 = sm_scale * LOG2E;
 
-    // gather of tile t: 72 wave-instructions of 64 x 16 B; instruction qi fills tile bytes
-    // [1024 qi, +1024), lane l the chunk slot 64 qi + l
-    auto issue = [&](int seg_n, int t, int buf) {
-        for (int qi = wave; qi < MT * CH / 64; qi += NW) {
-            const int slot = qi * 64 + lane;
-            const int r = slot / CH, cs = slot - r * CH;
-            const int c = cs ^ (r & 7);
-            const int j = t * MT + r;
-            const int s = j < seg_n ? s_idx[j] : -1;
-            const uint16_t* src = kvr + (int64_t)(s >= 0 ? s : 0) * 576 + c * 8;
-            __builtin_amdgcn_global_load_lds((gbl_void_t*)src,
-                                             (lds_void_t*)(&s_tile[buf][qi * 1024]), 16, 0, 0);
+    // index of key t*MT + lane of the slice: loaded raw (from a clamped, always valid
+    // address, so that no wait is forced before the value is used) and checked at use
+    // (-1: past the slice, padding or out of range)
+    auto load_idx = [&](int t) -> int {
+        return idxr[min(t * MT + lane, max(nkeys - 1, 0))];
+    };
+    auto check_idx = [&](int t, int s) -> int {
+        return (t * MT + lane < nkeys && s >= 0 && s < Lr) ? s : -1;
+    };
+    // Gather of a tile into dst (tidx: lane r holds row r's index, -1 for padding, which loads
+    // row 0 and is masked later).  Latent parts: wave w moves rows [RPW w, RPW w + RPW), one
+    // instruction per row, lane l loading the source chunk stored in slot l (chunk l ^ (r & 7)).
+    // Rope parts: instruction j moves rows 8j .. 8j+7, lane l row 8j + l/8, slot l%8 (source
+    // chunk 64 + ((l%8) ^ (l/8)), whatever j).
+    constexpr int RPW = MT / NW;                       // latent rows per wave
+    constexpr int JPW = 8 / NW;                        // rope instructions per wave
+    const uint32_t rope_src = 16u * (64u + (uint32_t)((lane & 7) ^ (lane >> 3)));
+    const uint32_t lds_tiles = __builtin_amdgcn_readfirstlane(lds_addr(s_tile[0]));
+    auto issue = [&](int buf, int tidx) {
+        const uint32_t dst = lds_tiles + (uint32_t)buf * TILE_BYTES;
+#pragma unroll 2
+        for (int i0 = 0; i0 < RPW; i0 += 8)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int r = wave * RPW + i0 + i;         // r & 7 == i
+                const int sx = max(__builtin_amdgcn_readlane(tidx, r), 0);
+                dma16_s(16u * (uint32_t)(lane ^ i), kvr + (int64_t)sx * 576, dst + r * LROW);
+            }
+#pragma unroll
+        for (int jj = 0; jj < JPW; ++jj) {
+            const int j = wave * JPW + jj;
+            const int sx = max(__builtin_amdgcn_ds_bpermute((8 * j + (lane >> 3)) * 4, tidx), 0);
+            dma16(reinterpret_cast<const uint8_t*>(kvr + (int64_t)sx * 576) + rope_src,
+                  dst + ROPE_OFF + j * 1024);
         }
     };
 
+    v4f O[NG][DPW];                     // O[hg][d]: heads 16 hg + 4g + r, dims 16 (n0 + d) + c16
+    float m_ref[2], m_max[2] = {-__builtin_huge_valf(), -__builtin_huge_valf()}, l_run[2];
+
 #pragma unroll 1
-    for (int seg0 = jbeg; seg0 < jend; seg0 += IDX_SEG) {
-        const int seg_n = min(IDX_SEG, jend - seg0);
-        __syncthreads();                               // previous segment fully consumed
-        for (int j = tid; j < seg_n; j += NT) {
-            const int s = idx[(int64_t)row * k + seg0 + j];
-            s_idx[j] = (s >= 0 && s < Lr) ? s : -1;
+    for (int pass = 0; pass < 2; ++pass) {
+#pragma unroll
+        for (int hg = 0; hg < NG; ++hg)
+#pragma unroll
+            for (int d = 0; d < DPW; ++d) O[hg][d] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int hq = 0; hq < 2; ++hq) {
+            l_run[hq] = 0.f;
+            m_ref[hq] = pass ? m_max[hq] : -__builtin_huge_valf();
         }
-        __syncthreads();
-        const int ntile = (seg_n + MT - 1) / MT;
-        issue(seg_n, 0, 0);
-#pragma unroll 1
-        for (int t = 0; t < ntile; ++t) {
+        bool over = false;
+        int idx_cur = 0, idx_nxt = 0;
+        if (ntile > 0) {
+            idx_cur = check_idx(0, load_idx(0));
+            idx_nxt = load_idx(1);
+            issue(0, idx_cur);
+        }
+        // one tile: tb holds it, the other buffer receives the next one
+        auto step = [&](int t, const uint8_t* tb) {
             __builtin_amdgcn_s_waitcnt(0);             // this wave's part of tile t landed
-            __syncthreads();                           // everyone's part; tile t-1 consumed
-            if (t + 1 < ntile) issue(seg_n, t + 1, (t + 1) & 1);
-            const uint8_t* tb = s_tile[t & 1];
-            // validity of the tile's 64 keys as one wave-uniform mask
-            const int jt = t * MT + lane;
-            const uint64_t vmask = __ballot(jt < seg_n && s_idx[jt] >= 0);
+            __syncthreads();                           // everyone's part; tile t-1 and P consumed
+            const uint64_t vmask = __ballot(idx_cur >= 0);
+            idx_nxt = check_idx(t + 1, idx_nxt);
+            if (t + 1 < ntile) issue((t + 1) & 1, idx_nxt);
+            idx_cur = idx_nxt;
+            idx_nxt = load_idx(t + 2);
 #pragma unroll 1
             for (int half = 0; half < 2; ++half) {
-                // S^T[key][head] for keys 32 half + 16 kt + (4g + r);
-                // A = row 32 half + 16 kt + c16, dims [32s + 8g, +8): chunk 4s + g
-                // four independent accumulation chains (2 key groups x even/odd K steps),
-                // A operands read QD steps ahead
-                v4f S[2], S2[2];
-                const uint8_t* rb[2];
-                int oo[2][2];
+                // S^T[key][head] for keys 32 half + 16 kt + (4g + r), heads 16 hq + c16;
+                // A = row 32 half + 16 kt + c16, dims [32s + 8g, +8): chunk 4s + g, each A
+                // read feeding both head groups; A operands read QD steps ahead
+                v4f S[2][2];
 #pragma unroll
-                for (int kt = 0; kt < 2; ++kt) {
-                    const int r = half * 32 + kt * 16 + c16;
-                    rb[kt] = tb + row_base(r);
-                    oo[kt][0] = sub_off(r, g);
-                    oo[kt][1] = sub_off(r, 4 + g);
-                    S[kt] = v4f{0.f, 0.f, 0.f, 0.f};
-                    S2[kt] = v4f{0.f, 0.f, 0.f, 0.f};
-                }
+                for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                    for (int hq = 0; hq < 2; ++hq) S[kt][hq] = v4f{0.f, 0.f, 0.f, 0.f};
+                const uint8_t* rb = tb + row_base(half * 32 + c16);    // kt adds 16 rows
+                const uint8_t* rr = tb + ROPE_OFF + RROW * (half * 32 + c16);
+                int oo[2];
+                oo[0] = sub_off(c16, g);                // row & 7 == c16 & 7 for these rows
+                oo[1] = sub_off(c16, 4 + g);
+                // Software pipeline with fixed stages: stage s issues the reads of step s + QD
+                // and the four MFMAs of step s; the scheduling barriers keep the compiler from
+                // collapsing it into read -> wait -> MFMA (one wave per SIMD leaves nothing
+                // else to hide LDS latency).
                 constexpr int QD = 3;
                 u32x4 abuf[QD][2];
 #pragma unroll
                 for (int s = 0; s < QD; ++s)
 #pragma unroll
                     for (int kt = 0; kt < 2; ++kt)
-                        abuf[s][kt] = *reinterpret_cast<const u32x4*>(rb[kt] + 128 * (s >> 1) + oo[kt][s & 1]);
+                        abuf[s][kt] = *reinterpret_cast<const u32x4*>(rb + kt * 16 * LROW + 128 * (s >> 1) + oo[s & 1]);
 #pragma unroll
                 for (int s = 0; s < 18; ++s) {
+                    __builtin_amdgcn_sched_barrier(0);
                     u32x4 a[2] = {abuf[s % QD][0], abuf[s % QD][1]};
                     if (s + QD < 18) {
                         const int m = s + QD;
 #pragma unroll
                         for (int kt = 0; kt < 2; ++kt)
-                            abuf[s % QD][kt] = *reinterpret_cast<const u32x4*>(rb[kt] + 128 * (m >> 1) + oo[kt][m & 1]);
+                            abuf[s % QD][kt] = *reinterpret_cast<const u32x4*>(
+                                m < 16 ? rb + kt * 16 * LROW + 128 * (m >> 1) + oo[m & 1]
+                                       : rr + kt * 16 * RROW + oo[m & 1]);
                     }
+#pragma unroll
+                    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                        for (int hq = 0; hq < 2; ++hq)
+                            S[kt][hq] = mfma_bf16(as_bf16x8(a[kt]), as_bf16x8(qreg[hq][s]), S[kt][hq]);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                // softmax for heads 16 hq + c16 over this half's 32 keys
+#pragma unroll
+                for (int hq = 0; hq < 2; ++hq) {
+                    float x[2][4];
+                    float mloc = -__builtin_huge_valf();
 #pragma unroll
                     for (int kt = 0; kt < 2; ++kt) {
-                        if (s & 1) S2[kt] = mfma_bf16(as_bf16x8(a[kt]), as_bf16x8(qreg[s]), S2[kt]);
-                        else S[kt] = mfma_bf16(as_bf16x8(a[kt]), as_bf16x8(qreg[s]), S[kt]);
+                        const uint32_t bits = (uint32_t)(vmask >> (half * 32 + kt * 16 + 4 * g));
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            x[kt][r] = ((bits >> r) & 1u) ? S[kt][hq][r] * scale2 : -__builtin_huge_valf();
+                            mloc = fmaxf(mloc, x[kt][r]);
+                        }
                     }
-                }
+                    mloc = max_xor32(max_xor16(mloc));
+                    m_max[hq] = fmaxf(m_max[hq], mloc);
+                    // the first valid logits fix the reference (O and l are still zero then)
+                    if (m_ref[hq] == -__builtin_huge_valf()) m_ref[hq] = mloc;
+                    over |= mloc > m_ref[hq] + OVF_SLACK;
+                    // no valid logit yet: keep exp2(-inf - m) = 0 rather than exp2(-inf + inf)
+                    const float m_sub = m_ref[hq] == -__builtin_huge_valf() ? 0.f : m_ref[hq];
+                    float p[2][4];
+                    float psum = 0.f;
 #pragma unroll
-                for (int kt = 0; kt < 2; ++kt) S[kt] += S2[kt];
-                // softmax statistics for head c16 over this half's 32 keys
-                float x[2][4];
-                float mloc = -__builtin_huge_valf();
+                    for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-                for (int kt = 0; kt < 2; ++kt) {
-                    const uint32_t bits = (uint32_t)(vmask >> (half * 32 + kt * 16 + 4 * g));
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        x[kt][r] = ((bits >> r) & 1u) ? S[kt][r] * scale2 : -__builtin_huge_valf();
-                        mloc = fmaxf(mloc, x[kt][r]);
-                    }
-                }
-                mloc = fmaxf(mloc, shfl_xor_f(mloc, 16));
-                mloc = fmaxf(mloc, shfl_xor_f(mloc, 32));
-                // move the reference only when the new max clears the headroom
-                const bool move = mloc > m_ref + REF_SLACK;
-                const float m_new = move ? mloc : m_ref;
-                const float alpha = move ? __builtin_amdgcn_exp2f(m_ref - m_new) : 1.f;
-                const bool rescale = move && m_ref != -__builtin_huge_valf();
-                m_ref = m_new;
-                // no valid logit yet: keep exp2(-inf - m) = 0 rather than exp2(-inf + inf)
-                const float m_sub = m_new == -__builtin_huge_valf() ? 0.f : m_new;
-                float p[2][4];
-                float psum = 0.f;
-#pragma unroll
-                for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        p[kt][r] = __builtin_amdgcn_exp2f(x[kt][r] - m_sub);
-                        psum += p[kt][r];
-                    }
-                l_run = l_run * alpha + psum;
-                if (__any(rescale)) {                  // rare: some head's reference moved
-                    float ar[4];
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) ar[r] = __shfl(alpha, 4 * g + r, 64);
-#pragma unroll
-                    for (int n = 0; n < 32; ++n)
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) O[n][r] *= ar[r];
-                }
-                // A operand of P V: head c16, K = keys {4g..4g+3} of each 16-key group
-                const v8bf pav = __builtin_convertvector(
-                    (v8f){p[0][0], p[0][1], p[0][2], p[0][3], p[1][0], p[1][1], p[1][2], p[1][3]},
-                    v8bf);
-                // V operand: column 16n + c16, keys 32 half + 16 kt + 4g + r, by transpose reads:
-                // lane (g, i) addresses row 32 half + 16 kt + 4g + i/4, dims 16n + 4(i%4) .. +3,
-                // i.e. chunk 2n + (i%4)/2 = 8(n/4) + (2(n%4) + (i%4)/2), byte 8 (i%2) within it
-                const int rv0 = half * 32 + 4 * g + (c16 >> 2), rv1 = rv0 + 16;
-                const int cpart = (c16 & 3) >> 1, boff = (c16 & 1) * 8;
-                const uint8_t* vb0 = tb + row_base(rv0) + boff;
-                const uint8_t* vb1 = tb + row_base(rv1) + boff;
-                int vo0[4], vo1[4];
-#pragma unroll
-                for (int m = 0; m < 4; ++m) {
-                    vo0[m] = sub_off(rv0, 2 * m + cpart);
-                    vo1[m] = sub_off(rv1, 2 * m + cpart);
-                }
-                // software-pipelined: the V operand of MFMA n is read PD MFMAs ahead
-                constexpr int PD = 4;
-                u32x2 vlo[PD], vhi[PD];
-#pragma unroll
-                for (int n = 0; n < PD; ++n) {
-                    vlo[n] = ds_read_tr(vb0 + 128 * (n >> 2) + vo0[n & 3]);
-                    vhi[n] = ds_read_tr(vb1 + 128 * (n >> 2) + vo1[n & 3]);
-                }
-#pragma unroll
-                for (int n = 0; n < 32; ++n) {
-                    u32x4 vb;
-                    vb[0] = vlo[n % PD][0]; vb[1] = vlo[n % PD][1];
-                    vb[2] = vhi[n % PD][0]; vb[3] = vhi[n % PD][1];
-                    if (n + PD < 32) {
-                        const int m = n + PD;
-                        vlo[n % PD] = ds_read_tr(vb0 + 128 * (m >> 2) + vo0[m & 3]);
-                        vhi[n % PD] = ds_read_tr(vb1 + 128 * (m >> 2) + vo1[m & 3]);
-                    }
-                    O[n] = mfma_bf16(pav, as_bf16x8(vb), O[n]);
+                        for (int r = 0; r < 4; ++r) {
+                            p[kt][r] = __builtin_amdgcn_exp2f(x[kt][r] - m_sub);
+                            psum += p[kt][r];
+                        }
+                    l_run[hq] += psum;
+                    // A operand of P V: head c16, K = keys {4g..4g+3} of each 16-key group
+                    const v8bf pav = __builtin_convertvector(
+                        (v8f){p[0][0], p[0][1], p[0][2], p[0][3], p[1][0], p[1][1], p[1][2], p[1][3]},
+                        v8bf);
+                    *reinterpret_cast<v8bf*>(&s_p[(((2 * wave + hq) * 2 + half) * 64 + lane) * 16]) = pav;
                 }
             }
-        }
+            __syncthreads();                           // P of every head group visible
+
+            // O[hg][d] += P[hg] V[:, dims of block n0 + d] over the tile's two 32-key steps.
+            // V operand: column 16n + c16, keys 32 ks + 16 kt + 4g + r, by transpose reads:
+            // lane (g, i) addresses row 32 ks + 16 kt + 4g + i/4, dims 16n + 4(i%4) .. +3,
+            // i.e. chunk 2n + (i%4)/2 = 8(n/4) + (2(n%4) + (i%4)/2), byte 8 (i%2) within it
+            const int cpart = (c16 & 3) >> 1, boff = (c16 & 1) * 8;
+            const int rv = 4 * g + (c16 >> 2);         // row within each 16-key group
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                const int vrow = row_base(ks * 32 + rv) + boff;
+                // V operands of DC owned blocks held at a time, P streamed per head group
+                constexpr int DC = DPW < 8 ? DPW : 8;
+#pragma unroll
+                for (int d0 = 0; d0 < DPW; d0 += DC) {
+                    u32x4 vop[DC];
+#pragma unroll
+                    for (int d = 0; d < DC; ++d) {
+                        const int n = n0 + d0 + d;
+                        const int o = vrow + 128 * (n >> 2) + sub_off(rv, 2 * (n & 3) + cpart);
+                        const u32x2 lo = ds_read_tr(tb + o);
+                        const u32x2 hi = ds_read_tr(tb + o + 16 * LROW);
+                        vop[d] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+                    }
+                    constexpr int PD = NG < 2 ? NG : 2;
+                    u32x4 pbuf[PD];
+#pragma unroll
+                    for (int hg = 0; hg < PD; ++hg)
+                        pbuf[hg] = *reinterpret_cast<const u32x4*>(&s_p[((hg * 2 + ks) * 64 + lane) * 16]);
+#pragma unroll
+                    for (int hg = 0; hg < NG; ++hg) {
+                        __builtin_amdgcn_sched_barrier(0);     // stage hg: P read of hg + PD
+                        const u32x4 pa = pbuf[hg % PD];
+                        if (hg + PD < NG)
+                            pbuf[hg % PD] = *reinterpret_cast<const u32x4*>(&s_p[(((hg + PD) * 2 + ks) * 64 + lane) * 16]);
+#pragma unroll
+                        for (int d = 0; d < DC; ++d)
+                            O[hg][d0 + d] = mfma_bf16(as_bf16x8(pa), as_bf16x8(vop[d]), O[hg][d0 + d]);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+        };
+#pragma unroll 1
+        for (int t = 0; t < ntile; ++t) step(t, s_tile[t & 1]);
+        // every wave must agree on a recomputation: flags through LDS
+        __syncthreads();                               // last tile's P V done everywhere
+        int* s_flag = reinterpret_cast<int*>(s_p);
+        const bool wave_over = __any(over);
+        if (lane == 0) s_flag[wave] = wave_over ? 1 : 0;
+        __syncthreads();
+        bool redo = false;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) redo |= s_flag[w] != 0;
+        __syncthreads();                               // flags read before s_p is reused
+        if (!redo) break;
     }
 
-    // totals per head c16, then per O row (head 4g + r)
-    float l_tot = l_run + shfl_xor_f(l_run, 16);
-    l_tot += shfl_xor_f(l_tot, 32);
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    const float my_lse = l_tot > 0.f ? m_ref * LN2 + logf(l_tot) : -__builtin_huge_valf();
-    float ir[4];
+    // totals per head (owner wave), shared with the waves holding that head's O columns
+    float* s_inv = reinterpret_cast<float*>(s_p);
+    float my_lse[2];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) ir[r] = __shfl(inv, 4 * g + r, 64);
+    for (int hq = 0; hq < 2; ++hq) {
+        float l_tot = l_run[hq] + shfl_xor_f(l_run[hq], 16);
+        l_tot += shfl_xor_f(l_tot, 32);
+        my_lse[hq] = l_tot > 0.f ? m_ref[hq] * LN2 + logf(l_tot) : -__builtin_huge_valf();
+        if (g == 0) s_inv[wave * 32 + hq * 16 + c16] = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    }
+    __syncthreads();
 
     if (splits == 1) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int hh = h0 + 4 * g + r;
-            if (hh >= H) continue;
-            uint16_t* orow = out + ((int64_t)row * H + hh) * 512;
+        for (int hg = 0; hg < NG; ++hg)
 #pragma unroll
-            for (int n = 0; n < 32; ++n) orow[16 * n + c16] = (uint16_t)bf16_bits(O[n][r] * ir[r]);
-        }
-        if (lse && g == 0 && head < H) lse[(int64_t)row * H + head] = my_lse;
+            for (int r = 0; r < 4; ++r) {
+                const int hh = hg * 16 + 4 * g + r;
+                if (hh >= H) continue;
+                const float ir = s_inv[hh];
+                uint16_t* orow = out + ((int64_t)row * H + hh) * 512;
+#pragma unroll
+                for (int d = 0; d < DPW; ++d)
+                    orow[16 * (n0 + d) + c16] = (uint16_t)bf16_bits(O[hg][d][r] * ir);
+            }
+        if (lse && g == 0)
+#pragma unroll
+            for (int hq = 0; hq < 2; ++hq) {
+                const int hh = wave * 32 + hq * 16 + c16;
+                if (hh < H) lse[(int64_t)row * H + hh] = my_lse[hq];
+            }
     } else {
         const int64_t pb = ((int64_t)row * splits + split) * H;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int hh = h0 + 4 * g + r;
-            if (hh >= H) continue;
-            float* orow = part_o + (pb + hh) * 512;
+        for (int hg = 0; hg < NG; ++hg)
 #pragma unroll
-            for (int n = 0; n < 32; ++n) orow[16 * n + c16] = O[n][r] * ir[r];
-        }
-        if (g == 0 && head < H) part_lse[pb + head] = my_lse;
+            for (int r = 0; r < 4; ++r) {
+                const int hh = hg * 16 + 4 * g + r;
+                if (hh >= H) continue;
+                const float ir = s_inv[hh];
+                float* orow = part_o + (pb + hh) * 512;
+#pragma unroll
+                for (int d = 0; d < DPW; ++d) orow[16 * (n0 + d) + c16] = O[hg][d][r] * ir;
+            }
+        if (g == 0)
+#pragma unroll
+            for (int hq = 0; hq < 2; ++hq) {
+                const int hh = wave * 32 + hq * 16 + c16;
+                if (hh < H) part_lse[pb + hh] = my_lse[hq];
+            }
     }
 }
 
@@ -345,15 +453,10 @@ hipError_t launch_sparse_mla(const uint16_t* q, const uint16_t* kv, const int32_
                              float* part_o, float* part_lse, hipStream_t stream)
 {
     if (T <= 0) return hipSuccess;
-    const int nw = (H + 15) / 16;                       // 16 heads per wave
-#define DSA_MLA_CASE(NW) \
-    case NW: return launch_nw<NW>(q, kv, idx, seq_start, T, L, H, k, sm_scale, splits, out, lse, part_o, part_lse, stream);
-    switch (nw) {
-        DSA_MLA_CASE(1) DSA_MLA_CASE(2) DSA_MLA_CASE(3) DSA_MLA_CASE(4)
-        DSA_MLA_CASE(5) DSA_MLA_CASE(6) DSA_MLA_CASE(7) DSA_MLA_CASE(8)
-        default: return hipErrorInvalidValue;
-    }
-#undef DSA_MLA_CASE
+    // four waves of 32 head slots; fewer heads leave slots empty (their queries read as zero
+    // and their outputs are not written): one shape, whose registers fit without spilling
+    if (H <= 128) return launch_nw<4>(q, kv, idx, seq_start, T, L, H, k, sm_scale, splits, out, lse, part_o, part_lse, stream);
+    return hipErrorInvalidValue;
 }
 
 hipError_t launch_mla_combine(const float* part_o, const float* part_lse, int T, int H,
