@@ -16,8 +16,11 @@ namespace {
 
 // ---------------------------------------------------------------- prefill geometry
 constexpr int IP_WAVES = 8;                // waves per workgroup
-constexpr int IP_ROWS = 128;               // (token, head) rows per wave
-constexpr int IP_NT = IP_ROWS / 16;        // 16-row MFMA tiles per wave
+// (token, head) rows per wave: 64 (four waves per SIMD, so that one wave's MFMA burst runs
+// while others work through their epilogues), except 128 for H_I = 128, whose head sum
+// needs a whole token in one wave
+template <int HI> constexpr int ip_rows() { return HI >= 128 ? 128 : 64; }
+template <int HI> constexpr int ip_waves_per_simd() { return (HI >= 128 || HI <= 2) ? 2 : 4; }
 constexpr int IP_KT = 128;                 // keys per LDS tile
 constexpr int IP_KSPLIT = 4096;            // keys per workgroup (grid.y)
 
@@ -30,15 +33,15 @@ __device__ __forceinline__ int ktile_off(int key, int chunk)
 
 // Head reduction of one 32-key step.  acc[kb][j][r] holds D for tile row 4g + r of tile j
 // and key kb*16 + c16.  Calls emit(token_in_wave, kb, value) once per distinct output.
-template <int HI, typename Emit>
-__device__ __forceinline__ void reduce_heads(const v4f (&acc)[2][IP_NT],
-                                             const float (&wp)[IP_NT][4], int lane,
+template <int HI, int NT, typename Emit>
+__device__ __forceinline__ void reduce_heads(const v4f (&acc)[2][NT],
+                                             const float (&wp)[NT][4], int lane,
                                              Emit&& emit)
 {
     const int g = lane >> 4;
     const bool odd = (g & 1) != 0;
     if constexpr (HI >= 16) {
-        constexpr int TPW = IP_ROWS / HI;      // tokens per wave
+        constexpr int TPW = NT * 16 / HI;      // tokens per wave
         constexpr int TPT = HI / 16;           // tiles per token
         constexpr int NO = 2 * TPW;            // (token, key block) partials per lane
         constexpr int N1 = NO / 2;
@@ -78,7 +81,7 @@ __device__ __forceinline__ void reduce_heads(const v4f (&acc)[2][IP_NT],
     } else if constexpr (HI == 8) {
         // tile j: rows 0-7 token 2j, rows 8-15 token 2j+1; group g: token 2j + g/2
 #pragma unroll
-        for (int j = 0; j < IP_NT; ++j) {
+        for (int j = 0; j < NT; ++j) {
             float p0 = 0.f, p1 = 0.f;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
@@ -91,7 +94,7 @@ __device__ __forceinline__ void reduce_heads(const v4f (&acc)[2][IP_NT],
         // HI in {1, 2, 4}: the lane's four rows hold 4/HI whole tokens
         constexpr int UPL = 4 / HI;
 #pragma unroll
-        for (int j = 0; j < IP_NT; ++j) {
+        for (int j = 0; j < NT; ++j) {
 #pragma unroll
             for (int u = 0; u < UPL; ++u) {
 #pragma unroll
@@ -107,16 +110,18 @@ __device__ __forceinline__ void reduce_heads(const v4f (&acc)[2][IP_NT],
     }
 }
 
-// Grid: x = token blocks of IP_WAVES * 128/HI rows (heaviest, i.e. latest, first),
+// Grid: x = token blocks of IP_WAVES * ip_rows/HI tokens (heaviest, i.e. latest, first),
 //       y = key ranges of IP_KSPLIT keys.  Each wave keeps 128 (token, head) query rows
 // in registers as MFMA A operands; the workgroup streams 128-key tiles through a
 // double-buffered LDS ring that all eight waves read as B operands.
 template <int HI>
-__global__ __launch_bounds__(IP_WAVES * 64) void indexer_prefill_kernel(
+__global__ __launch_bounds__(IP_WAVES * 64, ip_waves_per_simd<HI>()) void indexer_prefill_kernel(
     const uint8_t* __restrict__ q8, const float* __restrict__ qs, const float* __restrict__ w,
     const uint8_t* __restrict__ k8, const float* __restrict__ ks, int T, int q_pos0, float c,
     float* __restrict__ scores, int64_t ld)
 {
+    constexpr int IP_ROWS = ip_rows<HI>();
+    constexpr int IP_NT = IP_ROWS / 16;        // 16-row MFMA tiles per wave
     constexpr int TPW = IP_ROWS / HI;
     constexpr int TB = IP_WAVES * TPW;
     __shared__ __attribute__((aligned(16))) uint8_t s_key[2][IP_KT * 128];
@@ -209,7 +214,7 @@ __global__ __launch_bounds__(IP_WAVES * 64) void indexer_prefill_kernel(
                 // issue the step's MFMAs as one burst; the epilogue then trails the matrix
                 // pipe instead of waiting on each result in turn
                 __builtin_amdgcn_sched_barrier(0);
-                reduce_heads<HI>(acc, wp, lane, [&](int tok, int kb, float v) {
+                reduce_heads<HI, IP_NT>(acc, wp, lane, [&](int tok, int kb, float v) {
                     const int t = tw0 + tok;
                     const int s = key0 + kb * 16 + c16;
                     if (t < T && s <= q_pos0 + t && s < kend)
@@ -312,7 +317,7 @@ hipError_t launch_prefill_hi(const uint8_t* q8, const float* qs, const float* w,
                              const uint8_t* k8, const float* ks, int T, int L, int q_pos0,
                              float c, float* scores, int64_t ld, hipStream_t stream)
 {
-    constexpr int TB = IP_WAVES * (IP_ROWS / HI);
+    constexpr int TB = IP_WAVES * (ip_rows<HI>() / HI);
     const int keys = min(L, q_pos0 + T);               // keys any row can see
     dim3 grid((T + TB - 1) / TB, (keys + IP_KSPLIT - 1) / IP_KSPLIT);
     hipLaunchKernelGGL(indexer_prefill_kernel<HI>, grid, dim3(IP_WAVES * 64), 0, stream, q8,

@@ -169,6 +169,48 @@ def test_sparse_mla_parity(dsa, H, L, k):
     check_mla(bf16_to_f64(out), _np(lse), oo, ol, "mla H=%d L=%d k=%d" % (H, L, k))
 
 
+@pytest.mark.parametrize("L,k", [(9000, 6000), (8300, 8192)])
+def test_sparse_mla_long_index_lists(dsa, L, k):
+    """Index lists longer than the kernel's 4096-key validity segment (two segments, padding
+    holes in both): every row against the oracle."""
+    cfg = _cfg(L, k, 4, 128, seed=k, T=4, q_pos0=L - 4)
+    inp = make_prefill(cfg)
+    h, d = host_arrays(inp), to_device(inp)
+    idx = _random_idx(cfg.rows, L, k, cfg.q_pos0, np.random.default_rng(k))
+    idx[:, ::7] = -1                                   # holes in every 32-key tile
+    out, lse = dsa.dsa_sparse_mla(d["q"], d["kv"], torch.from_numpy(idx).cuda(), cfg.sm_scale)
+    torch.cuda.synchronize()
+    oo, ol = oracle.sparse_mla(h["q"], h["kv"], idx, cfg.sm_scale)
+    check_mla(bf16_to_f64(out), _np(lse), oo, ol, "mla long L=%d k=%d" % (L, k))
+
+
+def test_sparse_mla_late_dominant_logit_recomputes(dsa):
+    """The kernel fixes each head's softmax reference from the first valid logits and
+    recomputes the row with the exact maximum when a later logit exceeds that reference by
+    more than 2^64 in the exp2 domain.  Here the first 32 selected keys have logits of order
+    1 and a key late in the list has logit 96 for every head: results must still match the
+    oracle (and be finite)."""
+    L, k, T, H = 200, 100, 3, 128
+    cfg = _cfg(L, k, 4, H, seed=11, T=T, q_pos0=L - T)
+    inp = make_prefill(cfg)
+    inp["q"] = torch.full_like(inp["q"], 2.0)          # q . kv[big] = 2 * 2 * 576 = 2304
+    kv = inp["kv"].clone()
+    kv[150] = 2.0
+    inp["kv"] = kv
+    h, d = host_arrays(inp), to_device(inp)
+    rng = np.random.default_rng(5)
+    idx = np.full((T, k), -1, np.int32)
+    for t in range(T):
+        sel = rng.choice(np.setdiff1d(np.arange(L - T + t + 1), [150]), size=k - 1, replace=False)
+        idx[t, :k - 1] = sel
+        idx[t, 60 + t] , idx[t, k - 1] = 150, idx[t, 60 + t]   # key 150 at position 60 + t
+    out, lse = dsa.dsa_sparse_mla(d["q"], d["kv"], torch.from_numpy(idx).cuda(), cfg.sm_scale)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out.float()).all() and torch.isfinite(lse).all()
+    oo, ol = oracle.sparse_mla(h["q"], h["kv"], idx, cfg.sm_scale)
+    check_mla(bf16_to_f64(out), _np(lse), oo, ol, "mla late dominant logit")
+
+
 def test_sparse_mla_single_row_closed_form_and_empty_rows(dsa):
     """A row selecting only token 0 returns kv[0, :512] exactly (softmax weight 1); a row
     with no valid index (all -1 or out of range) returns zeros and lse = -inf."""
