@@ -280,21 +280,35 @@ __global__ __launch_bounds__(ID_WAVES * 64) void indexer_decode_kernel(
         }
     }
 
-#pragma unroll 1
-    for (int it = 0; it < ID_KPW / 64; ++it) {
+    // All of the wave's key rows (and their scales) are requested before any is used, so
+    // 32 KB per wave are in flight: the loop is bound by HBM latency otherwise.
+    constexpr int NS = ID_KPW / 64;                  // 64-key steps per wave
+    u32x4 kd[NS][4][2];
+    float ksv[NS];
+#pragma unroll
+    for (int it = 0; it < NS; ++it) {
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+            const int key = sw0 + it * 64 + kb * 16 + c16;
+            kd[it][kb][0] = u32x4{0u, 0u, 0u, 0u};
+            kd[it][kb][1] = u32x4{0u, 0u, 0u, 0u};
+            if (key < Lb) {
+                const uint8_t* src = k8 + (a + key) * 128;
+                kd[it][kb][0] = *reinterpret_cast<const u32x4*>(src + 16 * g);
+                kd[it][kb][1] = *reinterpret_cast<const u32x4*>(src + 64 + 16 * g);
+            }
+        }
+        const int key = sw0 + it * 64 + g * 16 + c16;
+        ksv[it] = key < Lb ? ks[a + key] : 0.f;
+    }
+#pragma unroll
+    for (int it = 0; it < NS; ++it) {
         const int s0 = sw0 + it * 64;
         if (s0 >= Lb) break;
         float P[4];
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
-            const int key = s0 + kb * 16 + c16;
-            u32x4 lo = {0u, 0u, 0u, 0u}, hi = {0u, 0u, 0u, 0u};
-            if (key < Lb) {
-                const uint8_t* src = k8 + (a + key) * 128;
-                lo = *reinterpret_cast<const u32x4*>(src + 16 * g);
-                hi = *reinterpret_cast<const u32x4*>(src + 64 + 16 * g);
-            }
-            const v8i bb = as_i8(lo, hi);
+            const v8i bb = as_i8(kd[it][kb][0], kd[it][kb][1]);
             float s = 0.f;
 #pragma unroll
             for (int j = 0; j < NTQ; ++j) {
@@ -308,7 +322,7 @@ __global__ __launch_bounds__(ID_WAVES * 64) void indexer_decode_kernel(
         const float Q0 = fold32(P[0], P[2]), Q1 = fold32(P[1], P[3]);
         const float v = fold16(Q0, Q1);
         const int key = s0 + g * 16 + c16;
-        if (key < Lb) scores[a + key] = v * ks[a + key];
+        if (key < Lb) scores[a + key] = v * ksv[it];
     }
 }
 
