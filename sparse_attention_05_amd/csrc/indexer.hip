@@ -195,7 +195,49 @@ __global__ __launch_bounds__(IP_WAVES * 64, ip_waves_per_simd<HI>()) void indexe
         const int buf = it & 1;
         if (it + 1 < ntiles) gload(it + 1);
         const int tbase = kbeg + it * IP_KT;
-        if (wave_active && tbase <= pw_last) {
+        if constexpr (TPW == 1) {
+            // one token per wave: 64-key steps of two 32-key MFMA bursts, each folded into
+            // per-16-key-block partials right away; one reduce-scatter then leaves lane group
+            // g with the finished sum of key block g, so every lane emits one output
+            if (wave_active && tbase <= pw_last) {
+                float* srow = scores + (int64_t)tw0 * ld + tbase;   // wave-uniform
+#pragma unroll
+                for (int step = 0; step < IP_KT / 64; ++step) {
+                    const int key0 = tbase + step * 64;
+                    if (key0 > pw_last) break;
+                    float P[4];
+#pragma unroll
+                    for (int half = 0; half < 2; ++half) {
+                        v4f acc[2][IP_NT];
+#pragma unroll
+                        for (int kb = 0; kb < 2; ++kb) {
+                            const int kl = step * 64 + half * 32 + kb * 16 + c16;
+                            const u32x4 lo = *reinterpret_cast<const u32x4*>(&s_key[buf][ktile_off(kl, 2 * g)]);
+                            const u32x4 hi = *reinterpret_cast<const u32x4*>(&s_key[buf][ktile_off(kl, 2 * g + 1)]);
+                            const v8i bb = as_i8(lo, hi);
+#pragma unroll
+                            for (int j = 0; j < IP_NT; ++j)
+                                acc[kb][j] = mfma_f8(qa[j], bb, v4f{0.f, 0.f, 0.f, 0.f});
+                        }
+                        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                        for (int kb = 0; kb < 2; ++kb) {
+                            float sum = 0.f;
+#pragma unroll
+                            for (int j = 0; j < IP_NT; ++j)
+#pragma unroll
+                                for (int r = 0; r < 4; ++r)
+                                    sum = fmaf(wp[j][r], fmaxf(acc[kb][j][r], 0.f), sum);
+                            P[2 * half + kb] = sum;
+                        }
+                    }
+                    const float v = fold16(fold32(P[0], P[2]), fold32(P[1], P[3]));
+                    const int sl = step * 64 + 16 * g + c16;          // key within the tile
+                    if (tbase + sl <= pw_last && tbase + sl < kend)
+                        srow[sl] = v * s_ks[buf][sl];
+                }
+            }
+        } else if (wave_active && tbase <= pw_last) {
 #pragma unroll 1
             for (int step = 0; step < IP_KT / 32; ++step) {
                 const int key0 = tbase + step * 32;

@@ -53,26 +53,45 @@ __device__ __forceinline__ RowRef row_of(int row, const float* scores, int64_t l
     }
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave: shifts of 1, 2, 4 and 8 lanes within each
+// 16-lane row, then the row totals carried forward by the row broadcasts of lane 15 (into rows
+// 1 and 3) and lane 31 (into rows 2 and 3).  Data-parallel-primitive moves, no LDS traffic.
+__device__ __forceinline__ int wave_incl_scan(int x)
+{
+    x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, true);    // row_shr:1
+    x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, true);    // row_shr:2
+    x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, true);    // row_shr:4
+    x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, true);    // row_shr:8
+    x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);   // row_bcast:15
+    x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);   // row_bcast:31
+    return x;
+}
+
+// Per-wave totals of the block scans, in two alternating slots: a call writes the slot the
+// previous call did not use, and every thread finished reading that slot (two calls back)
+// before it reached the previous call's barrier, so one barrier per scan suffices.  Every
+// thread of the workgroup makes the same sequence of calls.
+struct ScanBuf {
+    int* w;                                   // 2 * TK_WAVES ints of LDS
+    int par;
+};
+
 // Block-wide exclusive prefix sum (ascending thread order) and total.
-__device__ __forceinline__ int block_excl_scan(int v, int* s_wave, int* total)
+__device__ __forceinline__ int block_excl_scan(int v, ScanBuf& sb, int* total)
 {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    int x = v;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const int y = __shfl_up(x, o, 64);
-        if (lane >= o) x += y;
-    }
-    if (lane == 63) s_wave[wave] = x;
+    int* w = sb.w + sb.par * TK_WAVES;
+    sb.par ^= 1;
+    const int x = wave_incl_scan(v);
+    if (lane == 63) w[wave] = x;
     __syncthreads();
     int off = 0, tot = 0;
 #pragma unroll
     for (int i = 0; i < TK_WAVES; ++i) {
-        const int c = s_wave[i];
+        const int c = w[i];
         off += (i < wave) ? c : 0;
         tot += c;
     }
-    __syncthreads();
     *total = tot;
     return off + x - v;
 }
@@ -81,7 +100,7 @@ __device__ __forceinline__ int block_excl_scan(int v, int* s_wave, int* total)
 // <= count(bins >= B).  Returns B and stores need - count(bins > B) in *rem.  Thread i
 // covers bins NB-1-i*PER downwards.
 template <int NB>
-__device__ __forceinline__ int boundary_bin(const int* hist, int need, int* s_wave, int* s_res,
+__device__ __forceinline__ int boundary_bin(const int* hist, int need, ScanBuf& s_wave, int* s_res,
                                             int* rem)
 {
     constexpr int PER = NB / TK_THREADS;
@@ -110,33 +129,80 @@ __device__ __forceinline__ int boundary_bin(const int* hist, int need, int* s_wa
     return b;
 }
 
-// Exact kth-largest key among keys[0..nk) held in LDS (1 <= kth <= nk): three radix
-// levels of 11, 11 and 10 bits.  Returns the key and stores in *need_eq how many keys equal
-// to it belong to the top kth.
-__device__ __forceinline__ uint32_t lds_select(const uint32_t* keys, int nk, int kth, int* hist,
-                                               int* s_wave, int* s_res, int* need_eq)
+// Running maximum over the 64 lanes of a wave (lane 63 ends with the wave's maximum): the
+// same shift-and-broadcast pattern as wave_incl_scan, 0 being the identity of unsigned max.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t x)
 {
-    const int tid = threadIdx.x;
-    uint32_t prefix = 0;
+    x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xf, 0xf, true));
+    x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xf, 0xf, true));
+    x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xf, 0xf, true));
+    x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xf, 0xf, true));
+    x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xa, 0xf, false));
+    x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xc, 0xf, false));
+    return (uint32_t)__builtin_amdgcn_readlane((int)x, 63);
+}
+
+// Exact kth-largest key among keys[0..nk) held in LDS (1 <= kth <= nk).  The keys' common
+// high bits (those where the smallest and largest key agree) are skipped; the bits below are
+// resolved by radix levels of up to 11 bits, starting at the highest bit where keys differ,
+// so the first histogram spreads the keys over the range they actually span (candidates
+// above a threshold share most of their high bits, and a histogram over those bits would
+// pile them onto a few LDS counters).  Returns the key and stores in *need_eq how many keys
+// equal to it belong to the top kth.  hist: 2048 + TK_WAVES ints.
+__device__ __forceinline__ uint32_t lds_select(const uint32_t* keys, int nk, int kth, int* hist,
+                                               ScanBuf& s_wave, int* s_res, int* need_eq)
+{
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    uint32_t lmax = 0, lnmin = 0;                 // max of the keys and of their complements
+    for (int i = tid; i < nk; i += TK_THREADS) {
+        const uint32_t u = keys[i];
+        lmax = max(lmax, u);
+        lnmin = max(lnmin, ~u);
+    }
+    lmax = wave_max_u32(lmax);
+    lnmin = wave_max_u32(lnmin);
+    uint32_t* wmm = reinterpret_cast<uint32_t*>(hist + 2048);
+    if (lane == 0) {
+        wmm[wave] = lmax;
+        wmm[TK_WAVES + wave] = lnmin;
+    }
+    for (int i = tid; i < 2048; i += TK_THREADS) hist[i] = 0;
+    __syncthreads();
+    uint32_t kmax = 0, knmin = 0;
+#pragma unroll
+    for (int i = 0; i < TK_WAVES; ++i) {
+        kmax = max(kmax, wmm[i]);
+        knmin = max(knmin, wmm[TK_WAVES + i]);
+    }
+    const uint32_t diff = kmax ^ ~knmin;
+    if (diff == 0) {                              // every key equal
+        *need_eq = kth;
+        return kmax;
+    }
+    int hi = 31 - __clz((int)diff);               // highest bit where the keys differ
+    uint32_t prefix = (uint32_t)((uint64_t)kmax >> (hi + 1));
     int need = kth;
+    bool first = true;
 #pragma unroll 1
-    for (int lvl = 0; lvl < 3; ++lvl) {
-        const int sh = lvl == 0 ? 21 : (lvl == 1 ? 10 : 0);
-        const int above = lvl == 0 ? 32 : (lvl == 1 ? 21 : 10);   // bits fixed so far start here
-        const int nb = lvl == 2 ? 1024 : 2048;
-        for (int i = tid; i < nb; i += TK_THREADS) hist[i] = 0;
-        __syncthreads();
+    while (hi >= 0) {
+        const int width = min(11, hi + 1);
+        const int sh = hi + 1 - width;
+        if (!first) {
+            for (int i = tid; i < 2048; i += TK_THREADS) hist[i] = 0;
+            __syncthreads();
+        }
+        first = false;
         for (int i = tid; i < nk; i += TK_THREADS) {
             const uint32_t u = keys[i];
-            const bool match = lvl == 0 || (u >> above) == prefix;
-            if (match) atomicAdd(&hist[(u >> sh) & (nb - 1)], 1);
+            if ((uint32_t)((uint64_t)u >> (hi + 1)) == prefix)
+                atomicAdd(&hist[(u >> sh) & ((1u << width) - 1)], 1);
         }
         __syncthreads();
         int rem;
-        const int d = lvl == 2 ? boundary_bin<1024>(hist, need, s_wave, s_res, &rem)
-                               : boundary_bin<2048>(hist, need, s_wave, s_res, &rem);
-        prefix = (prefix << (lvl == 2 ? 10 : 11)) | (uint32_t)d;
+        const int d = boundary_bin<2048>(hist, need, s_wave, s_res, &rem);
+        prefix = (prefix << width) | (uint32_t)d;
         need = rem;
+        hi = sh - 1;
     }
     *need_eq = need;
     return prefix;
@@ -152,32 +218,47 @@ __device__ __forceinline__ uint32_t lds_select(const uint32_t* keys, int nk, int
 constexpr int RPT = 4;
 constexpr int KPT = 4 * RPT;                            // keys per thread per round
 
-template <typename F>
-__device__ __forceinline__ void for_row_rounds(const RowRef& rr, F&& f)
+// pre() runs once, after the first round's loads are issued and before f is first called
+// (work that f depends on but the loads do not, such as finding a threshold).
+struct NoPre {
+    __device__ void operator()() const {}
+};
+
+template <typename F, typename P = NoPre>
+__device__ __forceinline__ void for_row_rounds(const RowRef& rr, F&& f, P&& pre = P{})
 {
     const int tid = threadIdx.x;
     const int n = rr.n;
     const int mis = (int)((reinterpret_cast<uintptr_t>(rr.p) >> 2) & 3);
     const int head = min(n, (4 - mis) & 3);            // scalars until 16-byte aligned
+    const int body = (n - head) & ~3;
+    const v4f* p4 = reinterpret_cast<const v4f*>(rr.p + head);
+    // The loads of round r + 1 are issued before f runs on round r, so the workgroup's
+    // scans and LDS work overlap the memory latency of the next round.
+    v4f v[RPT];
+    auto fetch = [&](int base) {
+        const int e = base + KPT * tid;
+        const int c = max(0, min(KPT, body - e));
+#pragma unroll
+        for (int i = 0; i < RPT; ++i)
+            if (4 * i < c) v[i] = p4[(e >> 2) + i];
+    };
+    if (body > 0) fetch(0);
+    pre();
     uint32_t key[KPT] = {};
     if (head > 0) {                                     // uniform
         const int c = tid < head ? 1 : 0;
         key[0] = c ? score_key(rr.p[tid]) : 0u;
         f(tid, key, c);
     }
-    const int body = (n - head) & ~3;
-    const v4f* p4 = reinterpret_cast<const v4f*>(rr.p + head);
     for (int base = 0; base < body; base += KPT * TK_THREADS) {
         const int e = base + KPT * tid;                 // first position (in the body)
         const int c = max(0, min(KPT, body - e));       // a multiple of 4
-        v4f v[RPT];
-#pragma unroll
-        for (int i = 0; i < RPT; ++i)
-            if (4 * i < c) v[i] = p4[(e >> 2) + i];
 #pragma unroll
         for (int i = 0; i < RPT; ++i)
 #pragma unroll
             for (int j = 0; j < 4; ++j) key[4 * i + j] = 4 * i < c ? score_key(v[i][j]) : 0u;
+        if (base + KPT * TK_THREADS < body) fetch(base + KPT * TK_THREADS);
         f(head + e, key, c);
     }
     const int tail = n - head - body;                   // 0..3
@@ -193,7 +274,7 @@ __device__ __forceinline__ void for_row_rounds(const RowRef& rr, F&& f)
 // slot = #(> tau before) + min(#ties before, need_eq).
 __device__ __forceinline__ void emit_sorted(const uint32_t* ckey, const int* cpos, int nc,
                                             uint32_t tau, int need_eq, int k, int32_t* out,
-                                            int* s_wave)
+                                            ScanBuf& s_wave)
 {
     const int tid = threadIdx.x;
     int base_g = 0, base_e = 0;
@@ -236,7 +317,8 @@ __global__ __launch_bounds__(TK_THREADS) void topk_kernel(
     int q_pos0, int k, int32_t* __restrict__ idx)
 {
     __shared__ __attribute__((aligned(16))) uint8_t s_buf[LDS_BYTES];
-    __shared__ int s_wave[TK_WAVES];
+    __shared__ int s_wave_mem[2 * TK_WAVES];
+    ScanBuf s_wave{s_wave_mem, 0};
     __shared__ int s_res[4];
     int* hist = reinterpret_cast<int*>(s_buf + OFF_HIST);
 
@@ -254,8 +336,15 @@ __global__ __launch_bounds__(TK_THREADS) void topk_kernel(
     uint32_t* ckey = reinterpret_cast<uint32_t*>(s_buf + OFF_A);
     int* cpos = reinterpret_cast<int*>(s_buf + OFF_A + 4 * CAND_CAP);
     if (n <= CAND_CAP) {
-        // ---- the whole row fits: stage it, select, emit
-        for (int i = tid; i < n; i += TK_THREADS) ckey[i] = score_key(rr.p[i]);
+        // ---- the whole row fits: stage it (all loads in flight at once), select, emit
+        constexpr int SPL = (CAND_CAP + TK_THREADS - 1) / TK_THREADS;
+        float sv[SPL];
+#pragma unroll
+        for (int j = 0; j < SPL; ++j)
+            if (tid + j * TK_THREADS < n) sv[j] = rr.p[tid + j * TK_THREADS];
+#pragma unroll
+        for (int j = 0; j < SPL; ++j)
+            if (tid + j * TK_THREADS < n) ckey[tid + j * TK_THREADS] = score_key(sv[j]);
         __syncthreads();
         int need_eq;
         const uint32_t tau = lds_select(ckey, n, k, hist, s_wave, s_res, &need_eq);
@@ -275,10 +364,10 @@ __global__ __launch_bounds__(TK_THREADS) void topk_kernel(
     __syncthreads();
     // sample rank with about 2k of the n keys above it
     const int rs = (int)min<int64_t>(SAMPLE, ((int64_t)2 * k * SAMPLE + n - 1) / n);
-    int unused_eq;
-    const uint32_t tau_lo = lds_select(samp, SAMPLE, rs, hist, s_wave, s_res, &unused_eq);
+    uint32_t tau_lo = 0;
 
-    // ---- one ordered pass: candidates are the keys >= tau_lo
+    // ---- one ordered pass: candidates are the keys >= tau_lo (its first loads are in
+    // flight while tau_lo is selected from the sample)
     int nc = 0;
     for_row_rounds(rr, [&](int pos0, const uint32_t* key, int c) {
         int mine = 0;
@@ -297,6 +386,9 @@ __global__ __launch_bounds__(TK_THREADS) void topk_kernel(
             }
         }
         nc += tot;
+    }, [&]() {
+        int unused_eq;
+        tau_lo = lds_select(samp, SAMPLE, rs, hist, s_wave, s_res, &unused_eq);
     });
     __syncthreads();
     if (nc >= k && nc <= CAND_CAP) {
