@@ -97,36 +97,58 @@ __device__ __forceinline__ int block_excl_scan(int v, ScanBuf& sb, int* total)
 }
 
 // Boundary bin of a descending histogram of NB bins: the bin B with count(bins > B) < need
-// <= count(bins >= B).  Returns B and stores need - count(bins > B) in *rem.  Thread i
-// covers bins NB-1-i*PER downwards.
+// <= count(bins >= B) (requires need <= the histogram's total).  Returns B and stores
+// need - count(bins > B) in *rem.  Thread i covers bins NB-1-i*PER downwards.  One barrier:
+// after the per-wave totals are exchanged, every wave re-reads the bins of the wave that
+// holds the boundary and finds the boundary lane itself.
 template <int NB>
-__device__ __forceinline__ int boundary_bin(const int* hist, int need, ScanBuf& s_wave, int* s_res,
-                                            int* rem)
+__device__ __forceinline__ int boundary_bin(const int* hist, int need, ScanBuf& sb, int* rem)
 {
     constexpr int PER = NB / TK_THREADS;
     static_assert(PER * TK_THREADS == NB, "bins per thread");
-    const int tid = threadIdx.x;
-    int cnt[PER], sum = 0;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    int sum = 0;
 #pragma unroll
-    for (int q = 0; q < PER; ++q) {
-        cnt[q] = hist[NB - 1 - tid * PER - q];
-        sum += cnt[q];
-    }
-    int total;
-    int above = block_excl_scan(sum, s_wave, &total);
+    for (int q = 0; q < PER; ++q) sum += hist[NB - 1 - tid * PER - q];
+    const int x = wave_incl_scan(sum);
+    int* w = sb.w + sb.par * TK_WAVES;
+    sb.par ^= 1;
+    if (lane == 63) w[wave] = x;
+    __syncthreads();
+    int acc = 0, bw = 0, before = 0;            // the wave holding the boundary, counts before it
 #pragma unroll
-    for (int q = 0; q < PER; ++q) {
-        if (above < need && need <= above + cnt[q]) {
-            s_res[0] = NB - 1 - tid * PER - q;
-            s_res[1] = need - above;
+    for (int i = 0; i < TK_WAVES; ++i) {
+        const int c = w[i];
+        if (acc < need && need <= acc + c) {
+            bw = i;
+            before = acc;
         }
-        above += cnt[q];
+        acc += c;
     }
-    __syncthreads();
-    const int b = s_res[0];
-    *rem = s_res[1];
-    __syncthreads();
-    return b;
+    const int t2 = bw * 64 + lane;
+    int cnt[PER], s2 = 0;
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+        cnt[q] = hist[NB - 1 - t2 * PER - q];
+        s2 += cnt[q];
+    }
+    int a = before + wave_incl_scan(s2) - s2;   // counts in bins above this lane's bins
+    const bool mine = a < need && need <= a + s2;
+    int b_l = 0, rem_l = need;
+    if (mine) {
+#pragma unroll
+        for (int q = 0; q < PER; ++q) {
+            if (a < need && need <= a + cnt[q]) {
+                b_l = NB - 1 - t2 * PER - q;
+                rem_l = need - a;
+            }
+            a += cnt[q];
+        }
+    }
+    const uint64_t m = __ballot(mine);
+    const int src = m ? __builtin_ctzll(m) : 0;
+    *rem = __builtin_amdgcn_readlane(rem_l, src);
+    return __builtin_amdgcn_readlane(b_l, src);
 }
 
 // Running maximum over the 64 lanes of a wave (lane 63 ends with the wave's maximum): the
@@ -142,37 +164,75 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t x)
     return (uint32_t)__builtin_amdgcn_readlane((int)x, 63);
 }
 
-// Exact kth-largest key among keys[0..nk) held in LDS (1 <= kth <= nk).  The keys' common
-// high bits (those where the smallest and largest key agree) are skipped; the bits below are
-// resolved by radix levels of up to 11 bits, starting at the highest bit where keys differ,
-// so the first histogram spreads the keys over the range they actually span (candidates
-// above a threshold share most of their high bits, and a histogram over those bits would
-// pile them onto a few LDS counters).  Returns the key and stores in *need_eq how many keys
-// equal to it belong to the top kth.  hist: 2048 + TK_WAVES ints.
+// Keys per thread of the LDS-resident selections and emissions: covers CAND_CAP, SAMPLE and
+// FB_CAP.  Thread t owns the contiguous entries [SEL_PT * t, SEL_PT * t + SEL_PT).
+constexpr int SEL_PT = 12;
+static_assert(SEL_PT * TK_THREADS >= CAND_CAP && SEL_PT * TK_THREADS >= SAMPLE &&
+              SEL_PT * TK_THREADS >= FB_CAP, "selection entries per thread");
+
+// This thread's entries [SEL_PT * tid, ...) of an LDS array of n entries; returns how many
+// exist (0..SEL_PT).  Whole 16-byte loads when all SEL_PT exist.
+template <typename T>
+__device__ __forceinline__ int load_own(const T* a, int n, T (&r)[SEL_PT])
+{
+    static_assert(sizeof(T) == 4, "4-byte entries");
+    const int i0 = SEL_PT * (int)threadIdx.x;
+    const int cnt = max(0, min(SEL_PT, n - i0));
+    if (cnt == SEL_PT) {
+#pragma unroll
+        for (int q = 0; q < SEL_PT / 4; ++q) {
+            const u32x4 v = *reinterpret_cast<const u32x4*>(a + i0 + 4 * q);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const uint32_t e = v[j];        // a scalar first: bit_cast of a vector element
+                r[4 * q + j] = __builtin_bit_cast(T, e);   // reads element 0 with this compiler
+            }
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < SEL_PT; ++j) r[j] = j < cnt ? a[i0 + j] : T(0);
+    }
+    return cnt;
+}
+
+// Exact kth-largest key among keys[0..nk) held in LDS (1 <= kth <= nk <= SEL_PT * 512).
+// Each thread holds its keys in registers for all levels.  The keys' common high bits (where
+// the smallest and largest key agree) are skipped; the bits below are resolved by radix
+// levels of up to 11 bits, starting at the highest bit where keys differ, so the first
+// histogram spreads the keys over the range they actually span (candidates above a
+// threshold share most of their high bits).  Returns the key and stores in *need_eq how many
+// keys equal to it belong to the top kth.  With exact = false it stops after two levels and
+// returns the lowest key of the bin reached: a lower bound of the kth-largest key that at
+// most the keys of one 22-bit-resolved bin exceed beyond it.
+// hist: 4096 ints (levels alternate between its halves); s_mm: 2 * TK_WAVES ints.
 __device__ __forceinline__ uint32_t lds_select(const uint32_t* keys, int nk, int kth, int* hist,
-                                               ScanBuf& s_wave, int* s_res, int* need_eq)
+                                               ScanBuf& s_wave, uint32_t* s_mm, int* need_eq,
+                                               bool exact = true)
 {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    uint32_t kr[SEL_PT];
+    const int cnt = load_own(keys, nk, kr);
     uint32_t lmax = 0, lnmin = 0;                 // max of the keys and of their complements
-    for (int i = tid; i < nk; i += TK_THREADS) {
-        const uint32_t u = keys[i];
-        lmax = max(lmax, u);
-        lnmin = max(lnmin, ~u);
+#pragma unroll
+    for (int j = 0; j < SEL_PT; ++j) {
+        if (j < cnt) {
+            lmax = max(lmax, kr[j]);
+            lnmin = max(lnmin, ~kr[j]);
+        }
     }
     lmax = wave_max_u32(lmax);
     lnmin = wave_max_u32(lnmin);
-    uint32_t* wmm = reinterpret_cast<uint32_t*>(hist + 2048);
     if (lane == 0) {
-        wmm[wave] = lmax;
-        wmm[TK_WAVES + wave] = lnmin;
+        s_mm[wave] = lmax;
+        s_mm[TK_WAVES + wave] = lnmin;
     }
-    for (int i = tid; i < 2048; i += TK_THREADS) hist[i] = 0;
+    for (int i = tid; i < 4096; i += TK_THREADS) hist[i] = 0;     // both halves
     __syncthreads();
     uint32_t kmax = 0, knmin = 0;
 #pragma unroll
     for (int i = 0; i < TK_WAVES; ++i) {
-        kmax = max(kmax, wmm[i]);
-        knmin = max(knmin, wmm[TK_WAVES + i]);
+        kmax = max(kmax, s_mm[i]);
+        knmin = max(knmin, s_mm[TK_WAVES + i]);
     }
     const uint32_t diff = kmax ^ ~knmin;
     if (diff == 0) {                              // every key equal
@@ -182,24 +242,28 @@ __device__ __forceinline__ uint32_t lds_select(const uint32_t* keys, int nk, int
     int hi = 31 - __clz((int)diff);               // highest bit where the keys differ
     uint32_t prefix = (uint32_t)((uint64_t)kmax >> (hi + 1));
     int need = kth;
-    bool first = true;
 #pragma unroll 1
-    while (hi >= 0) {
+    for (int lvl = 0; hi >= 0; ++lvl) {
+        if (!exact && lvl == 2) {
+            *need_eq = 0;
+            return prefix << (hi + 1);            // hi + 1 <= 10 here
+        }
         const int width = min(11, hi + 1);
         const int sh = hi + 1 - width;
-        if (!first) {
-            for (int i = tid; i < 2048; i += TK_THREADS) hist[i] = 0;
+        int* h = hist + 2048 * (lvl & 1);
+        if (lvl >= 2) {                           // this half was used two levels ago
+            for (int i = tid; i < 2048; i += TK_THREADS) h[i] = 0;
             __syncthreads();
         }
-        first = false;
-        for (int i = tid; i < nk; i += TK_THREADS) {
-            const uint32_t u = keys[i];
-            if ((uint32_t)((uint64_t)u >> (hi + 1)) == prefix)
-                atomicAdd(&hist[(u >> sh) & ((1u << width) - 1)], 1);
+#pragma unroll
+        for (int j = 0; j < SEL_PT; ++j) {
+            // below the first level hi + 1 <= 21, so the shift is in range
+            if (j < cnt && (lvl == 0 || (kr[j] >> (hi + 1)) == prefix))
+                atomicAdd(&h[(kr[j] >> sh) & ((1u << width) - 1)], 1);
         }
         __syncthreads();
         int rem;
-        const int d = boundary_bin<2048>(hist, need, s_wave, s_res, &rem);
+        const int d = boundary_bin<2048>(h, need, s_wave, &rem);
         prefix = (prefix << width) | (uint32_t)d;
         need = rem;
         hi = sh - 1;
@@ -269,34 +333,36 @@ __device__ __forceinline__ void for_row_rounds(const RowRef& rr, F&& f, P&& pre 
     }
 }
 
-// Ordered emission from a position-ordered candidate list (cpos null: position = index):
-// every key > tau, plus the first need_eq keys equal to tau, at
-// slot = #(> tau before) + min(#ties before, need_eq).
+// Ordered emission from a position-ordered candidate list (cpos null: position = index;
+// nc <= SEL_PT * 512): every key > tau, plus the first need_eq keys equal to tau, at
+// slot = #(> tau before) + min(#ties before, need_eq).  One block scan: each thread takes
+// SEL_PT consecutive candidates.
 __device__ __forceinline__ void emit_sorted(const uint32_t* ckey, const int* cpos, int nc,
                                             uint32_t tau, int need_eq, int k, int32_t* out,
                                             ScanBuf& s_wave)
 {
-    const int tid = threadIdx.x;
-    int base_g = 0, base_e = 0;
-    for (int r0 = 0; r0 < nc; r0 += 4 * TK_THREADS) {
-        uint32_t ku[4];
-        int pp[4], ng = 0, ne = 0;
+    uint32_t ku[SEL_PT];
+    int pp[SEL_PT];
+    const int cnt = load_own(ckey, nc, ku);
+    if (cpos) {
+        load_own(cpos, nc, pp);
+    } else {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int i = r0 + 4 * tid + j;
-            ku[j] = i < nc ? ckey[i] : 0u;
-            pp[j] = i < nc ? (cpos ? cpos[i] : i) : -1;
-            ng += (i < nc) && ku[j] > tau;
-            ne += (i < nc) && ku[j] == tau;
-        }
-        int tot;
-        const int off = block_excl_scan(ng | (ne << 16), s_wave, &tot);
-        int gt_before = base_g + (off & 0xFFFF);
-        int eq_before = base_e + (off >> 16);
+        for (int j = 0; j < SEL_PT; ++j) pp[j] = SEL_PT * (int)threadIdx.x + j;
+    }
+    int ng = 0, ne = 0;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int i = r0 + 4 * tid + j;
-            if (i >= nc) break;
+    for (int j = 0; j < SEL_PT; ++j) {
+        ng += (j < cnt) && ku[j] > tau;
+        ne += (j < cnt) && ku[j] == tau;
+    }
+    int tot;
+    const int off = block_excl_scan(ng | (ne << 16), s_wave, &tot);
+    int gt_before = off & 0xFFFF;
+    int eq_before = off >> 16;
+#pragma unroll
+    for (int j = 0; j < SEL_PT; ++j) {
+        if (j < cnt) {
             if (ku[j] > tau) {
                 const int slot = gt_before + min(eq_before, need_eq);
                 if (slot < k) out[slot] = pp[j];
@@ -306,8 +372,6 @@ __device__ __forceinline__ void emit_sorted(const uint32_t* ckey, const int* cpo
                 ++eq_before;
             }
         }
-        base_g += tot & 0xFFFF;
-        base_e += tot >> 16;
     }
 }
 
@@ -319,7 +383,7 @@ __global__ __launch_bounds__(TK_THREADS) void topk_kernel(
     __shared__ __attribute__((aligned(16))) uint8_t s_buf[LDS_BYTES];
     __shared__ int s_wave_mem[2 * TK_WAVES];
     ScanBuf s_wave{s_wave_mem, 0};
-    __shared__ int s_res[4];
+    __shared__ uint32_t s_mm[2 * TK_WAVES];
     int* hist = reinterpret_cast<int*>(s_buf + OFF_HIST);
 
     const int row = blockIdx.x;
@@ -347,7 +411,7 @@ __global__ __launch_bounds__(TK_THREADS) void topk_kernel(
             if (tid + j * TK_THREADS < n) ckey[tid + j * TK_THREADS] = score_key(sv[j]);
         __syncthreads();
         int need_eq;
-        const uint32_t tau = lds_select(ckey, n, k, hist, s_wave, s_res, &need_eq);
+        const uint32_t tau = lds_select(ckey, n, k, hist, s_wave, s_mm, &need_eq);
         emit_sorted(ckey, nullptr, n, tau, need_eq, k, out, s_wave);
         return;
     }
@@ -388,12 +452,12 @@ __global__ __launch_bounds__(TK_THREADS) void topk_kernel(
         nc += tot;
     }, [&]() {
         int unused_eq;
-        tau_lo = lds_select(samp, SAMPLE, rs, hist, s_wave, s_res, &unused_eq);
+        tau_lo = lds_select(samp, SAMPLE, rs, hist, s_wave, s_mm, &unused_eq, false);
     });
     __syncthreads();
     if (nc >= k && nc <= CAND_CAP) {
         int need_eq;
-        const uint32_t tau = lds_select(ckey, nc, k, hist, s_wave, s_res, &need_eq);
+        const uint32_t tau = lds_select(ckey, nc, k, hist, s_wave, s_mm, &need_eq);
         emit_sorted(ckey, cpos, nc, tau, need_eq, k, out, s_wave);
         return;
     }
@@ -411,7 +475,7 @@ __global__ __launch_bounds__(TK_THREADS) void topk_kernel(
     });
     __syncthreads();
     int need_b;                                   // keys still needed from the boundary bin
-    const uint32_t b = (uint32_t)boundary_bin<FB_BINS>(hist, k, s_wave, s_res, &need_b);
+    const uint32_t b = (uint32_t)boundary_bin<FB_BINS>(hist, k, s_wave, &need_b);
     const int n_above = k - need_b;               // keys in bins above b (all selected)
     const int n_cand = hist[b];
     __syncthreads();
@@ -445,7 +509,7 @@ __global__ __launch_bounds__(TK_THREADS) void topk_kernel(
         });
         __syncthreads();
         int need_eq;
-        const uint32_t tau = lds_select(fkey, n_cand, need_b, hist, s_wave, s_res, &need_eq);
+        const uint32_t tau = lds_select(fkey, n_cand, need_b, hist, s_wave, s_mm, &need_eq);
         // chosen candidates -> C (in place over fkey, as positions), position order kept
         int base_g = 0, base_e = 0;
         for (int r0 = 0; r0 < n_cand; r0 += 4 * TK_THREADS) {
@@ -506,6 +570,7 @@ __global__ __launch_bounds__(TK_THREADS) void topk_kernel(
 #pragma unroll 1
     for (int lvl = 0; lvl < 2; ++lvl) {
         const int sh = lvl == 0 ? 10 : 0;
+        __syncthreads();                          // the previous boundary search read hist
         for (int i = tid; i < 1024; i += TK_THREADS) hist[i] = 0;
         __syncthreads();
         for_row_rounds(rr, [&](int, const uint32_t* key, int c) {
@@ -516,7 +581,7 @@ __global__ __launch_bounds__(TK_THREADS) void topk_kernel(
         });
         __syncthreads();
         int rem;
-        const int d = boundary_bin<1024>(hist, need, s_wave, s_res, &rem);
+        const int d = boundary_bin<1024>(hist, need, s_wave, &rem);
         prefix = (prefix << 10) | (uint32_t)d;
         need = rem;
     }
