@@ -66,10 +66,10 @@ int decode_splits(int k) { return std::min(8, std::max(1, (k + 511) / 512)); }
 
 struct DecodeWs {
     int splits;
-    size_t scores_off, idx_off, po_off, pl_off, total;
+    size_t scores_off, idx_off, po_off, pl_off, tk_off, tk_bytes, total;
 };
 
-DecodeWs decode_ws(int B, int64_t N, int H, int k)
+DecodeWs decode_ws(int B, int max_len, int64_t N, int H, int k)
 {
     DecodeWs w;
     w.splits = decode_splits(k);
@@ -77,7 +77,9 @@ DecodeWs decode_ws(int B, int64_t N, int H, int k)
     w.idx_off = align_up(size_t(N) * 4);
     w.po_off = w.idx_off + align_up(size_t(B) * size_t(k) * 4);
     w.pl_off = w.po_off + align_up(size_t(B) * w.splits * H * 512 * 4);
-    w.total = w.pl_off + align_up(size_t(B) * w.splits * H * 4);
+    w.tk_off = w.pl_off + align_up(size_t(B) * w.splits * H * 4);
+    w.tk_bytes = dsa::topk_decode_workspace_bytes(B, max_len);
+    w.total = w.tk_off + align_up(w.tk_bytes);
     return w;
 }
 
@@ -221,9 +223,8 @@ size_t dsa_decode_workspace_bytes(int B, int max_len, int64_t total_tokens, int 
                                   int k)
 {
     (void)H_I;
-    (void)max_len;
-    if (B <= 0 || total_tokens <= 0 || H < 1 || k < 1) return 0;
-    return decode_ws(B, total_tokens, H, k).total;
+    if (B <= 0 || max_len < 1 || total_tokens <= 0 || H < 1 || k < 1) return 0;
+    return decode_ws(B, max_len, total_tokens, H, k).total;
 }
 
 dsa_status_t dsa_decode(int B, const int64_t* seq_start, int max_len, int64_t total_tokens,
@@ -247,7 +248,7 @@ dsa_status_t dsa_decode(int B, const int64_t* seq_start, int max_len, int64_t to
     if (!aligned(q8, 16) || !aligned(k8_cache, 16) || !aligned(q, 16) ||
         !aligned(kv_cache, 16) || !aligned(out, 8))
         return DSA_ERR_INVALID_ARGUMENT;
-    const DecodeWs ws = decode_ws(B, total_tokens, H, k);
+    const DecodeWs ws = decode_ws(B, max_len, total_tokens, H, k);
     if (!workspace || workspace_bytes < ws.total) return DSA_ERR_WORKSPACE_TOO_SMALL;
     if (!aligned(workspace, kAlign)) return DSA_ERR_INVALID_ARGUMENT;
 
@@ -259,7 +260,9 @@ dsa_status_t dsa_decode(int B, const int64_t* seq_start, int max_len, int64_t to
     float* pl = reinterpret_cast<float*>(base + ws.pl_off);
     hipError_t e = dsa::launch_indexer_decode(q8, q_scale, w, k8_cache, k_scale_cache,
                                               seq_start, B, max_len, H_I, score_scale, scores, s);
-    if (e == hipSuccess) e = dsa::launch_topk_decode(scores, seq_start, B, k, idx, s);
+    if (e == hipSuccess)
+        e = dsa::launch_topk_decode(scores, seq_start, B, max_len, k, idx,
+                                    ws.tk_bytes ? base + ws.tk_off : nullptr, s);
     if (e == hipSuccess)
         e = dsa::launch_sparse_mla(q, kv_cache, idx, seq_start, B, max_len, H, k, sm_scale,
                                    ws.splits, out, lse, po, pl, s);

@@ -29,9 +29,13 @@ bool indexer_supports(int H_I);
 // Prefill rows: row t at scores + t * ld with n_t = min(L, q_pos0 + t + 1) visible scores.
 hipError_t launch_topk_prefill(const float* scores, int64_t ld, int T, int L, int q_pos0,
                                int k, int32_t* idx, hipStream_t stream);
-// Decode rows: row b at scores + seq_start[b] with seq_start[b+1] - seq_start[b] scores.
-hipError_t launch_topk_decode(const float* scores, const int64_t* seq_start, int B, int k,
-                              int32_t* idx, hipStream_t stream);
+// Decode rows: row b at scores + seq_start[b] with seq_start[b+1] - seq_start[b] <= max_len
+// scores.  Long rows are split over several workgroups when ws (at least
+// topk_decode_workspace_bytes(B, max_len) bytes, 16-byte aligned; may be null when that is
+// 0) is given; otherwise each row is selected by one workgroup.
+size_t topk_decode_workspace_bytes(int B, int max_len);
+hipError_t launch_topk_decode(const float* scores, const int64_t* seq_start, int B, int max_len,
+                              int k, int32_t* idx, void* ws, hipStream_t stream);
 
 // ---- sparse MLA -----------------------------------------------------------------------
 // Row t attends over kv rows idx[t, :] (entries outside [0, L) skipped).

@@ -375,10 +375,76 @@ __device__ __forceinline__ void emit_sorted(const uint32_t* ckey, const int* cpo
     }
 }
 
+// The threshold sample of a row of n > CAND_CAP keys: 64 contiguous 64-key blocks spread
+// evenly over the row, as keys, into samp[0..SAMPLE).  The caller synchronises.
+__device__ __forceinline__ void load_sample(const RowRef& rr, uint32_t* samp)
+{
+    constexpr int SPT = SAMPLE / TK_THREADS;                      // sampled keys per thread
+    const int i0 = threadIdx.x * SPT, blk = i0 >> 6, off = i0 & 63;
+    const int start = (int)(((int64_t)blk * (rr.n - 64)) / 63);    // n > CAND_CAP > 4096
+#pragma unroll
+    for (int j = 0; j < SPT; ++j) samp[i0 + j] = score_key(rr.p[start + off + j]);
+}
+
+// Sample rank with about 2k of the row's n keys above it.
+__device__ __forceinline__ int sample_rank(int n, int k)
+{
+    return (int)min<int64_t>(SAMPLE, ((int64_t)2 * k * SAMPLE + n - 1) / n);
+}
+
+// One ordered pass over the keys of rr (positions pos_base + 0 .. rr.n - 1): every key >=
+// the threshold goes to (ckey, cpos) in position order, the first CAND_CAP of them kept.
+// The threshold is the lower bound that lds_select derives from the row's sample (already
+// in samp, synchronised) at rank rs; its selection runs while the first loads are in
+// flight.  Returns the number of keys at or above it (possibly more than CAND_CAP).
+__device__ __forceinline__ int collect_candidates(const RowRef& rr, int pos_base,
+                                                  const uint32_t* samp, int rs, int* hist,
+                                                  ScanBuf& s_wave, uint32_t* s_mm,
+                                                  uint32_t* ckey, int* cpos)
+{
+    uint32_t tau_lo = 0;
+    int nc = 0;
+    for_row_rounds(rr, [&](int pos0, const uint32_t* key, int c) {
+        int mine = 0;
+#pragma unroll
+        for (int j = 0; j < KPT; ++j) mine += (j < c) && key[j] >= tau_lo;
+        int tot;
+        int o = nc + block_excl_scan(mine, s_wave, &tot);
+#pragma unroll
+        for (int j = 0; j < KPT; ++j) {
+            if (j < c && key[j] >= tau_lo) {
+                if (o < CAND_CAP) {
+                    ckey[o] = key[j];
+                    cpos[o] = pos_base + pos0 + j;
+                }
+                ++o;
+            }
+        }
+        nc += tot;
+    }, [&]() {
+        int unused_eq;
+        tau_lo = lds_select(samp, SAMPLE, rs, hist, s_wave, s_mm, &unused_eq, false);
+    });
+    return nc;
+}
+
+// Candidates of long decode rows gathered by topk_segment_kernel: segment s of row b
+// (keys [s * SEG, min(n, (s + 1) * SEG))) left its count in cnt[b * nseg + s] and its first
+// min(count, CAND_CAP) candidates, in position order, at key/pos + (b * nseg + s) * CAND_CAP.
+// nseg = 0: not used.
+constexpr int SEG = 16384;
+constexpr int SEG_MAX = 64;                   // rows of up to SEG * SEG_MAX keys are split
+struct SegCands {
+    const uint32_t* key;
+    const int32_t* pos;
+    const int32_t* cnt;
+    int nseg;
+};
+
 template <bool DECODE>
 __global__ __launch_bounds__(TK_THREADS) void topk_kernel(
     const float* __restrict__ scores, int64_t ld, const int64_t* __restrict__ seq_start, int L,
-    int q_pos0, int k, int32_t* __restrict__ idx)
+    int q_pos0, int k, int32_t* __restrict__ idx, SegCands seg)
 {
     __shared__ __attribute__((aligned(16))) uint8_t s_buf[LDS_BYTES];
     __shared__ int s_wave_mem[2 * TK_WAVES];
@@ -416,50 +482,64 @@ __global__ __launch_bounds__(TK_THREADS) void topk_kernel(
         return;
     }
 
-    // ---- threshold estimate from 64 contiguous 64-key blocks spread over the row
-    uint32_t* samp = reinterpret_cast<uint32_t*>(s_buf + OFF_A + 8 * CAND_CAP);
-    {
-        constexpr int SPT = SAMPLE / TK_THREADS;                  // sampled keys per thread
-        const int i0 = tid * SPT, blk = i0 >> 6, off = i0 & 63;
-        const int start = (int)(((int64_t)blk * (n - 64)) / 63);   // n > CAND_CAP > 4096
-#pragma unroll
-        for (int j = 0; j < SPT; ++j) samp[i0 + j] = score_key(rr.p[start + off + j]);
-    }
-    __syncthreads();
-    // sample rank with about 2k of the n keys above it
-    const int rs = (int)min<int64_t>(SAMPLE, ((int64_t)2 * k * SAMPLE + n - 1) / n);
-    uint32_t tau_lo = 0;
-
-    // ---- one ordered pass: candidates are the keys >= tau_lo (its first loads are in
-    // flight while tau_lo is selected from the sample)
-    int nc = 0;
-    for_row_rounds(rr, [&](int pos0, const uint32_t* key, int c) {
-        int mine = 0;
-#pragma unroll
-        for (int j = 0; j < KPT; ++j) mine += (j < c) && key[j] >= tau_lo;
+    const int ns = (n + SEG - 1) / SEG;
+    if (DECODE && seg.nseg > 0 && ns <= seg.nseg) {
+        // ---- a split row: the segments' candidates, concatenated in segment order (a row
+        // longer than the split covers -- outside the caller's contract -- takes the exact
+        // path below instead)
+        int* offs = hist;                                   // exclusive prefix, then total
+        int c = 0;
+        if (tid < ns) c = seg.cnt[row * seg.nseg + tid];
+        const bool over = __syncthreads_or(c > CAND_CAP);
         int tot;
-        int o = nc + block_excl_scan(mine, s_wave, &tot);
+        const int o = block_excl_scan(c, s_wave, &tot);
+        if (tid < ns) offs[tid] = o;
+        if (tid == 0) offs[ns] = tot;
+        __syncthreads();
+        if (!over && tot >= k && tot <= CAND_CAP) {
+            constexpr int PT = (CAND_CAP + TK_THREADS - 1) / TK_THREADS;
+            uint32_t kv[PT];
+            int pv[PT];
 #pragma unroll
-        for (int j = 0; j < KPT; ++j) {
-            if (j < c && key[j] >= tau_lo) {
-                if (o < CAND_CAP) {
-                    ckey[o] = key[j];
-                    cpos[o] = pos0 + j;
+            for (int j = 0; j < PT; ++j) {
+                const int i = tid + j * TK_THREADS;
+                if (i < tot) {
+                    int sg = 0;                             // last segment starting at or before i
+                    for (int q = 1; q < ns; ++q) sg += offs[q] <= i;
+                    const int64_t src = (int64_t)(row * seg.nseg + sg) * CAND_CAP + (i - offs[sg]);
+                    kv[j] = seg.key[src];
+                    pv[j] = seg.pos[src];
                 }
-                ++o;
             }
+#pragma unroll
+            for (int j = 0; j < PT; ++j) {
+                const int i = tid + j * TK_THREADS;
+                if (i < tot) {
+                    ckey[i] = kv[j];
+                    cpos[i] = pv[j];
+                }
+            }
+            __syncthreads();
+            int need_eq;
+            const uint32_t tau = lds_select(ckey, tot, k, hist, s_wave, s_mm, &need_eq);
+            emit_sorted(ckey, cpos, tot, tau, need_eq, k, out, s_wave);
+            return;
         }
-        nc += tot;
-    }, [&]() {
-        int unused_eq;
-        tau_lo = lds_select(samp, SAMPLE, rs, hist, s_wave, s_mm, &unused_eq, false);
-    });
-    __syncthreads();
-    if (nc >= k && nc <= CAND_CAP) {
-        int need_eq;
-        const uint32_t tau = lds_select(ckey, nc, k, hist, s_wave, s_mm, &need_eq);
-        emit_sorted(ckey, cpos, nc, tau, need_eq, k, out, s_wave);
-        return;
+        __syncthreads();                                    // offs read: hist free again
+    } else {
+        // ---- threshold from the row's sample, then one ordered pass for the candidates
+        uint32_t* samp = reinterpret_cast<uint32_t*>(s_buf + OFF_A + 8 * CAND_CAP);
+        load_sample(rr, samp);
+        __syncthreads();
+        const int nc = collect_candidates(rr, 0, samp, sample_rank(n, k), hist, s_wave, s_mm,
+                                          ckey, cpos);
+        __syncthreads();
+        if (nc >= k && nc <= CAND_CAP) {
+            int need_eq;
+            const uint32_t tau = lds_select(ckey, nc, k, hist, s_wave, s_mm, &need_eq);
+            emit_sorted(ckey, cpos, nc, tau, need_eq, k, out, s_wave);
+            return;
+        }
     }
 
     // ---- fallback: exact two-pass path
@@ -617,6 +697,40 @@ __global__ __launch_bounds__(TK_THREADS) void topk_kernel(
     });
 }
 
+// Segment sgi of decode row b (rows longer than CAND_CAP only): the row's sample threshold
+// (computed alike by every segment of the row), then one ordered pass over the segment's
+// keys, its candidates written out for the row kernel (see SegCands).
+__global__ __launch_bounds__(TK_THREADS) void topk_segment_kernel(
+    const float* __restrict__ scores, const int64_t* __restrict__ seq_start, int k, int nseg,
+    uint32_t* __restrict__ key_out, int32_t* __restrict__ pos_out, int32_t* __restrict__ cnt_out)
+{
+    __shared__ __attribute__((aligned(16))) uint8_t s_buf[LDS_BYTES];
+    __shared__ int s_wave_mem[2 * TK_WAVES];
+    ScanBuf s_wave{s_wave_mem, 0};
+    __shared__ uint32_t s_mm[2 * TK_WAVES];
+    int* hist = reinterpret_cast<int*>(s_buf + OFF_HIST);
+    uint32_t* ckey = reinterpret_cast<uint32_t*>(s_buf + OFF_A);
+    int* cpos = reinterpret_cast<int*>(s_buf + OFF_A + 4 * CAND_CAP);
+    uint32_t* samp = reinterpret_cast<uint32_t*>(s_buf + OFF_A + 8 * CAND_CAP);
+
+    const int sgi = blockIdx.x, row = blockIdx.y;
+    const RowRef rr = row_of<true>(row, scores, 0, seq_start, 0, 0);
+    const int n = rr.n, s0 = sgi * SEG;
+    if (n <= CAND_CAP || s0 >= n) return;              // uniform over the workgroup
+    load_sample(rr, samp);
+    __syncthreads();
+    const int nc = collect_candidates(RowRef{rr.p + s0, min(SEG, n - s0)}, s0, samp,
+                                      sample_rank(n, k), hist, s_wave, s_mm, ckey, cpos);
+    __syncthreads();
+    const int64_t slot = (int64_t)row * nseg + sgi;
+    if (threadIdx.x == 0) cnt_out[slot] = nc;
+    const int keep = min(nc, CAND_CAP);
+    for (int i = threadIdx.x; i < keep; i += TK_THREADS) {
+        key_out[slot * CAND_CAP + i] = ckey[i];
+        pos_out[slot * CAND_CAP + i] = cpos[i];
+    }
+}
+
 }  // namespace
 
 hipError_t launch_topk_prefill(const float* scores, int64_t ld, int T, int L, int q_pos0,
@@ -624,16 +738,43 @@ hipError_t launch_topk_prefill(const float* scores, int64_t ld, int T, int L, in
 {
     if (T <= 0) return hipSuccess;
     hipLaunchKernelGGL(topk_kernel<false>, dim3(T), dim3(TK_THREADS), 0, stream, scores, ld,
-                       (const int64_t*)nullptr, L, q_pos0, k, idx);
+                       (const int64_t*)nullptr, L, q_pos0, k, idx, SegCands{nullptr, nullptr, nullptr, 0});
     return hipGetLastError();
 }
 
-hipError_t launch_topk_decode(const float* scores, const int64_t* seq_start, int B, int k,
-                              int32_t* idx, hipStream_t stream)
+// Rows of more than CAND_CAP keys are split over segments when max_len needs at most
+// SEG_MAX of them: key and position buffers of B * nseg * CAND_CAP entries and nseg counts
+// per row.
+static int decode_nseg(int max_len)
+{
+    const int nseg = (max_len + SEG - 1) / SEG;
+    return (max_len > CAND_CAP && nseg <= SEG_MAX) ? nseg : 0;
+}
+
+size_t topk_decode_workspace_bytes(int B, int max_len)
+{
+    const size_t nseg = (size_t)decode_nseg(max_len);
+    if (B <= 0 || nseg == 0) return 0;
+    return (size_t)B * nseg * (8 * (size_t)CAND_CAP + 4) + 16;
+}
+
+hipError_t launch_topk_decode(const float* scores, const int64_t* seq_start, int B, int max_len,
+                              int k, int32_t* idx, void* ws, hipStream_t stream)
 {
     if (B <= 0) return hipSuccess;
+    SegCands seg{nullptr, nullptr, nullptr, 0};
+    const int nseg = decode_nseg(max_len);
+    if (nseg > 0 && ws) {
+        const size_t n = (size_t)B * nseg * CAND_CAP;
+        uint32_t* key = static_cast<uint32_t*>(ws);
+        int32_t* pos = reinterpret_cast<int32_t*>(key + n);
+        int32_t* cnt = pos + n;
+        hipLaunchKernelGGL(topk_segment_kernel, dim3(nseg, B), dim3(TK_THREADS), 0, stream,
+                           scores, seq_start, k, nseg, key, pos, cnt);
+        seg = SegCands{key, pos, cnt, nseg};
+    }
     hipLaunchKernelGGL(topk_kernel<true>, dim3(B), dim3(TK_THREADS), 0, stream, scores,
-                       (int64_t)0, seq_start, 0, 0, k, idx);
+                       (int64_t)0, seq_start, 0, 0, k, idx, seg);
     return hipGetLastError();
 }
 

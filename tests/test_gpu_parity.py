@@ -404,3 +404,58 @@ def test_decode_64_sequences_to_128k_sampled(dsa):
     lens = _np(inp["lens"])
     seqs = sorted({int(np.argmax(lens)), int(np.argmin(lens)), 0, 63, 17})
     _check_decode(dsa, inp, seqs, "decode B=64")
+
+
+def _decode_integer_scores(vals_per_seq, k, H=8, seed=0):
+    """Decode inputs whose indexer scores are exact small integers in any summation order:
+    H_I = 1, a one-hot fp8 query (1.0 in dimension 0), key dimension 0 = the integer value
+    (0..7, exact in e4m3), all other key dimensions 0, unit scales and weights."""
+    g = torch.Generator().manual_seed(seed)
+    lens = np.array([len(v) for v in vals_per_seq], np.int64)
+    B, N = len(lens), int(lens.sum())
+    st = np.zeros(B + 1, np.int64)
+    st[1:] = np.cumsum(lens)
+    code = torch.arange(8, dtype=torch.float32).to(torch.float8_e4m3fn).view(torch.uint8)
+    vals = np.concatenate(vals_per_seq).astype(np.int64)
+    k8 = torch.zeros((N, 128), dtype=torch.uint8)
+    k8[:, 0] = code[torch.from_numpy(vals)]
+    q8 = torch.zeros((B, 1, 128), dtype=torch.uint8)
+    q8[:, :, 0] = code[1]
+    inp = dict(B=B, N=N, H_I=1, H=H, k=k, max_len=int(lens.max()), lens=torch.from_numpy(lens),
+               seq_start=torch.from_numpy(st), score_scale=1.0, sm_scale=0.05, q8=q8,
+               qs=torch.ones((B, 1)), w=torch.ones((B, 1)), k8=k8, ks=torch.ones(N),
+               q=torch.randn((B, H, 576), generator=g).to(torch.bfloat16),
+               kv=torch.randn((N, 576), generator=g).to(torch.bfloat16))
+    return inp, st, vals
+
+
+def test_decode_topk_exact_on_integer_scores(dsa):
+    """Decode rows that the top-k splits over 16K-key segments, with exact integer scores so
+    that the selection (ties to the lower position) is compared exactly: ties at the
+    threshold spread over several segments (the segments' candidates merged), a row of equal
+    scores (segment candidate counts overflow: the exact path), a row staged whole, a row
+    shorter than k, and rows whose threshold falls either way."""
+    rng = np.random.default_rng(21)
+    k = 2048
+    r0 = rng.integers(0, 3, 40000)                      # 1000 sevens, 4000 sixes, rest 0..2
+    p = rng.permutation(40000)
+    r0[p[:1000]] = 7
+    r0[p[1000:5000]] = 6
+    r0[16383:16386] = 7                                 # around the first segment boundary
+    r1 = np.zeros(20000, np.int64)                      # every score equal
+    r2 = rng.integers(0, 8, 3000)                       # staged whole
+    r3 = rng.integers(0, 8, 1500)                       # fewer keys than k
+    r4 = rng.integers(0, 8, 33000)                      # about 4100 sevens
+    r5 = (7 - np.arange(16385) * 8 // 16385).astype(np.int64)   # a ramp into segment 2
+    inp, st, vals = _decode_integer_scores([r0, r1, r2, r3, r4, r5], k)
+    d = to_device(inp)
+    idx = torch.empty((inp["B"], k), dtype=torch.int32, device="cuda")
+    dsa.dsa_decode(d["seq_start"], inp["max_len"], d["q8"], d["qs"], d["w"], d["k8"], d["ks"],
+                   d["q"], d["kv"], k, 1.0, 0.05, idx_out=idx)
+    torch.cuda.synchronize()
+    gidx = _np(idx)
+    for b in range(inp["B"]):
+        sc = vals[st[b]:st[b + 1]].astype(np.float64)[None, :]
+        want = oracle.topk(sc, [len(sc[0])], k)
+        assert np.array_equal(gidx[b], want[0]), "decode top-k row %d (n=%d) differs" % (
+            b, len(sc[0]))
