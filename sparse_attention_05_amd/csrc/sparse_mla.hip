@@ -81,11 +81,17 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p)
     return (uint32_t)(uintptr_t)(const lds_void_t*)p;
 }
 
-// tile byte offset of latent dims [8c, 8c + 8) of row r (chunk c < 64).  The XOR only touches
-// the low three chunk bits, so for c = 8a + b: offset = row_base(r) + 128 a + 16 (b ^ (r & 7))
-// -- a per-lane base plus an immediate.  Rope chunk 64 + b: ROPE_OFF + RROW r + sub_off(r, b).
+// Tile layout.  Latent dims [8c, 8c + 8) of row r (16-byte chunk c < 64) sit at byte
+// row_base(r) + 16 (c ^ lat_x(r)); rope chunk b < 8 (dims 512 + 8b ..) at
+// ROPE_OFF + RROW r + 16 (b ^ rope_x(r)).  lat_x only touches chunk bits 1-3, so for
+// c = 16a + b the offset is a per-lane part for b plus the immediate 256 a.  With these
+// permutations the reads below are free of LDS bank conflicts (measured on gfx950, where a
+// 16-byte read serves lanes {0-7, 24-31}, {8-15, 16-23} and likewise in the upper half
+// together): the K operand reads (16 rows at one chunk per instruction, latent and rope) and
+// the transposing V reads (8-byte pieces of 8 rows, a 32-byte chunk pair per row).
 __device__ __forceinline__ int row_base(int r) { return r * LROW; }
-__device__ __forceinline__ int sub_off(int r, int b) { return (b ^ (r & 7)) << 4; }
+__device__ __forceinline__ int lat_x(int r) { return (r & 7) << 1; }
+__device__ __forceinline__ int rope_x(int r) { return (r >> 1) & 7; }
 
 // NW waves; wave w: heads [32w, 32w + 32) in S^T / softmax (two 16-head groups hq), 16-dim
 // blocks [DPW w, DPW w + DPW) of O for all 2 NW head groups in P V.
@@ -149,12 +155,14 @@ __global__ __launch_bounds__(NW * 64) void sparse_mla_kernel(
     };
     // Gather of a tile into dst (tidx: lane r holds row r's index, -1 for padding, which loads
     // row 0 and is masked later).  Latent parts: wave w moves rows [RPW w, RPW w + RPW), one
-    // instruction per row, lane l loading the source chunk stored in slot l (chunk l ^ (r & 7)).
-    // Rope parts: instruction j moves rows 8j .. 8j+7, lane l row 8j + l/8, slot l%8 (source
-    // chunk 64 + ((l%8) ^ (l/8)), whatever j).
+    // instruction per row, lane l loading the source chunk stored in slot l (chunk
+    // l ^ lat_x(r)).  Rope parts: instruction j moves rows 8j .. 8j+7, lane l row 8j + l/8,
+    // slot l%8, i.e. source chunk 64 + ((l%8) ^ rope_x(8j + l/8)) = 64 + ((l%8) ^ (4 (j%2) + l/16)).
     constexpr int RPW = MT / NW;                       // latent rows per wave
     constexpr int JPW = 8 / NW;                        // rope instructions per wave
-    const uint32_t rope_src = 16u * (64u + (uint32_t)((lane & 7) ^ (lane >> 3)));
+    static_assert(JPW % 2 == 0 && RPW % 8 == 0, "rope instruction parity and row groups per wave");
+    const uint32_t rope_src[2] = {16u * (64u + (uint32_t)((lane & 7) ^ (lane >> 4))),
+                                  16u * (64u + (uint32_t)((lane & 7) ^ (4 + (lane >> 4))))};
     const uint32_t lds_tiles = __builtin_amdgcn_readfirstlane(lds_addr(s_tile[0]));
     auto issue = [&](int buf, int tidx) {
         const uint32_t dst = lds_tiles + (uint32_t)buf * TILE_BYTES;
@@ -162,15 +170,15 @@ __global__ __launch_bounds__(NW * 64) void sparse_mla_kernel(
         for (int i0 = 0; i0 < RPW; i0 += 8)
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
-                const int r = wave * RPW + i0 + i;         // r & 7 == i
+                const int r = wave * RPW + i0 + i;         // r & 7 == i: lat_x(r) = 2 i
                 const int sx = max(__builtin_amdgcn_readlane(tidx, r), 0);
-                dma16_s(16u * (uint32_t)(lane ^ i), kvr + (int64_t)sx * 576, dst + r * LROW);
+                dma16_s(16u * (uint32_t)(lane ^ (2 * i)), kvr + (int64_t)sx * 576, dst + r * LROW);
             }
 #pragma unroll
         for (int jj = 0; jj < JPW; ++jj) {
             const int j = wave * JPW + jj;
             const int sx = max(__builtin_amdgcn_ds_bpermute((8 * j + (lane >> 3)) * 4, tidx), 0);
-            dma16(reinterpret_cast<const uint8_t*>(kvr + (int64_t)sx * 576) + rope_src,
+            dma16(reinterpret_cast<const uint8_t*>(kvr + (int64_t)sx * 576) + rope_src[jj & 1],
                   dst + ROPE_OFF + j * 1024);
         }
     };
@@ -217,9 +225,14 @@ __global__ __launch_bounds__(NW * 64) void sparse_mla_kernel(
                     for (int hq = 0; hq < 2; ++hq) S[kt][hq] = v4f{0.f, 0.f, 0.f, 0.f};
                 const uint8_t* rb = tb + row_base(half * 32 + c16);    // kt adds 16 rows
                 const uint8_t* rr = tb + ROPE_OFF + RROW * (half * 32 + c16);
-                int oo[2];
-                oo[0] = sub_off(c16, g);                // row & 7 == c16 & 7 for these rows
-                oo[1] = sub_off(c16, 4 + g);
+                // latent chunk 4m + g = 16 (m/4) + (4 (m%4) + g): per-lane offsets for m%4,
+                // rope chunk 4 (m - 16) + g for m = 16, 17 (row & 7 == c16 & 7 and
+                // (row >> 1) & 7 == c16 >> 1 for these rows)
+                int qo[4], ro[2];
+#pragma unroll
+                for (int b = 0; b < 4; ++b) qo[b] = ((4 * b + g) ^ lat_x(c16)) << 4;
+#pragma unroll
+                for (int b = 0; b < 2; ++b) ro[b] = ((4 * b + g) ^ rope_x(c16)) << 4;
                 // Software pipeline with fixed stages: stage s issues the reads of step s + QD
                 // and the four MFMAs of step s; the scheduling barriers keep the compiler from
                 // collapsing it into read -> wait -> MFMA (one wave per SIMD leaves nothing
@@ -230,7 +243,7 @@ __global__ __launch_bounds__(NW * 64) void sparse_mla_kernel(
                 for (int s = 0; s < QD; ++s)
 #pragma unroll
                     for (int kt = 0; kt < 2; ++kt)
-                        abuf[s][kt] = *reinterpret_cast<const u32x4*>(rb + kt * 16 * LROW + 128 * (s >> 1) + oo[s & 1]);
+                        abuf[s][kt] = *reinterpret_cast<const u32x4*>(rb + kt * 16 * LROW + 256 * (s >> 2) + qo[s & 3]);
 #pragma unroll
                 for (int s = 0; s < 18; ++s) {
                     __builtin_amdgcn_sched_barrier(0);
@@ -240,8 +253,8 @@ __global__ __launch_bounds__(NW * 64) void sparse_mla_kernel(
 #pragma unroll
                         for (int kt = 0; kt < 2; ++kt)
                             abuf[s % QD][kt] = *reinterpret_cast<const u32x4*>(
-                                m < 16 ? rb + kt * 16 * LROW + 128 * (m >> 1) + oo[m & 1]
-                                       : rr + kt * 16 * RROW + oo[m & 1]);
+                                m < 16 ? rb + kt * 16 * LROW + 256 * (m >> 2) + qo[m & 3]
+                                       : rr + kt * 16 * RROW + ro[m & 1]);
                     }
 #pragma unroll
                     for (int kt = 0; kt < 2; ++kt)
@@ -296,6 +309,11 @@ __global__ __launch_bounds__(NW * 64) void sparse_mla_kernel(
             // i.e. chunk 2n + (i%4)/2 = 8(n/4) + (2(n%4) + (i%4)/2), byte 8 (i%2) within it
             const int cpart = (c16 & 3) >> 1, boff = (c16 & 1) * 8;
             const int rv = 4 * g + (c16 >> 2);         // row within each 16-key group
+            // physical chunk (2n + cpart) ^ lat_x(rv) = 8 ((n/4) ^ vq) + 2 ((n%4) ^ (rv%4)) + cpart
+            const int vq = (rv >> 2) & 1;
+            int vo[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) vo[j] = 32 * (j ^ (rv & 3)) + 16 * cpart;
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
                 const int vrow = row_base(ks * 32 + rv) + boff;
@@ -307,7 +325,7 @@ __global__ __launch_bounds__(NW * 64) void sparse_mla_kernel(
 #pragma unroll
                     for (int d = 0; d < DC; ++d) {
                         const int n = n0 + d0 + d;
-                        const int o = vrow + 128 * (n >> 2) + sub_off(rv, 2 * (n & 3) + cpart);
+                        const int o = vrow + 128 * ((n >> 2) ^ vq) + vo[n & 3];
                         const u32x2 lo = ds_read_tr(tb + o);
                         const u32x2 hi = ds_read_tr(tb + o + 16 * LROW);
                         vop[d] = u32x4{lo[0], lo[1], hi[0], hi[1]};
