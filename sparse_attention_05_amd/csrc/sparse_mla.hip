@@ -266,6 +266,9 @@ __global__ __launch_bounds__(NW * 64) void sparse_mla_kernel(
                 // softmax for heads 16 hq + c16 over this half's 32 keys
 #pragma unroll
                 for (int hq = 0; hq < 2; ++hq) {
+                    // raw logits (masked: -inf); the scale is applied inside the exponent's
+                    // fma, and to the maximum once: scale2 > 0 and rounding is monotonic, so
+                    // max(x) * scale2 is exactly the maximum of the rounded x * scale2
                     float x[2][4];
                     float mloc = -__builtin_huge_valf();
 #pragma unroll
@@ -273,11 +276,11 @@ __global__ __launch_bounds__(NW * 64) void sparse_mla_kernel(
                         const uint32_t bits = (uint32_t)(vmask >> (half * 32 + kt * 16 + 4 * g));
 #pragma unroll
                         for (int r = 0; r < 4; ++r) {
-                            x[kt][r] = ((bits >> r) & 1u) ? S[kt][hq][r] * scale2 : -__builtin_huge_valf();
+                            x[kt][r] = ((bits >> r) & 1u) ? S[kt][hq][r] : -__builtin_huge_valf();
                             mloc = fmaxf(mloc, x[kt][r]);
                         }
                     }
-                    mloc = max_xor32(max_xor16(mloc));
+                    mloc = max_xor32(max_xor16(mloc)) * scale2;
                     m_max[hq] = fmaxf(m_max[hq], mloc);
                     // the first valid logits fix the reference (O and l are still zero then)
                     if (m_ref[hq] == -__builtin_huge_valf()) m_ref[hq] = mloc;
@@ -290,7 +293,7 @@ __global__ __launch_bounds__(NW * 64) void sparse_mla_kernel(
                     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
                         for (int r = 0; r < 4; ++r) {
-                            p[kt][r] = __builtin_amdgcn_exp2f(x[kt][r] - m_sub);
+                            p[kt][r] = __builtin_amdgcn_exp2f(fmaf(x[kt][r], scale2, -m_sub));
                             psum += p[kt][r];
                         }
                     l_run[hq] += psum;
