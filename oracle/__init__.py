@@ -52,6 +52,8 @@ def _load():
             lib.ora_topk_select.argtypes = [P, i64, i64, P, i32, P]
             lib.ora_sparse_mla.argtypes = [P, P, P, i64, i32, i32, dbl, P, i64, P, P]
             lib.ora_dense_mla.argtypes = [P, P, i64, i32, i64, dbl, P, i64, P, P]
+            lib.ora_quantize_e4m3.argtypes = [P, i32, i64, P, P]
+            lib.ora_decode_append.argtypes = [i32, P, P, i32, P, P, P, P]
             lib.ora_num_threads.restype = i32
             _lib = lib
     return _lib
@@ -88,6 +90,35 @@ def e4m3fn_values(codes) -> np.ndarray:
 def bf16_values(bits) -> np.ndarray:
     lib = _load()
     return np.array([lib.ora_bf16_value(int(b)) for b in np.ravel(bits)], dtype=np.float64)
+
+
+def quantize_e4m3(x):
+    """Per-128-vector e4m3fn quantisation: x [..., 128] float32, or uint16 bf16 bits ->
+    (codes uint8 [..., 128], scales float32 [...])."""
+    x = np.asarray(x)
+    bf16 = x.dtype == np.uint16
+    x = _c(x, np.uint16 if bf16 else np.float32)
+    assert x.shape[-1] == 128
+    n = x.size // 128
+    q8 = np.empty(x.shape, np.uint8)
+    sc = np.empty(x.shape[:-1], np.float32)
+    _check(_load().ora_quantize_e4m3(_p(x), int(bf16), n, _p(q8), _p(sc)), "quantize_e4m3")
+    return q8, sc
+
+
+def decode_append(seq_start, k_new, kv_new, k8_cache, ks_cache, kv_cache):
+    """Write each sequence's new token into row seq_start[b+1]-1 of the caches (in place);
+    k_new [B,128] float32 or uint16 bf16 bits, kv_new [B,576] uint16."""
+    st = _c(seq_start, np.int64)
+    k_new = np.asarray(k_new)
+    bf16 = k_new.dtype == np.uint16
+    k_new = _c(k_new, np.uint16 if bf16 else np.float32)
+    kv_new = _c(kv_new, np.uint16)
+    for a, dt in ((k8_cache, np.uint8), (ks_cache, np.float32), (kv_cache, np.uint16)):
+        assert a.dtype == dt and a.flags["C_CONTIGUOUS"]
+    B = len(st) - 1
+    _check(_load().ora_decode_append(B, _p(st), _p(k_new), int(bf16), _p(kv_new), _p(k8_cache),
+                                     _p(ks_cache), _p(kv_cache)), "decode_append")
 
 
 def index_scores(q8, qs, w, k8, ks, q_pos0: int, c: float, rows=None, with_bound=False):

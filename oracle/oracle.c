@@ -309,3 +309,74 @@ int ora_dense_mla(const uint16_t* q, const uint16_t* kv, int64_t L, int H, int64
     }
     return bad ? -1 : 0;
 }
+
+/* ---- fp8 preparation of the indexer inputs, and the decode cache append ------------- */
+
+/* Nearest e4m3fn code to y (|y| <= 448, the largest finite value), ties to the even code,
+ * i.e. round to nearest even; the sign of y, zero included, goes to the sign bit. */
+static uint8_t e4m3fn_nearest(float y)
+{
+    const int neg = signbit(y) != 0;
+    const double a = fabs((double)y);
+    int best = 0;
+    double bd = INFINITY;
+    for (int c = 0; c <= 0x7E; ++c) {
+        const double d = fabs(ora_e4m3fn_value((uint8_t)c) - a);
+        if (d < bd || (d == bd && (c & 1) == 0)) {
+            bd = d;
+            best = c;
+        }
+    }
+    return (uint8_t)(best | (neg << 7));
+}
+
+static float vec_elem(const void* x, int x_bf16, int64_t i)
+{
+    if (x_bf16) {
+        const uint32_t u = (uint32_t)((const uint16_t*)x)[i] << 16;
+        float f;
+        memcpy(&f, &u, sizeof f);
+        return f;
+    }
+    return ((const float*)x)[i];
+}
+
+int ora_quantize_e4m3(const void* x, int x_bf16, int64_t n, uint8_t* q8, float* scale)
+{
+    if (!x || !q8 || !scale || n < 0) return -1;
+#pragma omp parallel for schedule(static)
+    for (int64_t v = 0; v < n; ++v) {
+        float amax = 0.f;
+        for (int d = 0; d < 128; ++d) {
+            const float a = fabsf(vec_elem(x, x_bf16, v * 128 + d));
+            if (a > amax) amax = a;
+        }
+        const float s = amax > 0.f ? amax / 448.0f : 1.0f;   /* fp32 division */
+        scale[v] = s;
+        for (int d = 0; d < 128; ++d) {
+            float y = vec_elem(x, x_bf16, v * 128 + d) / s;   /* rounded to fp32 */
+            if (y > 448.f) y = 448.f;
+            if (y < -448.f) y = -448.f;
+            q8[v * 128 + d] = e4m3fn_nearest(y);
+        }
+    }
+    return 0;
+}
+
+int ora_decode_append(int B, const int64_t* seq_start, const void* k_new, int k_bf16,
+                      const uint16_t* kv_new, uint8_t* k8_cache, float* k_scale_cache,
+                      uint16_t* kv_cache)
+{
+    if (B < 0 || !seq_start || !k_new || !kv_new || !k8_cache || !k_scale_cache || !kv_cache)
+        return -1;
+    for (int b = 0; b < B; ++b)
+        if (seq_start[b + 1] <= seq_start[b]) return -1;
+    const size_t esz = k_bf16 ? 2 : 4;
+    for (int b = 0; b < B; ++b) {
+        const int64_t r = seq_start[b + 1] - 1;
+        ora_quantize_e4m3((const uint8_t*)k_new + (size_t)b * 128 * esz, k_bf16, 1,
+                          k8_cache + r * 128, k_scale_cache + r);
+        memcpy(kv_cache + r * 576, kv_new + (size_t)b * 576, 576 * sizeof(uint16_t));
+    }
+    return 0;
+}

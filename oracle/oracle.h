@@ -71,6 +71,21 @@ int ora_dense_mla(const uint16_t* q, const uint16_t* kv, int64_t L, int H, int64
                   double* lse);
 
 /* Threads the OpenMP loops use. */
+/* fp8 preparation of the indexer inputs (the step upstream of the lightning indexer, which
+ * runs in FP8: [gxzdkb-dsa] 秘密武器：DSA, [csdn-workflow] §3 两大核心组件).  Per 128-wide
+ * vector: scale = amax / 448 in fp32 (1 for an all-zero vector); code d = the e4m3fn value
+ * nearest to clamp(x[d] / scale, -448, 448), the quotient rounded to fp32, ties to the even
+ * code.  x[n,128] fp32, or bf16 bits when x_bf16; q8[n,128]; scale[n]. */
+int ora_quantize_e4m3(const void* x, int x_bf16, int64_t n, uint8_t* q8, float* scale);
+
+/* Decode cache append ([gxzdkb-dsa] 原始 Attention 的计算逻辑: the new token's entries join
+ * the cache before the step attends): row r = seq_start[b+1] - 1 of the packed caches gets
+ * k8_cache[r], k_scale_cache[r] = the quantisation of k_new[b] (as above) and
+ * kv_cache[r] = kv_new[b] (576 bf16).  Every sequence must hold at least one row. */
+int ora_decode_append(int B, const int64_t* seq_start, const void* k_new, int k_bf16,
+                      const uint16_t* kv_new, uint8_t* k8_cache, float* k_scale_cache,
+                      uint16_t* kv_cache);
+
 int ora_num_threads(void);
 
 #ifdef __cplusplus

@@ -340,3 +340,82 @@ def test_decode_matches_prefill_last_row_and_dense_when_short():
                                  a["k8"][sl], a["ks"][sl], Lb - 1, a["score_scale"])
         assert np.array_equal(sc[0], r["scores"])
         assert np.all(np.isfinite(r["scores"]))
+
+
+# ----------------------------------------------------------------- fp8 input preparation
+
+def _torch_quant(x: torch.Tensor):
+    """The per-vector e4m3fn quantisation written with torch-CPU ops: fp32 amax / 448, fp32
+    quotient, clamp (torch's cast does not saturate), torch's round-to-nearest-even cast."""
+    amax = x.abs().amax(dim=-1)
+    s = torch.where(amax > 0, amax / 448.0, torch.ones_like(amax))
+    q = (x / s.unsqueeze(-1)).clamp(-448.0, 448.0).to(torch.float8_e4m3fn)
+    return q.view(torch.uint8).numpy(), s.numpy()
+
+
+def test_quantize_matches_torch_cast_random_scales():
+    g = torch.Generator().manual_seed(7)
+    parts = []
+    for mag in (1e-30, 1e-6, 1.0, 3.7, 1e4, 1e30):
+        parts.append(torch.randn((64, 128), generator=g) * mag)
+    x = torch.cat(parts)
+    x[5, :] = 0.0                                     # all-zero vector: scale 1
+    x[6, :] = -0.0                                    # negative zeros keep their sign
+    x[7, :] = 0.0
+    x[7, 9] = -2.5                                    # one non-zero element: it maps to -448
+    q, s = oracle.quantize_e4m3(x.numpy())
+    tq, ts = _torch_quant(x)
+    assert np.array_equal(s, ts)
+    assert np.array_equal(q, tq)
+    assert s[5] == 1.0 and q[5].max() == 0 and np.all(q[6] == 0x80) and q[7, 9] == 0xFE
+
+
+def test_quantize_ties_and_neighbours_match_torch_cast():
+    """Scale exactly 1 (448 in every vector), the other entries every midpoint between
+    adjacent e4m3fn values, those midpoints' fp32 neighbours, and the values themselves
+    (both signs): the round-to-nearest-even rule, subnormals and the top of the range."""
+    vals = torch.arange(0, 127, dtype=torch.uint8).view(torch.float8_e4m3fn).to(torch.float32)
+    mids = (vals[1:] + vals[:-1]) / 2                 # exact in fp32
+    up = torch.nextafter(mids, torch.full_like(mids, 1e9))
+    down = torch.nextafter(mids, torch.zeros_like(mids))
+    pool = torch.cat([vals, mids, up, down, torch.tensor([2.0 ** -11, 2.0 ** -10, 3 * 2.0 ** -11])])
+    pool = torch.cat([pool, -pool])
+    n = (len(pool) + 126) // 127
+    x = torch.zeros((n, 128))
+    flat = torch.cat([pool, torch.zeros(n * 127 - len(pool))])
+    x[:, 1:] = flat.view(n, 127)
+    x[:, 0] = 448.0
+    q, s = oracle.quantize_e4m3(x.numpy())
+    tq, ts = _torch_quant(x)
+    assert np.all(s == 1.0) and np.array_equal(ts, s)
+    assert np.array_equal(q, tq)
+
+
+def test_quantize_bf16_input_matches_fp32_of_the_same_values():
+    g = torch.Generator().manual_seed(3)
+    xb = (torch.randn((50, 128), generator=g) * 5).to(torch.bfloat16)
+    bits = xb.view(torch.int16).numpy().view(np.uint16)
+    q, s = oracle.quantize_e4m3(bits)
+    tq, ts = _torch_quant(xb.to(torch.float32))
+    assert np.array_equal(q, tq) and np.array_equal(s, ts)
+
+
+def test_decode_append_writes_exactly_the_last_row_of_each_sequence():
+    rng = np.random.default_rng(4)
+    lens = np.array([3, 1, 7, 2])
+    st = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    N = int(st[-1])
+    k8 = rng.integers(0, 256, (N, 128), dtype=np.uint8)
+    ks = rng.random(N).astype(np.float32)
+    kv = rng.integers(0, 65536, (N, 576), dtype=np.uint16)
+    k_new = rng.standard_normal((4, 128)).astype(np.float32)
+    kv_new = rng.integers(0, 65536, (4, 576), dtype=np.uint16)
+    k8_0, ks_0, kv_0 = k8.copy(), ks.copy(), kv.copy()
+    oracle.decode_append(st, k_new, kv_new, k8, ks, kv)
+    last = st[1:] - 1
+    others = np.setdiff1d(np.arange(N), last)
+    assert np.array_equal(k8[others], k8_0[others]) and np.array_equal(ks[others], ks_0[others])
+    assert np.array_equal(kv[others], kv_0[others])
+    tq, ts = _torch_quant(torch.from_numpy(k_new))
+    assert np.array_equal(k8[last], tq) and np.array_equal(ks[last], ts)
+    assert np.array_equal(kv[last], kv_new)
