@@ -71,6 +71,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-input-prep", action="store_true",
+                    help="skip timing the fp8 quantisation of the indexer inputs")
     ap.add_argument("--no-prefill", action="store_true",
                     help="decode only (for profiling runs; prints no prefill value)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -220,6 +222,9 @@ def main():
     # ---- decode
     decode = None if args.no_decode else run_decode(args, WORKLOADS[args.decode_workload], dev)
 
+    # ---- fp8 preparation of the same workload's indexer inputs (outside the step)
+    prep = None if args.no_input_prep else run_input_prep(args, cfg, dev)
+
     # ---- CPU oracle baseline on sampled rows of the same prefill workload
     cpu = None
     if not args.no_cpu_baseline:
@@ -244,6 +249,7 @@ def main():
         "roofline": roofline,
         "kernels": kern,
         "decode": decode,
+        "input_prep": prep,
         "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)
@@ -287,12 +293,66 @@ def run_decode(args, dcfg, dev):
            + B * dcfg.H_I * (D_I + 8) + B * dcfg.H * (D_QK * 2 + D_V * 2 + 4))
     gbs = hbm / (dms / 1e3) / 1e9
     log("decode %.4f ms/step, %.0f tokens/s, %.0f GB/s" % (dms, B / (dms / 1e3), gbs))
+    # the cache append that precedes a decode step (new key quantised, latent row copied)
+    g = torch.Generator(device=dev)
+    g.manual_seed(17)
+    k_new = torch.randn((B, D_I), generator=g, device=dev).to(torch.bfloat16)
+    kv_new = torch.randn((B, D_QK), generator=g, device=dev).to(torch.bfloat16)
+
+    def append():
+        dsa.dsa_decode_append(dinp["seq_start"], k_new, kv_new, dinp["k8"], dinp["ks"], dinp["kv"])
+
+    for _ in range(3):
+        append()
+    torch.cuda.synchronize()
+    d0.record(stream)
+    for _ in range(50):
+        append()
+    d1.record(stream)
+    torch.cuda.synchronize()
+    app_us = d0.elapsed_time(d1) / 50 * 1e3
+    log("decode cache append %.2f us" % app_us)
     return dict(workload=dcfg.name, ms_per_step=round(dms, 4),
                 tokens_per_s=round(B / (dms / 1e3), 1), sequences=B, context_tokens=int(N),
-                steps=dsteps,
+                steps=dsteps, append_us=round(app_us, 2),
                 roofline=dict(bound="hbm", achieved=round(gbs, 1), peak=HBM_PEAK_GBS,
                               unit="GB/s", frac=round(gbs / HBM_PEAK_GBS, 4),
                               algorithmic_bytes=int(hbm)))
+
+
+def run_input_prep(args, cfg, dev):
+    """Time dsa_quantize_fp8 on the workload's indexer inputs (T x H_I query vectors and L key
+    vectors, bf16, in one call): HBM-bound, 256 B read + 132 B written per vector."""
+    import torch
+
+    import sparse_attention_05_amd as dsa
+
+    n = cfg.L * cfg.H_I + cfg.L
+    g = torch.Generator(device=dev)
+    g.manual_seed(23)
+    x = torch.randn((n, D_I), generator=g, device=dev).to(torch.bfloat16)
+    q8 = torch.empty((n, D_I), dtype=torch.uint8, device=dev)
+    sc = torch.empty((n,), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    for _ in range(2):
+        dsa.dsa_quantize_fp8(x, q8, sc)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 5
+    e0.record(stream)
+    for _ in range(reps):
+        dsa.dsa_quantize_fp8(x, q8, sc)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    nbytes = n * (D_I * 2 + D_I + 4)
+    gbs = nbytes / (ms / 1e3) / 1e9
+    log("input prep: %d vectors in %.3f ms, %.0f GB/s" % (n, ms, gbs))
+    del x, q8, sc
+    return dict(workload="fp8 quantisation of %s indexer inputs (bf16)" % cfg.name, vectors=n,
+                ms=round(ms, 4), vectors_per_s=round(n / (ms / 1e3), 1),
+                roofline=dict(bound="hbm", achieved=round(gbs, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                              frac=round(gbs / HBM_PEAK_GBS, 4), algorithmic_bytes=int(nbytes)))
 
 
 def cpu_baseline(inp, cfg, seconds):

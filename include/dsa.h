@@ -58,7 +58,7 @@ typedef enum {
 /* Static, human-readable name of a status code. */
 const char* dsa_status_string(dsa_status_t status);
 
-/* ABI version: major * 100 + minor. */
+/* ABI version: major * 100 + minor (1.01: dsa_quantize_fp8, dsa_decode_append). */
 int dsa_version(void);
 
 /* Lightning-indexer scores ([csdn-workflow] §4 步骤二, [devpress-dsa] §三 第二步):
@@ -131,6 +131,31 @@ dsa_status_t dsa_decode(int B, const int64_t* seq_start, int max_len, int64_t to
                         dsa_stream_t stream);
 size_t dsa_decode_workspace_bytes(int B, int max_len, int64_t total_tokens, int H_I, int H,
                                   int k);
+
+/* fp8 preparation of the indexer's inputs, the step upstream of dsa_index_scores (the
+ * indexer runs in FP8: [gxzdkb-dsa] 秘密武器：DSA, [csdn-workflow] §3 两大核心组件).  Each
+ * 128-wide vector i of x (fp32, or bf16 bits when x_is_bf16 = 1) becomes
+ *   scale[i] = amax_i / 448 (fp32; 1 for an all-zero vector) and
+ *   q8[i,d]  = the e4m3fn value nearest to clamp(x[i,d] / scale[i], -448, 448), the quotient
+ *              rounded to fp32, ties to even, the sign of zero kept,
+ * the format dsa_index_scores reads (q8 with q_scale, k8 with k_scale).
+ *   x [n,128] 16-byte aligned; q8 [n,128] 8-byte aligned; scale [n] fp32.  x must be finite.
+ * n = 0 is a no-op. */
+dsa_status_t dsa_quantize_fp8(const void* x, int x_is_bf16, int64_t n, uint8_t* q8,
+                              float* scale, dsa_stream_t stream);
+
+/* Decode cache append ([gxzdkb-dsa] 原始 Attention 的计算逻辑: the new token's entries join
+ * the cache before the step attends), the step before dsa_decode: for each sequence b, row
+ * r = seq_start[b+1] - 1 of the packed caches receives the new token,
+ *   k8_cache[r,:], k_scale_cache[r] = the quantisation of k_new[b,:] (as dsa_quantize_fp8),
+ *   kv_cache[r,:] = kv_new[b,:].
+ *   seq_start DEVICE int64 [B+1] as in dsa_decode, already counting the new tokens (a
+ *   sequence with no row is skipped); k_new [B,128] fp32, or bf16 bits when k_is_bf16 = 1,
+ *   16-byte aligned; kv_new [B,576] and kv_cache 16-byte aligned; k8_cache 8-byte aligned.
+ * B = 0 is a no-op; B <= 65535. */
+dsa_status_t dsa_decode_append(int B, const int64_t* seq_start, const void* k_new, int k_is_bf16,
+                               const uint16_t* kv_new, uint8_t* k8_cache, float* k_scale_cache,
+                               uint16_t* kv_cache, dsa_stream_t stream);
 
 #ifdef __cplusplus
 }

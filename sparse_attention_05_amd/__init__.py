@@ -29,7 +29,7 @@ DSA_ERR_WORKSPACE_TOO_SMALL, DSA_ERR_HIP = 3, 4
 EXPORTS = ("dsa_status_string", "dsa_version", "dsa_index_scores", "dsa_topk",
            "dsa_topk_workspace_bytes", "dsa_sparse_mla", "dsa_prefill",
            "dsa_prefill_workspace_bytes", "dsa_prefill_chunk_rows", "dsa_decode",
-           "dsa_decode_workspace_bytes")
+           "dsa_decode_workspace_bytes", "dsa_quantize_fp8", "dsa_decode_append")
 
 
 class DSAError(RuntimeError):
@@ -66,8 +66,10 @@ def load(path: str = LIB_PATH):
                                        f32, P, P, P, P, sz, P]
             lib.dsa_decode_workspace_bytes.restype = sz
             lib.dsa_decode_workspace_bytes.argtypes = [i32, i32, i64, i32, i32, i32]
+            lib.dsa_quantize_fp8.argtypes = [P, i32, i64, P, P, P]
+            lib.dsa_decode_append.argtypes = [i32, P, P, i32, P, P, P, P, P]
             for fn in ("dsa_index_scores", "dsa_topk", "dsa_sparse_mla", "dsa_prefill",
-                       "dsa_decode"):
+                       "dsa_decode", "dsa_quantize_fp8", "dsa_decode_append"):
                 getattr(lib, fn).restype = i32
             _lib = lib
     return _lib
@@ -242,3 +244,49 @@ def dsa_decode(seq_start, max_len: int, q8, q_scale, w, k8, k_scale, q, kv, k: i
                           sm_scale, _ptr(out), _ptr(lse), _ptr(idx_out), _ptr(workspace),
                           workspace.numel(), _stream()), "dsa_decode")
     return out, lse, idx_out
+
+
+def dsa_quantize_fp8(x, q8=None, scale=None):
+    """Per-128-vector e4m3fn quantisation of x [..., 128] (float32 or bfloat16):
+    (q8 uint8 [..., 128], scale float32 [...])."""
+    lib = load()
+    if not isinstance(x, torch.Tensor) or not x.is_cuda or x.dtype not in (torch.float32,
+                                                                            torch.bfloat16):
+        raise TypeError("x must be a float32 or bfloat16 CUDA tensor")
+    if x.shape[-1] != 128 or not x.is_contiguous():
+        raise ValueError("x must be contiguous [..., 128]")
+    lead = tuple(x.shape[:-1])
+    n = x.numel() // 128
+    if q8 is None:
+        q8 = torch.empty(lead + (128,), dtype=torch.uint8, device=x.device)
+    if scale is None:
+        scale = torch.empty(lead, dtype=torch.float32, device=x.device)
+    _req(q8, torch.uint8, lead + (128,), "q8")
+    _req(scale, torch.float32, lead, "scale")
+    _check(lib.dsa_quantize_fp8(_ptr(x), int(x.dtype == torch.bfloat16), n, _ptr(q8),
+                                _ptr(scale), _stream()), "dsa_quantize_fp8")
+    return q8, scale
+
+
+def dsa_decode_append(seq_start, k_new, kv_new, k8_cache, k_scale_cache, kv_cache):
+    """Write each sequence's new token into row seq_start[b+1]-1 of the packed caches
+    (in place): k_new [B,128] float32/bfloat16, kv_new [B,576] bfloat16."""
+    lib = load()
+    B = k_new.shape[0]
+    N = kv_cache.shape[0]
+    _req(seq_start, torch.int64, (B + 1,), "seq_start")
+    if not isinstance(k_new, torch.Tensor) or not k_new.is_cuda or k_new.dtype not in (
+            torch.float32, torch.bfloat16):
+        raise TypeError("k_new must be a float32 or bfloat16 CUDA tensor")
+    if tuple(k_new.shape) != (B, 128) or not k_new.is_contiguous():
+        raise ValueError("k_new must be contiguous [B, 128]")
+    _req(kv_new, torch.bfloat16, (B, 576), "kv_new")
+    k8_cache = _u8(k8_cache)
+    _req(k8_cache, torch.uint8, (N, 128), "k8_cache")
+    _req(k_scale_cache, torch.float32, (N,), "k_scale_cache")
+    _req(kv_cache, torch.bfloat16, (N, 576), "kv_cache")
+    _check(lib.dsa_decode_append(B, _ptr(seq_start), _ptr(k_new),
+                                 int(k_new.dtype == torch.bfloat16), _ptr(kv_new),
+                                 _ptr(k8_cache), _ptr(k_scale_cache), _ptr(kv_cache),
+                                 _stream()), "dsa_decode_append")
+    return k8_cache, k_scale_cache, kv_cache

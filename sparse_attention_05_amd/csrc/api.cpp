@@ -99,7 +99,7 @@ const char* dsa_status_string(dsa_status_t status)
     return "DSA_ERR_UNKNOWN";
 }
 
-int dsa_version(void) { return 100; }
+int dsa_version(void) { return 101; }
 
 dsa_status_t dsa_index_scores(const uint8_t* q8, const float* q_scale, const float* w,
                               const uint8_t* k8, const float* k_scale, int T, int L, int H_I,
@@ -269,6 +269,34 @@ dsa_status_t dsa_decode(int B, const int64_t* seq_start, int max_len, int64_t to
     if (e == hipSuccess && ws.splits > 1)
         e = dsa::launch_mla_combine(po, pl, B, H, ws.splits, out, lse, s);
     return from_hip(e);
+}
+
+dsa_status_t dsa_quantize_fp8(const void* x, int x_is_bf16, int64_t n, uint8_t* q8,
+                              float* scale, dsa_stream_t stream)
+{
+    if (n < 0 || (x_is_bf16 != 0 && x_is_bf16 != 1)) return DSA_ERR_INVALID_ARGUMENT;
+    if (n == 0) return DSA_OK;
+    if (!x || !q8 || !scale) return DSA_ERR_INVALID_ARGUMENT;
+    if (n > kMaxElems / 128) return DSA_ERR_UNSUPPORTED;
+    if (!aligned(x, 16) || !aligned(q8, 8) || !aligned(scale, 4)) return DSA_ERR_INVALID_ARGUMENT;
+    return from_hip(dsa::launch_quantize_fp8(x, x_is_bf16 != 0, n, q8, scale, as_hip(stream)));
+}
+
+dsa_status_t dsa_decode_append(int B, const int64_t* seq_start, const void* k_new, int k_is_bf16,
+                               const uint16_t* kv_new, uint8_t* k8_cache, float* k_scale_cache,
+                               uint16_t* kv_cache, dsa_stream_t stream)
+{
+    if (B < 0 || (k_is_bf16 != 0 && k_is_bf16 != 1)) return DSA_ERR_INVALID_ARGUMENT;
+    if (B == 0) return DSA_OK;
+    if (B > 65535) return DSA_ERR_UNSUPPORTED;
+    if (!seq_start || !k_new || !kv_new || !k8_cache || !k_scale_cache || !kv_cache)
+        return DSA_ERR_INVALID_ARGUMENT;
+    if (!aligned(k_new, 16) || !aligned(kv_new, 16) || !aligned(k8_cache, 8) ||
+        !aligned(k_scale_cache, 4) || !aligned(kv_cache, 16))
+        return DSA_ERR_INVALID_ARGUMENT;
+    return from_hip(dsa::launch_decode_append(B, seq_start, k_new, k_is_bf16 != 0, kv_new,
+                                              k8_cache, k_scale_cache, kv_cache,
+                                              as_hip(stream)));
 }
 
 }  // extern "C"

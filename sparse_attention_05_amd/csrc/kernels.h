@@ -50,4 +50,14 @@ hipError_t launch_sparse_mla(const uint16_t* q, const uint16_t* kv, const int32_
 hipError_t launch_mla_combine(const float* part_o, const float* part_lse, int T, int H,
                               int splits, uint16_t* out, float* lse, hipStream_t stream);
 
+// ---- fp8 preparation of the indexer inputs ------------------------------------------
+// x [n,128] fp32 (or bf16 bits) -> q8 [n,128] e4m3fn, scale [n]: scale = amax / 448 (1 if 0),
+// code = nearest-even e4m3fn of clamp(x / scale, +-448).  x 16-byte aligned, q8 8-byte.
+hipError_t launch_quantize_fp8(const void* x, bool bf16, int64_t n, uint8_t* q8, float* scale,
+                               hipStream_t stream);
+// Row seq_start[b+1] - 1 of the packed caches gets the new token of sequence b.
+hipError_t launch_decode_append(int B, const int64_t* seq_start, const void* k_new, bool bf16,
+                                const uint16_t* kv_new, uint8_t* k8_cache, float* ks_cache,
+                                uint16_t* kv_cache, hipStream_t stream);
+
 }  // namespace dsa

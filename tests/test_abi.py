@@ -24,7 +24,7 @@ def lib():
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(dsa_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(dsa_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_exports_every_declared_symbol(lib):
@@ -35,7 +35,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_status_strings_and_version(lib):
-    assert lib.dsa_version() == 100
+    assert lib.dsa_version() == 101
     for code, name in [(0, b"DSA_OK"), (1, b"DSA_ERR_INVALID_ARGUMENT"),
                        (2, b"DSA_ERR_UNSUPPORTED"), (3, b"DSA_ERR_WORKSPACE_TOO_SMALL"),
                        (4, b"DSA_ERR_HIP")]:
@@ -120,3 +120,22 @@ def test_decode_validation_and_workspace(lib):
     assert f(ws=NULL) == dsa.DSA_ERR_WORKSPACE_TOO_SMALL
     assert f(wsb=need - 1) == dsa.DSA_ERR_WORKSPACE_TOO_SMALL
     assert f(B=0, p=NULL) == dsa.DSA_OK
+
+
+def test_quantize_and_append_validation(lib):
+    q = lib.dsa_quantize_fp8
+    assert q(FAKE, 0, -1, FAKE, FAKE, NULL) == dsa.DSA_ERR_INVALID_ARGUMENT
+    assert q(FAKE, 2, 4, FAKE, FAKE, NULL) == dsa.DSA_ERR_INVALID_ARGUMENT    # dtype flag
+    assert q(NULL, 0, 4, FAKE, FAKE, NULL) == dsa.DSA_ERR_INVALID_ARGUMENT
+    assert q(FAKE, 0, 4, NULL, FAKE, NULL) == dsa.DSA_ERR_INVALID_ARGUMENT
+    assert q(ctypes.c_void_p((1 << 20) + 8), 0, 4, FAKE, FAKE, NULL) == dsa.DSA_ERR_INVALID_ARGUMENT
+    assert q(NULL, 0, 0, NULL, NULL, NULL) == dsa.DSA_OK                       # nothing to do
+    assert q(FAKE, 1, 1 << 40, FAKE, FAKE, NULL) == dsa.DSA_ERR_UNSUPPORTED
+    a = lib.dsa_decode_append
+    assert a(-1, FAKE, FAKE, 0, FAKE, FAKE, FAKE, FAKE, NULL) == dsa.DSA_ERR_INVALID_ARGUMENT
+    assert a(2, FAKE, FAKE, 3, FAKE, FAKE, FAKE, FAKE, NULL) == dsa.DSA_ERR_INVALID_ARGUMENT
+    assert a(2, NULL, FAKE, 0, FAKE, FAKE, FAKE, FAKE, NULL) == dsa.DSA_ERR_INVALID_ARGUMENT
+    assert a(2, FAKE, FAKE, 0, FAKE, FAKE, FAKE, ctypes.c_void_p((1 << 20) + 4),
+             NULL) == dsa.DSA_ERR_INVALID_ARGUMENT
+    assert a(70000, FAKE, FAKE, 0, FAKE, FAKE, FAKE, FAKE, NULL) == dsa.DSA_ERR_UNSUPPORTED
+    assert a(0, NULL, NULL, 0, NULL, NULL, NULL, NULL, NULL) == dsa.DSA_OK
