@@ -54,6 +54,8 @@ def _load():
             lib.ora_dense_mla.argtypes = [P, P, i64, i32, i64, dbl, P, i64, P, P]
             lib.ora_quantize_e4m3.argtypes = [P, i32, i64, P, P]
             lib.ora_decode_append.argtypes = [i32, P, P, i32, P, P, P, P]
+            lib.ora_window_indices.argtypes = [i64, i64, i32, P]
+            lib.ora_local_selected.argtypes = [P, i64, i32, i64, i32, P]
             lib.ora_num_threads.restype = i32
             _lib = lib
     return _lib
@@ -119,6 +121,22 @@ def decode_append(seq_start, k_new, kv_new, k8_cache, ks_cache, kv_cache):
     B = len(st) - 1
     _check(_load().ora_decode_append(B, _p(st), _p(k_new), int(bf16), _p(kv_new), _p(k8_cache),
                                      _p(ks_cache), _p(kv_cache)), "decode_append")
+
+
+def window_indices(T: int, q_pos0: int, W: int):
+    """int32 [T, W]: positions max(0, p-W+1) .. p of each row, ascending, -1 padded."""
+    out = np.empty((T, W), np.int32)
+    _check(_load().ora_window_indices(T, q_pos0, W, _p(out)), "window_indices")
+    return out
+
+
+def local_selected(sel, q_pos0: int, W: int):
+    """int32 [T, W + k]: ascending union of each row's window and its selected positions."""
+    sel = _c(sel, np.int32)
+    T, k = sel.shape
+    out = np.empty((T, W + k), np.int32)
+    _check(_load().ora_local_selected(_p(sel), T, k, q_pos0, W, _p(out)), "local_selected")
+    return out
 
 
 def index_scores(q8, qs, w, k8, ks, q_pos0: int, c: float, rows=None, with_bound=False):

@@ -380,3 +380,39 @@ int ora_decode_append(int B, const int64_t* seq_start, const void* k_new, int k_
     }
     return 0;
 }
+
+/* ---- alternative index rules ------------------------------------------------------- */
+
+int ora_window_indices(int64_t T, int64_t q_pos0, int W, int32_t* idx)
+{
+    if (T < 0 || q_pos0 < 0 || W < 1 || !idx) return -1;
+    for (int64_t t = 0; t < T; ++t) {
+        const int64_t p = q_pos0 + t;
+        int j = 0;
+        for (int64_t s = 0; s <= p; ++s)               /* the W positions ending at p */
+            if (s > p - W) idx[t * W + j++] = (int32_t)s;
+        for (; j < W; ++j) idx[t * W + j] = -1;
+    }
+    return 0;
+}
+
+int ora_local_selected(const int32_t* sel, int64_t T, int k, int64_t q_pos0, int W, int32_t* out)
+{
+    if (!sel || !out || T < 0 || k < 1 || W < 1 || q_pos0 < 0) return -1;
+    const int M = W + k;
+    for (int64_t t = 0; t < T; ++t) {
+        const int64_t p = q_pos0 + t;
+        unsigned char* in = calloc((size_t)p + 1, 1);  /* membership over positions 0..p */
+        if (!in) return -1;
+        for (int64_t s = 0; s <= p; ++s) if (s > p - W) in[s] = 1;
+        for (int j = 0; j < k; ++j) {
+            const int32_t s = sel[t * k + j];
+            if (s >= 0 && s <= p) in[s] = 1;
+        }
+        int j = 0;
+        for (int64_t s = 0; s <= p && j < M; ++s) if (in[s]) out[t * M + j++] = (int32_t)s;
+        for (; j < M; ++j) out[t * M + j] = -1;
+        free(in);
+    }
+    return 0;
+}

@@ -13,6 +13,7 @@
  *   [gxzdkb-dsa]    gxzdkb.com explainer of DSA -- sections 原始 Attention 的计算逻辑,
  *                   秘密武器：DSA, 实测效果.
  *   [yufo-notes]    ele-yufo.com notes "DeepSeek V3.2-Exp" -- §三 两步跑通稀疏路由.
+ *   [oilbeater-dsa] oilbeater.com "DeepSeek Sparse Attention" -- section Sparse Attention.
  *
  * Conventions shared by every function:
  *   fp8 operands are OCP e4m3fn bytes; bf16 operands are raw uint16 bits.
@@ -85,6 +86,15 @@ int ora_quantize_e4m3(const void* x, int x_bf16, int64_t n, uint8_t* q8, float* 
 int ora_decode_append(int B, const int64_t* seq_start, const void* k_new, int k_bf16,
                       const uint16_t* kv_new, uint8_t* k8_cache, float* k_scale_cache,
                       uint16_t* kv_cache);
+
+/* Alternative index rules feeding the sparse MLA ([gxzdkb-dsa] 秘密武器：DSA: DSA generalises
+ * sliding-window attention; [oilbeater-dsa] oilbeater.com "DeepSeek Sparse Attention", section
+ * Sparse Attention: a local sliding window, alone or joined by globally chosen tokens).
+ * Window: row t (position p = q_pos0 + t) keeps the W positions max(0, p-W+1) .. p, ascending,
+ * -1 padded: idx [T, W].  Local + selected: the ascending union of that window and the valid
+ * entries (0 <= s <= p) of sel[t, 0:k], -1 padded: out [T, W + k]. */
+int ora_window_indices(int64_t T, int64_t q_pos0, int W, int32_t* idx);
+int ora_local_selected(const int32_t* sel, int64_t T, int k, int64_t q_pos0, int W, int32_t* out);
 
 int ora_num_threads(void);
 

@@ -419,3 +419,49 @@ def test_decode_append_writes_exactly_the_last_row_of_each_sequence():
     tq, ts = _torch_quant(torch.from_numpy(k_new))
     assert np.array_equal(k8[last], tq) and np.array_equal(ks[last], ts)
     assert np.array_equal(kv[last], kv_new)
+
+
+# ------------------------------------------------------------------ alternative index rules
+
+def test_window_attention_matches_banded_sdpa():
+    """Sliding-window attention as index lists: the sparse MLA over each row's window equals
+    torch's attention with a band mask (tril/triu) of width W ending at the row's position."""
+    a = _small_prefill(L=60, H=3, k=8, seed=17, q_pos0=10, T=50)
+    T, L, W, q0 = 50, 60, 7, 10
+    idx = oracle.window_indices(T, q0, W)
+    out, lse = oracle.sparse_mla(a["q"], a["kv"], idx, 0.06)
+    band = torch.ones((T, L), dtype=torch.bool).tril(q0).triu(q0 - W + 1)
+    q = _deq16(a["q"]).permute(1, 0, 2).unsqueeze(0)
+    kv = _deq16(a["kv"])
+    K = kv.expand(3, L, 576).unsqueeze(0).contiguous()
+    V = kv[:, :512].expand(3, L, 512).unsqueeze(0).contiguous()
+    ro = torch.nn.functional.scaled_dot_product_attention(q, K, V, attn_mask=band, scale=0.06)
+    assert np.allclose(out, ro[0].permute(1, 0, 2).numpy(), rtol=1e-10, atol=1e-12)
+    # a window as long as the context is the dense causal attention
+    full = oracle.window_indices(T, q0, L)
+    fo, fl = oracle.sparse_mla(a["q"], a["kv"], full, 0.06)
+    do, dl = oracle.dense_mla(a["q"], a["kv"], q0, 0.06)
+    assert np.allclose(fo, do, rtol=1e-12, atol=1e-13) and np.allclose(fl, dl, rtol=1e-12)
+
+
+def test_local_selected_is_the_sorted_union():
+    rng = np.random.default_rng(9)
+    T, k, W, q0 = 40, 6, 5, 20
+    sel = np.full((T, k), -1, np.int32)
+    for t in range(T):
+        p = q0 + t
+        m = int(rng.integers(0, k + 1))
+        sel[t, :m] = np.sort(rng.choice(p + 1, size=m, replace=False))
+    sel[3, 1] = -1                                    # a hole among the valid entries
+    out = oracle.local_selected(sel, q0, W)
+    assert out.shape == (T, W + k)
+    for t in range(T):
+        p = q0 + t
+        win = torch.arange(max(0, p - W + 1), p + 1).numpy()
+        want = np.union1d(win, sel[t][sel[t] >= 0])
+        got = out[t]
+        assert np.array_equal(got[:len(want)], want) and np.all(got[len(want):] == -1)
+    # a window covering every visible position absorbs any selection
+    wide = oracle.local_selected(sel, q0, q0 + T)
+    for t in range(T):
+        assert np.array_equal(wide[t][:q0 + t + 1], np.arange(q0 + t + 1))
