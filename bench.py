@@ -71,6 +71,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-window", action="store_true",
+                    help="skip timing sliding-window attention through the sparse MLA")
     ap.add_argument("--no-input-prep", action="store_true",
                     help="skip timing the fp8 quantisation of the indexer inputs")
     ap.add_argument("--no-prefill", action="store_true",
@@ -222,6 +224,9 @@ def main():
     # ---- decode
     decode = None if args.no_decode else run_decode(args, WORKLOADS[args.decode_workload], dev)
 
+    # ---- sliding-window attention through the same sparse MLA (an alternative index rule)
+    window = None if args.no_window else run_window(args, cfg, inp, out, lse, chunk, dev)
+
     # ---- fp8 preparation of the same workload's indexer inputs (outside the step)
     prep = None if args.no_input_prep else run_input_prep(args, cfg, dev)
 
@@ -250,6 +255,7 @@ def main():
         "kernels": kern,
         "decode": decode,
         "input_prep": prep,
+        "window_attention": window,
         "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)
@@ -318,6 +324,45 @@ def run_decode(args, dcfg, dev):
                 roofline=dict(bound="hbm", achieved=round(gbs, 1), peak=HBM_PEAK_GBS,
                               unit="GB/s", frac=round(gbs / HBM_PEAK_GBS, 4),
                               algorithmic_bytes=int(hbm)))
+
+
+def run_window(args, cfg, inp, out, lse, chunk, dev, W=2048):
+    """Time sliding-window attention (window W = k) over the workload's query rows: per chunk
+    of `chunk` rows, the window index lists (dsa_window_indices) and dsa_sparse_mla on them.
+    The same flops per selected row as the DSA path; the gathered rows are contiguous."""
+    import torch
+
+    import sparse_attention_05_amd as dsa
+
+    L, T, H = cfg.L, cfg.rows, cfg.H
+    idx = torch.empty((chunk, W), dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def run():
+        for r0 in range(0, T, chunk):
+            r1 = min(T, r0 + chunk)
+            ic = idx[:r1 - r0]
+            dsa.dsa_window_indices(r1 - r0, L, cfg.q_pos0 + r0, W, idx=ic)
+            dsa.dsa_sparse_mla(inp["q"][r0:r1], inp["kv"], ic, cfg.sm_scale, out=out[r0:r1],
+                               lse=lse[r0:r1])
+
+    run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 2
+    e0.record(stream)
+    for _ in range(reps):
+        run()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    sel = sum(min(cfg.q_pos0 + t + 1, W) for t in range(T))
+    tflops = sel * 2.0 * H * (D_QK + D_V) / (ms / 1e3) / 1e12
+    log("window attention W=%d: %.2f ms, %.0f TFLOP/s" % (W, ms, tflops))
+    return dict(workload="%s, window %d" % (cfg.name, W), ms=round(ms, 3),
+                tokens_per_s=round(T / (ms / 1e3), 1), selected_rows=int(sel),
+                roofline=dict(bound="mfma", achieved=round(tflops, 2), peak=PEAK["bf16"],
+                              unit="TFLOP/s", frac=round(tflops / PEAK["bf16"], 4)))
 
 
 def run_input_prep(args, cfg, dev):

@@ -9,6 +9,8 @@
  *                   k = 2048 and select-all for short contexts, 步骤四 sparse MLA).
  *   [devpress-dsa]  《狂降75%！大模型DeepSeek-V3.2 API杀疯了…》 (devpress.csdn.net):
  *                   §三 第二步–第四步 (the same four steps).
+ *   [oilbeater-dsa] oilbeater.com "DeepSeek Sparse Attention": section Sparse Attention
+ *                   (sliding windows, local windows joined by global tokens).
  *   [gxzdkb-dsa]    gxzdkb.com DSA explainer: 秘密武器：DSA (fp8 indexer, ReLU),
  *                   原始 Attention 的计算逻辑 (decode appends to the cache first).
  *
@@ -58,7 +60,8 @@ typedef enum {
 /* Static, human-readable name of a status code. */
 const char* dsa_status_string(dsa_status_t status);
 
-/* ABI version: major * 100 + minor (1.01: dsa_quantize_fp8, dsa_decode_append). */
+/* ABI version: major * 100 + minor (1.02: + dsa_quantize_fp8, dsa_decode_append, dsa_window_indices,
+ * dsa_local_selected_indices). */
 int dsa_version(void);
 
 /* Lightning-indexer scores ([csdn-workflow] §4 步骤二, [devpress-dsa] §三 第二步):
@@ -156,6 +159,19 @@ dsa_status_t dsa_quantize_fp8(const void* x, int x_is_bf16, int64_t n, uint8_t* 
 dsa_status_t dsa_decode_append(int B, const int64_t* seq_start, const void* k_new, int k_is_bf16,
                                const uint16_t* kv_new, uint8_t* k8_cache, float* k_scale_cache,
                                uint16_t* kv_cache, dsa_stream_t stream);
+
+/* Alternative index rules that feed dsa_sparse_mla ([gxzdkb-dsa] 秘密武器：DSA: DSA
+ * generalises sliding-window attention; [oilbeater-dsa] Sparse Attention: a local window,
+ * alone or joined by globally chosen tokens).  Row t sits at p = q_pos0 + t (q_pos0 + T <= L).
+ * dsa_window_indices: idx [T, window] = max(0, p-window+1) .. p ascending, then -1.
+ * dsa_local_selected_indices: out [T, window + k] = the ascending union of that window and
+ *   the valid entries of sel [T, k] (positions 0 <= s <= p, in ascending order as dsa_topk
+ *   writes them; -1 entries anywhere are skipped), then -1.
+ * Either list is the idx argument of dsa_sparse_mla with k = its width. */
+dsa_status_t dsa_window_indices(int T, int L, int q_pos0, int window, int32_t* idx,
+                                dsa_stream_t stream);
+dsa_status_t dsa_local_selected_indices(const int32_t* sel, int T, int L, int q_pos0, int k,
+                                        int window, int32_t* out, dsa_stream_t stream);
 
 #ifdef __cplusplus
 }

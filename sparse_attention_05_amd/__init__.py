@@ -29,7 +29,8 @@ DSA_ERR_WORKSPACE_TOO_SMALL, DSA_ERR_HIP = 3, 4
 EXPORTS = ("dsa_status_string", "dsa_version", "dsa_index_scores", "dsa_topk",
            "dsa_topk_workspace_bytes", "dsa_sparse_mla", "dsa_prefill",
            "dsa_prefill_workspace_bytes", "dsa_prefill_chunk_rows", "dsa_decode",
-           "dsa_decode_workspace_bytes", "dsa_quantize_fp8", "dsa_decode_append")
+           "dsa_decode_workspace_bytes", "dsa_quantize_fp8", "dsa_decode_append",
+           "dsa_window_indices", "dsa_local_selected_indices")
 
 
 class DSAError(RuntimeError):
@@ -68,8 +69,11 @@ def load(path: str = LIB_PATH):
             lib.dsa_decode_workspace_bytes.argtypes = [i32, i32, i64, i32, i32, i32]
             lib.dsa_quantize_fp8.argtypes = [P, i32, i64, P, P, P]
             lib.dsa_decode_append.argtypes = [i32, P, P, i32, P, P, P, P, P]
+            lib.dsa_window_indices.argtypes = [i32, i32, i32, i32, P, P]
+            lib.dsa_local_selected_indices.argtypes = [P, i32, i32, i32, i32, i32, P, P]
             for fn in ("dsa_index_scores", "dsa_topk", "dsa_sparse_mla", "dsa_prefill",
-                       "dsa_decode", "dsa_quantize_fp8", "dsa_decode_append"):
+                       "dsa_decode", "dsa_quantize_fp8", "dsa_decode_append",
+                       "dsa_window_indices", "dsa_local_selected_indices"):
                 getattr(lib, fn).restype = i32
             _lib = lib
     return _lib
@@ -290,3 +294,28 @@ def dsa_decode_append(seq_start, k_new, kv_new, k8_cache, k_scale_cache, kv_cach
                                  _ptr(k8_cache), _ptr(k_scale_cache), _ptr(kv_cache),
                                  _stream()), "dsa_decode_append")
     return k8_cache, k_scale_cache, kv_cache
+
+
+def dsa_window_indices(T: int, L: int, q_pos0: int, window: int, idx=None, device="cuda"):
+    """Sliding-window index lists int32 [T, window]: max(0, p-window+1) .. p, -1 padded."""
+    lib = load()
+    if idx is None:
+        idx = torch.empty((T, window), dtype=torch.int32, device=device)
+    _req(idx, torch.int32, (T, window), "idx")
+    _check(lib.dsa_window_indices(T, L, q_pos0, window, _ptr(idx), _stream()),
+           "dsa_window_indices")
+    return idx
+
+
+def dsa_local_selected_indices(sel, L: int, q_pos0: int, window: int, out=None):
+    """Ascending union of each row's window and its selected positions sel [T, k] (ascending,
+    as dsa_topk writes them): int32 [T, window + k], -1 padded."""
+    lib = load()
+    T, k = sel.shape
+    _req(sel, torch.int32, (T, k), "sel")
+    if out is None:
+        out = torch.empty((T, window + k), dtype=torch.int32, device=sel.device)
+    _req(out, torch.int32, (T, window + k), "out")
+    _check(lib.dsa_local_selected_indices(_ptr(sel), T, L, q_pos0, k, window, _ptr(out),
+                                          _stream()), "dsa_local_selected_indices")
+    return out

@@ -99,7 +99,7 @@ const char* dsa_status_string(dsa_status_t status)
     return "DSA_ERR_UNKNOWN";
 }
 
-int dsa_version(void) { return 101; }
+int dsa_version(void) { return 102; }
 
 dsa_status_t dsa_index_scores(const uint8_t* q8, const float* q_scale, const float* w,
                               const uint8_t* k8, const float* k_scale, int T, int L, int H_I,
@@ -297,6 +297,29 @@ dsa_status_t dsa_decode_append(int B, const int64_t* seq_start, const void* k_ne
     return from_hip(dsa::launch_decode_append(B, seq_start, k_new, k_is_bf16 != 0, kv_new,
                                               k8_cache, k_scale_cache, kv_cache,
                                               as_hip(stream)));
+}
+
+dsa_status_t dsa_window_indices(int T, int L, int q_pos0, int window, int32_t* idx,
+                                dsa_stream_t stream)
+{
+    if (check_rows(T, L, q_pos0) != DSA_OK || window < 1) return DSA_ERR_INVALID_ARGUMENT;
+    if (T == 0) return DSA_OK;
+    if (!idx) return DSA_ERR_INVALID_ARGUMENT;
+    if ((int64_t)T * window > kMaxElems) return DSA_ERR_UNSUPPORTED;
+    return from_hip(dsa::launch_window_indices(T, q_pos0, window, idx, as_hip(stream)));
+}
+
+dsa_status_t dsa_local_selected_indices(const int32_t* sel, int T, int L, int q_pos0, int k,
+                                        int window, int32_t* out, dsa_stream_t stream)
+{
+    if (check_rows(T, L, q_pos0) != DSA_OK || window < 1 || k < 1)
+        return DSA_ERR_INVALID_ARGUMENT;
+    if (T == 0) return DSA_OK;
+    if (!sel || !out) return DSA_ERR_INVALID_ARGUMENT;
+    if ((int64_t)window + k > (int64_t(1) << 30) ||
+        (int64_t)T * (window + k) > kMaxElems)
+        return DSA_ERR_UNSUPPORTED;
+    return from_hip(dsa::launch_local_selected(sel, T, k, q_pos0, window, out, as_hip(stream)));
 }
 
 }  // extern "C"

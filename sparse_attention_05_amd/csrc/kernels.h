@@ -60,4 +60,11 @@ hipError_t launch_decode_append(int B, const int64_t* seq_start, const void* k_n
                                 const uint16_t* kv_new, uint8_t* k8_cache, float* ks_cache,
                                 uint16_t* kv_cache, hipStream_t stream);
 
+// ---- alternative index rules ----------------------------------------------------------
+// window: idx [T, W], row t = max(0, p-W+1) .. p (p = q_pos0 + t), -1 padded.
+hipError_t launch_window_indices(int T, int q_pos0, int W, int32_t* idx, hipStream_t stream);
+// local + selected: out [T, W + k] = ascending union of the window and sel [T, k].
+hipError_t launch_local_selected(const int32_t* sel, int T, int k, int q_pos0, int W,
+                                 int32_t* out, hipStream_t stream);
+
 }  // namespace dsa

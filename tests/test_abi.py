@@ -35,7 +35,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_status_strings_and_version(lib):
-    assert lib.dsa_version() == 101
+    assert lib.dsa_version() == 102
     for code, name in [(0, b"DSA_OK"), (1, b"DSA_ERR_INVALID_ARGUMENT"),
                        (2, b"DSA_ERR_UNSUPPORTED"), (3, b"DSA_ERR_WORKSPACE_TOO_SMALL"),
                        (4, b"DSA_ERR_HIP")]:
@@ -139,3 +139,16 @@ def test_quantize_and_append_validation(lib):
              NULL) == dsa.DSA_ERR_INVALID_ARGUMENT
     assert a(70000, FAKE, FAKE, 0, FAKE, FAKE, FAKE, FAKE, NULL) == dsa.DSA_ERR_UNSUPPORTED
     assert a(0, NULL, NULL, 0, NULL, NULL, NULL, NULL, NULL) == dsa.DSA_OK
+
+
+def test_index_rule_validation(lib):
+    w = lib.dsa_window_indices
+    assert w(4, 8, 5, 3, FAKE, NULL) == dsa.DSA_ERR_INVALID_ARGUMENT       # q_pos0 + T > L
+    assert w(4, 8, 0, 0, FAKE, NULL) == dsa.DSA_ERR_INVALID_ARGUMENT       # window < 1
+    assert w(4, 8, 0, 3, NULL, NULL) == dsa.DSA_ERR_INVALID_ARGUMENT
+    assert w(0, 8, 0, 3, NULL, NULL) == dsa.DSA_OK
+    u = lib.dsa_local_selected_indices
+    assert u(FAKE, 4, 8, 0, 0, 3, FAKE, NULL) == dsa.DSA_ERR_INVALID_ARGUMENT  # k < 1
+    assert u(NULL, 4, 8, 0, 2, 3, FAKE, NULL) == dsa.DSA_ERR_INVALID_ARGUMENT
+    assert u(FAKE, 4, 8, 0, 2, (1 << 30), FAKE, NULL) == dsa.DSA_ERR_UNSUPPORTED
+    assert u(NULL, 0, 8, 0, 2, 3, NULL, NULL) == dsa.DSA_OK
