@@ -211,6 +211,35 @@ def prefill(inp: dict, rows=None, with_bound=False):
     return dict(rows=r, scores=scores, bound=bound, n_vis=n_vis, idx=idx, out=out, lse=lse)
 
 
+def prefill_varlen(inp: dict, seqs=None, with_bound=False):
+    """Packed prefill of B sequences on host arrays (see synth.make_varlen): sequence b owns
+    query rows [cu_q[b], cu_q[b+1]) and key rows [cu_k[b], cu_k[b+1]); its T_b queries are
+    its last T_b tokens, so row t of it sits at position L_b - T_b + t and sees that
+    sequence's tokens 0 .. L_b - T_b + t only.  Each sequence is one prefill call on its own
+    slices; returns one prefill() result per requested sequence (indices are positions within
+    the sequence)."""
+    cu_q = np.asarray(inp["cu_q"], np.int64)
+    cu_k = np.asarray(inp["cu_k"], np.int64)
+    seqs = range(len(cu_q) - 1) if seqs is None else seqs
+    res = []
+    for b in seqs:
+        qa, qe, ka, ke = int(cu_q[b]), int(cu_q[b + 1]), int(cu_k[b]), int(cu_k[b + 1])
+        T, L = qe - qa, ke - ka
+        if T == 0:
+            res.append(None)
+            continue
+        one = dict(T=T, L=L, k=inp["k"], q_pos0=L - T, score_scale=inp["score_scale"],
+                   sm_scale=inp["sm_scale"])
+        for key in ("q8", "qs", "w", "q"):
+            one[key] = inp[key][qa:qe]
+        for key in ("k8", "ks", "kv"):
+            one[key] = inp[key][ka:ke]
+        r = prefill(one, with_bound=with_bound)
+        r.update(seq=int(b), T=T, L=L, q_pos0=L - T)
+        res.append(r)
+    return res
+
+
 def decode(inp: dict, seqs=None, with_bound=False):
     """Decode step on host arrays: sequence b owns cache rows [seq_start[b], seq_start[b+1])
     and its one query sits at position L_b - 1 (it sees its whole cache, itself included)."""

@@ -8,9 +8,12 @@ and the CPU oracle consume the bytes it produces.
 from .gen import (  # noqa: F401
     PrefillCfg,
     DecodeCfg,
+    VarlenCfg,
     WORKLOADS,
     make_prefill,
     make_decode,
+    make_varlen,
+    make_varlen_cfg,
     quantize_e4m3_rows,
     host_arrays,
 )

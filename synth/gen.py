@@ -74,6 +74,44 @@ class DecodeCfg:
         return replace(self, **kw)
 
 
+@dataclass(frozen=True)
+class VarlenCfg:
+    """A packed batch of B sequences.  Sequence b holds L_b tokens (uniform in
+    [len_lo, len_hi]); its query rows are its last T_b tokens.  Even-numbered sequences are
+    fresh prefills (T_b = L_b); odd-numbered ones prefill a chunk of T_b tokens (uniform in
+    [chunk_lo, min(chunk_hi, L_b)]) against the cache of their first L_b - T_b tokens."""
+    name: str
+    B: int
+    len_lo: int
+    len_hi: int
+    chunk_lo: int
+    chunk_hi: int
+    k: int
+    H_I: int
+    H: int
+    w_std: float
+    seed: int
+    planted_frac: float = 0.0
+    score_scale: float = D_I ** -0.5
+    sm_scale: float = D_QK ** -0.5
+
+    def lengths(self):
+        """(T_b, L_b) lists drawn from a CPU generator (host-side sizes)."""
+        g = torch.Generator()
+        g.manual_seed(self.seed)
+        L = torch.randint(self.len_lo, self.len_hi + 1, (self.B,), generator=g).tolist()
+        u = torch.rand((self.B,), generator=g, dtype=torch.float64).tolist()
+        T = []
+        for b in range(self.B):
+            if b % 2 == 0:
+                T.append(L[b])
+            else:
+                hi = min(self.chunk_hi, L[b])
+                lo = min(self.chunk_lo, hi)
+                T.append(lo + min(hi - lo, int(u[b] * (hi - lo + 1))))
+        return T, L
+
+
 WORKLOADS = {
     # small prefill, few heads: the case the oracle finishes in seconds
     "prefill-L1024-k256": PrefillCfg("prefill-L1024-k256", L=1024, k=256, H_I=4, H=8,
@@ -88,6 +126,13 @@ WORKLOADS = {
     "decode-B64-L4096-131072-k2048": DecodeCfg("decode-B64-L4096-131072-k2048", B=64,
                                                len_lo=4096, len_hi=131072, k=2048, H_I=64,
                                                H=128, w_std=1 / 8, seed=1005),
+    # a packed serving batch: 16 sequences of 1K..32K tokens, every other one a chunk of
+    # 512..8192 new tokens against its cached prefix (shapes and value distributions of the
+    # 32K prefill workload)
+    "varlen-B16-L1024-32768-k2048": VarlenCfg("varlen-B16-L1024-32768-k2048", B=16,
+                                              len_lo=1024, len_hi=32768, chunk_lo=512,
+                                              chunk_hi=8192, k=2048, H_I=64, H=128,
+                                              w_std=1 / 8, seed=1006, planted_frac=0.01),
 }
 
 
@@ -152,6 +197,53 @@ def make_prefill(cfg: PrefillCfg, device="cpu", seed: Optional[int] = None) -> d
                 score_scale=cfg.score_scale, sm_scale=cfg.sm_scale,
                 q8=q8.contiguous(), qs=qs.contiguous(), w=w.contiguous(),
                 k8=k8.contiguous(), ks=ks.contiguous(), q=q, kv=kv, planted=planted)
+
+
+def make_varlen(lens_q, lens_k, k: int, H_I: int, H: int, w_std: float, seed: int,
+                planted_frac: float = 0.0, device="cpu", name="varlen") -> dict:
+    """Packed inputs of B sequences: sequence b contributes T_b = lens_q[b] query rows (its
+    last T_b tokens, at positions L_b - T_b ..) and L_b = lens_k[b] cached tokens.  Queries
+    are packed along rows by cu_seqlens_q, keys by cu_seqlens_k (host int64 [B + 1]).  Each
+    sequence is drawn as its own prefill workload with seed (seed, b)."""
+    device = torch.device(device)
+    B = len(lens_k)
+    assert len(lens_q) == B and all(0 <= t <= l for t, l in zip(lens_q, lens_k))
+    cu_q = torch.zeros(B + 1, dtype=torch.int64)
+    cu_k = torch.zeros(B + 1, dtype=torch.int64)
+    cu_q[1:] = torch.cumsum(torch.tensor(lens_q, dtype=torch.int64), 0)
+    cu_k[1:] = torch.cumsum(torch.tensor(lens_k, dtype=torch.int64), 0)
+    Tq, Lk = int(cu_q[-1]), int(cu_k[-1])
+    out = dict(q8=torch.empty((Tq, H_I, D_I), dtype=torch.uint8, device=device),
+               qs=torch.empty((Tq, H_I), dtype=torch.float32, device=device),
+               w=torch.empty((Tq, H_I), dtype=torch.float32, device=device),
+               q=torch.empty((Tq, H, D_QK), dtype=torch.bfloat16, device=device),
+               k8=torch.empty((Lk, D_I), dtype=torch.uint8, device=device),
+               ks=torch.empty((Lk,), dtype=torch.float32, device=device),
+               kv=torch.empty((Lk, D_QK), dtype=torch.bfloat16, device=device))
+    for b in range(B):
+        if lens_k[b] == 0:
+            continue
+        cfg = PrefillCfg("%s-seq%d" % (name, b), L=lens_k[b], k=k, H_I=H_I, H=H, w_std=w_std,
+                         seed=seed * 1009 + b, planted_frac=planted_frac, T=lens_q[b],
+                         q_pos0=lens_k[b] - lens_q[b])
+        one = make_prefill(cfg, device)
+        qa, qe, ka, ke = int(cu_q[b]), int(cu_q[b + 1]), int(cu_k[b]), int(cu_k[b + 1])
+        for key in ("q8", "qs", "w", "q"):
+            out[key][qa:qe] = one[key]
+        for key in ("k8", "ks", "kv"):
+            out[key][ka:ke] = one[key]
+        del one
+    return dict(kind="varlen", B=B, Tq=Tq, Lk=Lk, H_I=H_I, H=H, k=k,
+                lens_q=list(lens_q), lens_k=list(lens_k), cu_q=cu_q, cu_k=cu_k,
+                score_scale=D_I ** -0.5, sm_scale=D_QK ** -0.5, **out)
+
+
+def make_varlen_cfg(cfg: VarlenCfg, device="cpu") -> dict:
+    T, L = cfg.lengths()
+    d = make_varlen(T, L, cfg.k, cfg.H_I, cfg.H, cfg.w_std, cfg.seed, cfg.planted_frac,
+                    device, cfg.name)
+    d.update(cfg=cfg, score_scale=cfg.score_scale, sm_scale=cfg.sm_scale)
+    return d
 
 
 def make_decode(cfg: DecodeCfg, device="cpu", seed: Optional[int] = None) -> dict:

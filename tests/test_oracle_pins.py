@@ -465,3 +465,101 @@ def test_local_selected_is_the_sorted_union():
     wide = oracle.local_selected(sel, q0, q0 + T)
     for t in range(T):
         assert np.array_equal(wide[t][:q0 + t + 1], np.arange(q0 + t + 1))
+
+
+# ------------------------------------------------------------------ packed (varlen) prefill
+
+def _pack_full(seqs, lens_q, k):
+    """A packed batch built from whole-sequence prefill inputs: sequence b keeps all its keys
+    and its last lens_q[b] query rows."""
+    cu_q = np.concatenate([[0], np.cumsum(lens_q)]).astype(np.int64)
+    cu_k = np.concatenate([[0], np.cumsum([s["L"] for s in seqs])]).astype(np.int64)
+    pk = dict(k=k, cu_q=cu_q, cu_k=cu_k, score_scale=seqs[0]["score_scale"],
+              sm_scale=seqs[0]["sm_scale"])
+    for key in ("q8", "qs", "w", "q"):
+        pk[key] = np.concatenate([s[key][s["T"] - t:] for s, t in zip(seqs, lens_q)])
+    for key in ("k8", "ks", "kv"):
+        pk[key] = np.concatenate([s[key] for s in seqs])
+    return pk
+
+
+def _full_seqs(lens_k, k, H_I, H, seed):
+    return [host_arrays(make_prefill(PrefillCfg("t", L=L, k=k, H_I=H_I, H=H, w_std=0.5,
+                                                seed=seed + b)))
+            for b, L in enumerate(lens_k)]
+
+
+def test_varlen_dense_equals_block_diagonal_sdpa():
+    """Every sequence shorter than k: the packed batch is one attention over all packed
+    tokens under a block-diagonal causal mask (query of sequence b at position
+    L_b - T_b + t sees keys of sequence b at positions <= that), computed by torch."""
+    lens_k, lens_q, k = [5, 3, 20, 7, 9], [5, 0, 12, 7, 1], 32
+    pk = _pack_full(_full_seqs(lens_k, k, 4, 2, seed=70), lens_q, k)
+    res = oracle.prefill_varlen(pk)
+    assert res[1] is None
+    for r in res:
+        if r is not None:
+            for t in range(r["T"]):
+                n = r["q_pos0"] + t + 1
+                assert r["idx"][t].tolist() == list(range(n)) + [-1] * (k - n)
+    out = np.concatenate([r["out"] for r in res if r is not None])
+    lse = np.concatenate([r["lse"] for r in res if r is not None])
+    seq_q = np.repeat(np.arange(5), lens_q)
+    pos_q = np.concatenate([np.arange(L - T, L) for T, L in zip(lens_q, lens_k)])
+    seq_k = np.repeat(np.arange(5), lens_k)
+    pos_k = np.concatenate([np.arange(L) for L in lens_k])
+    mask = (seq_q[:, None] == seq_k[None, :]) & (pos_k[None, :] <= pos_q[:, None])
+    q = _deq16(pk["q"]).permute(1, 0, 2).unsqueeze(0)
+    kv = _deq16(pk["kv"])
+    H, N = q.shape[1], kv.shape[0]
+    K = kv.expand(H, N, 576).unsqueeze(0).contiguous()
+    V = kv[:, :512].expand(H, N, 512).unsqueeze(0).contiguous()
+    m = torch.from_numpy(mask)
+    ro = torch.nn.functional.scaled_dot_product_attention(q, K, V, attn_mask=m,
+                                                          scale=pk["sm_scale"])
+    rl = torch.logsumexp((q @ K.transpose(-1, -2) * pk["sm_scale"]).masked_fill(~m, -math.inf),
+                         dim=-1)
+    assert np.allclose(out, ro[0].permute(1, 0, 2).numpy(), rtol=1e-10, atol=1e-12)
+    assert np.allclose(lse, rl[0].permute(1, 0).numpy(), rtol=1e-12, atol=1e-12)
+
+
+def test_varlen_chunk_rows_equal_rows_of_the_whole_sequence_prefill():
+    """Causality: a chunk of T_b new tokens prefilled against the cache of the first
+    L_b - T_b tokens gives exactly the last T_b rows of prefilling the whole sequence
+    (selection included, with k well below L_b)."""
+    lens_k, lens_q, k = [30, 40, 6, 25, 64], [30, 11, 0, 1, 33], 8
+    seqs = _full_seqs(lens_k, k, 4, 3, seed=80)
+    res = oracle.prefill_varlen(_pack_full(seqs, lens_q, k))
+    for b, (s, T) in enumerate(zip(seqs, lens_q)):
+        if T == 0:
+            assert res[b] is None
+            continue
+        full = oracle.prefill(s)
+        L = s["L"]
+        assert np.array_equal(res[b]["idx"], full["idx"][L - T:])
+        assert np.array_equal(res[b]["n_vis"], full["n_vis"][L - T:])
+        assert np.allclose(res[b]["scores"], full["scores"][L - T:], rtol=0, atol=0)
+        assert np.allclose(res[b]["out"], full["out"][L - T:], rtol=1e-14, atol=1e-15)
+        assert np.allclose(res[b]["lse"], full["lse"][L - T:], rtol=1e-14, atol=1e-15)
+
+
+def test_varlen_sequences_are_isolated_and_order_free():
+    """Reordering the sequences, or changing one sequence's keys, leaves every other
+    sequence's result unchanged."""
+    lens_k, lens_q, k = [26, 50, 19], [26, 20, 7], 6
+    seqs = _full_seqs(lens_k, k, 2, 2, seed=90)
+    base = oracle.prefill_varlen(_pack_full(seqs, lens_q, k))
+    order = [2, 0, 1]
+    perm = oracle.prefill_varlen(_pack_full([seqs[i] for i in order],
+                                            [lens_q[i] for i in order], k))
+    for j, i in enumerate(order):
+        for key in ("idx", "out", "lse"):
+            assert np.array_equal(perm[j][key], base[i][key])
+    changed = [dict(s) for s in seqs]
+    changed[1]["kv"] = changed[1]["kv"][::-1].copy()
+    changed[1]["k8"] = changed[1]["k8"][::-1].copy()
+    alt = oracle.prefill_varlen(_pack_full(changed, lens_q, k))
+    assert not np.array_equal(alt[1]["out"], base[1]["out"])
+    for i in (0, 2):
+        for key in ("idx", "out", "lse"):
+            assert np.array_equal(alt[i][key], base[i][key])

@@ -61,3 +61,23 @@ def test_decode_lengths_and_packing():
     assert np.all((lens >= 10) & (lens <= 50))
     assert a["seq_start"][0] == 0 and a["seq_start"][-1] == a["N"] == a["k8"].shape[0]
     assert a["kv"].shape == (a["N"], 576) and a["q"].shape == (6, 2, 576)
+
+
+def test_varlen_lengths_and_packing():
+    from synth import WORKLOADS, make_varlen
+    cfg = WORKLOADS["varlen-B16-L1024-32768-k2048"]
+    T, L = cfg.lengths()
+    assert (T, L) == cfg.lengths() and len(T) == len(L) == cfg.B
+    for b, (t, l) in enumerate(zip(T, L)):
+        assert cfg.len_lo <= l <= cfg.len_hi
+        assert t == l if b % 2 == 0 else min(cfg.chunk_lo, l) <= t <= min(cfg.chunk_hi, l)
+    a = make_varlen([3, 0, 5], [4, 2, 5], k=4, H_I=2, H=2, w_std=0.5, seed=1)
+    b = make_varlen([3, 0, 5], [4, 2, 5], k=4, H_I=2, H=2, w_std=0.5, seed=1)
+    assert a["cu_q"].tolist() == [0, 3, 3, 8] and a["cu_k"].tolist() == [0, 4, 6, 11]
+    assert a["q8"].shape == (8, 2, 128) and a["kv"].shape == (11, 576)
+    for key in ("q8", "qs", "w", "q", "k8", "ks", "kv"):
+        assert torch.equal(a[key], b[key])
+    # each sequence is the prefill workload of its own seed: its last T_b query rows
+    one = make_prefill(PrefillCfg("varlen-seq2", L=5, k=4, H_I=2, H=2, w_std=0.5,
+                                  seed=1 * 1009 + 2, T=5))
+    assert torch.equal(a["q"][3:8], one["q"]) and torch.equal(a["kv"][6:11], one["kv"])
