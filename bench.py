@@ -75,6 +75,9 @@ def parse():
                     help="skip timing sliding-window attention through the sparse MLA")
     ap.add_argument("--no-input-prep", action="store_true",
                     help="skip timing the fp8 quantisation of the indexer inputs")
+    ap.add_argument("--varlen-workload", default="varlen-B16-L1024-32768-k2048")
+    ap.add_argument("--no-varlen", action="store_true",
+                    help="skip timing the packed multi-sequence prefill")
     ap.add_argument("--no-prefill", action="store_true",
                     help="decode only (for profiling runs; prints no prefill value)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -230,6 +233,9 @@ def main():
     # ---- fp8 preparation of the same workload's indexer inputs (outside the step)
     prep = None if args.no_input_prep else run_input_prep(args, cfg, dev)
 
+    # ---- packed multi-sequence prefill (fresh prefills and chunks against caches)
+    varlen = None if args.no_varlen else run_varlen(args, WORKLOADS[args.varlen_workload], dev)
+
     # ---- CPU oracle baseline on sampled rows of the same prefill workload
     cpu = None
     if not args.no_cpu_baseline:
@@ -256,6 +262,7 @@ def main():
         "decode": decode,
         "input_prep": prep,
         "window_attention": window,
+        "varlen_prefill": varlen,
         "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)
@@ -363,6 +370,57 @@ def run_window(args, cfg, inp, out, lse, chunk, dev, W=2048):
                 tokens_per_s=round(T / (ms / 1e3), 1), selected_rows=int(sel),
                 roofline=dict(bound="mfma", achieved=round(tflops, 2), peak=PEAK["bf16"],
                               unit="TFLOP/s", frac=round(tflops / PEAK["bf16"], 4)))
+
+
+def run_varlen(args, vcfg, dev):
+    """Time dsa_prefill_varlen on a packed batch of sequences (host cu_seqlens): every query
+    row of every sequence through indexer -> top-k -> sparse MLA, as in the main step."""
+    import torch
+
+    import sparse_attention_05_amd as dsa
+    from synth import make_varlen_cfg
+
+    log("generating", vcfg.name)
+    d = make_varlen_cfg(vcfg, device=dev)
+    Tq, H = d["Tq"], vcfg.H
+    out = torch.empty((Tq, H, D_V), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((Tq, H), dtype=torch.float32, device=dev)
+    ws = torch.empty((max(1, dsa.dsa_prefill_varlen_workspace_bytes(d["cu_q"], d["cu_k"],
+                                                                    vcfg.H_I, H, vcfg.k)),),
+                     dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def run():
+        dsa.dsa_prefill_varlen(d["cu_q"], d["cu_k"], d["q8"], d["qs"], d["w"], d["k8"],
+                               d["ks"], d["q"], d["kv"], vcfg.k, vcfg.score_scale,
+                               vcfg.sm_scale, out=out, lse=lse, workspace=ws)
+
+    run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 3
+    e0.record(stream)
+    for _ in range(reps):
+        run()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    pairs = sel = 0
+    for T, L in zip(d["lens_q"], d["lens_k"]):
+        p, s_ = prefill_units(L, T, L - T, vcfg.k, 0, T)
+        pairs += p
+        sel += s_
+    flops = pairs * 2.0 * vcfg.H_I * D_I + sel * 2.0 * H * (D_QK + D_V)
+    log("varlen prefill %s: %d query rows over %d cached tokens, %.2f ms, %.0f tokens/s"
+        % (vcfg.name, Tq, d["Lk"], ms, Tq / (ms / 1e3)))
+    res = dict(workload=vcfg.name, sequences=vcfg.B, query_rows=Tq, key_rows=d["Lk"],
+               lens_q=d["lens_q"], lens_k=d["lens_k"], ms=round(ms, 3),
+               tokens_per_s=round(Tq / (ms / 1e3), 1),
+               algorithmic_tflop=round(flops / 1e12, 3),
+               effective_tflop_s=round(flops / (ms / 1e3) / 1e12, 1))
+    del d, out, lse, ws
+    torch.cuda.empty_cache()
+    return res
 
 
 def run_input_prep(args, cfg, dev):

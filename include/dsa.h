@@ -12,7 +12,9 @@
  *   [oilbeater-dsa] oilbeater.com "DeepSeek Sparse Attention": section Sparse Attention
  *                   (sliding windows, local windows joined by global tokens).
  *   [gxzdkb-dsa]    gxzdkb.com DSA explainer: 秘密武器：DSA (fp8 indexer, ReLU),
- *                   原始 Attention 的计算逻辑 (decode appends to the cache first).
+ *                   原始 Attention 的计算逻辑 (decode appends to the cache first),
+ *                   致命问题：平方级复杂度拖垮效率 (rollout inference = prefill, which builds
+ *                   every token's cache entry and output, then decode).
  *
  * Conventions for every entry point
  *   - All tensor pointers are DEVICE pointers owned by the caller.  Tensors are row-major
@@ -61,7 +63,7 @@ typedef enum {
 const char* dsa_status_string(dsa_status_t status);
 
 /* ABI version: major * 100 + minor (1.02: + dsa_quantize_fp8, dsa_decode_append, dsa_window_indices,
- * dsa_local_selected_indices). */
+ * dsa_local_selected_indices; 1.03: + dsa_prefill_varlen, dsa_prefill_varlen_workspace_bytes). */
 int dsa_version(void);
 
 /* Lightning-indexer scores ([csdn-workflow] §4 步骤二, [devpress-dsa] §三 第二步):
@@ -114,6 +116,31 @@ size_t dsa_prefill_workspace_bytes(int T, int L, int H_I, int H, int k);
  * dsa_index_scores (write_masked = 0, rows that see more than k tokens only) ->
  * dsa_topk -> dsa_sparse_mla on that chunk.  Returns 0 for invalid sizes. */
 int dsa_prefill_chunk_rows(int T, int L);
+
+/* Prefill of a packed batch of B sequences ([gxzdkb-dsa] 致命问题：平方级复杂度拖垮效率:
+ * the prefill of many rollouts at once), fresh or continuing an existing cache.
+ * Sequence b owns query rows [cu_seqlens_q[b], cu_seqlens_q[b+1]) of q8, q_scale, w, q, out,
+ * lse and idx_out, and key rows [cu_seqlens_k[b], cu_seqlens_k[b+1]) of k8, k_scale, kv.
+ * With T_b and L_b those counts, its queries are its last T_b tokens: query row t of it sits
+ * at position L_b - T_b + t of that sequence and sees that sequence's keys 0 .. L_b - T_b + t
+ * only (T_b = L_b is a fresh prefill; T_b < L_b prefills a chunk against a cache of
+ * L_b - T_b tokens).  Each sequence is computed exactly as dsa_prefill with q_pos0 =
+ * L_b - T_b on its own rows; idx_out (nullable) holds positions within the sequence.
+ *   cu_seqlens_q, cu_seqlens_k  HOST int64 [B+1], each starting at 0, with
+ *                               0 <= T_b <= L_b for every b (they size the launches).
+ * Other tensors and sizes as dsa_prefill.  workspace: at least
+ * dsa_prefill_varlen_workspace_bytes(...) bytes (the largest sequence's prefill workspace),
+ * 256-byte aligned; shared by the sequences in turn.  B = 0 or no query rows is a no-op;
+ * malformed cu_seqlens give DSA_ERR_INVALID_ARGUMENT. */
+dsa_status_t dsa_prefill_varlen(int B, const int64_t* cu_seqlens_q, const int64_t* cu_seqlens_k,
+                                const uint8_t* q8, const float* q_scale, const float* w,
+                                const uint8_t* k8, const float* k_scale, const uint16_t* q,
+                                const uint16_t* kv, int H_I, int H, int k, float score_scale,
+                                float sm_scale, uint16_t* out, float* lse, int32_t* idx_out,
+                                void* workspace, size_t workspace_bytes, dsa_stream_t stream);
+/* 0 for malformed cu_seqlens or when no sequence has query rows. */
+size_t dsa_prefill_varlen_workspace_bytes(int B, const int64_t* cu_seqlens_q,
+                                          const int64_t* cu_seqlens_k, int H_I, int H, int k);
 
 /* One decode step for B sequences ([gxzdkb-dsa] 原始 Attention 的计算逻辑: the new token's
  * cache entries are appended before attending).  Sequence b owns the packed cache rows

@@ -30,7 +30,8 @@ EXPORTS = ("dsa_status_string", "dsa_version", "dsa_index_scores", "dsa_topk",
            "dsa_topk_workspace_bytes", "dsa_sparse_mla", "dsa_prefill",
            "dsa_prefill_workspace_bytes", "dsa_prefill_chunk_rows", "dsa_decode",
            "dsa_decode_workspace_bytes", "dsa_quantize_fp8", "dsa_decode_append",
-           "dsa_window_indices", "dsa_local_selected_indices")
+           "dsa_window_indices", "dsa_local_selected_indices", "dsa_prefill_varlen",
+           "dsa_prefill_varlen_workspace_bytes")
 
 
 class DSAError(RuntimeError):
@@ -71,9 +72,14 @@ def load(path: str = LIB_PATH):
             lib.dsa_decode_append.argtypes = [i32, P, P, i32, P, P, P, P, P]
             lib.dsa_window_indices.argtypes = [i32, i32, i32, i32, P, P]
             lib.dsa_local_selected_indices.argtypes = [P, i32, i32, i32, i32, i32, P, P]
+            lib.dsa_prefill_varlen.argtypes = [i32, P, P, P, P, P, P, P, P, P, i32, i32, i32,
+                                               f32, f32, P, P, P, P, sz, P]
+            lib.dsa_prefill_varlen_workspace_bytes.restype = sz
+            lib.dsa_prefill_varlen_workspace_bytes.argtypes = [i32, P, P, i32, i32, i32]
             for fn in ("dsa_index_scores", "dsa_topk", "dsa_sparse_mla", "dsa_prefill",
                        "dsa_decode", "dsa_quantize_fp8", "dsa_decode_append",
-                       "dsa_window_indices", "dsa_local_selected_indices"):
+                       "dsa_window_indices", "dsa_local_selected_indices", "dsa_prefill_varlen",
+           "dsa_prefill_varlen_workspace_bytes"):
                 getattr(lib, fn).restype = i32
             _lib = lib
     return _lib
@@ -212,6 +218,65 @@ def dsa_prefill(q8, q_scale, w, k8, k_scale, q, kv, k: int, q_pos0: int, score_s
                            _ptr(kv), T, L, H_I, H, k, q_pos0, score_scale, sm_scale, _ptr(out),
                            _ptr(lse), _ptr(idx_out), _ptr(workspace), workspace.numel(),
                            _stream()), "dsa_prefill")
+    return out, lse, idx_out
+
+
+def _host_cu(cu, name):
+    """cu_seqlens as a contiguous host int64 array (they size the launches)."""
+    t = torch.as_tensor(cu, dtype=torch.int64)
+    if t.is_cuda or t.dim() != 1 or t.numel() < 1:
+        raise TypeError("%s must be a host int64 vector [B+1]" % name)
+    return t.contiguous()
+
+
+def dsa_prefill_varlen_workspace_bytes(cu_seqlens_q, cu_seqlens_k, H_I: int, H: int,
+                                       k: int) -> int:
+    cq, ck = _host_cu(cu_seqlens_q, "cu_seqlens_q"), _host_cu(cu_seqlens_k, "cu_seqlens_k")
+    if cq.numel() != ck.numel():
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must have the same length")
+    return int(load().dsa_prefill_varlen_workspace_bytes(cq.numel() - 1, _ptr(cq), _ptr(ck),
+                                                         H_I, H, k))
+
+
+def dsa_prefill_varlen(cu_seqlens_q, cu_seqlens_k, q8, q_scale, w, k8, k_scale, q, kv, k: int,
+                       score_scale: float, sm_scale: float, out=None, lse=None, idx_out=None,
+                       workspace=None):
+    """Packed prefill of B sequences (host cu_seqlens [B+1]); sequence b's queries are its
+    last T_b tokens.  Returns (out [Tq,H,512], lse [Tq,H], idx_out)."""
+    lib = load()
+    cq, ck = _host_cu(cu_seqlens_q, "cu_seqlens_q"), _host_cu(cu_seqlens_k, "cu_seqlens_k")
+    if cq.numel() != ck.numel():
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must have the same length")
+    B = cq.numel() - 1
+    q8, k8 = _u8(q8), _u8(k8)
+    Tq, H_I = q8.shape[0], q8.shape[1]
+    Lk, H = k8.shape[0], q.shape[1]
+    if int(cq[-1]) != Tq or int(ck[-1]) != Lk:
+        raise ValueError("cu_seqlens must end at the packed row counts (%d, %d)" % (Tq, Lk))
+    _req(q8, torch.uint8, (Tq, H_I, 128), "q8")
+    _req(q_scale, torch.float32, (Tq, H_I), "q_scale")
+    _req(w, torch.float32, (Tq, H_I), "w")
+    _req(k8, torch.uint8, (Lk, 128), "k8")
+    _req(k_scale, torch.float32, (Lk,), "k_scale")
+    _req(q, torch.bfloat16, (Tq, H, 576), "q")
+    _req(kv, torch.bfloat16, (Lk, 576), "kv")
+    dev = q.device
+    if out is None:
+        out = torch.empty((Tq, H, 512), dtype=torch.bfloat16, device=dev)
+    if lse is None:
+        lse = torch.empty((Tq, H), dtype=torch.float32, device=dev)
+    _req(out, torch.bfloat16, (Tq, H, 512), "out")
+    _req(lse, torch.float32, (Tq, H), "lse")
+    if idx_out is not None:
+        _req(idx_out, torch.int32, (Tq, k), "idx_out")
+    need = int(lib.dsa_prefill_varlen_workspace_bytes(B, _ptr(cq), _ptr(ck), H_I, H, k))
+    if workspace is None:
+        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=dev)
+    _check(lib.dsa_prefill_varlen(B, _ptr(cq), _ptr(ck), _ptr(q8), _ptr(q_scale), _ptr(w),
+                                  _ptr(k8), _ptr(k_scale), _ptr(q), _ptr(kv), H_I, H, k,
+                                  score_scale, sm_scale, _ptr(out), _ptr(lse), _ptr(idx_out),
+                                  _ptr(workspace), workspace.numel(), _stream()),
+           "dsa_prefill_varlen")
     return out, lse, idx_out
 
 

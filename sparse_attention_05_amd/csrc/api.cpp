@@ -99,7 +99,7 @@ const char* dsa_status_string(dsa_status_t status)
     return "DSA_ERR_UNKNOWN";
 }
 
-int dsa_version(void) { return 102; }
+int dsa_version(void) { return 103; }
 
 dsa_status_t dsa_index_scores(const uint8_t* q8, const float* q_scale, const float* w,
                               const uint8_t* k8, const float* k_scale, int T, int L, int H_I,
@@ -167,29 +167,15 @@ size_t dsa_prefill_workspace_bytes(int T, int L, int H_I, int H, int k)
     return prefill_ws(T, L, k).total;
 }
 
-dsa_status_t dsa_prefill(const uint8_t* q8, const float* q_scale, const float* w,
+// One prefill call after validation: query chunks of ws.chunk rows, each indexer (rows that
+// see more than k tokens) -> top-k -> sparse MLA.  Pointers are at the call's first row / key.
+static dsa_status_t prefill_run(const uint8_t* q8, const float* q_scale, const float* w,
                          const uint8_t* k8, const float* k_scale, const uint16_t* q,
-                         const uint16_t* kv, int T, int L, int H_I, int H, int k, int q_pos0,
-                         float score_scale, float sm_scale, uint16_t* out, float* lse,
-                         int32_t* idx_out, void* workspace, size_t workspace_bytes,
-                         dsa_stream_t stream)
+                                const uint16_t* kv, int T, int L, int H_I, int H, int k,
+                                int q_pos0, float score_scale, float sm_scale, uint16_t* out,
+                                float* lse, int32_t* idx_out, void* workspace, hipStream_t s)
 {
-    if (dsa_status_t st = check_rows(T, L, q_pos0)) return st;
-    if (T > 0 && (!q8 || !q_scale || !w || !k8 || !k_scale || !q || !kv || !out))
-        return DSA_ERR_INVALID_ARGUMENT;
-    if (k < 1 || H < 1) return DSA_ERR_INVALID_ARGUMENT;
-    if (!(score_scale > 0.f) || !(sm_scale > 0.f)) return DSA_ERR_INVALID_ARGUMENT;
-    if (!dsa::indexer_supports(H_I) || !heads_ok(H) || !k_ok(k)) return DSA_ERR_UNSUPPORTED;
-    if ((int64_t)T * std::max(L, k) > kMaxElems) return DSA_ERR_UNSUPPORTED;
-    if (!aligned(q8, 16) || !aligned(k8, 16) || !aligned(q, 16) || !aligned(kv, 16) ||
-        !aligned(out, 4))
-        return DSA_ERR_INVALID_ARGUMENT;
-    if (T == 0) return DSA_OK;
     const PrefillWs ws = prefill_ws(T, L, k);
-    if (!workspace || workspace_bytes < ws.total) return DSA_ERR_WORKSPACE_TOO_SMALL;
-    if (!aligned(workspace, kAlign)) return DSA_ERR_INVALID_ARGUMENT;
-
-    hipStream_t s = as_hip(stream);
     uint8_t* base = static_cast<uint8_t*>(workspace);
     float* scores = reinterpret_cast<float*>(base + ws.scores_off);
     int32_t* idx_ws = reinterpret_cast<int32_t*>(base + ws.idx_off);
@@ -215,6 +201,95 @@ dsa_status_t dsa_prefill(const uint8_t* q8, const float* q_scale, const float* w
                                        lse ? lse + (int64_t)r0 * H : nullptr, nullptr, nullptr,
                                        s);
         if (e != hipSuccess) return DSA_ERR_HIP;
+    }
+    return DSA_OK;
+}
+
+dsa_status_t dsa_prefill(const uint8_t* q8, const float* q_scale, const float* w,
+                         const uint8_t* k8, const float* k_scale, const uint16_t* q,
+                         const uint16_t* kv, int T, int L, int H_I, int H, int k, int q_pos0,
+                         float score_scale, float sm_scale, uint16_t* out, float* lse,
+                         int32_t* idx_out, void* workspace, size_t workspace_bytes,
+                         dsa_stream_t stream)
+{
+    if (dsa_status_t st = check_rows(T, L, q_pos0)) return st;
+    if (T > 0 && (!q8 || !q_scale || !w || !k8 || !k_scale || !q || !kv || !out))
+        return DSA_ERR_INVALID_ARGUMENT;
+    if (k < 1 || H < 1) return DSA_ERR_INVALID_ARGUMENT;
+    if (!(score_scale > 0.f) || !(sm_scale > 0.f)) return DSA_ERR_INVALID_ARGUMENT;
+    if (!dsa::indexer_supports(H_I) || !heads_ok(H) || !k_ok(k)) return DSA_ERR_UNSUPPORTED;
+    if ((int64_t)T * std::max(L, k) > kMaxElems) return DSA_ERR_UNSUPPORTED;
+    if (!aligned(q8, 16) || !aligned(k8, 16) || !aligned(q, 16) || !aligned(kv, 16) ||
+        !aligned(out, 4))
+        return DSA_ERR_INVALID_ARGUMENT;
+    if (T == 0) return DSA_OK;
+    if (!workspace || workspace_bytes < prefill_ws(T, L, k).total) return DSA_ERR_WORKSPACE_TOO_SMALL;
+    if (!aligned(workspace, kAlign)) return DSA_ERR_INVALID_ARGUMENT;
+
+    return prefill_run(q8, q_scale, w, k8, k_scale, q, kv, T, L, H_I, H, k, q_pos0, score_scale,
+                       sm_scale, out, lse, idx_out, workspace, as_hip(stream));
+}
+
+// Validates a packed batch (cu_q[0] = cu_k[0] = 0, 0 <= T_b <= L_b, sizes within the
+// single-call limits) and returns the largest per-sequence prefill workspace, or -1.
+static int64_t varlen_ws(int B, const int64_t* cu_q, const int64_t* cu_k, int k)
+{
+    if (B < 0 || k < 1) return -1;
+    if (B == 0) return 0;
+    if (!cu_q || !cu_k || cu_q[0] != 0 || cu_k[0] != 0) return -1;
+    size_t need = 0;
+    for (int b = 0; b < B; ++b) {
+        const int64_t T = cu_q[b + 1] - cu_q[b], L = cu_k[b + 1] - cu_k[b];
+        if (T < 0 || L < T || L > INT32_MAX) return -1;
+        if (T == 0) continue;
+        if (T * std::max<int64_t>(L, k) > kMaxElems) return -1;
+        need = std::max(need, prefill_ws((int)T, (int)L, k).total);
+    }
+    return (int64_t)need;
+}
+
+size_t dsa_prefill_varlen_workspace_bytes(int B, const int64_t* cu_seqlens_q,
+                                          const int64_t* cu_seqlens_k, int H_I, int H, int k)
+{
+    (void)H_I;
+    (void)H;
+    const int64_t ws = varlen_ws(B, cu_seqlens_q, cu_seqlens_k, k);
+    return ws < 0 ? 0 : (size_t)ws;
+}
+
+dsa_status_t dsa_prefill_varlen(int B, const int64_t* cu_seqlens_q, const int64_t* cu_seqlens_k,
+                                const uint8_t* q8, const float* q_scale, const float* w,
+                                const uint8_t* k8, const float* k_scale, const uint16_t* q,
+                                const uint16_t* kv, int H_I, int H, int k, float score_scale,
+                                float sm_scale, uint16_t* out, float* lse, int32_t* idx_out,
+                                void* workspace, size_t workspace_bytes, dsa_stream_t stream)
+{
+    if (k < 1 || H < 1) return DSA_ERR_INVALID_ARGUMENT;
+    const int64_t need = varlen_ws(B, cu_seqlens_q, cu_seqlens_k, k);
+    if (need < 0) return DSA_ERR_INVALID_ARGUMENT;
+    if (!(score_scale > 0.f) || !(sm_scale > 0.f)) return DSA_ERR_INVALID_ARGUMENT;
+    if (!dsa::indexer_supports(H_I) || !heads_ok(H) || !k_ok(k)) return DSA_ERR_UNSUPPORTED;
+    if (B == 0 || cu_seqlens_q[B] == 0) return DSA_OK;   // no query rows
+    if (!q8 || !q_scale || !w || !k8 || !k_scale || !q || !kv || !out)
+        return DSA_ERR_INVALID_ARGUMENT;
+    if (!aligned(q8, 16) || !aligned(k8, 16) || !aligned(q, 16) || !aligned(kv, 16) ||
+        !aligned(out, 4))
+        return DSA_ERR_INVALID_ARGUMENT;
+    if (!workspace || workspace_bytes < (size_t)need) return DSA_ERR_WORKSPACE_TOO_SMALL;
+    if (!aligned(workspace, kAlign)) return DSA_ERR_INVALID_ARGUMENT;
+
+    hipStream_t s = as_hip(stream);
+    for (int b = 0; b < B; ++b) {
+        const int64_t qa = cu_seqlens_q[b], ka = cu_seqlens_k[b];
+        const int T = (int)(cu_seqlens_q[b + 1] - qa), L = (int)(cu_seqlens_k[b + 1] - ka);
+        if (T == 0) continue;
+        // the sequence's queries are its last T tokens
+        const dsa_status_t st = prefill_run(
+            q8 + qa * H_I * 128, q_scale + qa * H_I, w + qa * H_I, k8 + ka * 128, k_scale + ka,
+            q + qa * H * 576, kv + ka * 576, T, L, H_I, H, k, L - T, score_scale, sm_scale,
+            out + qa * H * 512, lse ? lse + qa * H : nullptr, idx_out ? idx_out + qa * k : nullptr,
+            workspace, s);
+        if (st != DSA_OK) return st;
     }
     return DSA_OK;
 }

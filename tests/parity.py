@@ -96,3 +96,39 @@ def check_mla(out_g: np.ndarray, lse_g: np.ndarray, out_o: np.ndarray, lse_o: np
     dl = np.abs(lse_g[fin] - lse_o[fin])
     assert dl.max(initial=0.0) <= LSE_ATOL, "%s: max |dlse| %.3g" % (what, dl.max())
     return float(d.max(initial=0.0)), float(rel.max(initial=0.0)), float(dl.max(initial=0.0))
+
+
+def _np(t):
+    return t.detach().cpu().numpy()
+
+
+def _u16(t):
+    return t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+def oracle_prefill_rows(d: dict, rows, k):
+    """Oracle prefill of selected rows, one at a time (inputs copied from the device)."""
+    k8, ks, kv = _np(d["k8"]), _np(d["ks"]), _u16(d["kv"])
+    res = []
+    for t in rows:
+        t = int(t)
+        p = d["q_pos0"] + t
+        sc, bd = oracle.index_scores(_np(d["q8"][t:t + 1]), _np(d["qs"][t:t + 1]),
+                                     _np(d["w"][t:t + 1]), k8, ks, p, d["score_scale"],
+                                     with_bound=True)
+        idx = oracle.topk(sc, [p + 1], k)
+        res.append(dict(t=t, n=p + 1, scores=sc[0], bound=bd[0], idx=idx[0]))
+    return res
+
+
+def check_prefill_rows(d, out, lse, gidx, rows, k, what):
+    ora = oracle_prefill_rows(d, rows, k)
+    kv = _u16(d["kv"])
+    swaps = 0
+    for r in ora:
+        t = r["t"]
+        swaps += check_indices_near_ties(gidx[t:t + 1], r["idx"][None], r["scores"][None],
+                                         r["bound"][None], [r["n"]], k, "%s row %d" % (what, t))
+        oo, ol = oracle.sparse_mla(_u16(d["q"][t:t + 1]), kv, gidx[t:t + 1], d["sm_scale"])
+        check_mla(bf16_to_f64(out[t:t + 1]), _np(lse[t:t + 1]), oo, ol, "%s row %d" % (what, t))
+    return swaps

@@ -35,7 +35,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_status_strings_and_version(lib):
-    assert lib.dsa_version() == 102
+    assert lib.dsa_version() == 103
     for code, name in [(0, b"DSA_OK"), (1, b"DSA_ERR_INVALID_ARGUMENT"),
                        (2, b"DSA_ERR_UNSUPPORTED"), (3, b"DSA_ERR_WORKSPACE_TOO_SMALL"),
                        (4, b"DSA_ERR_HIP")]:
@@ -152,3 +152,35 @@ def test_index_rule_validation(lib):
     assert u(NULL, 4, 8, 0, 2, 3, FAKE, NULL) == dsa.DSA_ERR_INVALID_ARGUMENT
     assert u(FAKE, 4, 8, 0, 2, (1 << 30), FAKE, NULL) == dsa.DSA_ERR_UNSUPPORTED
     assert u(NULL, 0, 8, 0, 2, 3, NULL, NULL) == dsa.DSA_OK
+
+
+def test_prefill_varlen_validation_and_workspace(lib):
+    def cu(*v):
+        return (ctypes.c_int64 * len(v))(*v)
+    cq, ck = cu(0, 16, 16, 40), cu(0, 20, 30, 40)       # T = 16, 0, 24; L = 20, 10, 10
+    # sequence 2 has T = 24 > L = 10: malformed
+    assert lib.dsa_prefill_varlen_workspace_bytes(3, cq, ck, 4, 8, 4) == 0
+    cq, ck = cu(0, 16, 16, 40), cu(0, 20, 30, 3000)
+    need = lib.dsa_prefill_varlen_workspace_bytes(3, cq, ck, 4, 8, 4)
+    assert need == max(lib.dsa_prefill_workspace_bytes(16, 20, 4, 8, 4),
+                       lib.dsa_prefill_workspace_bytes(24, 2970, 4, 8, 4))
+    assert lib.dsa_prefill_varlen_workspace_bytes(3, cu(0, 0, 0, 0), ck, 4, 8, 4) == 0
+
+    def f(B=3, q_=cq, k_=ck, H_I=4, H=16, k=4, ws=FAKE, wsb=None, p=FAKE):
+        wsb = need if wsb is None else wsb
+        return lib.dsa_prefill_varlen(B, q_, k_, p, p, p, p, p, p, p, H_I, H, k, 0.1, 0.05,
+                                      p, p, NULL, ws, wsb, NULL)
+    assert f(B=0, q_=NULL, k_=NULL, p=NULL) == dsa.DSA_OK                 # empty batch
+    assert f(q_=cu(0, 0, 0, 0), k_=ck, p=NULL) == dsa.DSA_OK              # no query rows
+    assert f(B=-1) == dsa.DSA_ERR_INVALID_ARGUMENT
+    assert f(q_=NULL) == dsa.DSA_ERR_INVALID_ARGUMENT
+    assert f(p=NULL) == dsa.DSA_ERR_INVALID_ARGUMENT
+    assert f(q_=cu(1, 16, 16, 40)) == dsa.DSA_ERR_INVALID_ARGUMENT        # does not start at 0
+    assert f(k_=cu(0, 20, 10, 3000)) == dsa.DSA_ERR_INVALID_ARGUMENT      # decreasing
+    assert f(q_=cu(0, 21, 21, 40)) == dsa.DSA_ERR_INVALID_ARGUMENT        # T_0 = 21 > L_0 = 20
+    assert f(k=0) == dsa.DSA_ERR_INVALID_ARGUMENT
+    assert f(H_I=3) == dsa.DSA_ERR_UNSUPPORTED
+    assert f(ws=NULL) == dsa.DSA_ERR_WORKSPACE_TOO_SMALL
+    assert f(wsb=need - 1) == dsa.DSA_ERR_WORKSPACE_TOO_SMALL
+    assert f(ws=ctypes.c_void_p((1 << 20) + 128)) == dsa.DSA_ERR_INVALID_ARGUMENT
+    assert f(p=ctypes.c_void_p((1 << 20) + 8)) == dsa.DSA_ERR_INVALID_ARGUMENT  # alignment

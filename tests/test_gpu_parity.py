@@ -11,8 +11,8 @@ import pytest
 import torch
 
 import oracle
-from parity import (check_indices_near_ties, check_mla, check_scores, check_topk_exact,
-                    bf16_to_f64, to_device)
+from parity import (check_indices_near_ties, check_mla, check_prefill_rows, check_scores,
+                    check_topk_exact, bf16_to_f64, to_device)
 from synth import WORKLOADS, DecodeCfg, PrefillCfg, host_arrays, make_decode, make_prefill
 
 pytestmark = pytest.mark.gpu
@@ -232,34 +232,6 @@ def test_sparse_mla_single_row_closed_form_and_empty_rows(dsa):
 
 # ------------------------------------------------------------------- prefill, end to end
 
-def _oracle_rows_from_device(d: dict, rows, k):
-    """Oracle prefill of selected rows, one at a time (inputs copied from the device)."""
-    k8, ks, kv = _np(d["k8"]), _np(d["ks"]), _u16(d["kv"])
-    res = []
-    for t in rows:
-        t = int(t)
-        p = d["q_pos0"] + t
-        sc, bd = oracle.index_scores(_np(d["q8"][t:t + 1]), _np(d["qs"][t:t + 1]),
-                                     _np(d["w"][t:t + 1]), k8, ks, p, d["score_scale"],
-                                     with_bound=True)
-        idx = oracle.topk(sc, [p + 1], k)
-        res.append(dict(t=t, n=p + 1, scores=sc[0], bound=bd[0], idx=idx[0]))
-    return res
-
-
-def _check_prefill_rows(d, out, lse, gidx, rows, k, what):
-    ora = _oracle_rows_from_device(d, rows, k)
-    kv = _u16(d["kv"])
-    swaps = 0
-    for r in ora:
-        t = r["t"]
-        swaps += check_indices_near_ties(gidx[t:t + 1], r["idx"][None], r["scores"][None],
-                                         r["bound"][None], [r["n"]], k, "%s row %d" % (what, t))
-        oo, ol = oracle.sparse_mla(_u16(d["q"][t:t + 1]), kv, gidx[t:t + 1], d["sm_scale"])
-        check_mla(bf16_to_f64(out[t:t + 1]), _np(lse[t:t + 1]), oo, ol, "%s row %d" % (what, t))
-    return swaps
-
-
 def test_prefill_small_every_row(dsa):
     cfg = WORKLOADS["prefill-L1024-k256"]
     inp = make_prefill(cfg)
@@ -349,7 +321,7 @@ def test_prefill_long_context_sampled_rows(dsa, name, extra):
     sub_out = out[torch.from_numpy(rows).cuda()]
     sub_lse = lse[torch.from_numpy(rows).cuda()]
     sub = dict(d)
-    ora = _oracle_rows_from_device(d, rows, cfg.k)
+    ora = oracle_prefill_rows(d, rows, cfg.k)
     kv = _u16(d["kv"])
     for i, r in enumerate(ora):
         t = r["t"]
