@@ -56,6 +56,7 @@ def _load():
             lib.ora_decode_append.argtypes = [i32, P, P, i32, P, P, P, P]
             lib.ora_window_indices.argtypes = [i64, i64, i32, P]
             lib.ora_local_selected.argtypes = [P, i64, i32, i64, i32, P]
+            lib.ora_warmup.argtypes = [P, P, P, P, i64, P, P, i64, i32, i32, dbl, dbl] + [P] * 14
             lib.ora_num_threads.restype = i32
             _lib = lib
     return _lib
@@ -92,6 +93,65 @@ def e4m3fn_values(codes) -> np.ndarray:
 def bf16_values(bits) -> np.ndarray:
     lib = _load()
     return np.array([lib.ora_bf16_value(int(b)) for b in np.ravel(bits)], dtype=np.float64)
+
+
+_TABLES = {}
+
+
+def _decode_tables():
+    """fp64 value of every e4m3fn code and every bf16 bit pattern (the pinned decoders)."""
+    if not _TABLES:
+        _TABLES["e4m3"] = e4m3fn_values(np.arange(256))
+        _TABLES["bf16"] = bf16_values(np.arange(65536))
+    return _TABLES["e4m3"], _TABLES["bf16"]
+
+
+def warmup_inputs(inp: dict, rows=None):
+    """Real-valued (fp64) warm-up inputs from the stored formats: the indexer's dequantised
+    query and key vectors QI = qs * q8, KI = ks * k8, the weights w, and the MLA query and
+    cache rows, for the given query rows (positions q_pos0 + row)."""
+    e4, b16 = _decode_tables()
+    T = inp["q8"].shape[0]
+    r = _rows(rows, T)
+    q8, qs = np.asarray(inp["q8"])[r], np.asarray(inp["qs"], np.float64)[r]
+    return dict(QI=e4[q8] * qs[..., None], w=np.asarray(inp["w"], np.float64)[r],
+                q=b16[np.asarray(inp["q"])[r]], pos=inp["q_pos0"] + r,
+                KI=e4[np.asarray(inp["k8"])] * np.asarray(inp["ks"], np.float64)[:, None],
+                kv=b16[np.asarray(inp["kv"])], c=float(inp["score_scale"]),
+                sm_scale=float(inp["sm_scale"]))
+
+
+def warmup(x: dict, want_dk=False, bounds=False, dist=False):
+    """Indexer warm-up loss and gradient on real-valued inputs (see warmup_inputs): per row
+    kl, teacher lse_t [., H], student lse_i, dq [., H_I, 128], dw [., H_I]; with want_dk the
+    key gradient dk [L, 128] summed over the given rows; with dist the target P and the score
+    gradient G [., L]; with bounds the magnitude sums the tolerances are built from."""
+    QI, w, q, KI, kv = (_c(x[k], np.float64) for k in ("QI", "w", "q", "KI", "kv"))
+    pos = _c(x["pos"], np.int64)
+    n, H_I = QI.shape[0], QI.shape[1]
+    H, L = q.shape[1], KI.shape[0]
+    assert QI.shape[2] == 128 and q.shape == (n, H, 576) and kv.shape == (L, 576)
+    out = dict(kl=np.empty(n), lse_t=np.empty((n, H)), lse_i=np.empty(n),
+               dq=np.empty((n, H_I, 128)), dw=np.empty((n, H_I)))
+    opt = {}
+    if dist:
+        opt["P"], opt["G"] = np.empty((n, L)), np.empty((n, L))
+    if want_dk:
+        opt["dk"] = np.empty((L, 128))
+    if bounds:
+        opt.update(kl_bnd=np.empty(n), dw_bnd=np.empty((n, H_I)), dq_bnd=np.empty((n, H_I, 128)),
+                   dq_amb=np.empty((n, H_I, 128)))
+        if want_dk:
+            opt.update(dk_bnd=np.empty((L, 128)), dk_amb=np.empty((L, 128)))
+    out.update(opt)
+    ptr = lambda k: _p(out[k]) if k in out else None
+    rc = _load().ora_warmup(_p(QI), _p(w), _p(q), _p(pos), n, _p(KI), _p(kv), L, H_I, H,
+                            x["c"], x["sm_scale"], ptr("kl"), ptr("lse_t"), ptr("lse_i"),
+                            ptr("dq"), ptr("dw"), ptr("P"), ptr("G"), ptr("dk"), ptr("kl_bnd"),
+                            ptr("dw_bnd"), ptr("dq_bnd"), ptr("dq_amb"), ptr("dk_bnd"),
+                            ptr("dk_amb"))
+    _check(rc, "warmup")
+    return out
 
 
 def quantize_e4m3(x):

@@ -416,3 +416,161 @@ int ora_local_selected(const int32_t* sel, int64_t T, int k, int64_t q_pos0, int
     }
     return 0;
 }
+
+/* ---- indexer warm-up: KL to the head-averaged dense attention, and its gradient ------ */
+
+static double dot_n(const double* a, const double* b, int n, double* abs_sum)
+{
+    double acc = 0.0, acc_abs = 0.0;
+    for (int d = 0; d < n; ++d) {
+        acc += a[d] * b[d];
+        acc_abs += fabs(a[d] * b[d]);
+    }
+    if (abs_sum) *abs_sum = acc_abs;
+    return acc;
+}
+
+/* whether a rounded evaluation of x = <a, b> might land on the other side of zero */
+static int relu_ambiguous(double x, double abs_sum) { return fabs(x) <= ldexp(abs_sum, -16); }
+
+int ora_warmup(const double* QI, const double* w, const double* q, const int64_t* pos,
+               int64_t n_rows, const double* KI, const double* kv, int64_t L, int H_I, int H,
+               double c, double sm_scale, double* kl, double* lse_t, double* lse_i, double* dq,
+               double* dw, double* P, double* G, double* dk, double* kl_bnd, double* dw_bnd,
+               double* dq_bnd, double* dq_amb, double* dk_bnd, double* dk_amb)
+{
+    if (L <= 0 || H_I <= 0 || H <= 0 || n_rows < 0) return -1;
+    for (int64_t r = 0; r < n_rows; ++r)
+        if (pos[r] < 0 || pos[r] >= L) return -1;
+    /* the gradient row G of every given row is kept when dk is wanted */
+    double* Gall = NULL;
+    if (dk || dk_bnd || dk_amb) {
+        Gall = (double*)calloc((size_t)n_rows * (size_t)L, sizeof(double));
+        if (!Gall) return -1;
+    }
+    int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : bad)
+    for (int64_t r = 0; r < n_rows; ++r) {
+        const int64_t n = pos[r] + 1;
+        double* logit = (double*)malloc(sizeof(double) * (size_t)n);
+        double* Pr = (double*)calloc((size_t)n, sizeof(double));
+        double* I = (double*)malloc(sizeof(double) * (size_t)n);
+        double* x = (double*)malloc(sizeof(double) * (size_t)n * (size_t)H_I);
+        double* xa = (double*)malloc(sizeof(double) * (size_t)n * (size_t)H_I);
+        double* Gr = (double*)malloc(sizeof(double) * (size_t)n);
+        if (!logit || !Pr || !I || !x || !xa || !Gr) {
+            bad = 1;
+            free(logit); free(Pr); free(I); free(x); free(xa); free(Gr);
+            continue;
+        }
+        /* teacher: each head's softmax over the visible keys, averaged over heads */
+        for (int h = 0; h < H; ++h) {
+            const double* qh = q + (r * H + h) * 576;
+            double mx = -INFINITY;
+            for (int64_t s = 0; s < n; ++s) {
+                logit[s] = sm_scale * dot_n(qh, kv + s * 576, 576, NULL);
+                if (logit[s] > mx) mx = logit[s];
+            }
+            double sum = 0.0;
+            for (int64_t s = 0; s < n; ++s) sum += exp(logit[s] - mx);
+            const double lse = mx + log(sum);
+            lse_t[r * H + h] = lse;
+            for (int64_t s = 0; s < n; ++s) Pr[s] += exp(logit[s] - lse) / H;
+        }
+        /* student: indexer scores and their softmax over the same keys */
+        double mx = -INFINITY;
+        for (int64_t s = 0; s < n; ++s) {
+            double acc = 0.0;
+            for (int h = 0; h < H_I; ++h) {
+                const double xv = dot_n(QI + (r * H_I + h) * 128, KI + s * 128, 128,
+                                        &xa[s * H_I + h]);
+                x[s * H_I + h] = xv;
+                acc += w[r * H_I + h] * (xv > 0.0 ? xv : 0.0);
+            }
+            I[s] = c * acc;
+            if (I[s] > mx) mx = I[s];
+        }
+        double sum = 0.0;
+        for (int64_t s = 0; s < n; ++s) sum += exp(I[s] - mx);
+        const double lsei = mx + log(sum);
+        lse_i[r] = lsei;
+        /* KL(P || Q) and its gradient with respect to the scores */
+        double klr = 0.0, klb = 0.0;
+        for (int64_t s = 0; s < n; ++s) {
+            const double logq = I[s] - lsei;
+            if (Pr[s] > 0.0) {
+                klr += Pr[s] * (log(Pr[s]) - logq);
+                klb += Pr[s] * (fabs(log(Pr[s])) + fabs(logq));
+            }
+            Gr[s] = exp(logq) - Pr[s];
+        }
+        kl[r] = klr;
+        if (kl_bnd) kl_bnd[r] = klb;
+        /* back through the indexer into w and the query vectors */
+        for (int h = 0; h < H_I; ++h) {
+            const double wh = w[r * H_I + h];
+            double dwh = 0.0, dwb = 0.0;
+            double* dqh = dq + (r * H_I + h) * 128;
+            for (int d = 0; d < 128; ++d) dqh[d] = 0.0;
+            if (dq_bnd) for (int d = 0; d < 128; ++d) dq_bnd[(r * H_I + h) * 128 + d] = 0.0;
+            if (dq_amb) for (int d = 0; d < 128; ++d) dq_amb[(r * H_I + h) * 128 + d] = 0.0;
+            for (int64_t s = 0; s < n; ++s) {
+                const double xv = x[s * H_I + h];
+                dwh += Gr[s] * (xv > 0.0 ? xv : 0.0);
+                dwb += fabs(Gr[s] * xv);
+                const double* ks_ = KI + s * 128;
+                if (xv > 0.0) {
+                    for (int d = 0; d < 128; ++d) dqh[d] += Gr[s] * ks_[d];
+                    if (dq_bnd)
+                        for (int d = 0; d < 128; ++d)
+                            dq_bnd[(r * H_I + h) * 128 + d] += fabs(c * wh * Gr[s] * ks_[d]);
+                }
+                if (dq_amb && relu_ambiguous(xv, xa[s * H_I + h]))
+                    for (int d = 0; d < 128; ++d)
+                        dq_amb[(r * H_I + h) * 128 + d] += fabs(c * wh * Gr[s] * ks_[d]);
+            }
+            for (int d = 0; d < 128; ++d) dqh[d] *= c * wh;
+            dw[r * H_I + h] = c * dwh;
+            if (dw_bnd) dw_bnd[r * H_I + h] = fabs(c) * dwb;
+        }
+        for (int64_t s = 0; s < L; ++s) {
+            const double pv = s < n ? Pr[s] : 0.0, gv = s < n ? Gr[s] : 0.0;
+            if (P) P[r * L + s] = pv;
+            if (G) G[r * L + s] = gv;
+            if (Gall) Gall[r * L + s] = gv;
+        }
+        free(logit); free(Pr); free(I); free(x); free(xa); free(Gr);
+    }
+    if (!bad && Gall) {
+        /* dk: each key collects the rows that see it */
+#pragma omp parallel for schedule(dynamic, 16)
+        for (int64_t s = 0; s < L; ++s) {
+            double acc[128], accb[128], acca[128];
+            for (int d = 0; d < 128; ++d) acc[d] = accb[d] = acca[d] = 0.0;
+            for (int64_t r = 0; r < n_rows; ++r) {
+                if (pos[r] < s) continue;
+                const double gv = Gall[r * L + s];
+                for (int h = 0; h < H_I; ++h) {
+                    const double* qh = QI + (r * H_I + h) * 128;
+                    double xa_;
+                    const double xv = dot_n(qh, KI + s * 128, 128, &xa_);
+                    const double f = c * gv * w[r * H_I + h];
+                    if (xv > 0.0)
+                        for (int d = 0; d < 128; ++d) {
+                            acc[d] += f * qh[d];
+                            accb[d] += fabs(f * qh[d]);
+                        }
+                    if (relu_ambiguous(xv, xa_))
+                        for (int d = 0; d < 128; ++d) acca[d] += fabs(f * qh[d]);
+                }
+            }
+            for (int d = 0; d < 128; ++d) {
+                if (dk) dk[s * 128 + d] = acc[d];
+                if (dk_bnd) dk_bnd[s * 128 + d] = accb[d];
+                if (dk_amb) dk_amb[s * 128 + d] = acca[d];
+            }
+        }
+    }
+    free(Gall);
+    return bad ? -1 : 0;
+}

@@ -12,7 +12,8 @@
  *                   “黑科技”里》 (devpress.csdn.net) -- §二 两大核心武器, §三 四步工作流.
  *   [gxzdkb-dsa]    gxzdkb.com explainer of DSA -- sections 原始 Attention 的计算逻辑,
  *                   秘密武器：DSA, 实测效果.
- *   [yufo-notes]    ele-yufo.com notes "DeepSeek V3.2-Exp" -- §三 两步跑通稀疏路由.
+ *   [yufo-notes]    ele-yufo.com notes "DeepSeek V3.2-Exp" -- §三 两步跑通稀疏路由,
+ *                   §四 训练的两步走冷启动 (第一阶段 Warm-up).
  *   [oilbeater-dsa] oilbeater.com "DeepSeek Sparse Attention" -- section Sparse Attention.
  *
  * Conventions shared by every function:
@@ -95,6 +96,33 @@ int ora_decode_append(int B, const int64_t* seq_start, const void* k_new, int k_
  * entries (0 <= s <= p) of sel[t, 0:k], -1 padded: out [T, W + k]. */
 int ora_window_indices(int64_t T, int64_t q_pos0, int W, int32_t* idx);
 int ora_local_selected(const int32_t* sel, int64_t T, int k, int64_t q_pos0, int W, int32_t* out);
+
+/* Indexer warm-up loss and its gradient ([yufo-notes] §四 训练的两步走冷启动, 第一阶段
+ * Warm-up: the frozen main model's dense attention gives each token's weight distribution
+ * as the target, and the indexer alone is trained to fit it with a KL divergence).  For a
+ * query at position p (n = p + 1 visible keys):
+ *   teacher  l_h[s] = sm_scale <q[h,:], kv[s,:]> (576 dims),  lse_t[h] = log sum_s exp l_h[s],
+ *            P[s]   = (1/H) sum_h exp(l_h[s] - lse_t[h])        (head-averaged, sums to 1)
+ *   student  x_h[s] = <QI[h,:], KI[s,:]>,  I[s] = c sum_h w[h] max(x_h[s], 0),
+ *            lse_i  = log sum_s exp I[s],  Q[s] = exp(I[s] - lse_i)
+ *   loss     kl = sum_s P[s] (log P[s] - log Q[s])   (terms with P[s] = 0 contribute 0)
+ *   gradient G[s] = dkl/dI[s] = Q[s] - P[s];
+ *            dw[h]     = c sum_s G[s] max(x_h[s], 0)
+ *            dq[h,d]   = c w[h] sum_s G[s] [x_h[s] > 0] KI[s,d]
+ *            dk[s,d]  += c G[s] sum_h w[h] [x_h[s] > 0] QI[h,d]     (summed over the rows given)
+ * Inputs are real-valued (fp64): QI [n_rows,H_I,128], w [n_rows,H_I], q [n_rows,H,576],
+ * pos [n_rows] (each < L), KI [L,128], kv [L,576].  Outputs per row: kl, lse_t [.,H],
+ * lse_i, dq [.,H_I,128], dw [.,H_I]; P and G [n_rows, L] (entries s > p are 0) nullable;
+ * dk [L,128] nullable.  Magnitude bounds (all nullable): kl_bnd = sum_s P (|log P| +
+ * |log Q|); dw_bnd[h] = c sum_s |G| |x_h|; dq_bnd / dk_bnd = the same sums as dq / dk with
+ * every term replaced by its absolute value; dq_amb / dk_amb = those absolute sums taken
+ * only over the (h, s) whose |x_h[s]| <= 2^-16 sum_d |QI[h,d] KI[s,d]| (where a rounded
+ * evaluation of x may take the other side of the ReLU). */
+int ora_warmup(const double* QI, const double* w, const double* q, const int64_t* pos,
+               int64_t n_rows, const double* KI, const double* kv, int64_t L, int H_I, int H,
+               double c, double sm_scale, double* kl, double* lse_t, double* lse_i, double* dq,
+               double* dw, double* P, double* G, double* dk, double* kl_bnd, double* dw_bnd,
+               double* dq_bnd, double* dq_amb, double* dk_bnd, double* dk_amb);
 
 int ora_num_threads(void);
 

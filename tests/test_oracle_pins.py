@@ -563,3 +563,85 @@ def test_varlen_sequences_are_isolated_and_order_free():
     for i in (0, 2):
         for key in ("idx", "out", "lse"):
             assert np.array_equal(alt[i][key], base[i][key])
+
+
+# ------------------------------------------------------------------ indexer warm-up (KL)
+
+def _torch_warmup(x):
+    """The warm-up loss written with torch float64 library ops, differentiated by autograd."""
+    QI = torch.tensor(x["QI"], requires_grad=True)
+    KI = torch.tensor(x["KI"], requires_grad=True)
+    w = torch.tensor(x["w"], requires_grad=True)
+    q, kv = torch.tensor(x["q"]), torch.tensor(x["kv"])
+    pos = torch.tensor(x["pos"])
+    L = KI.shape[0]
+    vis = torch.arange(L)[None, :] <= pos[:, None]                       # [n, L]
+    logits = torch.einsum("nhd,sd->nhs", q, kv) * x["sm_scale"]
+    logits = logits.masked_fill(~vis[:, None, :], -math.inf)
+    P = torch.softmax(logits, dim=-1).mean(dim=1)                        # head average
+    I = x["c"] * (w[:, :, None] * torch.relu(torch.einsum("nhd,sd->nhs", QI, KI))).sum(1)
+    logQ = torch.log_softmax(I.masked_fill(~vis, -math.inf), dim=-1).masked_fill(~vis, 0.0)
+    kl = torch.nn.functional.kl_div(logQ, P, reduction="none").sum(-1)
+    kl.sum().backward()
+    G = (torch.exp(logQ) * vis - P).detach()
+    return dict(kl=kl.detach().numpy(), P=P.detach().numpy(), G=G.numpy(),
+                lse_t=torch.logsumexp(logits, -1).detach().numpy(),
+                lse_i=torch.logsumexp(I.masked_fill(~vis, -math.inf), -1).detach().numpy(),
+                dq=QI.grad.numpy(), dk=KI.grad.numpy(), dw=w.grad.numpy())
+
+
+@pytest.mark.parametrize("L,T,q_pos0,H_I,H,seed", [(40, 40, 0, 3, 4, 1), (57, 30, 27, 4, 2, 2),
+                                                    (33, 33, 0, 1, 3, 3)])
+def test_warmup_matches_torch_autograd(L, T, q_pos0, H_I, H, seed):
+    a = host_arrays(make_prefill(PrefillCfg("t", L=L, k=8, H_I=H_I, H=H, w_std=0.7, seed=seed,
+                                            q_pos0=q_pos0, T=T)))
+    x = oracle.warmup_inputs(a)
+    o = oracle.warmup(x, want_dk=True, dist=True)
+    ref = _torch_warmup(x)
+    for key in ("kl", "P", "G", "lse_t", "lse_i", "dq", "dk", "dw"):
+        scale = np.abs(ref[key]).max()
+        assert np.allclose(o[key], ref[key], rtol=1e-9, atol=1e-12 * max(scale, 1.0)), key
+
+
+def test_warmup_homogeneity_identities_and_bounds():
+    """The scores are homogeneous of degree one in w, in each query vector and in each key
+    vector, so <dw, w> = <dq, QI> = sum_s G I per row, and <dk, KI> is their sum over rows;
+    every bound dominates its value."""
+    a = host_arrays(make_prefill(PrefillCfg("t", L=50, k=8, H_I=4, H=3, w_std=0.7, seed=7)))
+    x = oracle.warmup_inputs(a)
+    o = oracle.warmup(x, want_dk=True, dist=True, bounds=True)
+    xv = np.einsum("nhd,sd->nhs", x["QI"], x["KI"])
+    I = x["c"] * (x["w"][:, :, None] * np.maximum(xv, 0)).sum(1)
+    vis = np.arange(50)[None, :] <= x["pos"][:, None]
+    gi = (o["G"] * np.where(vis, I, 0)).sum(1)
+    assert np.allclose((o["dw"] * x["w"]).sum(1), gi, rtol=1e-10, atol=1e-14)
+    assert np.allclose((o["dq"] * x["QI"]).sum((1, 2)), gi, rtol=1e-10, atol=1e-14)
+    assert np.isclose((o["dk"] * x["KI"]).sum(), gi.sum(), rtol=1e-10, atol=1e-14)
+    assert np.allclose(o["P"].sum(1), 1.0, rtol=1e-13) and np.allclose(o["G"].sum(1), 0, atol=1e-14)
+    assert (o["kl"] >= -1e-15).all() and (o["kl_bnd"] >= np.abs(o["kl"])).all()
+    assert (o["dw_bnd"] >= np.abs(o["dw"]) - 1e-15).all()
+    assert (o["dq_bnd"] >= np.abs(o["dq"]) - 1e-15).all()
+    assert (o["dk_bnd"] >= np.abs(o["dk"]) - 1e-15).all()
+    assert (o["dq_amb"] <= o["dq_bnd"] + np.abs(o["dq_amb"])).all()
+
+
+def test_warmup_student_equal_to_teacher_has_zero_loss():
+    """When the indexer's distribution is the target itself the loss and every gradient
+    vanish: one indexer head with QI = e_0, KI[s] = log-target in dimension 0 (positive
+    part only is kept by the ReLU, so the target is made of positive log-ratios), w = 1/c."""
+    L = 6
+    rng = np.random.default_rng(3)
+    target = rng.uniform(1.0, 3.0, L)                 # I[s] for the last row
+    x = dict(QI=np.zeros((1, 1, 128)), w=np.array([[1.0 / 0.25]]), KI=np.zeros((L, 128)),
+             q=np.zeros((1, 2, 576)), kv=np.zeros((L, 576)), pos=np.array([L - 1]), c=0.25,
+             sm_scale=0.1)
+    x["QI"][0, 0, 0] = 1.0
+    x["KI"][:, 0] = target
+    # teacher logits sm_scale <q_h, kv_s> = target[s] for both heads: q_h = e_0 / sm_scale
+    x["q"][0, :, 0] = 1.0 / 0.1
+    x["kv"][:, 0] = target
+    o = oracle.warmup(x, want_dk=True, dist=True)
+    assert abs(o["kl"][0]) < 1e-14
+    assert np.abs(o["G"]).max() < 1e-15
+    assert np.abs(o["dq"]).max() < 1e-13 and np.abs(o["dk"]).max() < 1e-13
+    assert np.abs(o["dw"]).max() < 1e-13
