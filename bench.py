@@ -78,6 +78,9 @@ def parse():
     ap.add_argument("--varlen-workload", default="varlen-B16-L1024-32768-k2048")
     ap.add_argument("--no-varlen", action="store_true",
                     help="skip timing the packed multi-sequence prefill")
+    ap.add_argument("--warmup-workload", default="prefill-L32768-k2048")
+    ap.add_argument("--no-warmup-kl", action="store_true",
+                    help="skip timing the indexer warm-up loss and gradient")
     ap.add_argument("--no-prefill", action="store_true",
                     help="decode only (for profiling runs; prints no prefill value)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -236,6 +239,9 @@ def main():
     # ---- packed multi-sequence prefill (fresh prefills and chunks against caches)
     varlen = None if args.no_varlen else run_varlen(args, WORKLOADS[args.varlen_workload], dev)
 
+    # ---- indexer warm-up: KL to the dense attention distribution and its gradient
+    warm = None if args.no_warmup_kl else run_warmup_kl(args, WORKLOADS[args.warmup_workload], dev)
+
     # ---- CPU oracle baseline on sampled rows of the same prefill workload
     cpu = None
     if not args.no_cpu_baseline:
@@ -263,6 +269,7 @@ def main():
         "input_prep": prep,
         "window_attention": window,
         "varlen_prefill": varlen,
+        "indexer_warmup": warm,
         "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)
@@ -419,6 +426,85 @@ def run_varlen(args, vcfg, dev):
                algorithmic_tflop=round(flops / 1e12, 3),
                effective_tflop_s=round(flops / (ms / 1e3) / 1e12, 1))
     del d, out, lse, ws
+    torch.cuda.empty_cache()
+    return res
+
+
+def run_warmup_kl(args, wcfg, dev):
+    """Time dsa_indexer_warmup (teacher lse and distribution, indexer scores, per-row KL and
+    G, the dq/dw and dk contractions) over every query row of the workload; the two teacher
+    passes are also timed per chunk through their own entry points (HIP events on the same
+    stream) for the roofline of the dominant kernel."""
+    import torch
+
+    import sparse_attention_05_amd as dsa
+    from synth import make_prefill
+
+    log("generating", wcfg.name, "for the warm-up step")
+    d = make_prefill(wcfg, device=dev)
+    T, L, H_I, H = wcfg.rows, wcfg.L, wcfg.H_I, wcfg.H
+    out = dict(kl=torch.empty((T,), dtype=torch.float32, device=dev),
+               dq=torch.empty((T, H_I, 128), dtype=torch.float32, device=dev),
+               dw=torch.empty((T, H_I), dtype=torch.float32, device=dev),
+               dk=torch.empty((L, 128), dtype=torch.float32, device=dev),
+               lse_teacher=torch.empty((T, H), dtype=torch.float32, device=dev),
+               lse_index=torch.empty((T,), dtype=torch.float32, device=dev))
+    ws = torch.empty((dsa.dsa_indexer_warmup_workspace_bytes(T, L, H_I, H),), dtype=torch.uint8,
+                     device=dev)
+    stream = torch.cuda.current_stream()
+
+    def run():
+        dsa.dsa_indexer_warmup(d["q8"], d["qs"], d["w"], d["k8"], d["ks"], d["q"], d["kv"],
+                               wcfg.q_pos0, wcfg.score_scale, wcfg.sm_scale, out=out, workspace=ws)
+
+    run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 3
+    e0.record(stream)
+    for _ in range(reps):
+        run()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+
+    # teacher passes per chunk (the call's own chunking), events around each launch
+    chunk = dsa.dsa_prefill_chunk_rows(T, L)
+    P = ws[: chunk * L * 4].view(torch.float32).view(chunk, L)
+    evs = []
+    for r0 in range(0, T, chunk):
+        rows = min(chunk, T - r0)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        ev[0].record(stream)
+        dsa.dsa_attention_lse(d["q"][r0:r0 + rows], d["kv"], wcfg.q_pos0 + r0, wcfg.sm_scale,
+                              lse=out["lse_teacher"][r0:r0 + rows])
+        ev[1].record(stream)
+        dsa.dsa_attention_distribution(d["q"][r0:r0 + rows], d["kv"],
+                                       out["lse_teacher"][r0:r0 + rows], wcfg.q_pos0 + r0,
+                                       wcfg.sm_scale, P=P[:rows])
+        ev[2].record(stream)
+        evs.append(ev)
+    torch.cuda.synchronize()
+    t_lse = sum(e[0].elapsed_time(e[1]) for e in evs)
+    t_dist = sum(e[1].elapsed_time(e[2]) for e in evs)
+    pairs = sum(min(L, wcfg.q_pos0 + t + 1) for t in range(T))
+    f_teacher = pairs * 2.0 * H * D_QK                 # one pass over the dense logits
+    f_index = pairs * 2.0 * H_I * D_I                  # indexer scores (fp8)
+    f_back = 2 * (pairs * 2.0 * H_I * D_I) * 2         # dq and dk: fp8 recompute + bf16 contraction
+    flops = 2 * f_teacher + f_index + f_back
+    ach = f_teacher / (t_dist / 1e3) / 1e12
+    log("indexer warm-up %s: %.2f ms (teacher lse %.2f ms, distribution %.2f ms), %.0f tokens/s"
+        % (wcfg.name, ms, t_lse, t_dist, T / (ms / 1e3)))
+    res = dict(workload="%s, indexer warm-up (KL to the dense distribution + gradient)" % wcfg.name,
+               ms=round(ms, 3), tokens_per_s=round(T / (ms / 1e3), 1),
+               teacher_lse_ms=round(t_lse, 3), teacher_dist_ms=round(t_dist, 3),
+               chunk_rows=chunk, launches_per_pass=len(evs),
+               algorithmic_tflop=round(flops / 1e12, 3),
+               effective_tflop_s=round(flops / (ms / 1e3) / 1e12, 1),
+               roofline=dict(kernel="teacher distribution", bound="mfma", achieved=round(ach, 2),
+                             peak=PEAK["bf16"], unit="TFLOP/s", frac=round(ach / PEAK["bf16"], 4),
+                             avg_launch_ms=round(t_dist / len(evs), 4)))
+    del d, out, ws, P
     torch.cuda.empty_cache()
     return res
 

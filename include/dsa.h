@@ -11,6 +11,9 @@
  *                   §三 第二步–第四步 (the same four steps).
  *   [oilbeater-dsa] oilbeater.com "DeepSeek Sparse Attention": section Sparse Attention
  *                   (sliding windows, local windows joined by global tokens).
+ *   [yufo-notes]    ele-yufo.com notes "DeepSeek V3.2-Exp": §四 训练的两步走冷启动, 第一阶段
+ *                   Warm-up (the frozen main model's dense attention distribution is the
+ *                   target the indexer alone is fitted to, by KL divergence).
  *   [gxzdkb-dsa]    gxzdkb.com DSA explainer: 秘密武器：DSA (fp8 indexer, ReLU),
  *                   原始 Attention 的计算逻辑 (decode appends to the cache first),
  *                   致命问题：平方级复杂度拖垮效率 (rollout inference = prefill, which builds
@@ -63,7 +66,9 @@ typedef enum {
 const char* dsa_status_string(dsa_status_t status);
 
 /* ABI version: major * 100 + minor (1.02: + dsa_quantize_fp8, dsa_decode_append, dsa_window_indices,
- * dsa_local_selected_indices; 1.03: + dsa_prefill_varlen, dsa_prefill_varlen_workspace_bytes). */
+ * dsa_local_selected_indices; 1.03: + dsa_prefill_varlen, dsa_prefill_varlen_workspace_bytes;
+ * 1.04: + dsa_attention_lse, dsa_attention_distribution, dsa_indexer_warmup,
+ * dsa_indexer_warmup_workspace_bytes). */
 int dsa_version(void);
 
 /* Lightning-indexer scores ([csdn-workflow] §4 步骤二, [devpress-dsa] §三 第二步):
@@ -141,6 +146,42 @@ dsa_status_t dsa_prefill_varlen(int B, const int64_t* cu_seqlens_q, const int64_
 /* 0 for malformed cu_seqlens or when no sequence has query rows. */
 size_t dsa_prefill_varlen_workspace_bytes(int B, const int64_t* cu_seqlens_q,
                                           const int64_t* cu_seqlens_k, int H_I, int H, int k);
+
+/* Dense causal attention of the (frozen) main model, the warm-up target's source
+ * ([yufo-notes] §四 第一阶段 Warm-up): for row t (position p_t) and head h,
+ *   l[t,h,s] = sm_scale * <q[t,h,0:576], kv[s,0:576]>  for s <= p_t,
+ * dsa_attention_lse:          lse[t,h] = log sum_s exp l[t,h,s]          (lse [T,H] f32);
+ * dsa_attention_distribution: P[t,s] = (1/H) sum_h exp(l[t,h,s] - lse[t,h]) for s <= p_t,
+ *   the head-averaged attention distribution (rows of P at stride ld >= L; entries s > p_t
+ *   are not written).  q [T,H,576] bf16, kv [L,576] bf16, H <= 128; products exact in
+ *   fp32, fp32 accumulation and statistics. */
+dsa_status_t dsa_attention_lse(const uint16_t* q, const uint16_t* kv, int T, int L, int H,
+                               int q_pos0, float sm_scale, float* lse, dsa_stream_t stream);
+dsa_status_t dsa_attention_distribution(const uint16_t* q, const uint16_t* kv, const float* lse,
+                                        int T, int L, int H, int q_pos0, float sm_scale,
+                                        float* P, int64_t ld, dsa_stream_t stream);
+
+/* Indexer warm-up step ([yufo-notes] §四 第一阶段 Warm-up): the KL divergence from the
+ * dense distribution P (above) to the indexer's softmax Q[t,s] = softmax_{s <= p_t} I[t,s]
+ * (I = dsa_index_scores), and its gradient.  With x[t,h,s] = <QI[t,h], KI[s]> for the
+ * dequantised vectors QI = q_scale * q8, KI = k_scale * k8, and G = Q - P:
+ *   kl[t]      = sum_s P log(P / Q)                                  kl [T] f32
+ *   dw[t,h]    = score_scale * sum_s G max(x, 0)                     dw [T,H_I] f32
+ *   dq[t,h,:]  = score_scale * w[t,h] sum_s G [x > 0] KI[s,:]        dq [T,H_I,128] f32
+ *   dk[s,:]    = score_scale * sum_t sum_h G w[t,h] [x > 0] QI[t,h,:] dk [L,128] f32
+ * i.e. the gradients with respect to QI, KI and w (the fp8 rounding is treated as the
+ * identity); dk rows no query sees are 0.  lse_teacher [T,H] and lse_index [T] (both
+ * nullable) receive the teacher lse and log sum_s exp I.  The gradient contractions run on
+ * bf16 MFMA (G rounded to bf16, fp32 accumulation).  H_I in {16,32,64,128}, H <= 128.
+ * Other arguments as dsa_prefill; workspace at least dsa_indexer_warmup_workspace_bytes
+ * bytes, 256-byte aligned. */
+dsa_status_t dsa_indexer_warmup(const uint8_t* q8, const float* q_scale, const float* w,
+                                const uint8_t* k8, const float* k_scale, const uint16_t* q,
+                                const uint16_t* kv, int T, int L, int H_I, int H, int q_pos0,
+                                float score_scale, float sm_scale, float* kl, float* dq,
+                                float* dw, float* dk, float* lse_teacher, float* lse_index,
+                                void* workspace, size_t workspace_bytes, dsa_stream_t stream);
+size_t dsa_indexer_warmup_workspace_bytes(int T, int L, int H_I, int H);
 
 /* One decode step for B sequences ([gxzdkb-dsa] 原始 Attention 的计算逻辑: the new token's
  * cache entries are appended before attending).  Sequence b owns the packed cache rows

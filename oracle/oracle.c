@@ -443,10 +443,15 @@ int ora_warmup(const double* QI, const double* w, const double* q, const int64_t
     for (int64_t r = 0; r < n_rows; ++r)
         if (pos[r] < 0 || pos[r] >= L) return -1;
     /* the gradient row G of every given row is kept when dk is wanted */
-    double* Gall = NULL;
+    double *Gall = NULL, *Aall = NULL;
     if (dk || dk_bnd || dk_amb) {
         Gall = (double*)calloc((size_t)n_rows * (size_t)L, sizeof(double));
-        if (!Gall) return -1;
+        Aall = (double*)calloc((size_t)n_rows * (size_t)L, sizeof(double));
+        if (!Gall || !Aall) {
+            free(Gall);
+            free(Aall);
+            return -1;
+        }
     }
     int bad = 0;
 #pragma omp parallel for schedule(dynamic, 1) reduction(| : bad)
@@ -458,9 +463,10 @@ int ora_warmup(const double* QI, const double* w, const double* q, const int64_t
         double* x = (double*)malloc(sizeof(double) * (size_t)n * (size_t)H_I);
         double* xa = (double*)malloc(sizeof(double) * (size_t)n * (size_t)H_I);
         double* Gr = (double*)malloc(sizeof(double) * (size_t)n);
-        if (!logit || !Pr || !I || !x || !xa || !Gr) {
+        double* Ar = (double*)malloc(sizeof(double) * (size_t)n);
+        if (!logit || !Pr || !I || !x || !xa || !Gr || !Ar) {
             bad = 1;
-            free(logit); free(Pr); free(I); free(x); free(xa); free(Gr);
+            free(logit); free(Pr); free(I); free(x); free(xa); free(Gr); free(Ar);
             continue;
         }
         /* teacher: each head's softmax over the visible keys, averaged over heads */
@@ -503,6 +509,7 @@ int ora_warmup(const double* QI, const double* w, const double* q, const int64_t
                 klb += Pr[s] * (fabs(log(Pr[s])) + fabs(logq));
             }
             Gr[s] = exp(logq) - Pr[s];
+            Ar[s] = exp(logq) + Pr[s];
         }
         kl[r] = klr;
         if (kl_bnd) kl_bnd[r] = klb;
@@ -517,17 +524,17 @@ int ora_warmup(const double* QI, const double* w, const double* q, const int64_t
             for (int64_t s = 0; s < n; ++s) {
                 const double xv = x[s * H_I + h];
                 dwh += Gr[s] * (xv > 0.0 ? xv : 0.0);
-                dwb += fabs(Gr[s] * xv);
+                dwb += Ar[s] * fabs(xv);
                 const double* ks_ = KI + s * 128;
                 if (xv > 0.0) {
                     for (int d = 0; d < 128; ++d) dqh[d] += Gr[s] * ks_[d];
                     if (dq_bnd)
                         for (int d = 0; d < 128; ++d)
-                            dq_bnd[(r * H_I + h) * 128 + d] += fabs(c * wh * Gr[s] * ks_[d]);
+                            dq_bnd[(r * H_I + h) * 128 + d] += fabs(c * wh * ks_[d]) * Ar[s];
                 }
                 if (dq_amb && relu_ambiguous(xv, xa[s * H_I + h]))
                     for (int d = 0; d < 128; ++d)
-                        dq_amb[(r * H_I + h) * 128 + d] += fabs(c * wh * Gr[s] * ks_[d]);
+                        dq_amb[(r * H_I + h) * 128 + d] += fabs(c * wh * ks_[d]) * Ar[s];
             }
             for (int d = 0; d < 128; ++d) dqh[d] *= c * wh;
             dw[r * H_I + h] = c * dwh;
@@ -537,9 +544,12 @@ int ora_warmup(const double* QI, const double* w, const double* q, const int64_t
             const double pv = s < n ? Pr[s] : 0.0, gv = s < n ? Gr[s] : 0.0;
             if (P) P[r * L + s] = pv;
             if (G) G[r * L + s] = gv;
-            if (Gall) Gall[r * L + s] = gv;
+            if (Gall) {
+                Gall[r * L + s] = gv;
+                Aall[r * L + s] = s < n ? Ar[s] : 0.0;
+            }
         }
-        free(logit); free(Pr); free(I); free(x); free(xa); free(Gr);
+        free(logit); free(Pr); free(I); free(x); free(xa); free(Gr); free(Ar);
     }
     if (!bad && Gall) {
         /* dk: each key collects the rows that see it */
@@ -549,19 +559,20 @@ int ora_warmup(const double* QI, const double* w, const double* q, const int64_t
             for (int d = 0; d < 128; ++d) acc[d] = accb[d] = acca[d] = 0.0;
             for (int64_t r = 0; r < n_rows; ++r) {
                 if (pos[r] < s) continue;
-                const double gv = Gall[r * L + s];
+                const double gv = Gall[r * L + s], av = Aall[r * L + s];
                 for (int h = 0; h < H_I; ++h) {
                     const double* qh = QI + (r * H_I + h) * 128;
                     double xa_;
                     const double xv = dot_n(qh, KI + s * 128, 128, &xa_);
                     const double f = c * gv * w[r * H_I + h];
+                    const double fb = fabs(c * w[r * H_I + h]) * av;
                     if (xv > 0.0)
                         for (int d = 0; d < 128; ++d) {
                             acc[d] += f * qh[d];
-                            accb[d] += fabs(f * qh[d]);
+                            accb[d] += fb * fabs(qh[d]);
                         }
                     if (relu_ambiguous(xv, xa_))
-                        for (int d = 0; d < 128; ++d) acca[d] += fabs(f * qh[d]);
+                        for (int d = 0; d < 128; ++d) acca[d] += fb * fabs(qh[d]);
                 }
             }
             for (int d = 0; d < 128; ++d) {
@@ -572,5 +583,6 @@ int ora_warmup(const double* QI, const double* w, const double* q, const int64_t
         }
     }
     free(Gall);
+    free(Aall);
     return bad ? -1 : 0;
 }

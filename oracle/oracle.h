@@ -113,11 +113,12 @@ int ora_local_selected(const int32_t* sel, int64_t T, int k, int64_t q_pos0, int
  * Inputs are real-valued (fp64): QI [n_rows,H_I,128], w [n_rows,H_I], q [n_rows,H,576],
  * pos [n_rows] (each < L), KI [L,128], kv [L,576].  Outputs per row: kl, lse_t [.,H],
  * lse_i, dq [.,H_I,128], dw [.,H_I]; P and G [n_rows, L] (entries s > p are 0) nullable;
- * dk [L,128] nullable.  Magnitude bounds (all nullable): kl_bnd = sum_s P (|log P| +
- * |log Q|); dw_bnd[h] = c sum_s |G| |x_h|; dq_bnd / dk_bnd = the same sums as dq / dk with
- * every term replaced by its absolute value; dq_amb / dk_amb = those absolute sums taken
- * only over the (h, s) whose |x_h[s]| <= 2^-16 sum_d |QI[h,d] KI[s,d]| (where a rounded
- * evaluation of x may take the other side of the ReLU). */
+ * dk [L,128] nullable.  Magnitude bounds (all nullable), with A[s] = Q[s] + P[s] >= |G[s]|
+ * standing for G: kl_bnd = sum_s P (|log P| + |log Q|); dw_bnd[h] = c sum_s A |x_h|;
+ * dq_bnd / dk_bnd = the sums of dq / dk with G replaced by A and every other factor by its
+ * absolute value; dq_amb / dk_amb = those sums taken only over the (h, s) whose
+ * |x_h[s]| <= 2^-16 sum_d |QI[h,d] KI[s,d]| (where a rounded evaluation of x may take the
+ * other side of the ReLU). */
 int ora_warmup(const double* QI, const double* w, const double* q, const int64_t* pos,
                int64_t n_rows, const double* KI, const double* kv, int64_t L, int H_I, int H,
                double c, double sm_scale, double* kl, double* lse_t, double* lse_i, double* dq,

@@ -31,7 +31,8 @@ EXPORTS = ("dsa_status_string", "dsa_version", "dsa_index_scores", "dsa_topk",
            "dsa_prefill_workspace_bytes", "dsa_prefill_chunk_rows", "dsa_decode",
            "dsa_decode_workspace_bytes", "dsa_quantize_fp8", "dsa_decode_append",
            "dsa_window_indices", "dsa_local_selected_indices", "dsa_prefill_varlen",
-           "dsa_prefill_varlen_workspace_bytes")
+           "dsa_prefill_varlen_workspace_bytes", "dsa_attention_lse",
+           "dsa_attention_distribution", "dsa_indexer_warmup", "dsa_indexer_warmup_workspace_bytes")
 
 
 class DSAError(RuntimeError):
@@ -76,10 +77,17 @@ def load(path: str = LIB_PATH):
                                                f32, f32, P, P, P, P, sz, P]
             lib.dsa_prefill_varlen_workspace_bytes.restype = sz
             lib.dsa_prefill_varlen_workspace_bytes.argtypes = [i32, P, P, i32, i32, i32]
+            lib.dsa_attention_lse.argtypes = [P, P, i32, i32, i32, i32, f32, P, P]
+            lib.dsa_attention_distribution.argtypes = [P, P, P, i32, i32, i32, i32, f32, P, i64, P]
+            lib.dsa_indexer_warmup.argtypes = [P, P, P, P, P, P, P, i32, i32, i32, i32, i32, f32,
+                                               f32, P, P, P, P, P, P, P, sz, P]
+            lib.dsa_indexer_warmup_workspace_bytes.restype = sz
+            lib.dsa_indexer_warmup_workspace_bytes.argtypes = [i32, i32, i32, i32]
             for fn in ("dsa_index_scores", "dsa_topk", "dsa_sparse_mla", "dsa_prefill",
                        "dsa_decode", "dsa_quantize_fp8", "dsa_decode_append",
                        "dsa_window_indices", "dsa_local_selected_indices", "dsa_prefill_varlen",
-           "dsa_prefill_varlen_workspace_bytes"):
+           "dsa_prefill_varlen_workspace_bytes", "dsa_attention_lse",
+           "dsa_attention_distribution", "dsa_indexer_warmup", "dsa_indexer_warmup_workspace_bytes"):
                 getattr(lib, fn).restype = i32
             _lib = lib
     return _lib
@@ -278,6 +286,78 @@ def dsa_prefill_varlen(cu_seqlens_q, cu_seqlens_k, q8, q_scale, w, k8, k_scale, 
                                   _ptr(workspace), workspace.numel(), _stream()),
            "dsa_prefill_varlen")
     return out, lse, idx_out
+
+
+def dsa_attention_lse(q, kv, q_pos0: int, sm_scale: float, lse=None):
+    """Per-head log-sum-exp [T, H] of dense causal attention of q [T,H,576] over kv [L,576]."""
+    lib = load()
+    T, H, L = q.shape[0], q.shape[1], kv.shape[0]
+    _req(q, torch.bfloat16, (T, H, 576), "q")
+    _req(kv, torch.bfloat16, (L, 576), "kv")
+    if lse is None:
+        lse = torch.empty((T, H), dtype=torch.float32, device=q.device)
+    _req(lse, torch.float32, (T, H), "lse")
+    _check(lib.dsa_attention_lse(_ptr(q), _ptr(kv), T, L, H, q_pos0, sm_scale, _ptr(lse),
+                                 _stream()), "dsa_attention_lse")
+    return lse
+
+
+def dsa_attention_distribution(q, kv, lse, q_pos0: int, sm_scale: float, P=None):
+    """Head-averaged dense attention distribution P [T, >=L] (entries past each row's
+    position are left as they were)."""
+    lib = load()
+    T, H, L = q.shape[0], q.shape[1], kv.shape[0]
+    _req(q, torch.bfloat16, (T, H, 576), "q")
+    _req(kv, torch.bfloat16, (L, 576), "kv")
+    _req(lse, torch.float32, (T, H), "lse")
+    if P is None:
+        P = torch.zeros((T, L), dtype=torch.float32, device=q.device)
+    if P.dtype != torch.float32 or P.dim() != 2 or P.shape[0] != T or P.stride(1) != 1 \
+            or P.shape[1] < L:
+        raise ValueError("P must be float32 [T, >=L] with unit column stride")
+    _check(lib.dsa_attention_distribution(_ptr(q), _ptr(kv), _ptr(lse), T, L, H, q_pos0,
+                                          sm_scale, _ptr(P), P.stride(0), _stream()),
+           "dsa_attention_distribution")
+    return P
+
+
+def dsa_indexer_warmup_workspace_bytes(T: int, L: int, H_I: int, H: int) -> int:
+    return int(load().dsa_indexer_warmup_workspace_bytes(T, L, H_I, H))
+
+
+def dsa_indexer_warmup(q8, q_scale, w, k8, k_scale, q, kv, q_pos0: int, score_scale: float,
+                       sm_scale: float, out=None, workspace=None):
+    """Indexer warm-up loss and gradient: dict of kl [T], dq [T,H_I,128], dw [T,H_I],
+    dk [L,128], lse_teacher [T,H], lse_index [T] (float32; `out` may supply any of them)."""
+    lib = load()
+    q8, k8 = _u8(q8), _u8(k8)
+    T, H_I = q8.shape[0], q8.shape[1]
+    L, H = k8.shape[0], q.shape[1]
+    _req(q8, torch.uint8, (T, H_I, 128), "q8")
+    _req(q_scale, torch.float32, (T, H_I), "q_scale")
+    _req(w, torch.float32, (T, H_I), "w")
+    _req(k8, torch.uint8, (L, 128), "k8")
+    _req(k_scale, torch.float32, (L,), "k_scale")
+    _req(q, torch.bfloat16, (T, H, 576), "q")
+    _req(kv, torch.bfloat16, (L, 576), "kv")
+    dev = q.device
+    shapes = dict(kl=(T,), dq=(T, H_I, 128), dw=(T, H_I), dk=(L, 128), lse_teacher=(T, H),
+                  lse_index=(T,))
+    res = dict(out or {})
+    for key, shp in shapes.items():
+        if key not in res:
+            res[key] = torch.empty(shp, dtype=torch.float32, device=dev)
+        _req(res[key], torch.float32, shp, key)
+    need = dsa_indexer_warmup_workspace_bytes(T, L, H_I, H)
+    if workspace is None:
+        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=dev)
+    _check(lib.dsa_indexer_warmup(_ptr(q8), _ptr(q_scale), _ptr(w), _ptr(k8), _ptr(k_scale),
+                                  _ptr(q), _ptr(kv), T, L, H_I, H, q_pos0, score_scale, sm_scale,
+                                  _ptr(res["kl"]), _ptr(res["dq"]), _ptr(res["dw"]),
+                                  _ptr(res["dk"]), _ptr(res["lse_teacher"]),
+                                  _ptr(res["lse_index"]), _ptr(workspace), workspace.numel(),
+                                  _stream()), "dsa_indexer_warmup")
+    return res
 
 
 def dsa_decode(seq_start, max_len: int, q8, q_scale, w, k8, k_scale, q, kv, k: int,

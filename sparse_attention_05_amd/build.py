@@ -17,11 +17,12 @@ ROOT = os.path.dirname(HERE)
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libdsa.so")
 OBJDIR = os.path.join(HERE, "_build")
-SOURCES = ["api.cpp", "indexer.hip", "topk.hip", "sparse_mla.hip", "quantize.hip", "index_rules.hip"]
+SOURCES = ["api.cpp", "indexer.hip", "topk.hip", "sparse_mla.hip", "quantize.hip", "index_rules.hip", "warmup.hip"]
 # Per-source flags.  Inputs are NaN-free by contract (finite scales and bf16 values, no NaN
 # fp8 codes), so fmaxf needs no NaN-quieting canonicalisation (the indexer's ReLU, the
 # attention's running max).  Infinities are still honoured (masked logits are -inf).
-EXTRA = {"indexer.hip": ["-fno-honor-nans"], "sparse_mla.hip": ["-fno-honor-nans"]}
+EXTRA = {"indexer.hip": ["-fno-honor-nans"], "sparse_mla.hip": ["-fno-honor-nans"],
+         "warmup.hip": ["-fno-honor-nans"]}
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -99,7 +99,7 @@ const char* dsa_status_string(dsa_status_t status)
     return "DSA_ERR_UNKNOWN";
 }
 
-int dsa_version(void) { return 103; }
+int dsa_version(void) { return 104; }
 
 dsa_status_t dsa_index_scores(const uint8_t* q8, const float* q_scale, const float* w,
                               const uint8_t* k8, const float* k_scale, int T, int L, int H_I,
@@ -292,6 +292,121 @@ dsa_status_t dsa_prefill_varlen(int B, const int64_t* cu_seqlens_q, const int64_
         if (st != DSA_OK) return st;
     }
     return DSA_OK;
+}
+
+// ---- indexer warm-up: query chunks with two fp32 [rows, L] buffers (P then G, and the
+// indexer scores) and the chunk's teacher lse when the caller does not keep it
+struct WarmupWs {
+    int chunk;
+    size_t pg_off, i_off, lse_off, dkp_off, total;
+};
+
+// + the key gradient's per-16-head-group partials [H_I/16][L][128]
+static WarmupWs warmup_ws(int T, int L, int H_I, int H)
+{
+    WarmupWs w;
+    w.chunk = prefill_chunk_rows(T, L);
+    w.pg_off = 0;
+    w.i_off = align_up(size_t(w.chunk) * size_t(L) * 4);
+    w.lse_off = w.i_off + align_up(size_t(w.chunk) * size_t(L) * 4);
+    w.dkp_off = w.lse_off + align_up(size_t(w.chunk) * size_t(H) * 4);
+    w.total = w.dkp_off + align_up(size_t(std::max(H_I / 16, 1)) * size_t(L) * 128 * 4);
+    return w;
+}
+
+static dsa_status_t check_teacher(const uint16_t* q, const uint16_t* kv, int T, int L, int H,
+                                  int q_pos0, float sm_scale)
+{
+    if (dsa_status_t st = check_rows(T, L, q_pos0)) return st;
+    if (T > 0 && (!q || !kv)) return DSA_ERR_INVALID_ARGUMENT;
+    if (H < 1 || !(sm_scale > 0.f)) return DSA_ERR_INVALID_ARGUMENT;
+    if (H > 128) return DSA_ERR_UNSUPPORTED;
+    if (!aligned(q, 16) || !aligned(kv, 16)) return DSA_ERR_INVALID_ARGUMENT;
+    return DSA_OK;
+}
+
+dsa_status_t dsa_attention_lse(const uint16_t* q, const uint16_t* kv, int T, int L, int H,
+                               int q_pos0, float sm_scale, float* lse, dsa_stream_t stream)
+{
+    if (dsa_status_t st = check_teacher(q, kv, T, L, H, q_pos0, sm_scale)) return st;
+    if (T == 0) return DSA_OK;
+    if (!lse) return DSA_ERR_INVALID_ARGUMENT;
+    return from_hip(dsa::launch_attention_lse(q, kv, T, H, q_pos0, sm_scale, lse, as_hip(stream)));
+}
+
+dsa_status_t dsa_attention_distribution(const uint16_t* q, const uint16_t* kv, const float* lse,
+                                        int T, int L, int H, int q_pos0, float sm_scale,
+                                        float* P, int64_t ld, dsa_stream_t stream)
+{
+    if (dsa_status_t st = check_teacher(q, kv, T, L, H, q_pos0, sm_scale)) return st;
+    if (ld < L) return DSA_ERR_INVALID_ARGUMENT;
+    if ((int64_t)T * ld > kMaxElems) return DSA_ERR_UNSUPPORTED;
+    if (T == 0) return DSA_OK;
+    if (!lse || !P) return DSA_ERR_INVALID_ARGUMENT;
+    return from_hip(dsa::launch_attention_dist(q, kv, lse, T, H, q_pos0, sm_scale, P, ld,
+                                               as_hip(stream)));
+}
+
+size_t dsa_indexer_warmup_workspace_bytes(int T, int L, int H_I, int H)
+{
+    if (T <= 0 || L <= 0 || H < 1 || H_I < 1) return 0;
+    return warmup_ws(T, L, H_I, H).total;
+}
+
+dsa_status_t dsa_indexer_warmup(const uint8_t* q8, const float* q_scale, const float* w,
+                                const uint8_t* k8, const float* k_scale, const uint16_t* q,
+                                const uint16_t* kv, int T, int L, int H_I, int H, int q_pos0,
+                                float score_scale, float sm_scale, float* kl, float* dq,
+                                float* dw, float* dk, float* lse_teacher, float* lse_index,
+                                void* workspace, size_t workspace_bytes, dsa_stream_t stream)
+{
+    if (dsa_status_t st = check_teacher(q, kv, T, L, H, q_pos0, sm_scale)) return st;
+    if (!(score_scale > 0.f)) return DSA_ERR_INVALID_ARGUMENT;
+    if (!dsa::warmup_supports(H_I, H)) return DSA_ERR_UNSUPPORTED;
+    if ((int64_t)T * L > kMaxElems) return DSA_ERR_UNSUPPORTED;
+    if (!dk) return DSA_ERR_INVALID_ARGUMENT;
+    if (T > 0 && (!q8 || !q_scale || !w || !k8 || !k_scale || !kl || !dq || !dw))
+        return DSA_ERR_INVALID_ARGUMENT;
+    if (!aligned(q8, 16) || !aligned(k8, 16) || !aligned(dq, 16) || !aligned(dk, 16))
+        return DSA_ERR_INVALID_ARGUMENT;
+    hipStream_t s = as_hip(stream);
+    if (T == 0)                                       // no rows: the key gradient is zero
+        return from_hip(dsa::launch_zero(dk, (int64_t)L * 128, s));
+    const WarmupWs ws = warmup_ws(T, L, H_I, H);
+    if (!workspace || workspace_bytes < ws.total) return DSA_ERR_WORKSPACE_TOO_SMALL;
+    if (!aligned(workspace, kAlign)) return DSA_ERR_INVALID_ARGUMENT;
+
+    uint8_t* base = static_cast<uint8_t*>(workspace);
+    float* pg = reinterpret_cast<float*>(base + ws.pg_off);
+    float* sc = reinterpret_cast<float*>(base + ws.i_off);
+    float* lse_ws = reinterpret_cast<float*>(base + ws.lse_off);
+    float* dkp = reinterpret_cast<float*>(base + ws.dkp_off);
+    const int ngroups = H_I / 16;
+    hipError_t e = dsa::launch_zero(dkp, (int64_t)ngroups * L * 128, s);
+    for (int r0 = 0; r0 < T && e == hipSuccess; r0 += ws.chunk) {
+        const int rows = std::min(ws.chunk, T - r0);
+        const int qp = q_pos0 + r0;
+        const uint16_t* qc = q + (int64_t)r0 * H * 576;
+        float* lt = lse_teacher ? lse_teacher + (int64_t)r0 * H : lse_ws;
+        const int64_t o = (int64_t)r0 * H_I;
+        e = dsa::launch_attention_lse(qc, kv, rows, H, qp, sm_scale, lt, s);
+        if (e == hipSuccess)
+            e = dsa::launch_attention_dist(qc, kv, lt, rows, H, qp, sm_scale, pg, L, s);
+        if (e == hipSuccess)
+            e = dsa::launch_indexer_prefill(q8 + o * 128, q_scale + o, w + o, k8, k_scale, rows, L,
+                                            H_I, qp, score_scale, sc, L, s);
+        if (e == hipSuccess)
+            e = dsa::launch_warmup_rows(sc, pg, L, rows, qp, kl + r0,
+                                        lse_index ? lse_index + r0 : nullptr, s);
+        if (e == hipSuccess)
+            e = dsa::launch_warmup_dq(q8 + o * 128, q_scale + o, w + o, k8, k_scale, pg, L, rows,
+                                      H_I, qp, score_scale, dq + o * 128, dw + o, s);
+        if (e == hipSuccess)
+            e = dsa::launch_warmup_dk(q8 + o * 128, q_scale + o, w + o, k8, pg, L, rows, H_I, qp,
+                                      score_scale, L, dkp, s);
+    }
+    if (e == hipSuccess) e = dsa::launch_warmup_dk_reduce(dkp, ngroups, (int64_t)L * 128, dk, s);
+    return from_hip(e);
 }
 
 size_t dsa_decode_workspace_bytes(int B, int max_len, int64_t total_tokens, int H_I, int H,

@@ -67,4 +67,28 @@ hipError_t launch_window_indices(int T, int q_pos0, int W, int32_t* idx, hipStre
 hipError_t launch_local_selected(const int32_t* sel, int T, int k, int q_pos0, int W,
                                  int32_t* out, hipStream_t stream);
 
+// ---- indexer warm-up (KL to the dense attention distribution) --------------------------
+bool warmup_supports(int H_I, int H);
+// lse [T,H] of dense causal attention of q [T,H,576] over kv rows 0..q_pos0+t.
+hipError_t launch_attention_lse(const uint16_t* q, const uint16_t* kv, int T, int H, int q_pos0,
+                                float sm_scale, float* lse, hipStream_t stream);
+// P[t, s <= q_pos0 + t] = (1/H) sum_h exp(logit - lse[t,h]); P rows at stride ld.
+hipError_t launch_attention_dist(const uint16_t* q, const uint16_t* kv, const float* lse, int T,
+                                 int H, int q_pos0, float sm_scale, float* P, int64_t ld,
+                                 hipStream_t stream);
+// Per row over s <= q_pos0 + t: kl[t], lse_i[t] (nullable) and G = softmax(I) - P over PG.
+hipError_t launch_warmup_rows(const float* I, float* PG, int64_t ld, int T, int q_pos0,
+                              float* kl, float* lse_i, hipStream_t stream);
+hipError_t launch_warmup_dq(const uint8_t* q8, const float* qs, const float* w, const uint8_t* k8,
+                            const float* ks, const float* G, int64_t ld, int T, int H_I,
+                            int q_pos0, float c, float* dq, float* dw, hipStream_t stream);
+// Adds this call's rows' contribution to the per-16-head-group partials dkp [H_I/16][L][128]
+// (keys 0 .. q_pos0 + T - 1); dk = their sum over groups (launch_warmup_dk_reduce).
+hipError_t launch_warmup_dk(const uint8_t* q8, const float* qs, const float* w, const uint8_t* k8,
+                            const float* G, int64_t ld, int T, int H_I, int q_pos0, float c,
+                            int64_t L, float* dkp, hipStream_t stream);
+hipError_t launch_warmup_dk_reduce(const float* dkp, int ngroups, int64_t n, float* dk,
+                                   hipStream_t stream);
+hipError_t launch_zero(float* p, int64_t n, hipStream_t stream);
+
 }  // namespace dsa

@@ -44,43 +44,6 @@ constexpr float LN2 = 0.6931471805599453f;
 // row sum stays below 2^77 for k <= 8192 and fp32 keeps its relative precision throughout.
 constexpr float OVF_SLACK = 64.f;
 
-typedef short v4s __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) void lds_void_t;
-typedef __attribute__((address_space(3))) v4s lds_v4s_t;
-typedef __attribute__((address_space(1))) void gbl_void_t;
-
-__device__ __forceinline__ u32x2 ds_read_tr(const uint8_t* p)
-{
-    const v4s v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_t*)(p));
-    return __builtin_bit_cast(u32x2, v);
-}
-
-// Direct global->LDS load of 16 bytes per lane: lane l's bytes land at LDS byte address
-// lds_dst + 16 l (lds_dst wave-uniform, passed in M0).  Written as one asm statement because
-// the compiler cannot tell that the LDS reads which follow it (of the other tile buffer) do not
-// touch the bytes in flight, and would otherwise wait for the load before each of them.  The
-// statement has no register results; completion is awaited explicitly (s_waitcnt 0 and a
-// barrier) before the destination buffer is read.
-__device__ __forceinline__ void dma16(const void* src, uint32_t lds_dst)
-{
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-                 :
-                 : "v"(src), "s"(lds_dst)
-                 : "memory", "m0");
-}
-// the same with a wave-uniform 64-bit base in SGPRs and a 32-bit per-lane byte offset
-__device__ __forceinline__ void dma16_s(uint32_t voff, const void* sbase, uint32_t lds_dst)
-{
-    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
-                 :
-                 : "v"(voff), "s"(sbase), "s"(lds_dst)
-                 : "memory", "m0");
-}
-__device__ __forceinline__ uint32_t lds_addr(const void* p)
-{
-    return (uint32_t)(uintptr_t)(const lds_void_t*)p;
-}
-
 // Tile layout.  Latent dims [8c, 8c + 8) of row r (16-byte chunk c < 64) sit at byte
 // row_base(r) + 16 (c ^ lat_x(r)); rope chunk b < 8 (dims 512 + 8b ..) at
 // ROPE_OFF + RROW r + 16 (b ^ rope_x(r)).  lat_x only touches chunk bits 1-3, so for

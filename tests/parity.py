@@ -132,3 +132,59 @@ def check_prefill_rows(d, out, lse, gidx, rows, k, what):
         oo, ol = oracle.sparse_mla(_u16(d["q"][t:t + 1]), kv, gidx[t:t + 1], d["sm_scale"])
         check_mla(bf16_to_f64(out[t:t + 1]), _np(lse[t:t + 1]), oo, ol, "%s row %d" % (what, t))
     return swaps
+
+
+# ---------------------------------------------------------------- indexer warm-up (KL)
+# Teacher logits are exact bf16 products summed in fp32; lse to 1e-4, P to 2e-3 relative.
+# The gradient contractions round e = G * (key scale | w qs) * [x > 0] to bf16 (relative
+# 2^-9) and accumulate in fp32, and G = Q - P itself carries fp32 error relative to Q + P:
+# hence |delta| <= 2^-8 bnd + amb, with bnd the oracle's sum of |terms| with Q + P >= |G| in
+# place of G, and amb the terms whose ReLU decision a rounded x may flip.  dw is accumulated
+# in fp32 from unrounded e: 1e-3 of its bound.  kl: an error dI in the scores moves kl by
+# sum_s G dI (|G| sums to <= 2) and P's relative error by that fraction of kl_bnd.
+WU_LSE_ATOL = 1e-4
+WU_P_RTOL = 2e-3
+WU_GRAD_REL = 2.0 ** -8
+WU_DW_REL = 1e-3
+WU_KL_ATOL, WU_KL_REL = 5e-4, 1e-3
+WU_LSEI_ATOL = 1e-3
+
+
+def check_warmup_rows(g: dict, o: dict, rows_g, what=""):
+    """GPU warm-up outputs (numpy, rows rows_g of them) against the oracle's rows.  Returns
+    the worst error / tolerance ratio of each output."""
+    worst = {}
+    r = np.asarray(rows_g)
+    dl = np.abs(g["lse_teacher"][r] - o["lse_t"])
+    assert dl.max(initial=0) <= WU_LSE_ATOL, "%s: teacher lse off by %.3g" % (what, dl.max())
+    worst["lse_teacher"] = dl.max(initial=0) / WU_LSE_ATOL
+    di = np.abs(g["lse_index"][r] - o["lse_i"])
+    assert di.max(initial=0) <= WU_LSEI_ATOL, "%s: index lse off by %.3g" % (what, di.max())
+    worst["lse_index"] = di.max(initial=0) / WU_LSEI_ATOL
+    dk_ = np.abs(g["kl"][r] - o["kl"])
+    tol = WU_KL_ATOL + WU_KL_REL * o["kl_bnd"]
+    assert (dk_ <= tol).all(), "%s: kl off by %.3g (tol %.3g)" % (what, dk_.max(), tol[np.argmax(dk_)])
+    worst["kl"] = (dk_ / tol).max(initial=0)
+    floor = 1e-7 * max(1.0, o["dq_bnd"].max(initial=0))
+    d = np.abs(g["dq"][r] - o["dq"])
+    tol = WU_GRAD_REL * o["dq_bnd"] + o["dq_amb"] + floor
+    bad = d > tol
+    assert not bad.any(), "%s: %d dq entries out of tolerance, worst %.3g (tol %.3g)" % (
+        what, bad.sum(), d[bad].max(), tol[bad][np.argmax(d[bad])])
+    worst["dq"] = (d / tol).max(initial=0)
+    d = np.abs(g["dw"][r] - o["dw"])
+    tol = WU_DW_REL * o["dw_bnd"] + 1e-9
+    bad = d > tol
+    assert not bad.any(), "%s: %d dw entries out of tolerance, worst %.3g" % (what, bad.sum(), d[bad].max())
+    worst["dw"] = (d / tol).max(initial=0)
+    return worst
+
+
+def check_warmup_dk(g_dk: np.ndarray, o: dict, what=""):
+    floor = 1e-7 * max(1.0, o["dk_bnd"].max(initial=0))
+    d = np.abs(g_dk - o["dk"])
+    tol = WU_GRAD_REL * o["dk_bnd"] + o["dk_amb"] + floor
+    bad = d > tol
+    assert not bad.any(), "%s: %d dk entries out of tolerance, worst %.3g (tol %.3g)" % (
+        what, bad.sum(), d[bad].max(), tol[bad][np.argmax(d[bad])])
+    return (d / tol).max(initial=0)

@@ -35,7 +35,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_status_strings_and_version(lib):
-    assert lib.dsa_version() == 103
+    assert lib.dsa_version() == 104
     for code, name in [(0, b"DSA_OK"), (1, b"DSA_ERR_INVALID_ARGUMENT"),
                        (2, b"DSA_ERR_UNSUPPORTED"), (3, b"DSA_ERR_WORKSPACE_TOO_SMALL"),
                        (4, b"DSA_ERR_HIP")]:
@@ -184,3 +184,38 @@ def test_prefill_varlen_validation_and_workspace(lib):
     assert f(wsb=need - 1) == dsa.DSA_ERR_WORKSPACE_TOO_SMALL
     assert f(ws=ctypes.c_void_p((1 << 20) + 128)) == dsa.DSA_ERR_INVALID_ARGUMENT
     assert f(p=ctypes.c_void_p((1 << 20) + 8)) == dsa.DSA_ERR_INVALID_ARGUMENT  # alignment
+
+
+def test_warmup_validation_and_workspace(lib):
+    need = lib.dsa_indexer_warmup_workspace_bytes(1000, 1000, 64, 16)
+    assert need >= 2 * 1000 * 1000 * 4 + 1000 * 16 * 4
+    assert lib.dsa_indexer_warmup_workspace_bytes(0, 1000, 64, 16) == 0
+
+    def f(T=16, L=16, H_I=64, H=16, q=0, c=0.1, sm=0.05, ws=FAKE, wsb=None, p=FAKE, dk=FAKE):
+        wsb = need if wsb is None else wsb
+        return lib.dsa_indexer_warmup(p, p, p, p, p, p, p, T, L, H_I, H, q, c, sm, p, p, p, dk,
+                                      NULL, NULL, ws, wsb, NULL)
+    assert f(p=NULL) == dsa.DSA_ERR_INVALID_ARGUMENT
+    assert f(dk=NULL) == dsa.DSA_ERR_INVALID_ARGUMENT
+    assert f(q=1) == dsa.DSA_ERR_INVALID_ARGUMENT                 # q_pos0 + T > L
+    assert f(c=0.0) == dsa.DSA_ERR_INVALID_ARGUMENT
+    assert f(sm=float("nan")) == dsa.DSA_ERR_INVALID_ARGUMENT
+    assert f(H_I=8) == dsa.DSA_ERR_UNSUPPORTED                    # warm-up needs H_I >= 16
+    assert f(H=129) == dsa.DSA_ERR_UNSUPPORTED
+    assert f(ws=NULL) == dsa.DSA_ERR_WORKSPACE_TOO_SMALL
+    assert f(wsb=1) == dsa.DSA_ERR_WORKSPACE_TOO_SMALL
+    assert f(ws=ctypes.c_void_p((1 << 20) + 128)) == dsa.DSA_ERR_INVALID_ARGUMENT
+    assert f(p=ctypes.c_void_p((1 << 20) + 8)) == dsa.DSA_ERR_INVALID_ARGUMENT  # alignment
+
+    lse = lambda T=4, L=8, H=8, q=0, sm=0.1, p=FAKE, out=FAKE: lib.dsa_attention_lse(
+        p, p, T, L, H, q, sm, out, NULL)
+    assert lse(p=NULL) == dsa.DSA_ERR_INVALID_ARGUMENT
+    assert lse(out=NULL) == dsa.DSA_ERR_INVALID_ARGUMENT
+    assert lse(q=5) == dsa.DSA_ERR_INVALID_ARGUMENT
+    assert lse(H=0) == dsa.DSA_ERR_INVALID_ARGUMENT
+    assert lse(H=200) == dsa.DSA_ERR_UNSUPPORTED
+    assert lse(T=0, p=NULL, out=NULL) == dsa.DSA_OK
+    dist = lambda ld=8, out=FAKE: lib.dsa_attention_distribution(FAKE, FAKE, FAKE, 4, 8, 8, 0, 0.1,
+                                                                 out, ld, NULL)
+    assert dist(ld=7) == dsa.DSA_ERR_INVALID_ARGUMENT
+    assert dist(out=NULL) == dsa.DSA_ERR_INVALID_ARGUMENT
