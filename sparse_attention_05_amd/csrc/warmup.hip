@@ -19,13 +19,13 @@
 //    MODE 0 keeps each head's running max and sum (-> lse); MODE 1 sums exp(logit - lse) over
 //    the heads of each key (-> P).
 //  * row_kernel: one workgroup per row: lse of the scores, G (over P, in place) and kl.
-//  * dq_kernel: 256 (token, head) rows per workgroup held as fp8 B operands; 64-key tiles
-//    staged in LDS as fp8 (A of D^T) and bf16 (A of dq^T = K^T e^T); e^T = G ks [D > 0] goes
-//    from the D^T accumulators straight into the B operand of the bf16 MFMA (the contraction
-//    takes the keys in the accumulator's order).
-//  * dk_kernel: the mirror image: 256 keys x 16 indexer heads per workgroup, the keys in
-//    registers, 64-row tiles of (token, head) rows streamed; e = G w qs [D > 0]; per-head-group
-//    partial sums accumulated across query chunks, then summed over the groups.
+//  * dq_kernel: 256 (token, head) rows per workgroup (eight waves, two per SIMD) held as fp8
+//    B operands; 64-key tiles staged in LDS as fp8 (A of D^T) and bf16 (A of dq^T = K^T e^T);
+//    e^T = G ks [D > 0] goes from the D^T accumulators straight into the B operand of the bf16
+//    MFMA (the contraction takes the keys in the accumulator's order).
+//  * dk_kernel: the mirror image: 256 keys x 16 indexer heads per workgroup (eight waves), the
+//    keys in registers, 64-row tiles of (token, head) rows streamed; e = G w qs [D > 0];
+//    per-head-group partial sums accumulated across query chunks, then summed over the groups.
 #include "dsa_device.h"
 #include "kernels.h"
 
@@ -337,10 +337,11 @@ __device__ __forceinline__ u32x4 pack_e(const float (&e)[2][4])
     return __builtin_bit_cast(u32x4, b);
 }
 
-// dq / dw.  Workgroup: 4 waves x 64 rows of the T * H_I (token, head) rows (H_I >= 16: a
-// 16-row tile is one token); keys 0 .. p_last in 64-key tiles.  G ks is staged per (token,
-// key), so a lane reads the four consecutive keys of its accumulator rows in one 16-byte read.
-__global__ __launch_bounds__(256) void dq_kernel(const uint8_t* __restrict__ q8,
+// dq / dw.  Workgroup: 8 waves (two per SIMD) x 32 rows of the T * H_I (token, head) rows
+// (H_I >= 16: a 16-row tile is one token); keys 0 .. p_last in 64-key tiles staged once for
+// all eight waves.  G ks is staged per (token, key), so a lane reads the four consecutive keys
+// of its accumulator rows in one 16-byte read.
+__global__ __launch_bounds__(512) void dq_kernel(const uint8_t* __restrict__ q8,
                                                  const float* __restrict__ qs,
                                                  const float* __restrict__ w,
                                                  const uint8_t* __restrict__ k8,
@@ -349,73 +350,65 @@ __global__ __launch_bounds__(256) void dq_kernel(const uint8_t* __restrict__ q8,
                                                  int H_I, int q_pos0, float c,
                                                  float* __restrict__ dq, float* __restrict__ dw)
 {
-    constexpr int TOKS = 16;                           // tokens per workgroup at H_I = 16
+    constexpr int TOKS = 16;
+    constexpr int NJ = 2;
     __shared__ __attribute__((aligned(16))) uint8_t s_k8[2][BK * F8ROW];
     __shared__ __attribute__((aligned(16))) uint8_t s_kb[2][BK * BFROW];
     __shared__ __attribute__((aligned(16))) float s_gk[2][TOKS][BK];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int g = lane >> 4, c16 = lane & 15;
-    const int shift = 31 - __builtin_clz(H_I);         // log2 H_I
-    const int blk = gridDim.x - 1 - blockIdx.x;        // latest rows first
-    const int row0 = blk * 256;                        // first (token, head) row
+    const int shift = 31 - __builtin_clz(H_I);
+    const int blk = gridDim.x - 1 - blockIdx.x;
+    const int row0 = blk * 256;
     const int64_t nrows = (int64_t)T * H_I;
     const int tok0 = row0 >> shift;
     const int ntok = min(256 >> shift, T - tok0);
     const int p_last = q_pos0 + tok0 + ntok - 1;
     const int ntile = p_last / BK + 1;
 
-    // B operands of D^T: row 64 wave + 16 j + c16, bytes [32 g, +32)
-    v8i qb[4];
-    int tokj[4];                                       // token (in block) of column tile j
+    v8i qb[NJ];
+    int tokj[NJ];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int64_t R = row0 + wave * 64 + 16 * j + c16;
+    for (int j = 0; j < NJ; ++j) {
+        const int64_t R = row0 + wave * 32 + 16 * j + c16;
         const u32x4* src = reinterpret_cast<const u32x4*>(q8 + min(R, nrows - 1) * 128 + 32 * g);
         qb[j] = as_i8(src[0], src[1]);
-        tokj[j] = min(((row0 + wave * 64 + 16 * j) >> shift) - tok0, TOKS - 1);
+        tokj[j] = min(((row0 + wave * 32 + 16 * j) >> shift) - tok0, TOKS - 1);
     }
-    v4f acc[4][8];                                     // dq^T: dims 16 n + 4 g + r, column j
+    v4f acc[NJ][8];
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < NJ; ++j)
 #pragma unroll
         for (int n = 0; n < 8; ++n) acc[j][n] = v4f{0.f, 0.f, 0.f, 0.f};
-    float dwp[4] = {0.f, 0.f, 0.f, 0.f};
+    float dwp[NJ] = {0.f, 0.f};
 
-    // staging: 64 keys x 8 parts of 16 bytes, two per thread (keys tid/8 and 32 + tid/8,
-    // part tid%8); G ks: 16 tokens x 64 keys, four per thread, all at key tid%64
+    // staging: 64 keys x 8 parts of 16 bytes, one per thread (key tid/8, part tid%8); G ks:
+    // 16 tokens x 64 keys, two per thread, both at key tid%64
     const int sk = tid >> 3, sp = tid & 7;
-    u32x4 pre[2];
-    float pre_g[4];
+    u32x4 pre;
+    float pre_g[2];
     auto gload = [&](int tile) {
         const int kb = tile * BK;
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int s = min(kb + sk + 32 * i, p_last);
-            pre[i] = *reinterpret_cast<const u32x4*>(k8 + (int64_t)s * 128 + 16 * sp);
-        }
+        pre = *reinterpret_cast<const u32x4*>(k8 + (int64_t)min(kb + sk, p_last) * 128 + 16 * sp);
         const int s = kb + (tid & 63);
         const float ksv = ks[min(s, p_last)];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int tk = (tid >> 6) + 4 * i;
+        for (int i = 0; i < 2; ++i) {
+            const int tk = (tid >> 6) + 8 * i;
             pre_g[i] = (tk < ntok && s <= q_pos0 + tok0 + tk)
                            ? G[(int64_t)(tok0 + tk) * ld + s] * ksv : 0.f;
         }
     };
     auto lstore = [&](int buf) {
+        *reinterpret_cast<u32x4*>(&s_k8[buf][sk * F8ROW + 16 * sp]) = pre;
+        uint32_t o[8];
+        fp8x16_to_bf16(pre, o);
+        u32x4* d = reinterpret_cast<u32x4*>(&s_kb[buf][sk * BFROW + 32 * sp]);
+        d[0] = u32x4{o[0], o[1], o[2], o[3]};
+        d[1] = u32x4{o[4], o[5], o[6], o[7]};
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int key = sk + 32 * i;
-            *reinterpret_cast<u32x4*>(&s_k8[buf][key * F8ROW + 16 * sp]) = pre[i];
-            uint32_t o[8];
-            fp8x16_to_bf16(pre[i], o);
-            u32x4* d = reinterpret_cast<u32x4*>(&s_kb[buf][key * BFROW + 32 * sp]);
-            d[0] = u32x4{o[0], o[1], o[2], o[3]};
-            d[1] = u32x4{o[4], o[5], o[6], o[7]};
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) s_gk[buf][(tid >> 6) + 4 * i][tid & 63] = pre_g[i];
+        for (int i = 0; i < 2; ++i) s_gk[buf][(tid >> 6) + 8 * i][tid & 63] = pre_g[i];
     };
 
     gload(0);
@@ -427,20 +420,18 @@ __global__ __launch_bounds__(256) void dq_kernel(const uint8_t* __restrict__ q8,
         if (tile + 1 < ntile) gload(tile + 1);
 #pragma unroll
         for (int pr = 0; pr < 2; ++pr) {
-            // D^T[key 32 pr + 16 kt + 4 g + r][column 16 j + c16]
-            v4f D[2][4];
+            v4f D[2][NJ];
 #pragma unroll
             for (int kt = 0; kt < 2; ++kt) {
                 const u32x4* a = reinterpret_cast<const u32x4*>(
                     &s_k8[buf][(32 * pr + 16 * kt + c16) * F8ROW + 32 * g]);
                 const v8i ka = as_i8(a[0], a[1]);
 #pragma unroll
-                for (int j = 0; j < 4; ++j) D[kt][j] = mfma_f8(ka, qb[j], v4f{0.f, 0.f, 0.f, 0.f});
+                for (int j = 0; j < NJ; ++j) D[kt][j] = mfma_f8(ka, qb[j], v4f{0.f, 0.f, 0.f, 0.f});
             }
-            // e^T = G ks [D > 0] -> B operand (keys 32 pr + 16 kt + 4 g + r)
-            u32x4 eb[4];
+            u32x4 eb[NJ];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
+            for (int j = 0; j < NJ; ++j) {
                 float e[2][4];
 #pragma unroll
                 for (int kt = 0; kt < 2; ++kt) {
@@ -459,7 +450,7 @@ __global__ __launch_bounds__(256) void dq_kernel(const uint8_t* __restrict__ q8,
             for (int n = 0; n < 8; ++n) {
                 const u32x4 ka = tr_operand(s_kb[buf], pr, n, g, c16);
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
+                for (int j = 0; j < NJ; ++j)
                     acc[j][n] = mfma_bf16(as_bf16x8(ka), as_bf16x8(eb[j]), acc[j][n]);
             }
         }
@@ -467,10 +458,9 @@ __global__ __launch_bounds__(256) void dq_kernel(const uint8_t* __restrict__ q8,
         __syncthreads();
     }
 
-    // epilogue: dq[row, 16 n + 4 g + r] = c w acc; dw[row] = c qs sum
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int64_t R = row0 + wave * 64 + 16 * j + c16;
+    for (int j = 0; j < NJ; ++j) {
+        const int64_t R = row0 + wave * 32 + 16 * j + c16;
         float d = dwp[j] + shfl_xor_f(dwp[j], 16);
         d += shfl_xor_f(d, 32);
         if (R >= nrows) continue;
@@ -483,12 +473,12 @@ __global__ __launch_bounds__(256) void dq_kernel(const uint8_t* __restrict__ q8,
     }
 }
 
-// dk.  Grid: x = blocks of 256 keys, y = groups of 16 indexer heads.  Each wave holds 64
-// keys as fp8 B operands; the (token, head) rows of the group for the tokens that see the
-// block are streamed in 64-row tiles (4 tokens x 16 heads).  Each (group, key) is owned by one
-// workgroup per launch, which adds its sum into dkp[group] (accumulated across query chunks;
-// dk = the sum over groups, formed once at the end).
-__global__ __launch_bounds__(256) void dk_kernel(const uint8_t* __restrict__ q8,
+// dk.  Grid: x = blocks of 256 keys, y = groups of 16 indexer heads.  Eight waves (two per
+// SIMD) hold 32 keys each as fp8 B operands; the (token, head) rows of the group for the tokens
+// that see the block are streamed in 64-row tiles (4 tokens x 16 heads).  Each (group, key) is
+// owned by one workgroup per launch, which adds its sum into dkp[group] (accumulated across
+// query chunks; dk = the sum over groups, formed once at the end).
+__global__ __launch_bounds__(512) void dk_kernel(const uint8_t* __restrict__ q8,
                                                  const float* __restrict__ qs,
                                                  const float* __restrict__ w,
                                                  const uint8_t* __restrict__ k8,
@@ -496,7 +486,8 @@ __global__ __launch_bounds__(256) void dk_kernel(const uint8_t* __restrict__ q8,
                                                  int H_I, int q_pos0, float c, int64_t L,
                                                  float* __restrict__ dkp)
 {
-    constexpr int TPT = 4;                             // tokens per row tile
+    constexpr int TPT = 4;
+    constexpr int NK = 2;
     __shared__ __attribute__((aligned(16))) uint8_t s_q8[2][BK * F8ROW];
     __shared__ __attribute__((aligned(16))) uint8_t s_qb[2][BK * BFROW];
     __shared__ __attribute__((aligned(16))) float s_wq[2][BK];
@@ -504,70 +495,66 @@ __global__ __launch_bounds__(256) void dk_kernel(const uint8_t* __restrict__ q8,
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int g = lane >> 4, c16 = lane & 15;
-    const int s0 = blockIdx.x * 256;                   // first key of the workgroup
-    const int hg = blockIdx.y;                         // heads [16 hg, 16 hg + 16)
-    const int sw = s0 + wave * 64;                     // first key of this wave
+    const int s0 = blockIdx.x * 256;
+    const int hg = blockIdx.y;
+    const int sw = s0 + wave * 32;
     const int64_t nrows = (int64_t)T * H_I;
-    const int tmin = max(0, s0 - q_pos0);              // first token that sees key s0
+    const int tmin = max(0, s0 - q_pos0);
     if (tmin >= T) return;
     const int ntile = (T - tmin + TPT - 1) / TPT;
 
-    // B operands of D: key sw + 16 jk + c16, bytes [32 g, +32); keys past the last visible
-    // one (possibly past L) are never unmasked and read the last visible key instead
-    v8i kb8[4];
+    v8i kb8[NK];
 #pragma unroll
-    for (int jk = 0; jk < 4; ++jk) {
+    for (int jk = 0; jk < NK; ++jk) {
         const int s = min(sw + 16 * jk + c16, q_pos0 + T - 1);
         const u32x4* src = reinterpret_cast<const u32x4*>(k8 + (int64_t)s * 128 + 32 * g);
         kb8[jk] = as_i8(src[0], src[1]);
     }
-    v4f acc[4][8];                                     // dk^T: dims 16 n + 4 g + r, key jk
+    v4f acc[NK][8];
 #pragma unroll
-    for (int jk = 0; jk < 4; ++jk)
+    for (int jk = 0; jk < NK; ++jk)
 #pragma unroll
         for (int n = 0; n < 8; ++n) acc[jk][n] = v4f{0.f, 0.f, 0.f, 0.f};
 
-    // staging: tile row rl = 16 tk + hl is (token tmin + 4 tile + tk, head 16 hg + hl)
-    const int sr = tid >> 3, sp = tid & 7;             // rows sr, sr + 32; 16-byte part sp
+    // staging: tile row rl = 16 tk + hl is (token tmin + 4 tile + tk, head 16 hg + hl); one
+    // 16-byte part per thread (row tid/8, part tid%8)
+    const int sr = tid >> 3, sp = tid & 7;
     auto row_of = [&](int tile, int rl, bool& ok) -> int64_t {
         const int t = tmin + TPT * tile + (rl >> 4);
         ok = t < T;
         return ok ? (int64_t)t * H_I + 16 * hg + (rl & 15) : nrows - 1;
     };
-    u32x4 pre[2];
-    float pre_wq = 0.f, pre_g[4];
+    u32x4 pre;
+    float pre_wq = 0.f, pre_g[2];
     auto gload = [&](int tile) {
         bool ok;
+        const int64_t R = row_of(tile, sr, ok);
+        pre = *reinterpret_cast<const u32x4*>(q8 + R * 128 + 16 * sp);
+        if (tid < BK) {
+            const int64_t R2 = row_of(tile, tid, ok);
+            pre_wq = ok ? w[R2] * qs[R2] : 0.f;
+        }
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
-            const int64_t R = row_of(tile, sr + 32 * i, ok);
-            pre[i] = *reinterpret_cast<const u32x4*>(q8 + R * 128 + 16 * sp);
-        }
-        if (tid < BK) {
-            const int64_t R = row_of(tile, tid, ok);
-            pre_wq = ok ? w[R] * qs[R] : 0.f;
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int t = tmin + TPT * tile + i;
-            const int key = s0 + tid;
+            const int e = tid + 512 * i;
+            const int t = tmin + TPT * tile + (e >> 8);
+            const int key = s0 + (e & 255);
             pre_g[i] = (t < T && key <= q_pos0 + t) ? G[(int64_t)t * ld + key] : 0.f;
         }
     };
     auto lstore = [&](int buf) {
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int r = sr + 32 * i;
-            *reinterpret_cast<u32x4*>(&s_q8[buf][r * F8ROW + 16 * sp]) = pre[i];
-            uint32_t o[8];
-            fp8x16_to_bf16(pre[i], o);
-            u32x4* d = reinterpret_cast<u32x4*>(&s_qb[buf][r * BFROW + 32 * sp]);
-            d[0] = u32x4{o[0], o[1], o[2], o[3]};
-            d[1] = u32x4{o[4], o[5], o[6], o[7]};
-        }
+        *reinterpret_cast<u32x4*>(&s_q8[buf][sr * F8ROW + 16 * sp]) = pre;
+        uint32_t o[8];
+        fp8x16_to_bf16(pre, o);
+        u32x4* d = reinterpret_cast<u32x4*>(&s_qb[buf][sr * BFROW + 32 * sp]);
+        d[0] = u32x4{o[0], o[1], o[2], o[3]};
+        d[1] = u32x4{o[4], o[5], o[6], o[7]};
         if (tid < BK) s_wq[buf][tid] = pre_wq;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) s_g[buf][i][tid] = pre_g[i];
+        for (int i = 0; i < 2; ++i) {
+            const int e = tid + 512 * i;
+            s_g[buf][e >> 8][e & 255] = pre_g[i];
+        }
     };
 
     gload(0);
@@ -579,29 +566,26 @@ __global__ __launch_bounds__(256) void dk_kernel(const uint8_t* __restrict__ q8,
         if (tile + 1 < ntile) gload(tile + 1);
 #pragma unroll
         for (int pr = 0; pr < 2; ++pr) {
-            // D[row 32 pr + 16 jt + 4 g + r][key 16 jk + c16]; rows 32 pr + 16 jt are token
-            // 2 pr + jt of the tile
-            v4f D[2][4];
+            v4f D[2][NK];
 #pragma unroll
             for (int jt = 0; jt < 2; ++jt) {
                 const u32x4* a = reinterpret_cast<const u32x4*>(
                     &s_q8[buf][(32 * pr + 16 * jt + c16) * F8ROW + 32 * g]);
                 const v8i qa = as_i8(a[0], a[1]);
 #pragma unroll
-                for (int jk = 0; jk < 4; ++jk) D[jt][jk] = mfma_f8(qa, kb8[jk], v4f{0.f, 0.f, 0.f, 0.f});
+                for (int jk = 0; jk < NK; ++jk) D[jt][jk] = mfma_f8(qa, kb8[jk], v4f{0.f, 0.f, 0.f, 0.f});
             }
             v4f wq[2];
 #pragma unroll
             for (int jt = 0; jt < 2; ++jt)
                 wq[jt] = *reinterpret_cast<const v4f*>(&s_wq[buf][32 * pr + 16 * jt + 4 * g]);
-            // e = G w qs [D > 0] -> B operand (rows 32 pr + 16 jt + 4 g + r)
-            u32x4 eb[4];
+            u32x4 eb[NK];
 #pragma unroll
-            for (int jk = 0; jk < 4; ++jk) {
+            for (int jk = 0; jk < NK; ++jk) {
                 float e[2][4];
 #pragma unroll
                 for (int jt = 0; jt < 2; ++jt) {
-                    const float gv = s_g[buf][2 * pr + jt][wave * 64 + 16 * jk + c16];
+                    const float gv = s_g[buf][2 * pr + jt][wave * 32 + 16 * jk + c16];
 #pragma unroll
                     for (int r = 0; r < 4; ++r)
                         e[jt][r] = D[jt][jk][r] > 0.f ? gv * wq[jt][r] : 0.f;
@@ -612,7 +596,7 @@ __global__ __launch_bounds__(256) void dk_kernel(const uint8_t* __restrict__ q8,
             for (int n = 0; n < 8; ++n) {
                 const u32x4 qa = tr_operand(s_qb[buf], pr, n, g, c16);
 #pragma unroll
-                for (int jk = 0; jk < 4; ++jk)
+                for (int jk = 0; jk < NK; ++jk)
                     acc[jk][n] = mfma_bf16(as_bf16x8(qa), as_bf16x8(eb[jk]), acc[jk][n]);
             }
         }
@@ -620,10 +604,9 @@ __global__ __launch_bounds__(256) void dk_kernel(const uint8_t* __restrict__ q8,
         __syncthreads();
     }
 
-    // epilogue: dkp[group, key, 16 n + 4 g + r] += c acc
     float* part = dkp + (int64_t)hg * L * 128;
 #pragma unroll
-    for (int jk = 0; jk < 4; ++jk) {
+    for (int jk = 0; jk < NK; ++jk) {
         const int s = sw + 16 * jk + c16;
         if (s > q_pos0 + T - 1) continue;
         float* o = part + (int64_t)s * 128;
@@ -694,7 +677,7 @@ hipError_t launch_warmup_dq(const uint8_t* q8, const float* qs, const float* w, 
 {
     if (T <= 0) return hipSuccess;
     const int64_t rows = (int64_t)T * H_I;
-    hipLaunchKernelGGL(dq_kernel, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, stream, q8,
+    hipLaunchKernelGGL(dq_kernel, dim3((unsigned)((rows + 255) / 256)), dim3(512), 0, stream, q8,
                        qs, w, k8, ks, G, ld, T, H_I, q_pos0, c, dq, dw);
     return hipGetLastError();
 }
@@ -705,7 +688,7 @@ hipError_t launch_warmup_dk(const uint8_t* q8, const float* qs, const float* w, 
 {
     if (T <= 0) return hipSuccess;
     const int keys = q_pos0 + T;                       // keys any row sees
-    hipLaunchKernelGGL(dk_kernel, dim3((keys + 255) / 256, H_I / 16), dim3(256), 0, stream, q8,
+    hipLaunchKernelGGL(dk_kernel, dim3((keys + 255) / 256, H_I / 16), dim3(512), 0, stream, q8,
                        qs, w, k8, G, ld, T, H_I, q_pos0, c, L, dkp);
     return hipGetLastError();
 }
