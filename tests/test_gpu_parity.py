@@ -12,7 +12,7 @@ import torch
 
 import oracle
 from parity import (check_indices_near_ties, check_mla, check_prefill_rows, check_scores,
-                    check_topk_exact, bf16_to_f64, to_device)
+                    check_topk_exact, bf16_to_f64, oracle_prefill_rows, to_device)
 from synth import WORKLOADS, DecodeCfg, PrefillCfg, host_arrays, make_decode, make_prefill
 
 pytestmark = pytest.mark.gpu
