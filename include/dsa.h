@@ -172,7 +172,8 @@ dsa_status_t dsa_attention_distribution(const uint16_t* q, const uint16_t* kv, c
  * i.e. the gradients with respect to QI, KI and w (the fp8 rounding is treated as the
  * identity); dk rows no query sees are 0.  lse_teacher [T,H] and lse_index [T] (both
  * nullable) receive the teacher lse and log sum_s exp I.  The gradient contractions run on
- * bf16 MFMA (G rounded to bf16, fp32 accumulation).  H_I in {16,32,64,128}, H <= 128.
+ * bf16 MFMA (G rounded to bf16, fp32 accumulation).  H_I in {16,32,64,128}, H <= 128,
+ * T * H_I < 2^31 (DSA_ERR_UNSUPPORTED otherwise); T = 0 only zeroes dk.
  * Other arguments as dsa_prefill; workspace at least dsa_indexer_warmup_workspace_bytes
  * bytes, 256-byte aligned. */
 dsa_status_t dsa_indexer_warmup(const uint8_t* q8, const float* q_scale, const float* w,

@@ -363,7 +363,9 @@ dsa_status_t dsa_indexer_warmup(const uint8_t* q8, const float* q_scale, const f
     if (dsa_status_t st = check_teacher(q, kv, T, L, H, q_pos0, sm_scale)) return st;
     if (!(score_scale > 0.f)) return DSA_ERR_INVALID_ARGUMENT;
     if (!dsa::warmup_supports(H_I, H)) return DSA_ERR_UNSUPPORTED;
-    if ((int64_t)T * L > kMaxElems) return DSA_ERR_UNSUPPORTED;
+    // (token, head) rows are indexed with 32-bit integers inside the gradient kernels
+    if ((int64_t)T * L > kMaxElems || (int64_t)T * H_I >= (int64_t(1) << 31))
+        return DSA_ERR_UNSUPPORTED;
     if (!dk) return DSA_ERR_INVALID_ARGUMENT;
     if (T > 0 && (!q8 || !q_scale || !w || !k8 || !k_scale || !kl || !dq || !dw))
         return DSA_ERR_INVALID_ARGUMENT;

@@ -202,6 +202,7 @@ def test_warmup_validation_and_workspace(lib):
     assert f(sm=float("nan")) == dsa.DSA_ERR_INVALID_ARGUMENT
     assert f(H_I=8) == dsa.DSA_ERR_UNSUPPORTED                    # warm-up needs H_I >= 16
     assert f(H=129) == dsa.DSA_ERR_UNSUPPORTED
+    assert f(T=1 << 25, L=1 << 25, H_I=64) == dsa.DSA_ERR_UNSUPPORTED  # T * H_I >= 2^31
     assert f(ws=NULL) == dsa.DSA_ERR_WORKSPACE_TOO_SMALL
     assert f(wsb=1) == dsa.DSA_ERR_WORKSPACE_TOO_SMALL
     assert f(ws=ctypes.c_void_p((1 << 20) + 128)) == dsa.DSA_ERR_INVALID_ARGUMENT

@@ -84,6 +84,7 @@ def test_attention_lse_and_distribution(dsa, L, T, q_pos0, H):
     (257, 257, 0, 128, 32, 3),      # half-token row tiles
     (129, 65, 64, 32, 4, 4),
     (1100, 1100, 0, 64, 16, 5),     # many key tiles and five key blocks
+    (400, 100, 50, 64, 8, 7),       # keys 150..399 seen by no row: zero gradient
 ])
 def test_warmup_every_row_and_key(dsa, L, T, q_pos0, H_I, H, seed):
     d = _case(L, T, q_pos0, H_I, H, seed)
@@ -93,6 +94,17 @@ def test_warmup_every_row_and_key(dsa, L, T, q_pos0, H_I, H, seed):
     worst = check_warmup_rows(g, o, np.arange(T), what)
     worst["dk"] = check_warmup_dk(g["dk"], o, what)
     print(what, "worst error / tolerance:", {k: round(float(v), 4) for k, v in worst.items()})
+
+
+def test_warmup_without_query_rows_zeroes_the_key_gradient(dsa):
+    d = _case(300, 300, 0, 64, 8, seed=8)
+    dk = torch.full((300, 128), 7.0, dtype=torch.float32, device="cuda")
+    res = dsa.dsa_indexer_warmup(d["q8"][:0], d["qs"][:0], d["w"][:0], d["k8"], d["ks"],
+                                 d["q"][:0], d["kv"], 0, d["score_scale"], d["sm_scale"],
+                                 out=dict(dk=dk))
+    torch.cuda.synchronize()
+    assert res["kl"].shape == (0,) and res["dq"].shape == (0, 64, 128)
+    assert (dk == 0).all()
 
 
 def test_warmup_bitwise_repeatable(dsa):
