@@ -52,3 +52,29 @@ def test_window_attention_matches_oracle(dsa, W):
     oo, ol = oracle.sparse_mla(h["q"], h["kv"], oracle.window_indices(cfg.T, cfg.q_pos0, W),
                                cfg.sm_scale)
     check_mla(bf16_to_f64(out), _np(lse), oo, ol, "window %d" % W)
+
+
+def test_window_attention_128k_sampled_rows(dsa):
+    """Window 2048 over the 128K workload in the benchmark's launch configuration (1024-row
+    chunks: the window lists, then the sparse MLA on them); sampled rows of the launched chunks
+    against the oracle, indices exactly."""
+    from synth import WORKLOADS
+    cfg = WORKLOADS["prefill-L131072-k2048"]
+    W, chunk = 2048, dsa.dsa_prefill_chunk_rows(cfg.L, cfg.L)
+    d = make_prefill(cfg, device="cuda")
+    kv = _u16(d["kv"])
+    rows = np.array([0, 1, W - 2, W - 1, W, W + 1, 65535, 65536, 100001, cfg.L - 1])
+    idx = torch.empty((chunk, W), dtype=torch.int32, device="cuda")
+    for c in sorted(set((rows // chunk).tolist())):
+        r0 = c * chunk
+        r1 = min(cfg.L, r0 + chunk)
+        ic = idx[:r1 - r0]
+        dsa.dsa_window_indices(r1 - r0, cfg.L, r0, W, idx=ic)
+        out, lse = dsa.dsa_sparse_mla(d["q"][r0:r1], d["kv"], ic, cfg.sm_scale)
+        torch.cuda.synchronize()
+        for t in rows[(rows >= r0) & (rows < r1)]:
+            i = int(t) - r0
+            want = oracle.window_indices(1, int(t), W)
+            assert np.array_equal(_np(ic[i:i + 1]), want), "window row %d" % t
+            oo, ol = oracle.sparse_mla(_u16(d["q"][int(t):int(t) + 1]), kv, want, cfg.sm_scale)
+            check_mla(bf16_to_f64(out[i:i + 1]), _np(lse[i:i + 1]), oo, ol, "window row %d" % t)
