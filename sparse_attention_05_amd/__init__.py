@@ -83,11 +83,12 @@ def load(path: str = LIB_PATH):
                                                f32, P, P, P, P, P, P, P, sz, P]
             lib.dsa_indexer_warmup_workspace_bytes.restype = sz
             lib.dsa_indexer_warmup_workspace_bytes.argtypes = [i32, i32, i32, i32]
+            # entry points that return a dsa_status_t (the *_workspace_bytes queries return
+            # size_t and are set above)
             for fn in ("dsa_index_scores", "dsa_topk", "dsa_sparse_mla", "dsa_prefill",
                        "dsa_decode", "dsa_quantize_fp8", "dsa_decode_append",
                        "dsa_window_indices", "dsa_local_selected_indices", "dsa_prefill_varlen",
-           "dsa_prefill_varlen_workspace_bytes", "dsa_attention_lse",
-           "dsa_attention_distribution", "dsa_indexer_warmup", "dsa_indexer_warmup_workspace_bytes"):
+                       "dsa_attention_lse", "dsa_attention_distribution", "dsa_indexer_warmup"):
                 getattr(lib, fn).restype = i32
             _lib = lib
     return _lib

@@ -220,3 +220,17 @@ def test_warmup_validation_and_workspace(lib):
                                                                  out, ld, NULL)
     assert dist(ld=7) == dsa.DSA_ERR_INVALID_ARGUMENT
     assert dist(out=NULL) == dsa.DSA_ERR_INVALID_ARGUMENT
+
+
+def test_size_queries_return_full_size_t(lib):
+    """Workspace queries are size_t: sizes past 2^32 come back whole through the binding."""
+    import sparse_attention_05_amd as m
+    for fn in [n for n in m.EXPORTS if n.endswith("_workspace_bytes")]:
+        assert getattr(lib, fn).restype is ctypes.c_size_t, fn
+    # 3 sequences of 1M tokens with a chunk of queries each: the largest prefill workspace
+    cq = (ctypes.c_int64 * 4)(0, 1 << 20, 2 << 20, 3 << 20)
+    ck = (ctypes.c_int64 * 4)(0, 1 << 20, 2 << 20, 3 << 20)
+    v = lib.dsa_prefill_varlen_workspace_bytes(3, cq, ck, 64, 128, 2048)
+    assert v == lib.dsa_prefill_workspace_bytes(1 << 20, 1 << 20, 64, 128, 2048) > 0
+    w = lib.dsa_indexer_warmup_workspace_bytes(1 << 20, 1 << 20, 128, 128)
+    assert w > (1 << 32)      # the key-gradient partials alone: 8 x 2^20 x 512 bytes
