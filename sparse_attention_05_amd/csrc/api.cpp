@@ -37,7 +37,7 @@ dsa_status_t check_rows(int T, int L, int q_pos0)
 }
 
 // ---- prefill chunking: rows per chunk so one chunk's fp32 score rows stay bounded
-constexpr int64_t kChunkScoreBytes = int64_t(512) << 20;
+constexpr int64_t kChunkScoreBytes = int64_t(2048) << 20;   // 2 GiB
 
 int prefill_chunk_rows(int T, int L)
 {

@@ -88,7 +88,7 @@ def test_prefill_validation_and_workspace(lib):
     need = lib.dsa_prefill_workspace_bytes(1024, 1024, 4, 8, 256)
     assert need > 1024 * 1024 * 4
     assert lib.dsa_prefill_workspace_bytes(0, 1024, 4, 8, 256) == 0
-    assert lib.dsa_prefill_chunk_rows(131072, 131072) == 1024
+    assert lib.dsa_prefill_chunk_rows(131072, 131072) == 4096
     assert lib.dsa_prefill_chunk_rows(2048, 2048) == 2048
     assert lib.dsa_prefill_chunk_rows(0, 10) == 0
 

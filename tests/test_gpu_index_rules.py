@@ -55,8 +55,8 @@ def test_window_attention_matches_oracle(dsa, W):
 
 
 def test_window_attention_128k_sampled_rows(dsa):
-    """Window 2048 over the 128K workload in the benchmark's launch configuration (1024-row
-    chunks: the window lists, then the sparse MLA on them); sampled rows of the launched chunks
+    """Window 2048 over the 128K workload in the benchmark's launch configuration (the prefill's
+    query chunks: the window lists, then the sparse MLA on them); sampled rows of the launched chunks
     against the oracle, indices exactly."""
     from synth import WORKLOADS
     cfg = WORKLOADS["prefill-L131072-k2048"]
