@@ -34,9 +34,10 @@ KERNEL_SOURCES = {"indexer": ["indexer.hip", "dsa_device.h"],
                   "sparse_mla": ["sparse_mla.hip", "dsa_device.h"]}
 
 
-def measured_traffic(workload, kernel):
-    """Counter-measured HBM bytes per launch (fetch + write) of `kernel` on `workload`, or None
-    when no measurement exists or the kernel source has changed since it was taken."""
+def measured_traffic(workload, kernel, chunk_rows):
+    """Counter-measured HBM bytes per launch (fetch + write) of `kernel` on `workload` at
+    `chunk_rows` query rows per launch, or None when no such measurement exists or the kernel
+    source has changed since it was taken."""
     import hashlib
     path = TRAFFIC_FILES.get(workload)
     if path is None or not os.path.exists(os.path.join(ROOT, path)):
@@ -51,7 +52,8 @@ def measured_traffic(workload, kernel):
             if not line.startswith("traffic "):
                 continue
             kv = dict(item.split("=", 1) for item in line.split()[1:])
-            if kv.get("kernel") == kernel and kv.get("source") == digest:
+            if (kv.get("kernel") == kernel and kv.get("source") == digest
+                    and kv.get("chunk_rows") == str(chunk_rows)):
                 return int(float(kv["fetch_bytes"]) + float(kv["write_bytes"]))
     return None
 
@@ -217,7 +219,7 @@ def main():
                           avg_launch_ms=round(ktime[name] / kcount[name], 4),
                           achieved=round(ach, 2), unit=unit, peak=peak,
                           frac=round(ach / peak, 4), bound=bound,
-                          traffic=measured_traffic(cfg.name, name))
+                          traffic=measured_traffic(cfg.name, name, chunk))
     dom = max(kern, key=lambda n: kern[n]["total_ms"])
     log("kernels:", json.dumps(kern))
     roofline = dict(bound=kern[dom]["bound"], achieved=kern[dom]["achieved"],
