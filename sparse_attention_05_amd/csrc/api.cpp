@@ -150,7 +150,7 @@ dsa_status_t dsa_sparse_mla(const uint16_t* q, const uint16_t* kv, const int32_t
     if (!aligned(q, 16) || !aligned(kv, 16) || !aligned(out, 4)) return DSA_ERR_INVALID_ARGUMENT;
     if (T == 0) return DSA_OK;
     return from_hip(dsa::launch_sparse_mla(q, kv, idx, nullptr, T, L, H, k, sm_scale, 1, out,
-                                           lse, nullptr, nullptr, as_hip(stream)));
+                                           lse, nullptr, nullptr, -1, as_hip(stream)));
 }
 
 int dsa_prefill_chunk_rows(int T, int L)
@@ -199,7 +199,7 @@ static dsa_status_t prefill_run(const uint8_t* q8, const float* q_scale, const f
             e = dsa::launch_sparse_mla(q + (int64_t)r0 * H * 576, kv, idx, nullptr, rows, L, H,
                                        k, sm_scale, 1, out + (int64_t)r0 * H * 512,
                                        lse ? lse + (int64_t)r0 * H : nullptr, nullptr, nullptr,
-                                       s);
+                                       qp, s);
         if (e != hipSuccess) return DSA_ERR_HIP;
     }
     return DSA_OK;
@@ -457,7 +457,7 @@ dsa_status_t dsa_decode(int B, const int64_t* seq_start, int max_len, int64_t to
                                     ws.tk_bytes ? base + ws.tk_off : nullptr, s);
     if (e == hipSuccess)
         e = dsa::launch_sparse_mla(q, kv_cache, idx, seq_start, B, max_len, H, k, sm_scale,
-                                   ws.splits, out, lse, po, pl, s);
+                                   ws.splits, out, lse, po, pl, -1, s);
     if (e == hipSuccess && ws.splits > 1)
         e = dsa::launch_mla_combine(po, pl, B, H, ws.splits, out, lse, s);
     return from_hip(e);

@@ -63,7 +63,7 @@ __global__ __launch_bounds__(NW * 64) void sparse_mla_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
     const int32_t* __restrict__ idx, const int64_t* __restrict__ seq_start, int L, int H, int k,
     float sm_scale, int splits, uint16_t* __restrict__ out, float* __restrict__ lse,
-    float* __restrict__ part_o, float* __restrict__ part_lse)
+    float* __restrict__ part_o, float* __restrict__ part_lse, int valid_pos0)
 {
     constexpr int NG = 2 * NW;                         // 16-head groups
     constexpr int DPW = 32 / NW;                       // 16-dim blocks of O per wave
@@ -74,7 +74,9 @@ __global__ __launch_bounds__(NW * 64) void sparse_mla_kernel(
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 4, c16 = lane & 15;
-    const int row = blockIdx.x, split = blockIdx.y;
+    // prefill rows later in a launch see at least as many keys: start the heaviest first
+    const int row = seq_start ? (int)blockIdx.x : (int)(gridDim.x - 1 - blockIdx.x);
+    const int split = blockIdx.y;
     const int n0 = wave * DPW;                         // first 16-dim block of O owned here
 
     int64_t kv_base = 0;
@@ -84,9 +86,13 @@ __global__ __launch_bounds__(NW * 64) void sparse_mla_kernel(
         Lr = (int)(seq_start[row + 1] - kv_base);
     }
     const uint16_t* kvr = kv + kv_base * 576;
-    const int per = (k + splits - 1) / splits;
+    // valid_pos0 >= 0: the row's list holds its min(k, valid_pos0 + row + 1) valid entries
+    // first (a top-k selection at positions valid_pos0 + row), so the padding after them is
+    // not visited; otherwise padding may sit anywhere among the k entries
+    const int kr = valid_pos0 >= 0 ? min(k, valid_pos0 + row + 1) : k;
+    const int per = (kr + splits - 1) / splits;
     const int jbeg = split * per;
-    const int nkeys = max(0, min(k, jbeg + per) - jbeg);
+    const int nkeys = max(0, min(kr, jbeg + per) - jbeg);
     const int ntile = (nkeys + MT - 1) / MT;
     const int32_t* idxr = idx + (int64_t)row * k + jbeg;
 
@@ -421,11 +427,11 @@ template <int NW>
 hipError_t launch_nw(const uint16_t* q, const uint16_t* kv, const int32_t* idx,
                      const int64_t* seq_start, int T, int L, int H, int k, float sm_scale,
                      int splits, uint16_t* out, float* lse, float* part_o, float* part_lse,
-                     hipStream_t stream)
+                     int valid_pos0, hipStream_t stream)
 {
     auto kern = sparse_mla_kernel<NW>;
     hipLaunchKernelGGL(kern, dim3(T, splits), dim3(NW * 64), 0, stream, q, kv, idx, seq_start, L,
-                       H, k, sm_scale, splits, out, lse, part_o, part_lse);
+                       H, k, sm_scale, splits, out, lse, part_o, part_lse, valid_pos0);
     return hipGetLastError();
 }
 
@@ -434,12 +440,14 @@ hipError_t launch_nw(const uint16_t* q, const uint16_t* kv, const int32_t* idx,
 hipError_t launch_sparse_mla(const uint16_t* q, const uint16_t* kv, const int32_t* idx,
                              const int64_t* seq_start, int T, int L, int H, int k,
                              float sm_scale, int splits, uint16_t* out, float* lse,
-                             float* part_o, float* part_lse, hipStream_t stream)
+                             float* part_o, float* part_lse, int valid_pos0, hipStream_t stream)
 {
     if (T <= 0) return hipSuccess;
     // four waves of 32 head slots; fewer heads leave slots empty (their queries read as zero
     // and their outputs are not written): one shape, whose registers fit without spilling
-    if (H <= 128) return launch_nw<4>(q, kv, idx, seq_start, T, L, H, k, sm_scale, splits, out, lse, part_o, part_lse, stream);
+    if (H <= 128)
+        return launch_nw<4>(q, kv, idx, seq_start, T, L, H, k, sm_scale, splits, out, lse, part_o,
+                            part_lse, valid_pos0, stream);
     return hipErrorInvalidValue;
 }
 
