@@ -77,7 +77,8 @@ def parse():
                     help="skip timing sliding-window attention through the sparse MLA")
     ap.add_argument("--no-input-prep", action="store_true",
                     help="skip timing the fp8 quantisation of the indexer inputs")
-    ap.add_argument("--varlen-workload", default="varlen-B16-L1024-32768-k2048")
+    ap.add_argument("--varlen-workload", default="varlen-B16-L1024-32768-k2048,varlen-B128-L1024-k2048",
+                    help="comma-separated packed-batch workloads")
     ap.add_argument("--no-varlen", action="store_true",
                     help="skip timing the packed multi-sequence prefill")
     ap.add_argument("--warmup-workload", default="prefill-L32768-k2048")
@@ -239,7 +240,8 @@ def main():
     prep = None if args.no_input_prep else run_input_prep(args, cfg, dev)
 
     # ---- packed multi-sequence prefill (fresh prefills and chunks against caches)
-    varlen = None if args.no_varlen else run_varlen(args, WORKLOADS[args.varlen_workload], dev)
+    varlen = None if args.no_varlen else [run_varlen(args, WORKLOADS[w], dev)
+                                          for w in args.varlen_workload.split(",")]
 
     # ---- indexer warm-up: KL to the dense attention distribution and its gradient
     warm = None if args.no_warmup_kl else run_warmup_kl(args, WORKLOADS[args.warmup_workload], dev)

@@ -133,6 +133,11 @@ WORKLOADS = {
                                               len_lo=1024, len_hi=32768, chunk_lo=512,
                                               chunk_hi=8192, k=2048, H_I=64, H=128,
                                               w_std=1 / 8, seed=1006, planted_frac=0.01),
+    # many short prompts, each within k (every row selects all it sees): 128 fresh 1K-token
+    # prefills
+    "varlen-B128-L1024-k2048": VarlenCfg("varlen-B128-L1024-k2048", B=128, len_lo=1024,
+                                         len_hi=1024, chunk_lo=1024, chunk_hi=1024, k=2048,
+                                         H_I=64, H=128, w_std=1 / 8, seed=1007),
 }
 
 
