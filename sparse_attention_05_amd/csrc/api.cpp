@@ -457,7 +457,7 @@ dsa_status_t dsa_decode(int B, const int64_t* seq_start, int max_len, int64_t to
                                     ws.tk_bytes ? base + ws.tk_off : nullptr, s);
     if (e == hipSuccess)
         e = dsa::launch_sparse_mla(q, kv_cache, idx, seq_start, B, max_len, H, k, sm_scale,
-                                   ws.splits, out, lse, po, pl, -1, s);
+                                   ws.splits, out, lse, po, pl, 0, s);
     if (e == hipSuccess && ws.splits > 1)
         e = dsa::launch_mla_combine(po, pl, B, H, ws.splits, out, lse, s);
     return from_hip(e);

@@ -43,9 +43,10 @@ hipError_t launch_topk_decode(const float* scores, const int64_t* seq_start, int
 // kv[seq_start[t] .. seq_start[t+1]) and its indices are relative to that slice.
 // splits > 1: each split covers a contiguous slice of the index list and writes fp32
 // partials (o normalised by its own denominator, lse) that launch_mla_combine merges.
-// valid_pos0 >= 0: row t's list is a top-k selection at position valid_pos0 + t, i.e. its
-// min(k, valid_pos0 + t + 1) valid entries come first, and only those are visited; -1: the
-// whole list of k entries is visited (padding anywhere).
+// valid_pos0 >= 0: row t's list is a top-k selection with its valid entries first, min(k,
+// valid_pos0 + t + 1) of them (prefill: position valid_pos0 + t) or min(k, L_t) (decode, with
+// seq_start), and only those are visited; -1: the whole list of k entries is visited (padding
+// anywhere).
 hipError_t launch_sparse_mla(const uint16_t* q, const uint16_t* kv, const int32_t* idx,
                              const int64_t* seq_start, int T, int L, int H, int k,
                              float sm_scale, int splits, uint16_t* out, float* lse,

@@ -86,10 +86,11 @@ __global__ __launch_bounds__(NW * 64) void sparse_mla_kernel(
         Lr = (int)(seq_start[row + 1] - kv_base);
     }
     const uint16_t* kvr = kv + kv_base * 576;
-    // valid_pos0 >= 0: the row's list holds its min(k, valid_pos0 + row + 1) valid entries
-    // first (a top-k selection at positions valid_pos0 + row), so the padding after them is
-    // not visited; otherwise padding may sit anywhere among the k entries
-    const int kr = valid_pos0 >= 0 ? min(k, valid_pos0 + row + 1) : k;
+    // valid_pos0 >= 0: the row's list is a top-k selection, its valid entries first (min(k,
+    // valid_pos0 + row + 1) of them for a prefill row at position valid_pos0 + row, min(k, Lr)
+    // for a decode row over its cache), so the padding after them is not visited; otherwise
+    // padding may sit anywhere among the k entries
+    const int kr = valid_pos0 < 0 ? k : seq_start ? min(k, Lr) : min(k, valid_pos0 + row + 1);
     const int per = (kr + splits - 1) / splits;
     const int jbeg = split * per;
     const int nkeys = max(0, min(kr, jbeg + per) - jbeg);
