@@ -421,14 +421,21 @@ def run_varlen(args, vcfg, dev):
         p, s_ = prefill_units(L, T, L - T, vcfg.k, 0, T)
         pairs += p
         sel += s_
-    flops = pairs * 2.0 * vcfg.H_I * D_I + sel * 2.0 * H * (D_QK + D_V)
+    f_idx = pairs * 2.0 * vcfg.H_I * D_I                 # fp8 MFMA
+    f_mla = sel * 2.0 * H * (D_QK + D_V)                  # bf16 MFMA
+    flops = f_idx + f_mla
+    # the call's work at peak: indexer flops at the fp8 peak, attention flops at the bf16
+    # peak, the top-k's 4-byte score reads at HBM peak
+    ideal_ms = (f_idx / (PEAK["fp8"] * 1e12) + f_mla / (PEAK["bf16"] * 1e12)
+                + pairs * 4.0 / (HBM_PEAK_GBS * 1e9)) * 1e3
     log("varlen prefill %s: %d query rows over %d cached tokens, %.2f ms, %.0f tokens/s"
         % (vcfg.name, Tq, d["Lk"], ms, Tq / (ms / 1e3)))
     res = dict(workload=vcfg.name, sequences=vcfg.B, query_rows=Tq, key_rows=d["Lk"],
                lens_q=d["lens_q"], lens_k=d["lens_k"], ms=round(ms, 3),
                tokens_per_s=round(Tq / (ms / 1e3), 1),
                algorithmic_tflop=round(flops / 1e12, 3),
-               effective_tflop_s=round(flops / (ms / 1e3) / 1e12, 1))
+               effective_tflop_s=round(flops / (ms / 1e3) / 1e12, 1),
+               ms_at_peak=round(ideal_ms, 3), frac_of_peak=round(ideal_ms / ms, 4))
     del d, out, lse, ws
     torch.cuda.empty_cache()
     return res
