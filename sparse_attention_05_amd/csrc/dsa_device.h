@@ -106,7 +106,9 @@ typedef __attribute__((address_space(1))) void gbl_void_t;
 // the compiler cannot tell that the LDS reads which follow it (of the other tile buffer) do not
 // touch the bytes in flight, and would otherwise wait for the load before each of them.  The
 // statement has no register results; completion is awaited explicitly (s_waitcnt 0 and a
-// barrier) before the destination buffer is read.
+// barrier) before the destination buffer is read.  M0 is listed as clobbered (the compiler
+// notes that it is a reserved register): each statement loads it itself right before the
+// load, and on gfx950 nothing else in these kernels keeps a value in M0.
 __device__ __forceinline__ void dma16(const void* src, uint32_t lds_dst)
 {
     asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"

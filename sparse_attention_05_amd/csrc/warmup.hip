@@ -327,8 +327,6 @@ __device__ __forceinline__ u32x4 tr_operand(const uint8_t* tile, int pr, int n, 
     return u32x4{lo[0], lo[1], hi[0], hi[1]};
 }
 
-__device__ __forceinline__ uint32_t pack2(float a, float b) { return pack_bf16x2(a, b); }
-
 // e -> bf16 B operand (round to nearest even), elements in the K order of the accumulators
 __device__ __forceinline__ u32x4 pack_e(const float (&e)[2][4])
 {
