@@ -188,3 +188,29 @@ def check_warmup_dk(g_dk: np.ndarray, o: dict, what=""):
     assert not bad.any(), "%s: %d dk entries out of tolerance, worst %.3g (tol %.3g)" % (
         what, bad.sum(), d[bad].max(), tol[bad][np.argmax(d[bad])])
     return (d / tol).max(initial=0)
+
+
+def check_decode(dsa, inp, seqs, what):
+    """One dsa_decode call over a packed batch; sequences `seqs` against the oracle: indices
+    by the near-tie rule, output and lse against the oracle's sparse MLA on the GPU's
+    indices."""
+    d = inp if inp["q"].is_cuda else to_device(inp)
+    B, k = inp["B"], inp["k"]
+    idx = torch.empty((B, k), dtype=torch.int32, device="cuda")
+    out, lse, _ = dsa.dsa_decode(d["seq_start"], inp["max_len"], d["q8"], d["qs"], d["w"],
+                                 d["k8"], d["ks"], d["q"], d["kv"], k, inp["score_scale"],
+                                 inp["sm_scale"], idx_out=idx)
+    torch.cuda.synchronize()
+    st = _np(d["seq_start"])
+    gidx = _np(idx)
+    for b in seqs:
+        a, e = int(st[b]), int(st[b + 1])
+        Lb = e - a
+        sc, bd = oracle.index_scores(_np(d["q8"][b:b + 1]), _np(d["qs"][b:b + 1]),
+                                     _np(d["w"][b:b + 1]), _np(d["k8"][a:e]), _np(d["ks"][a:e]),
+                                     Lb - 1, inp["score_scale"], with_bound=True)
+        oidx = oracle.topk(sc, [Lb], k)
+        check_indices_near_ties(gidx[b:b + 1], oidx, sc, bd, [Lb], k, "%s seq %d" % (what, b))
+        oo, ol = oracle.sparse_mla(_u16(d["q"][b:b + 1]), _u16(d["kv"][a:e]), gidx[b:b + 1],
+                                   inp["sm_scale"])
+        check_mla(bf16_to_f64(out[b:b + 1]), _np(lse[b:b + 1]), oo, ol, "%s seq %d" % (what, b))

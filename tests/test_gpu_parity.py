@@ -11,8 +11,8 @@ import pytest
 import torch
 
 import oracle
-from parity import (check_indices_near_ties, check_mla, check_prefill_rows, check_scores,
-                    check_topk_exact, bf16_to_f64, oracle_prefill_rows, to_device)
+from parity import (check_decode, check_indices_near_ties, check_mla, check_prefill_rows,
+                    check_scores, check_topk_exact, bf16_to_f64, oracle_prefill_rows, to_device)
 from synth import WORKLOADS, DecodeCfg, PrefillCfg, host_arrays, make_decode, make_prefill
 
 pytestmark = pytest.mark.gpu
@@ -338,36 +338,13 @@ def test_prefill_long_context_sampled_rows(dsa, name, extra):
 
 # ---------------------------------------------------------------------------- decode
 
-def _check_decode(dsa, inp, seqs, what):
-    d = inp if inp["q"].is_cuda else to_device(inp)
-    B, k = inp["B"], inp["k"]
-    idx = torch.empty((B, k), dtype=torch.int32, device="cuda")
-    out, lse, _ = dsa.dsa_decode(d["seq_start"], inp["max_len"], d["q8"], d["qs"], d["w"],
-                                 d["k8"], d["ks"], d["q"], d["kv"], k, inp["score_scale"],
-                                 inp["sm_scale"], idx_out=idx)
-    torch.cuda.synchronize()
-    st = _np(d["seq_start"])
-    gidx = _np(idx)
-    for b in seqs:
-        a, e = int(st[b]), int(st[b + 1])
-        Lb = e - a
-        sc, bd = oracle.index_scores(_np(d["q8"][b:b + 1]), _np(d["qs"][b:b + 1]),
-                                     _np(d["w"][b:b + 1]), _np(d["k8"][a:e]), _np(d["ks"][a:e]),
-                                     Lb - 1, inp["score_scale"], with_bound=True)
-        oidx = oracle.topk(sc, [Lb], k)
-        check_indices_near_ties(gidx[b:b + 1], oidx, sc, bd, [Lb], k, "%s seq %d" % (what, b))
-        oo, ol = oracle.sparse_mla(_u16(d["q"][b:b + 1]), _u16(d["kv"][a:e]), gidx[b:b + 1],
-                                   inp["sm_scale"])
-        check_mla(bf16_to_f64(out[b:b + 1]), _np(lse[b:b + 1]), oo, ol, "%s seq %d" % (what, b))
-
-
 @pytest.mark.parametrize("B,lo,hi,k,H_I,H", [(8, 1, 9000, 2048, 64, 128), (5, 3, 700, 64, 4, 16),
                                              (3, 1, 40, 8, 128, 8)])
 def test_decode_every_sequence(dsa, B, lo, hi, k, H_I, H):
     cfg = DecodeCfg("case", B=B, len_lo=lo, len_hi=hi, k=k, H_I=H_I, H=H, w_std=H_I ** -0.5,
                     seed=B * 31 + k)
     inp = make_decode(cfg)
-    _check_decode(dsa, inp, range(B), "decode B=%d k=%d" % (B, k))
+    check_decode(dsa, inp, range(B), "decode B=%d k=%d" % (B, k))
 
 
 def test_decode_64_sequences_to_128k_sampled(dsa):
@@ -375,7 +352,7 @@ def test_decode_64_sequences_to_128k_sampled(dsa):
     inp = make_decode(cfg, device="cuda")
     lens = _np(inp["lens"])
     seqs = sorted({int(np.argmax(lens)), int(np.argmin(lens)), 0, 63, 17})
-    _check_decode(dsa, inp, seqs, "decode B=64")
+    check_decode(dsa, inp, seqs, "decode B=64")
 
 
 def _decode_integer_scores(vals_per_seq, k, H=8, seed=0):

@@ -1,14 +1,16 @@
-"""Seeded random small shapes through the fused prefill and the indexer warm-up, against the
-CPU oracle (needs an MI355X): odd and tiny T, L, q_pos0, k and head counts, including the
-degenerate ones (one key, one query row, k = 1, k >= L).  Tolerances: tests/parity.py."""
+"""Seeded random small shapes through the fused prefill, the decode step and the indexer
+warm-up, against the CPU oracle (needs an MI355X): odd and tiny T, L, q_pos0, k and head
+counts, including the degenerate ones (one key, one query row, k = 1, k >= L), and decode
+batches whose lengths straddle the top-k's whole-row staging limit and its 16K-key segments.
+Tolerances: tests/parity.py."""
 import numpy as np
 import pytest
 import torch
 
 import oracle
-from parity import (bf16_to_f64, check_indices_near_ties, check_mla, check_warmup_dk,
-                    check_warmup_rows)
-from synth import PrefillCfg, host_arrays, make_prefill
+from parity import (bf16_to_f64, check_decode, check_indices_near_ties, check_mla,
+                    check_warmup_dk, check_warmup_rows)
+from synth import DecodeCfg, PrefillCfg, host_arrays, make_decode, make_prefill
 
 pytestmark = pytest.mark.gpu
 
@@ -80,3 +82,27 @@ def test_warmup_random_shape(dsa, L, T, q0, k, H_I, H, seed):
     what = "warm-up L=%d T=%d q_pos0=%d H_I=%d H=%d" % (L, T, q0, H_I, H)
     check_warmup_rows(g, o, np.arange(T), what)
     check_warmup_dk(g["dk"], o, what)
+
+
+def _decode_shapes(seed, n):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        lo = int(rng.integers(1, 20001))
+        hi = lo + int(rng.integers(0, 20001))
+        H_I = int(rng.choice([1, 8, 32, 64, 128]))
+        out.append((int(rng.integers(1, 7)), lo, hi, int(rng.choice([1, 7, 64, 255, 2048, 8192])),
+                    H_I, int(rng.choice([1, 7, 16, 128])), 300 + i))
+    # one token; lengths within k; around the staging limit and a segment boundary
+    out += [(1, 1, 1, 1, 64, 8, 290), (3, 1, 3, 2048, 4, 16, 291),
+            (4, 5880, 5896, 2048, 64, 16, 292), (3, 16380, 16390, 2048, 16, 8, 293)]
+    return out
+
+
+@pytest.mark.parametrize("B,lo,hi,k,H_I,H,seed", _decode_shapes(13, 6))
+def test_decode_random_shape(dsa, B, lo, hi, k, H_I, H, seed):
+    cfg = DecodeCfg("rand", B=B, len_lo=lo, len_hi=hi, k=k, H_I=H_I, H=H, w_std=H_I ** -0.5,
+                    seed=seed)
+    inp = make_decode(cfg)
+    check_decode(dsa, inp, range(B), "decode B=%d L=[%d,%d] k=%d H_I=%d H=%d" % (
+        B, lo, hi, k, H_I, H))
