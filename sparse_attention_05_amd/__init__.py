@@ -119,6 +119,30 @@ def _req(t, dtype, shape, name):
     return t
 
 
+def _rows(t, T, L, name):
+    """A float32 CUDA matrix of T rows of at least L entries, unit column stride (scores, P)."""
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError("%s must be a CUDA tensor" % name)
+    if t.dtype != torch.float32 or t.dim() != 2 or t.shape[0] != T or t.shape[1] < L \
+            or t.stride(1) != 1 or (T > 1 and t.stride(0) < t.shape[1]):
+        raise ValueError("%s must be float32 [T, >=L] with unit column stride" % name)
+    return t
+
+
+def _workspace(ws, need, dev):
+    """The caller's workspace (a contiguous CUDA tensor; its size in bytes is passed on), or a
+    fresh one of the size the library asks for."""
+    if ws is None:
+        return torch.empty((max(need, 1),), dtype=torch.uint8, device=dev)
+    if not isinstance(ws, torch.Tensor) or not ws.is_cuda or not ws.is_contiguous():
+        raise TypeError("workspace must be a contiguous CUDA tensor")
+    return ws
+
+
+def _nbytes(t):
+    return t.numel() * t.element_size()
+
+
 def _u8(t):
     return t.view(torch.uint8) if t.dtype == torch.float8_e4m3fn else t
 
@@ -155,9 +179,7 @@ def dsa_index_scores(q8, q_scale, w, k8, k_scale, q_pos0: int, score_scale: floa
     _req(k_scale, torch.float32, (L,), "k_scale")
     if scores is None:
         scores = torch.empty((T, L), dtype=torch.float32, device=q8.device)
-    if scores.dtype != torch.float32 or scores.dim() != 2 or scores.shape[0] != T \
-            or scores.stride(1) != 1 or scores.shape[1] < L:
-        raise ValueError("scores must be float32 [T, >=L] with unit column stride")
+    _rows(scores, T, L, "scores")
     _check(lib.dsa_index_scores(_ptr(q8), _ptr(q_scale), _ptr(w), _ptr(k8), _ptr(k_scale), T, L,
                                 H_I, q_pos0, score_scale, _ptr(scores), scores.stride(0),
                                 int(bool(write_masked)), _stream()), "dsa_index_scores")
@@ -167,9 +189,10 @@ def dsa_index_scores(q8, q_scale, w, k8, k_scale, q_pos0: int, score_scale: floa
 def dsa_topk(scores, L: int, q_pos0: int, k: int, idx=None):
     """Per-row top-k of scores [T, >=L]: int32 [T, k], ascending positions, -1 padded."""
     lib = load()
-    T = scores.shape[0]
-    if scores.dtype != torch.float32 or scores.dim() != 2 or scores.stride(1) != 1:
+    if not isinstance(scores, torch.Tensor) or scores.dim() != 2:
         raise ValueError("scores must be float32 [T, >=L] with unit column stride")
+    T = scores.shape[0]
+    _rows(scores, T, L, "scores")
     if idx is None:
         idx = torch.empty((T, k), dtype=torch.int32, device=scores.device)
     _req(idx, torch.int32, (T, k), "idx")
@@ -221,11 +244,10 @@ def dsa_prefill(q8, q_scale, w, k8, k_scale, q, kv, k: int, q_pos0: int, score_s
     if idx_out is not None:
         _req(idx_out, torch.int32, (T, k), "idx_out")
     need = dsa_prefill_workspace_bytes(T, L, H_I, H, k)
-    if workspace is None:
-        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=dev)
+    workspace = _workspace(workspace, need, dev)
     _check(lib.dsa_prefill(_ptr(q8), _ptr(q_scale), _ptr(w), _ptr(k8), _ptr(k_scale), _ptr(q),
                            _ptr(kv), T, L, H_I, H, k, q_pos0, score_scale, sm_scale, _ptr(out),
-                           _ptr(lse), _ptr(idx_out), _ptr(workspace), workspace.numel(),
+                           _ptr(lse), _ptr(idx_out), _ptr(workspace), _nbytes(workspace),
                            _stream()), "dsa_prefill")
     return out, lse, idx_out
 
@@ -279,12 +301,11 @@ def dsa_prefill_varlen(cu_seqlens_q, cu_seqlens_k, q8, q_scale, w, k8, k_scale, 
     if idx_out is not None:
         _req(idx_out, torch.int32, (Tq, k), "idx_out")
     need = int(lib.dsa_prefill_varlen_workspace_bytes(B, _ptr(cq), _ptr(ck), H_I, H, k))
-    if workspace is None:
-        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=dev)
+    workspace = _workspace(workspace, need, dev)
     _check(lib.dsa_prefill_varlen(B, _ptr(cq), _ptr(ck), _ptr(q8), _ptr(q_scale), _ptr(w),
                                   _ptr(k8), _ptr(k_scale), _ptr(q), _ptr(kv), H_I, H, k,
                                   score_scale, sm_scale, _ptr(out), _ptr(lse), _ptr(idx_out),
-                                  _ptr(workspace), workspace.numel(), _stream()),
+                                  _ptr(workspace), _nbytes(workspace), _stream()),
            "dsa_prefill_varlen")
     return out, lse, idx_out
 
@@ -313,9 +334,7 @@ def dsa_attention_distribution(q, kv, lse, q_pos0: int, sm_scale: float, P=None)
     _req(lse, torch.float32, (T, H), "lse")
     if P is None:
         P = torch.zeros((T, L), dtype=torch.float32, device=q.device)
-    if P.dtype != torch.float32 or P.dim() != 2 or P.shape[0] != T or P.stride(1) != 1 \
-            or P.shape[1] < L:
-        raise ValueError("P must be float32 [T, >=L] with unit column stride")
+    _rows(P, T, L, "P")
     _check(lib.dsa_attention_distribution(_ptr(q), _ptr(kv), _ptr(lse), T, L, H, q_pos0,
                                           sm_scale, _ptr(P), P.stride(0), _stream()),
            "dsa_attention_distribution")
@@ -350,13 +369,12 @@ def dsa_indexer_warmup(q8, q_scale, w, k8, k_scale, q, kv, q_pos0: int, score_sc
             res[key] = torch.empty(shp, dtype=torch.float32, device=dev)
         _req(res[key], torch.float32, shp, key)
     need = dsa_indexer_warmup_workspace_bytes(T, L, H_I, H)
-    if workspace is None:
-        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=dev)
+    workspace = _workspace(workspace, need, dev)
     _check(lib.dsa_indexer_warmup(_ptr(q8), _ptr(q_scale), _ptr(w), _ptr(k8), _ptr(k_scale),
                                   _ptr(q), _ptr(kv), T, L, H_I, H, q_pos0, score_scale, sm_scale,
                                   _ptr(res["kl"]), _ptr(res["dq"]), _ptr(res["dw"]),
                                   _ptr(res["dk"]), _ptr(res["lse_teacher"]),
-                                  _ptr(res["lse_index"]), _ptr(workspace), workspace.numel(),
+                                  _ptr(res["lse_index"]), _ptr(workspace), _nbytes(workspace),
                                   _stream()), "dsa_indexer_warmup")
     return res
 
@@ -387,12 +405,11 @@ def dsa_decode(seq_start, max_len: int, q8, q_scale, w, k8, k_scale, q, kv, k: i
     if idx_out is not None:
         _req(idx_out, torch.int32, (B, k), "idx_out")
     need = dsa_decode_workspace_bytes(B, max_len, N, H_I, H, k)
-    if workspace is None:
-        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=dev)
+    workspace = _workspace(workspace, need, dev)
     _check(lib.dsa_decode(B, _ptr(seq_start), max_len, N, _ptr(q8), _ptr(q_scale), _ptr(w),
                           _ptr(k8), _ptr(k_scale), _ptr(q), _ptr(kv), H_I, H, k, score_scale,
                           sm_scale, _ptr(out), _ptr(lse), _ptr(idx_out), _ptr(workspace),
-                          workspace.numel(), _stream()), "dsa_decode")
+                          _nbytes(workspace), _stream()), "dsa_decode")
     return out, lse, idx_out
 
 

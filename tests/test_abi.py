@@ -234,3 +234,10 @@ def test_size_queries_return_full_size_t(lib):
     assert v == lib.dsa_prefill_workspace_bytes(1 << 20, 1 << 20, 64, 128, 2048) > 0
     w = lib.dsa_indexer_warmup_workspace_bytes(1 << 20, 1 << 20, 128, 128)
     assert w > (1 << 32)      # the key-gradient partials alone: 8 x 2^20 x 512 bytes
+
+
+def test_binding_refuses_host_score_matrices(lib):
+    """A host tensor never reaches the library as a device pointer."""
+    import torch
+    with pytest.raises(TypeError):
+        dsa.dsa_topk(torch.zeros((4, 8)), 8, 0, 2)
