@@ -130,6 +130,45 @@ def test_indexer_joint_head_permutation_invariance():
     assert np.allclose(acc[vis], base[vis], rtol=1e-12, atol=1e-12)
 
 
+@pytest.mark.parametrize("H_I,L,q_pos0,T,seed", [(4, 70, 0, None, 12), (64, 40, 9, 25, 13)])
+def test_indexer_bound_many_heads_is_weighted_abs_einsum(H_I, L, q_pos0, T, seed):
+    """The conditioning bound A[t,s] = ks[s] sum_h |w qs c| sum_d |q k| with several heads,
+    written as a torch float64 abs-einsum over the dequantised codes (torch's fp8 cast, not the
+    oracle's decoder).  Dropping the absolute value of a signed weight, a transposed head index
+    or a missing key scale changes A; masked entries carry no bound."""
+    a = _small_prefill(L=L, H_I=H_I, seed=seed, q_pos0=q_pos0, T=T)
+    c = 0.0883883
+    _, bound = oracle.index_scores(a["q8"], a["qs"], a["w"], a["k8"], a["ks"], q_pos0, c,
+                                   with_bound=True)
+    absdot = torch.einsum("thd,sd->ths", torch.abs(_e4m3_deq(a["q8"])),
+                          torch.abs(_e4m3_deq(a["k8"]))).numpy()
+    wp = np.abs(a["w"].astype(np.float64) * a["qs"].astype(np.float64) * c)       # [T, H_I]
+    ref = np.einsum("th,ths->ts", wp, absdot) * a["ks"].astype(np.float64)[None, :]
+    vis = np.arange(L)[None, :] <= (q_pos0 + np.arange(a["T"]))[:, None]
+    assert np.allclose(bound[vis], ref[vis], rtol=1e-13, atol=0)
+    assert np.all(bound[~vis] == 0.0)
+    # the signed weights matter: with |w| the bound is unchanged, with w it is not
+    assert (a["w"] < 0).any()
+
+
+def test_indexer_bound_covers_fp32_evaluation_error():
+    """The score tolerance floor 2^-16 A covers an fp32 evaluation of the same sum in another
+    order (per-head fp32 dots, fp32 weighted head sum), at 64 heads where signed heads cancel."""
+    a = _small_prefill(L=300, H_I=64, seed=14)
+    c = 128 ** -0.5
+    exact, bound = oracle.index_scores(a["q8"], a["qs"], a["w"], a["k8"], a["ks"], 0, c,
+                                       with_bound=True)
+    q = _e4m3_deq(a["q8"]).float()
+    k = _e4m3_deq(a["k8"]).float()
+    D = torch.einsum("thd,sd->ths", q, k)                                   # fp32
+    wp = (torch.from_numpy(a["w"]) * torch.from_numpy(a["qs"]) * c).float()
+    s32 = (torch.relu(D) * wp[:, :, None]).sum(1) * torch.from_numpy(a["ks"])[None, :]
+    vis = np.isfinite(exact)
+    err = np.abs(s32.double().numpy()[vis] - exact[vis])
+    assert np.all(err <= 1e-3 * np.abs(exact[vis]) + 2.0 ** -16 * bound[vis])
+    assert err.max() > 0                         # the fp32 evaluation really does round
+
+
 def test_indexer_bound_single_head_is_abs_matmul():
     a = _small_prefill(L=20, H_I=1, seed=4)
     c = 0.3
@@ -622,7 +661,100 @@ def test_warmup_homogeneity_identities_and_bounds():
     assert (o["dw_bnd"] >= np.abs(o["dw"]) - 1e-15).all()
     assert (o["dq_bnd"] >= np.abs(o["dq"]) - 1e-15).all()
     assert (o["dk_bnd"] >= np.abs(o["dk"]) - 1e-15).all()
-    assert (o["dq_amb"] <= o["dq_bnd"] + np.abs(o["dq_amb"])).all()
+
+
+def _exact_warmup_inputs(L, T, q_pos0, H_I, H, seed, planted):
+    """Warm-up inputs whose indexer dot products are exact in any summation order: query and
+    key vectors are e4m3 values times powers of two (products have at most 8 significant bits,
+    sums stay far inside fp64's 53).  `planted` (row, head, key) triples get a key that is the
+    query vector rotated pairwise, (a, b) -> (b, -a), so their dot product is exactly zero while
+    the sum of |products| is not: the terms whose ReLU decision a rounded dot may flip."""
+    g = torch.Generator().manual_seed(seed)
+    def e4(shape, exps):
+        v = (torch.randn(shape, generator=g) * 3).to(torch.float8_e4m3fn).to(torch.float64)
+        return v * (2.0 ** exps)
+    QI = e4((T, H_I, 128), torch.randint(-3, 3, (T, H_I, 1), generator=g).double())
+    KI = e4((L, 128), torch.randint(-2, 2, (L, 1), generator=g).double())
+    for r, h, s in planted:
+        v = QI[r, h]
+        rot = torch.stack([v[1::2], -v[0::2]], dim=1).reshape(128)
+        KI[s] = rot
+    w = torch.randn((T, H_I), generator=g, dtype=torch.float64) * 0.7
+    q = torch.randn((T, H, 576), generator=g).to(torch.bfloat16).double()
+    kv = torch.randn((L, 576), generator=g).to(torch.bfloat16).double()
+    return dict(QI=QI.numpy(), KI=KI.numpy(), w=w.numpy(), q=q.numpy(), kv=kv.numpy(),
+                pos=q_pos0 + np.arange(T), c=0.125, sm_scale=576 ** -0.5)
+
+
+def _tolerance_terms(x, P, logQ):
+    """The warm-up's tolerance ingredients from their definitions, vectorised in numpy, with
+    the target P and log Q taken from the torch autograd reference: A = Q + P (the magnitude
+    that stands in for |G| = |Q - P|), x = <QI, KI> per (row, head, key), |x|_1 = sum_d |QI KI|,
+    a term ambiguous when |x| <= 2^-16 |x|_1 (a rounded dot may land on either side of 0)."""
+    QI, KI, w, c = x["QI"], x["KI"], x["w"], x["c"]
+    L = KI.shape[0]
+    vis = np.arange(L)[None, :] <= x["pos"][:, None]                     # [n, L]
+    Q = np.where(vis, np.exp(logQ), 0.0)
+    A = np.where(vis, Q + P, 0.0)
+    xv = np.einsum("nhd,sd->nhs", QI, KI)
+    xa = np.einsum("nhd,sd->nhs", np.abs(QI), np.abs(KI))
+    pos_ = (xv > 0) & vis[:, None, :]
+    amb = (np.abs(xv) <= 2.0 ** -16 * xa) & vis[:, None, :]
+    cw = np.abs(c * w)                                                   # [n, H_I]
+    t = dict(amb_count=int(amb.sum()))
+    t["dq_bnd"] = cw[:, :, None] * np.einsum("nhs,ns,sd->nhd", pos_.astype(float), A, np.abs(KI))
+    t["dq_amb"] = cw[:, :, None] * np.einsum("nhs,ns,sd->nhd", amb.astype(float), A, np.abs(KI))
+    t["dk_bnd"] = np.einsum("nhs,nh,ns,nhd->sd", pos_.astype(float), cw, A, np.abs(QI))
+    t["dk_amb"] = np.einsum("nhs,nh,ns,nhd->sd", amb.astype(float), cw, A, np.abs(QI))
+    t["dw_bnd"] = abs(c) * np.einsum("ns,nhs->nh", A, np.abs(xv) * vis[:, None, :])
+    with np.errstate(divide="ignore", invalid="ignore"):
+        lp = np.where(P > 0, np.log(np.where(P > 0, P, 1.0)), 0.0)
+    t["kl_bnd"] = (np.where(P > 0, P * (np.abs(lp) + np.abs(np.where(vis, logQ, 0.0))), 0.0)).sum(1)
+    return t
+
+
+@pytest.mark.parametrize("L,T,q_pos0,H_I,H,seed", [(50, 50, 0, 4, 3, 21), (40, 25, 15, 64, 2, 22)])
+def test_warmup_tolerance_terms_equal_their_definitions(L, T, q_pos0, H_I, H, seed):
+    """Every tolerance ingredient of the warm-up parity check (dq/dk ambiguity sums and the
+    dq/dk/dw/kl magnitude sums) equals an independent numpy evaluation of its definition, on
+    inputs with planted exactly-cancelling (row, head, key) terms.  An ambiguity sum that
+    counted every term, or a magnitude sum over all keys instead of the ReLU-active ones,
+    fails here; so does a dropped |w| or a missing Q + P weight."""
+    planted = [(3, 1, 2), (7, 0, 5), (T - 1, H_I - 1, q_pos0 + T - 2), (10, 2, 9)]
+    x = _exact_warmup_inputs(L, T, q_pos0, H_I, H, seed, planted)
+    o = oracle.warmup(x, want_dk=True, dist=True, bounds=True)
+    ref = _torch_warmup(x)
+    # log Q = I - lse_i, with the student scores I from exact dots and lse_i from torch
+    I = x["c"] * np.einsum("nh,nhs->ns", x["w"], np.maximum(
+        np.einsum("nhd,sd->nhs", x["QI"], x["KI"]), 0.0))
+    vis = np.arange(L)[None, :] <= x["pos"][:, None]
+    logQ = np.where(vis, I - ref["lse_i"][:, None], 0.0)
+    t = _tolerance_terms(x, ref["P"], logQ)
+    assert t["amb_count"] >= len(planted)          # the plant is seen as ambiguous
+    for key in ("dq_bnd", "dq_amb", "dk_bnd", "dk_amb", "dw_bnd", "kl_bnd"):
+        scale = max(np.abs(t[key]).max(), 1e-300)
+        assert np.allclose(o[key], t[key], rtol=1e-11, atol=1e-13 * scale), key
+    # the ambiguity sums are nonzero exactly where a planted term sits, and zero elsewhere
+    for r, h, s in planted:
+        assert (o["dq_amb"][r, h] > 0).any() and (o["dk_amb"][s] > 0).any()
+    amb_rows = {(r, h) for r, h, _ in planted}
+    for r in range(T):
+        for h in range(H_I):
+            if (r, h) not in amb_rows and t["dq_amb"][r, h].max() == 0:
+                assert o["dq_amb"][r, h].max() == 0.0
+
+
+def test_warmup_ambiguity_sums_vanish_without_near_zero_dots():
+    """On inputs with no planted cancellation every (row, head, key) dot product is far from
+    zero relative to its |products| sum (checked in numpy), so the ambiguity sums are exactly
+    zero: they cannot widen the dq/dk tolerance when no ReLU decision is in doubt."""
+    x = _exact_warmup_inputs(45, 45, 0, 4, 2, 23, planted=[])
+    xv = np.einsum("nhd,sd->nhs", x["QI"], x["KI"])
+    xa = np.einsum("nhd,sd->nhs", np.abs(x["QI"]), np.abs(x["KI"]))
+    vis = np.arange(45)[None, None, :] <= x["pos"][:, None, None]
+    assert not ((np.abs(xv) <= 2.0 ** -16 * xa) & vis).any()
+    o = oracle.warmup(x, want_dk=True, bounds=True)
+    assert np.all(o["dq_amb"] == 0.0) and np.all(o["dk_amb"] == 0.0)
 
 
 def test_warmup_student_equal_to_teacher_has_zero_loss():
