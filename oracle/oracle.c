@@ -284,6 +284,8 @@ int ora_dense_mla(const uint16_t* q, const uint16_t* kv, int64_t L, int H, int64
         if (t < 0 || p >= L) { bad = 1; continue; }
         for (int h = 0; h < H; ++h) {
             const uint16_t* qrow = q + (t * H + h) * 576;
+            double qv[576];
+            for (int d = 0; d < 576; ++d) qv[d] = ora_bf16_value(qrow[d]);
             double* o = out + (r * H + h) * 512;
             double run_max = -INFINITY, run_sum = 0.0;
             for (int d = 0; d < 512; ++d) o[d] = 0.0;
@@ -291,7 +293,7 @@ int ora_dense_mla(const uint16_t* q, const uint16_t* kv, int64_t L, int H, int64
                 const uint16_t* row = kv + s * 576;
                 double dot = 0.0;
                 for (int d = 0; d < 576; ++d)
-                    dot += ora_bf16_value(qrow[d]) * ora_bf16_value(row[d]);
+                    dot += qv[d] * ora_bf16_value(row[d]);
                 const double logit = sm_scale * dot;
                 if (logit > run_max) {                 /* rescale what was summed so far */
                     const double f = exp(run_max - logit);

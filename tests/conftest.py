@@ -28,3 +28,22 @@ def dsa():
     import sparse_attention_05_amd as dsa_mod
     dsa_mod.load()
     return dsa_mod
+
+
+def pytest_terminal_summary(terminalreporter):
+    """Per-config parity statistics gathered by the GPU parity tests (near-tie swaps,
+    planted-token recall, worst errors)."""
+    try:
+        import parity
+    except ImportError:
+        return
+    if not parity.REPORT:
+        return
+    import json
+    terminalreporter.section("parity statistics per config")
+    for name in sorted(parity.REPORT):
+        terminalreporter.write_line("%s: %s" % (name, json.dumps(parity.REPORT[name], sort_keys=True)))
+    path = os.environ.get("DSA_PARITY_REPORT")
+    if path:
+        with open(path, "w") as fh:
+            json.dump(parity.REPORT, fh, indent=1, sort_keys=True)

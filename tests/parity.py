@@ -98,6 +98,16 @@ def check_mla(out_g: np.ndarray, lse_g: np.ndarray, out_o: np.ndarray, lse_o: np
     return float(d.max(initial=0.0)), float(rel.max(initial=0.0)), float(dl.max(initial=0.0))
 
 
+# ------------------------------------------------------------------------- reporting
+# Per-config parity statistics (near-tie swaps, planted-token recall, worst errors), printed
+# in pytest's terminal summary and, when DSA_PARITY_REPORT names a file, written there as JSON.
+REPORT: dict = {}
+
+
+def report(config: str, **stats):
+    REPORT.setdefault(config, {}).update(stats)
+
+
 def _np(t):
     return t.detach().cpu().numpy()
 
@@ -107,18 +117,63 @@ def _u16(t):
 
 
 def oracle_prefill_rows(d: dict, rows, k):
-    """Oracle prefill of selected rows, one at a time (inputs copied from the device)."""
-    k8, ks, kv = _np(d["k8"]), _np(d["ks"]), _u16(d["kv"])
-    res = []
-    for t in rows:
-        t = int(t)
-        p = d["q_pos0"] + t
-        sc, bd = oracle.index_scores(_np(d["q8"][t:t + 1]), _np(d["qs"][t:t + 1]),
-                                     _np(d["w"][t:t + 1]), k8, ks, p, d["score_scale"],
-                                     with_bound=True)
-        idx = oracle.topk(sc, [p + 1], k)
-        res.append(dict(t=t, n=p + 1, scores=sc[0], bound=bd[0], idx=idx[0]))
-    return res
+    """Oracle scores, bound and selection of selected rows of a device prefill workload, as
+    one dict per row (all rows in one oracle call: see oracle_rows)."""
+    h = dict(q8=_np(d["q8"]), qs=_np(d["qs"]), w=_np(d["w"]), k8=_np(d["k8"]), ks=_np(d["ks"]),
+             q_pos0=d["q_pos0"], score_scale=d["score_scale"])
+    o = oracle_rows(h, rows, k)
+    return [dict(t=int(t), n=int(o["n_vis"][i]), scores=o["scores"][i], bound=o["bound"][i],
+                 idx=o["idx"][i]) for i, t in enumerate(o["rows"])]
+
+
+def oracle_rows(h: dict, rows, k: int) -> dict:
+    """Oracle indexer scores (with their conditioning bound) and top-k selection of the given
+    query rows of a prefill workload (host arrays q8, qs, w, k8, ks and the scalars), in one
+    call per step so that the oracle's OpenMP loop spreads the rows over the host cores."""
+    r = np.asarray(rows, np.int64)
+    sc, bd = oracle.index_scores(h["q8"], h["qs"], h["w"], h["k8"], h["ks"], h["q_pos0"],
+                                 h["score_scale"], rows=r, with_bound=True)
+    n_vis = h["q_pos0"] + r + 1
+    return dict(rows=r, scores=sc, bound=bd, n_vis=n_vis, idx=oracle.topk(sc, n_vis, k))
+
+
+def host_prefill(d: dict, q_rows=None) -> dict:
+    """Host copies of a device prefill workload's indexer inputs and cache (and, if q_rows is
+    given, of those rows of the MLA query only)."""
+    h = dict(q8=_np(d["q8"]), qs=_np(d["qs"]), w=_np(d["w"]), k8=_np(d["k8"]), ks=_np(d["ks"]),
+             kv=_u16(d["kv"]), q_pos0=d["q_pos0"], score_scale=d["score_scale"],
+             sm_scale=d["sm_scale"])
+    if q_rows is not None:
+        h["q_rows"] = _u16(d["q"][torch.as_tensor(np.asarray(q_rows), device=d["q"].device)])
+    return h
+
+
+def check_prefill_sampled(dsa, d, h, out, lse, idx, rows, k, what, scores=True):
+    """dsa_prefill's outputs on the given rows against the oracle, all rows per oracle call:
+    the GPU's indexer score row of each (dsa_index_scores of that one query), its selection by
+    the near-tie rule, its output and lse against the oracle's sparse MLA on the GPU's own
+    indices.  Returns the statistics (also the number of near-tie swaps)."""
+    rows = np.asarray(rows, np.int64)
+    dev_rows = torch.as_tensor(rows, device=out.device)
+    ora = oracle_rows(h, rows, k)
+    gidx = _np(idx[dev_rows])
+    swaps = check_indices_near_ties(gidx, ora["idx"], ora["scores"], ora["bound"], ora["n_vis"],
+                                    k, what)
+    q_rows = h["q_rows"] if "q_rows" in h else _u16(d["q"][dev_rows])
+    oo, ol = oracle.sparse_mla(q_rows, h["kv"], gidx, h["sm_scale"])
+    dout, rel, dl = check_mla(bf16_to_f64(out[dev_rows]), _np(lse[dev_rows]), oo, ol, what)
+    stats = dict(rows_checked=int(len(rows)), near_tie_swaps=int(swaps), max_dout=dout,
+                 max_rel_l2=rel, max_dlse=dl)
+    if scores:
+        worst = 0.0
+        for i, t in enumerate(rows):
+            t = int(t)
+            g = dsa.dsa_index_scores(d["q8"][t:t + 1], d["qs"][t:t + 1], d["w"][t:t + 1],
+                                     d["k8"], d["ks"], d["q_pos0"] + t, d["score_scale"])
+            worst = max(worst, check_scores(_np(g), ora["scores"][i:i + 1],
+                                            ora["bound"][i:i + 1], "%s scores row %d" % (what, t)))
+        stats["max_dscore"] = worst
+    return stats
 
 
 def check_prefill_rows(d, out, lse, gidx, rows, k, what):
@@ -190,10 +245,28 @@ def check_warmup_dk(g_dk: np.ndarray, o: dict, what=""):
     return (d / tol).max(initial=0)
 
 
+def _worker_count() -> int:
+    """Host threads for per-sequence oracle calls: the CPUs this process may use, at most 16."""
+    import os
+    return max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+def _single_threaded_oracle():
+    """Make the calling thread's OpenMP regions (inside the oracle library) use one thread, so
+    that many Python threads can each run one sequence's oracle call side by side."""
+    import ctypes
+    try:
+        ctypes.CDLL("libgomp.so.1").omp_set_num_threads(1)
+    except OSError:
+        pass
+
+
 def check_decode(dsa, inp, seqs, what):
     """One dsa_decode call over a packed batch; sequences `seqs` against the oracle: indices
     by the near-tie rule, output and lse against the oracle's sparse MLA on the GPU's
-    indices."""
+    indices.  Sequences are checked on a pool of host threads (one oracle call per sequence
+    each).  Returns the statistics."""
+    from concurrent.futures import ThreadPoolExecutor
     d = inp if inp["q"].is_cuda else to_device(inp)
     B, k = inp["B"], inp["k"]
     idx = torch.empty((B, k), dtype=torch.int32, device="cuda")
@@ -203,14 +276,26 @@ def check_decode(dsa, inp, seqs, what):
     torch.cuda.synchronize()
     st = _np(d["seq_start"])
     gidx = _np(idx)
-    for b in seqs:
+    q8, qs, w, k8, ks = (_np(d[key]) for key in ("q8", "qs", "w", "k8", "ks"))
+    q, kv = _u16(d["q"]), _u16(d["kv"])
+    gout, glse = bf16_to_f64(out), _np(lse)
+
+    def one(b):
+        _single_threaded_oracle()
         a, e = int(st[b]), int(st[b + 1])
         Lb = e - a
-        sc, bd = oracle.index_scores(_np(d["q8"][b:b + 1]), _np(d["qs"][b:b + 1]),
-                                     _np(d["w"][b:b + 1]), _np(d["k8"][a:e]), _np(d["ks"][a:e]),
+        sc, bd = oracle.index_scores(q8[b:b + 1], qs[b:b + 1], w[b:b + 1], k8[a:e], ks[a:e],
                                      Lb - 1, inp["score_scale"], with_bound=True)
         oidx = oracle.topk(sc, [Lb], k)
-        check_indices_near_ties(gidx[b:b + 1], oidx, sc, bd, [Lb], k, "%s seq %d" % (what, b))
-        oo, ol = oracle.sparse_mla(_u16(d["q"][b:b + 1]), _u16(d["kv"][a:e]), gidx[b:b + 1],
-                                   inp["sm_scale"])
-        check_mla(bf16_to_f64(out[b:b + 1]), _np(lse[b:b + 1]), oo, ol, "%s seq %d" % (what, b))
+        sw = check_indices_near_ties(gidx[b:b + 1], oidx, sc, bd, [Lb], k,
+                                     "%s seq %d" % (what, b))
+        oo, ol = oracle.sparse_mla(q[b:b + 1], kv[a:e], gidx[b:b + 1], inp["sm_scale"])
+        errs = check_mla(gout[b:b + 1], glse[b:b + 1], oo, ol, "%s seq %d" % (what, b))
+        return sw, errs
+
+    with ThreadPoolExecutor(max_workers=_worker_count()) as ex:
+        res = list(ex.map(one, list(seqs)))
+    return dict(seqs_checked=len(res), near_tie_swaps=int(sum(r[0] for r in res)),
+                max_dout=max((r[1][0] for r in res), default=0.0),
+                max_rel_l2=max((r[1][1] for r in res), default=0.0),
+                max_dlse=max((r[1][2] for r in res), default=0.0))
