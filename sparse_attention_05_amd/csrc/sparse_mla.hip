@@ -13,19 +13,17 @@
 // [64 rows][128 B], 16-byte chunks XOR-swizzled by row: one gather instruction moves one
 // row's latent part (a wave-uniform scalar base address plus a fixed per-lane chunk offset)
 // or the rope parts of eight rows, so issuing the gather costs a few scalar instructions per
-// row.  LDS read bandwidth, not MFMA, bounds the arithmetic, so the two contractions split
-// the work to minimise LDS reads:
-//  * S^T = K Q^T: wave w owns 32 heads (A = gathered rows, each 16-byte operand read feeding
-//    two MFMAs; B = Q^T held in registers) and their softmax, and writes P (bf16, already
-//    in the A-operand layout of P V) to LDS;
-//  * O = P V: wave w owns 128 of the value dims for every head, so each V element is read
-//    (by the transposing read ds_read_b64_tr_b16, half the rate of a plain 16-byte read) by
-//    one wave only, and P by every wave (plain 16-byte reads).
+// row.  Wave w owns 32 heads from end to end:
+//  * S^T = K Q^T for its heads (A = gathered rows, each 16-byte operand read feeding two
+//    MFMAs; B = Q^T held in registers), then their softmax, whose bf16 probabilities come out
+//    of the accumulators already in the A-operand layout of P V;
+//  * O = P V for its heads over all 512 value dims (V read from the tile by the transposing
+//    read ds_read_b64_tr_b16), so P never leaves the wave's registers and the waves meet only
+//    once per tile (it has landed; the previous one is consumed).
 // Softmax runs in the exp2 domain with fp32 statistics against a per-head reference max
-// fixed by the first valid logits of the row; O is never rescaled, which is what lets other
-// waves accumulate a head's P V.  Should a later logit exceed the reference by more than
-// 2^OVF_SLACK (a logit spread no real attention row reaches), the row is recomputed once
-// with the exact per-head max as the reference.
+// fixed by the first valid logits of the row, so O is never rescaled.  Should a later logit
+// exceed the reference by more than 2^OVF_SLACK (a logit spread no real attention row
+// reaches), the row is recomputed once with the exact per-head max as the reference.
 #include "dsa_device.h"
 #include "kernels.h"
 
@@ -56,8 +54,9 @@ __device__ __forceinline__ int row_base(int r) { return r * LROW; }
 __device__ __forceinline__ int lat_x(int r) { return (r & 7) << 1; }
 __device__ __forceinline__ int rope_x(int r) { return (r >> 1) & 7; }
 
-// NW waves; wave w: heads [32w, 32w + 32) in S^T / softmax (two 16-head groups hq), 16-dim
-// blocks [DPW w, DPW w + DPW) of O for all 2 NW head groups in P V.
+// NW = 4 waves; wave w owns heads [32w, 32w + 32) throughout: S^T = K Q^T for them, their
+// softmax, and O = P V over all 512 value dims, so P never leaves the wave's registers and
+// the waves meet only once per tile (the tile has landed; the previous one is consumed).
 template <int NW>
 __global__ __launch_bounds__(NW * 64) void sparse_mla_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
@@ -65,11 +64,9 @@ __global__ __launch_bounds__(NW * 64) void sparse_mla_kernel(
     float sm_scale, int splits, uint16_t* __restrict__ out, float* __restrict__ lse,
     float* __restrict__ part_o, float* __restrict__ part_lse, int valid_pos0)
 {
-    constexpr int NG = 2 * NW;                         // 16-head groups
-    constexpr int DPW = 32 / NW;                       // 16-dim blocks of O per wave
-    // P of one tile: [head group][32-key step][lane][8 bf16], the PV A-operand layout
+    static_assert(NW == 4, "four waves of 32 heads");
     __shared__ __attribute__((aligned(16))) uint8_t s_tile[2][TILE_BYTES];
-    __shared__ __attribute__((aligned(16))) uint8_t s_p[NG * 2 * 64 * 16];
+    __shared__ int s_flag[NW];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -77,7 +74,6 @@ __global__ __launch_bounds__(NW * 64) void sparse_mla_kernel(
     // prefill rows later in a launch see at least as many keys: start the heaviest first
     const int row = seq_start ? (int)blockIdx.x : (int)(gridDim.x - 1 - blockIdx.x);
     const int split = blockIdx.y;
-    const int n0 = wave * DPW;                         // first 16-dim block of O owned here
 
     int64_t kv_base = 0;
     int Lr = L;
@@ -153,15 +149,32 @@ __global__ __launch_bounds__(NW * 64) void sparse_mla_kernel(
         }
     };
 
-    v4f O[NG][DPW];                     // O[hg][d]: heads 16 hg + 4g + r, dims 16 (n0 + d) + c16
+    // per-lane offsets of the operand reads (see the tile layout above)
+    int qo[4], ro[2];                  // S^T A operand: latent chunk 4m + g, rope chunk 4(m-16) + g
+#pragma unroll
+    for (int b = 0; b < 4; ++b) qo[b] = ((4 * b + g) ^ lat_x(c16)) << 4;
+#pragma unroll
+    for (int b = 0; b < 2; ++b) ro[b] = ((4 * b + g) ^ rope_x(c16)) << 4;
+    // V operand of P V for dim block n, keys 32 half + 16 kt + 4g + r: transposing reads, lane
+    // (g, i) addressing row 32 half + 16 kt + 4g + i/4, dims 16n + 4(i%4) .. +3, i.e. chunk
+    // 2n + (i%4)/2 (physical (2n + cpart) ^ lat_x(rv) = 8 ((n/4) ^ vq) + 2 ((n%4) ^ (rv%4)) +
+    // cpart), byte 8 (i%2) within it
+    const int rv = 4 * g + (c16 >> 2);
+    const int vq = (rv >> 2) & 1;
+    const int vbase = row_base(rv) + (c16 & 1) * 8;
+    int vo[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) vo[j] = 32 * (j ^ (rv & 3)) + 16 * ((c16 & 3) >> 1);
+
+    v4f O[2][32];                      // O[hq][n]: heads 32 wave + 16 hq + 4g + r, dims 16n + c16
     float m_ref[2], m_max[2] = {-__builtin_huge_valf(), -__builtin_huge_valf()}, l_run[2];
 
 #pragma unroll 1
     for (int pass = 0; pass < 2; ++pass) {
 #pragma unroll
-        for (int hg = 0; hg < NG; ++hg)
+        for (int hq = 0; hq < 2; ++hq)
 #pragma unroll
-            for (int d = 0; d < DPW; ++d) O[hg][d] = v4f{0.f, 0.f, 0.f, 0.f};
+            for (int n = 0; n < 32; ++n) O[hq][n] = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int hq = 0; hq < 2; ++hq) {
             l_run[hq] = 0.f;
@@ -177,7 +190,7 @@ __global__ __launch_bounds__(NW * 64) void sparse_mla_kernel(
         // one tile: tb holds it, the other buffer receives the next one
         auto step = [&](int t, const uint8_t* tb) {
             __builtin_amdgcn_s_waitcnt(0);             // this wave's part of tile t landed
-            __syncthreads();                           // everyone's part; tile t-1 and P consumed
+            __syncthreads();                           // everyone's part; tile t-1 consumed
             const uint64_t vmask = __ballot(idx_cur >= 0);
             idx_nxt = check_idx(t + 1, idx_nxt);
             if (t + 1 < ntile) issue((t + 1) & 1, idx_nxt);
@@ -195,18 +208,6 @@ __global__ __launch_bounds__(NW * 64) void sparse_mla_kernel(
                     for (int hq = 0; hq < 2; ++hq) S[kt][hq] = v4f{0.f, 0.f, 0.f, 0.f};
                 const uint8_t* rb = tb + row_base(half * 32 + c16);    // kt adds 16 rows
                 const uint8_t* rr = tb + ROPE_OFF + RROW * (half * 32 + c16);
-                // latent chunk 4m + g = 16 (m/4) + (4 (m%4) + g): per-lane offsets for m%4,
-                // rope chunk 4 (m - 16) + g for m = 16, 17 (row & 7 == c16 & 7 and
-                // (row >> 1) & 7 == c16 >> 1 for these rows)
-                int qo[4], ro[2];
-#pragma unroll
-                for (int b = 0; b < 4; ++b) qo[b] = ((4 * b + g) ^ lat_x(c16)) << 4;
-#pragma unroll
-                for (int b = 0; b < 2; ++b) ro[b] = ((4 * b + g) ^ rope_x(c16)) << 4;
-                // Software pipeline with fixed stages: stage s issues the reads of step s + QD
-                // and the four MFMAs of step s; the scheduling barriers keep the compiler from
-                // collapsing it into read -> wait -> MFMA (one wave per SIMD leaves nothing
-                // else to hide LDS latency).
                 constexpr int QD = 3;
                 u32x4 abuf[QD][2];
 #pragma unroll
@@ -233,7 +234,10 @@ __global__ __launch_bounds__(NW * 64) void sparse_mla_kernel(
                             S[kt][hq] = mfma_bf16(as_bf16x8(a[kt]), as_bf16x8(qreg[hq][s]), S[kt][hq]);
                 }
                 __builtin_amdgcn_sched_barrier(0);
-                // softmax for heads 16 hq + c16 over this half's 32 keys
+                // softmax for heads 16 hq + c16 over this half's 32 keys; P stays in
+                // registers as the A operand of P V (head c16, keys {4g..4g+3} of each
+                // 16-key group)
+                u32x4 pa[2];
 #pragma unroll
                 for (int hq = 0; hq < 2; ++hq) {
                     // raw logits (masked: -inf); the scale is applied inside the exponent's
@@ -267,100 +271,71 @@ __global__ __launch_bounds__(NW * 64) void sparse_mla_kernel(
                             psum += p[kt][r];
                         }
                     l_run[hq] += psum;
-                    // A operand of P V: head c16, K = keys {4g..4g+3} of each 16-key group
-                    const v8bf pav = __builtin_convertvector(
+                    pa[hq] = __builtin_bit_cast(u32x4, __builtin_convertvector(
                         (v8f){p[0][0], p[0][1], p[0][2], p[0][3], p[1][0], p[1][1], p[1][2], p[1][3]},
-                        v8bf);
-                    *reinterpret_cast<v8bf*>(&s_p[(((2 * wave + hq) * 2 + half) * 64 + lane) * 16]) = pav;
+                        v8bf));
                 }
-            }
-            __syncthreads();                           // P of every head group visible
-
-            // O[hg][d] += P[hg] V[:, dims of block n0 + d] over the tile's two 32-key steps.
-            // V operand: column 16n + c16, keys 32 ks + 16 kt + 4g + r, by transpose reads:
-            // lane (g, i) addresses row 32 ks + 16 kt + 4g + i/4, dims 16n + 4(i%4) .. +3,
-            // i.e. chunk 2n + (i%4)/2 = 8(n/4) + (2(n%4) + (i%4)/2), byte 8 (i%2) within it
-            const int cpart = (c16 & 3) >> 1, boff = (c16 & 1) * 8;
-            const int rv = 4 * g + (c16 >> 2);         // row within each 16-key group
-            // physical chunk (2n + cpart) ^ lat_x(rv) = 8 ((n/4) ^ vq) + 2 ((n%4) ^ (rv%4)) + cpart
-            const int vq = (rv >> 2) & 1;
-            int vo[4];
+                // O[hq][n] += P[hq] V[:, 16n .. 16n + 15] over this half's 32 keys; the V
+                // operands are read VD blocks ahead of their MFMAs
+                const uint8_t* vb = tb + half * 32 * LROW + vbase;
+                constexpr int VD = 4;
+                u32x4 vbuf[VD];
+                auto vread = [&](int n) -> u32x4 {
+                    const int o = 128 * ((n >> 2) ^ vq) + vo[n & 3];
+                    const u32x2 lo = ds_read_tr(vb + o);
+                    const u32x2 hi = ds_read_tr(vb + o + 16 * LROW);
+                    return u32x4{lo[0], lo[1], hi[0], hi[1]};
+                };
 #pragma unroll
-            for (int j = 0; j < 4; ++j) vo[j] = 32 * (j ^ (rv & 3)) + 16 * cpart;
+                for (int n = 0; n < VD; ++n) vbuf[n] = vread(n);
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                const int vrow = row_base(ks * 32 + rv) + boff;
-                // V operands of DC owned blocks held at a time, P streamed per head group
-                constexpr int DC = DPW < 8 ? DPW : 8;
-#pragma unroll
-                for (int d0 = 0; d0 < DPW; d0 += DC) {
-                    u32x4 vop[DC];
-#pragma unroll
-                    for (int d = 0; d < DC; ++d) {
-                        const int n = n0 + d0 + d;
-                        const int o = vrow + 128 * ((n >> 2) ^ vq) + vo[n & 3];
-                        const u32x2 lo = ds_read_tr(tb + o);
-                        const u32x2 hi = ds_read_tr(tb + o + 16 * LROW);
-                        vop[d] = u32x4{lo[0], lo[1], hi[0], hi[1]};
-                    }
-                    constexpr int PD = NG < 2 ? NG : 2;
-                    u32x4 pbuf[PD];
-#pragma unroll
-                    for (int hg = 0; hg < PD; ++hg)
-                        pbuf[hg] = *reinterpret_cast<const u32x4*>(&s_p[((hg * 2 + ks) * 64 + lane) * 16]);
-#pragma unroll
-                    for (int hg = 0; hg < NG; ++hg) {
-                        __builtin_amdgcn_sched_barrier(0);     // stage hg: P read of hg + PD
-                        const u32x4 pa = pbuf[hg % PD];
-                        if (hg + PD < NG)
-                            pbuf[hg % PD] = *reinterpret_cast<const u32x4*>(&s_p[(((hg + PD) * 2 + ks) * 64 + lane) * 16]);
-#pragma unroll
-                        for (int d = 0; d < DC; ++d)
-                            O[hg][d0 + d] = mfma_bf16(as_bf16x8(pa), as_bf16x8(vop[d]), O[hg][d0 + d]);
-                    }
+                for (int n = 0; n < 32; ++n) {
                     __builtin_amdgcn_sched_barrier(0);
+                    const u32x4 v = vbuf[n % VD];
+                    if (n + VD < 32) vbuf[n % VD] = vread(n + VD);
+#pragma unroll
+                    for (int hq = 0; hq < 2; ++hq)
+                        O[hq][n] = mfma_bf16(as_bf16x8(pa[hq]), as_bf16x8(v), O[hq][n]);
                 }
+                __builtin_amdgcn_sched_barrier(0);
             }
         };
 #pragma unroll 1
         for (int t = 0; t < ntile; ++t) step(t, s_tile[t & 1]);
-        // every wave must agree on a recomputation: flags through LDS
-        __syncthreads();                               // last tile's P V done everywhere
-        int* s_flag = reinterpret_cast<int*>(s_p);
+        // every wave must agree on a recomputation (the tile barriers pair up): flags through LDS
         const bool wave_over = __any(over);
         if (lane == 0) s_flag[wave] = wave_over ? 1 : 0;
         __syncthreads();
         bool redo = false;
 #pragma unroll
         for (int w = 0; w < NW; ++w) redo |= s_flag[w] != 0;
-        __syncthreads();                               // flags read before s_p is reused
+        __syncthreads();                               // flags read before the next pass
         if (!redo) break;
     }
 
-    // totals per head (owner wave), shared with the waves holding that head's O columns
-    float* s_inv = reinterpret_cast<float*>(s_p);
-    float my_lse[2];
+    // totals per head (lanes c16 of head group hq), then 1/total for the heads of O's rows
+    // (head 16 hq + 4g + r sits in lane 4g + r's column)
+    float my_lse[2], inv[2];
 #pragma unroll
     for (int hq = 0; hq < 2; ++hq) {
         float l_tot = l_run[hq] + shfl_xor_f(l_run[hq], 16);
         l_tot += shfl_xor_f(l_tot, 32);
         my_lse[hq] = l_tot > 0.f ? m_ref[hq] * LN2 + logf(l_tot) : -__builtin_huge_valf();
-        if (g == 0) s_inv[wave * 32 + hq * 16 + c16] = l_tot > 0.f ? 1.f / l_tot : 0.f;
+        inv[hq] = l_tot > 0.f ? 1.f / l_tot : 0.f;
     }
-    __syncthreads();
 
     if (splits == 1) {
 #pragma unroll
-        for (int hg = 0; hg < NG; ++hg)
+        for (int hq = 0; hq < 2; ++hq)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int hh = hg * 16 + 4 * g + r;
+                const int hh = wave * 32 + hq * 16 + 4 * g + r;
+                const float ir = __shfl(inv[hq], 4 * g + r, 64);
                 if (hh >= H) continue;
-                const float ir = s_inv[hh];
                 uint16_t* orow = out + ((int64_t)row * H + hh) * 512;
 #pragma unroll
-                for (int d = 0; d < DPW; ++d)
-                    orow[16 * (n0 + d) + c16] = (uint16_t)bf16_bits(O[hg][d][r] * ir);
+                for (int n = 0; n < 32; ++n)
+                    orow[16 * n + c16] = (uint16_t)bf16_bits(O[hq][n][r] * ir);
             }
         if (lse && g == 0)
 #pragma unroll
@@ -371,15 +346,15 @@ __global__ __launch_bounds__(NW * 64) void sparse_mla_kernel(
     } else {
         const int64_t pb = ((int64_t)row * splits + split) * H;
 #pragma unroll
-        for (int hg = 0; hg < NG; ++hg)
+        for (int hq = 0; hq < 2; ++hq)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int hh = hg * 16 + 4 * g + r;
+                const int hh = wave * 32 + hq * 16 + 4 * g + r;
+                const float ir = __shfl(inv[hq], 4 * g + r, 64);
                 if (hh >= H) continue;
-                const float ir = s_inv[hh];
                 float* orow = part_o + (pb + hh) * 512;
 #pragma unroll
-                for (int d = 0; d < DPW; ++d) orow[16 * (n0 + d) + c16] = O[hg][d][r] * ir;
+                for (int n = 0; n < 32; ++n) orow[16 * n + c16] = O[hq][n][r] * ir;
             }
         if (g == 0)
 #pragma unroll
@@ -445,7 +420,8 @@ hipError_t launch_sparse_mla(const uint16_t* q, const uint16_t* kv, const int32_
 {
     if (T <= 0) return hipSuccess;
     // four waves of 32 head slots; fewer heads leave slots empty (their queries read as zero
-    // and their outputs are not written): one shape, whose registers fit without spilling
+    // and their outputs are not written): one shape, which fits its 512 registers without
+    // spilling to scratch (checked by the CPU tests on the compiler's resource report)
     if (H <= 128)
         return launch_nw<4>(q, kv, idx, seq_start, T, L, H, k, sm_scale, splits, out, lse, part_o,
                             part_lse, valid_pos0, stream);
