@@ -36,6 +36,8 @@
  *     its status and launches nothing.  Launch failures return DSA_ERR_HIP.  The library
  *     allocates no memory and keeps no global state; calls are thread-safe.  The caller
  *     keeps every buffer alive until the stream has reached the call.
+ *   - DSA_LOG=1 in the environment prints one line per call (entry point, sizes, status)
+ *     to stderr.
  *   - Not checked on the device (the caller's contract): scales positive and finite, no
  *     NaN fp8 codes (0x7F/0xFF), finite bf16 values, index lists without duplicates.
  *   - Supported shapes: H_I in {1,2,4,8,16,32,64,128}; 1 <= H <= 128;
@@ -190,7 +192,8 @@ size_t dsa_indexer_warmup_workspace_bytes(int T, int L, int H_I, int H);
  * [N,576], N = total_tokens; its one query sits at position L_b - 1 = seq_start[b+1] -
  * seq_start[b] - 1 and sees its whole cache.
  *   seq_start  DEVICE int64 [B+1], non-decreasing, seq_start[0] = 0, seq_start[B] = N,
- *              every length in [1, max_len] (not checked: the host never reads it);
+ *              every length in [1, max_len] (not checked: the host never reads it; a
+ *              sequence longer than max_len selects nothing: out 0 and lse -inf);
  *   q8 [B,H_I,128]; q_scale, w [B,H_I]; q [B,H,576]; out [B,H,512]; lse [B,H] or NULL;
  *   idx_out [B,k] or NULL (positions within the sequence, ascending, -1 padded).
  * workspace >= dsa_decode_workspace_bytes(B, max_len, total_tokens, H_I, H, k) bytes. */
@@ -203,6 +206,7 @@ dsa_status_t dsa_decode(int B, const int64_t* seq_start, int max_len, int64_t to
                         dsa_stream_t stream);
 size_t dsa_decode_workspace_bytes(int B, int max_len, int64_t total_tokens, int H_I, int H,
                                   int k);
+
 
 /* fp8 preparation of the indexer's inputs, the step upstream of dsa_index_scores (the
  * indexer runs in FP8: [gxzdkb-dsa] 秘密武器：DSA, [csdn-workflow] §3 两大核心组件).  Each

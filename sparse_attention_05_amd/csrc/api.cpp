@@ -8,11 +8,38 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cstdarg>
 #include <cstdint>
+#include <cstdio>
+#include <cstdlib>
 
 #include "kernels.h"
 
 namespace {
+
+// ---- host launch log: DSA_LOG=1 in the environment prints one line per entry-point call
+// (name, sizes, status) to stderr; read once per process
+bool log_on()
+{
+    static const bool on = [] {
+        const char* v = std::getenv("DSA_LOG");
+        return v && v[0] && !(v[0] == '0' && v[1] == 0);
+    }();
+    return on;
+}
+
+__attribute__((format(printf, 2, 3))) dsa_status_t logged(dsa_status_t st, const char* fmt, ...)
+{
+    if (log_on()) {
+        char buf[512];
+        va_list ap;
+        va_start(ap, fmt);
+        vsnprintf(buf, sizeof buf, fmt, ap);
+        va_end(ap);
+        std::fprintf(stderr, "[dsa] %s -> %s\n", buf, dsa_status_string(st));
+    }
+    return st;
+}
 
 constexpr int64_t kMaxElems = int64_t(1) << 40;   // T * max(L, k) bound
 constexpr size_t kAlign = 256;
@@ -101,10 +128,10 @@ const char* dsa_status_string(dsa_status_t status)
 
 int dsa_version(void) { return 104; }
 
-dsa_status_t dsa_index_scores(const uint8_t* q8, const float* q_scale, const float* w,
-                              const uint8_t* k8, const float* k_scale, int T, int L, int H_I,
-                              int q_pos0, float score_scale, float* scores, int64_t ld_scores,
-                              int write_masked, dsa_stream_t stream)
+static dsa_status_t dsa_index_scores_impl(const uint8_t* q8, const float* q_scale, const float* w,
+                                          const uint8_t* k8, const float* k_scale, int T, int L,
+                                          int H_I, int q_pos0, float score_scale, float* scores,
+                                          int64_t ld_scores, int write_masked, dsa_stream_t stream)
 {
     if (dsa_status_t st = check_rows(T, L, q_pos0)) return st;
     if (T > 0 && (!q8 || !q_scale || !w || !k8 || !k_scale || !scores))
@@ -125,8 +152,8 @@ dsa_status_t dsa_index_scores(const uint8_t* q8, const float* q_scale, const flo
 
 size_t dsa_topk_workspace_bytes(int, int, int) { return 0; }
 
-dsa_status_t dsa_topk(const float* scores, int64_t ld_scores, int T, int L, int q_pos0, int k,
-                      int32_t* idx, void*, size_t, dsa_stream_t stream)
+static dsa_status_t dsa_topk_impl(const float* scores, int64_t ld_scores, int T, int L, int q_pos0,
+                                  int k, int32_t* idx, dsa_stream_t stream)
 {
     if (dsa_status_t st = check_rows(T, L, q_pos0)) return st;
     if (T > 0 && (!scores || !idx)) return DSA_ERR_INVALID_ARGUMENT;
@@ -138,9 +165,9 @@ dsa_status_t dsa_topk(const float* scores, int64_t ld_scores, int T, int L, int 
                                              as_hip(stream)));
 }
 
-dsa_status_t dsa_sparse_mla(const uint16_t* q, const uint16_t* kv, const int32_t* idx, int T,
-                            int L, int H, int k, float sm_scale, uint16_t* out, float* lse,
-                            dsa_stream_t stream)
+static dsa_status_t dsa_sparse_mla_impl(const uint16_t* q, const uint16_t* kv, const int32_t* idx,
+                                        int T, int L, int H, int k, float sm_scale, uint16_t* out,
+                                        float* lse, dsa_stream_t stream)
 {
     if (T < 0 || L <= 0 || k < 1) return DSA_ERR_INVALID_ARGUMENT;
     if (T > 0 && (!q || !kv || !idx || !out)) return DSA_ERR_INVALID_ARGUMENT;
@@ -205,12 +232,12 @@ static dsa_status_t prefill_run(const uint8_t* q8, const float* q_scale, const f
     return DSA_OK;
 }
 
-dsa_status_t dsa_prefill(const uint8_t* q8, const float* q_scale, const float* w,
-                         const uint8_t* k8, const float* k_scale, const uint16_t* q,
-                         const uint16_t* kv, int T, int L, int H_I, int H, int k, int q_pos0,
-                         float score_scale, float sm_scale, uint16_t* out, float* lse,
-                         int32_t* idx_out, void* workspace, size_t workspace_bytes,
-                         dsa_stream_t stream)
+static dsa_status_t dsa_prefill_impl(const uint8_t* q8, const float* q_scale, const float* w,
+                                     const uint8_t* k8, const float* k_scale, const uint16_t* q,
+                                     const uint16_t* kv, int T, int L, int H_I, int H, int k,
+                                     int q_pos0, float score_scale, float sm_scale, uint16_t* out,
+                                     float* lse, int32_t* idx_out, void* workspace,
+                                     size_t workspace_bytes, dsa_stream_t stream)
 {
     if (dsa_status_t st = check_rows(T, L, q_pos0)) return st;
     if (T > 0 && (!q8 || !q_scale || !w || !k8 || !k_scale || !q || !kv || !out))
@@ -257,12 +284,14 @@ size_t dsa_prefill_varlen_workspace_bytes(int B, const int64_t* cu_seqlens_q,
     return ws < 0 ? 0 : (size_t)ws;
 }
 
-dsa_status_t dsa_prefill_varlen(int B, const int64_t* cu_seqlens_q, const int64_t* cu_seqlens_k,
-                                const uint8_t* q8, const float* q_scale, const float* w,
-                                const uint8_t* k8, const float* k_scale, const uint16_t* q,
-                                const uint16_t* kv, int H_I, int H, int k, float score_scale,
-                                float sm_scale, uint16_t* out, float* lse, int32_t* idx_out,
-                                void* workspace, size_t workspace_bytes, dsa_stream_t stream)
+static dsa_status_t dsa_prefill_varlen_impl(int B, const int64_t* cu_seqlens_q,
+                                            const int64_t* cu_seqlens_k, const uint8_t* q8,
+                                            const float* q_scale, const float* w, const uint8_t* k8,
+                                            const float* k_scale, const uint16_t* q,
+                                            const uint16_t* kv, int H_I, int H, int k,
+                                            float score_scale, float sm_scale, uint16_t* out,
+                                            float* lse, int32_t* idx_out, void* workspace,
+                                            size_t workspace_bytes, dsa_stream_t stream)
 {
     if (k < 1 || H < 1) return DSA_ERR_INVALID_ARGUMENT;
     const int64_t need = varlen_ws(B, cu_seqlens_q, cu_seqlens_k, k);
@@ -325,8 +354,9 @@ static dsa_status_t check_teacher(const uint16_t* q, const uint16_t* kv, int T, 
     return DSA_OK;
 }
 
-dsa_status_t dsa_attention_lse(const uint16_t* q, const uint16_t* kv, int T, int L, int H,
-                               int q_pos0, float sm_scale, float* lse, dsa_stream_t stream)
+static dsa_status_t dsa_attention_lse_impl(const uint16_t* q, const uint16_t* kv, int T, int L,
+                                           int H, int q_pos0, float sm_scale, float* lse,
+                                           dsa_stream_t stream)
 {
     if (dsa_status_t st = check_teacher(q, kv, T, L, H, q_pos0, sm_scale)) return st;
     if (T == 0) return DSA_OK;
@@ -334,9 +364,10 @@ dsa_status_t dsa_attention_lse(const uint16_t* q, const uint16_t* kv, int T, int
     return from_hip(dsa::launch_attention_lse(q, kv, T, H, q_pos0, sm_scale, lse, as_hip(stream)));
 }
 
-dsa_status_t dsa_attention_distribution(const uint16_t* q, const uint16_t* kv, const float* lse,
-                                        int T, int L, int H, int q_pos0, float sm_scale,
-                                        float* P, int64_t ld, dsa_stream_t stream)
+static dsa_status_t dsa_attention_distribution_impl(const uint16_t* q, const uint16_t* kv,
+                                                    const float* lse, int T, int L, int H,
+                                                    int q_pos0, float sm_scale, float* P,
+                                                    int64_t ld, dsa_stream_t stream)
 {
     if (dsa_status_t st = check_teacher(q, kv, T, L, H, q_pos0, sm_scale)) return st;
     if (ld < L) return DSA_ERR_INVALID_ARGUMENT;
@@ -353,12 +384,14 @@ size_t dsa_indexer_warmup_workspace_bytes(int T, int L, int H_I, int H)
     return warmup_ws(T, L, H_I, H).total;
 }
 
-dsa_status_t dsa_indexer_warmup(const uint8_t* q8, const float* q_scale, const float* w,
-                                const uint8_t* k8, const float* k_scale, const uint16_t* q,
-                                const uint16_t* kv, int T, int L, int H_I, int H, int q_pos0,
-                                float score_scale, float sm_scale, float* kl, float* dq,
-                                float* dw, float* dk, float* lse_teacher, float* lse_index,
-                                void* workspace, size_t workspace_bytes, dsa_stream_t stream)
+static dsa_status_t dsa_indexer_warmup_impl(const uint8_t* q8, const float* q_scale, const float* w,
+                                            const uint8_t* k8, const float* k_scale,
+                                            const uint16_t* q, const uint16_t* kv, int T, int L,
+                                            int H_I, int H, int q_pos0, float score_scale,
+                                            float sm_scale, float* kl, float* dq, float* dw,
+                                            float* dk, float* lse_teacher, float* lse_index,
+                                            void* workspace, size_t workspace_bytes,
+                                            dsa_stream_t stream)
 {
     if (dsa_status_t st = check_teacher(q, kv, T, L, H, q_pos0, sm_scale)) return st;
     if (!(score_scale > 0.f)) return DSA_ERR_INVALID_ARGUMENT;
@@ -419,13 +452,13 @@ size_t dsa_decode_workspace_bytes(int B, int max_len, int64_t total_tokens, int 
     return decode_ws(B, max_len, total_tokens, H, k).total;
 }
 
-dsa_status_t dsa_decode(int B, const int64_t* seq_start, int max_len, int64_t total_tokens,
-                        const uint8_t* q8, const float* q_scale, const float* w,
-                        const uint8_t* k8_cache, const float* k_scale_cache,
-                        const uint16_t* q, const uint16_t* kv_cache, int H_I, int H, int k,
-                        float score_scale, float sm_scale, uint16_t* out, float* lse,
-                        int32_t* idx_out, void* workspace, size_t workspace_bytes,
-                        dsa_stream_t stream)
+// Validation shared by the decode entry points (everything but the workspace).
+static dsa_status_t decode_check(int B, const int64_t* seq_start, int max_len,
+                                 int64_t total_tokens, const uint8_t* q8, const float* q_scale,
+                                 const float* w, const uint8_t* k8_cache,
+                                 const float* k_scale_cache, const uint16_t* q,
+                                 const uint16_t* kv_cache, int H_I, int H, int k,
+                                 float score_scale, float sm_scale, const uint16_t* out)
 {
     if (B < 0) return DSA_ERR_INVALID_ARGUMENT;
     if (B == 0) return DSA_OK;                       // nothing to decode
@@ -440,12 +473,18 @@ dsa_status_t dsa_decode(int B, const int64_t* seq_start, int max_len, int64_t to
     if (!aligned(q8, 16) || !aligned(k8_cache, 16) || !aligned(q, 16) ||
         !aligned(kv_cache, 16) || !aligned(out, 8))
         return DSA_ERR_INVALID_ARGUMENT;
-    const DecodeWs ws = decode_ws(B, max_len, total_tokens, H, k);
-    if (!workspace || workspace_bytes < ws.total) return DSA_ERR_WORKSPACE_TOO_SMALL;
-    if (!aligned(workspace, kAlign)) return DSA_ERR_INVALID_ARGUMENT;
+    return DSA_OK;
+}
 
-    hipStream_t s = as_hip(stream);
-    uint8_t* base = static_cast<uint8_t*>(workspace);
+// The decode step after validation, on a workspace laid out by decode_ws.
+static dsa_status_t decode_run(int B, const int64_t* seq_start, int max_len, const uint8_t* q8,
+                               const float* q_scale, const float* w, const uint8_t* k8_cache,
+                               const float* k_scale_cache, const uint16_t* q,
+                               const uint16_t* kv_cache, int H_I, int H, int k,
+                               float score_scale, float sm_scale, uint16_t* out, float* lse,
+                               int32_t* idx_out, uint8_t* base, const DecodeWs& ws,
+                               hipStream_t s)
+{
     float* scores = reinterpret_cast<float*>(base + ws.scores_off);
     int32_t* idx = idx_out ? idx_out : reinterpret_cast<int32_t*>(base + ws.idx_off);
     float* po = reinterpret_cast<float*>(base + ws.po_off);
@@ -463,8 +502,31 @@ dsa_status_t dsa_decode(int B, const int64_t* seq_start, int max_len, int64_t to
     return from_hip(e);
 }
 
-dsa_status_t dsa_quantize_fp8(const void* x, int x_is_bf16, int64_t n, uint8_t* q8,
-                              float* scale, dsa_stream_t stream)
+static dsa_status_t dsa_decode_impl(int B, const int64_t* seq_start, int max_len,
+                                    int64_t total_tokens, const uint8_t* q8, const float* q_scale,
+                                    const float* w, const uint8_t* k8_cache,
+                                    const float* k_scale_cache, const uint16_t* q,
+                                    const uint16_t* kv_cache, int H_I, int H, int k,
+                                    float score_scale, float sm_scale, uint16_t* out, float* lse,
+                                    int32_t* idx_out, void* workspace, size_t workspace_bytes,
+                                    dsa_stream_t stream)
+{
+    if (dsa_status_t st = decode_check(B, seq_start, max_len, total_tokens, q8, q_scale, w,
+                                       k8_cache, k_scale_cache, q, kv_cache, H_I, H, k,
+                                       score_scale, sm_scale, out))
+        return st;
+    if (B == 0) return DSA_OK;
+    const DecodeWs ws = decode_ws(B, max_len, total_tokens, H, k);
+    if (!workspace || workspace_bytes < ws.total) return DSA_ERR_WORKSPACE_TOO_SMALL;
+    if (!aligned(workspace, kAlign)) return DSA_ERR_INVALID_ARGUMENT;
+    return decode_run(B, seq_start, max_len, q8, q_scale, w, k8_cache, k_scale_cache, q,
+                      kv_cache, H_I, H, k, score_scale, sm_scale, out, lse, idx_out,
+                      static_cast<uint8_t*>(workspace), ws, as_hip(stream));
+}
+
+
+static dsa_status_t dsa_quantize_fp8_impl(const void* x, int x_is_bf16, int64_t n, uint8_t* q8,
+                                          float* scale, dsa_stream_t stream)
 {
     if (n < 0 || (x_is_bf16 != 0 && x_is_bf16 != 1)) return DSA_ERR_INVALID_ARGUMENT;
     if (n == 0) return DSA_OK;
@@ -474,9 +536,10 @@ dsa_status_t dsa_quantize_fp8(const void* x, int x_is_bf16, int64_t n, uint8_t* 
     return from_hip(dsa::launch_quantize_fp8(x, x_is_bf16 != 0, n, q8, scale, as_hip(stream)));
 }
 
-dsa_status_t dsa_decode_append(int B, const int64_t* seq_start, const void* k_new, int k_is_bf16,
-                               const uint16_t* kv_new, uint8_t* k8_cache, float* k_scale_cache,
-                               uint16_t* kv_cache, dsa_stream_t stream)
+static dsa_status_t dsa_decode_append_impl(int B, const int64_t* seq_start, const void* k_new,
+                                           int k_is_bf16, const uint16_t* kv_new, uint8_t* k8_cache,
+                                           float* k_scale_cache, uint16_t* kv_cache,
+                                           dsa_stream_t stream)
 {
     if (B < 0 || (k_is_bf16 != 0 && k_is_bf16 != 1)) return DSA_ERR_INVALID_ARGUMENT;
     if (B == 0) return DSA_OK;
@@ -491,8 +554,8 @@ dsa_status_t dsa_decode_append(int B, const int64_t* seq_start, const void* k_ne
                                               as_hip(stream)));
 }
 
-dsa_status_t dsa_window_indices(int T, int L, int q_pos0, int window, int32_t* idx,
-                                dsa_stream_t stream)
+static dsa_status_t dsa_window_indices_impl(int T, int L, int q_pos0, int window, int32_t* idx,
+                                            dsa_stream_t stream)
 {
     if (check_rows(T, L, q_pos0) != DSA_OK || window < 1) return DSA_ERR_INVALID_ARGUMENT;
     if (T == 0) return DSA_OK;
@@ -501,8 +564,9 @@ dsa_status_t dsa_window_indices(int T, int L, int q_pos0, int window, int32_t* i
     return from_hip(dsa::launch_window_indices(T, q_pos0, window, idx, as_hip(stream)));
 }
 
-dsa_status_t dsa_local_selected_indices(const int32_t* sel, int T, int L, int q_pos0, int k,
-                                        int window, int32_t* out, dsa_stream_t stream)
+static dsa_status_t dsa_local_selected_indices_impl(const int32_t* sel, int T, int L, int q_pos0,
+                                                    int k, int window, int32_t* out,
+                                                    dsa_stream_t stream)
 {
     if (check_rows(T, L, q_pos0) != DSA_OK || window < 1 || k < 1)
         return DSA_ERR_INVALID_ARGUMENT;
@@ -512,6 +576,135 @@ dsa_status_t dsa_local_selected_indices(const int32_t* sel, int T, int L, int q_
         (int64_t)T * (window + k) > kMaxElems)
         return DSA_ERR_UNSUPPORTED;
     return from_hip(dsa::launch_local_selected(sel, T, k, q_pos0, window, out, as_hip(stream)));
+}
+
+// ---- the exported entry points: the implementations above, with the DSA_LOG launch log
+
+dsa_status_t dsa_index_scores(const uint8_t* q8, const float* q_scale, const float* w,
+                              const uint8_t* k8, const float* k_scale, int T, int L, int H_I,
+                              int q_pos0, float score_scale, float* scores, int64_t ld_scores,
+                              int write_masked, dsa_stream_t stream)
+{
+    return logged(dsa_index_scores_impl(q8, q_scale, w, k8, k_scale, T, L, H_I, q_pos0, score_scale,
+                  scores, ld_scores, write_masked, stream),
+                  "dsa_index_scores T=%d L=%d H_I=%d q_pos0=%d", T, L, H_I, q_pos0);
+}
+
+dsa_status_t dsa_topk(const float* scores, int64_t ld_scores, int T, int L, int q_pos0, int k,
+                      int32_t* idx, void* workspace, size_t workspace_bytes, dsa_stream_t stream)
+{
+    (void)workspace;                                 // dsa_topk needs no workspace
+    (void)workspace_bytes;
+    return logged(dsa_topk_impl(scores, ld_scores, T, L, q_pos0, k, idx, stream),
+                  "dsa_topk T=%d L=%d q_pos0=%d k=%d", T, L, q_pos0, k);
+}
+
+dsa_status_t dsa_sparse_mla(const uint16_t* q, const uint16_t* kv, const int32_t* idx, int T,
+                            int L, int H, int k, float sm_scale, uint16_t* out, float* lse,
+                            dsa_stream_t stream)
+{
+    return logged(dsa_sparse_mla_impl(q, kv, idx, T, L, H, k, sm_scale, out, lse, stream),
+                  "dsa_sparse_mla T=%d L=%d H=%d k=%d", T, L, H, k);
+}
+
+dsa_status_t dsa_prefill(const uint8_t* q8, const float* q_scale, const float* w,
+                         const uint8_t* k8, const float* k_scale, const uint16_t* q,
+                         const uint16_t* kv, int T, int L, int H_I, int H, int k, int q_pos0,
+                         float score_scale, float sm_scale, uint16_t* out, float* lse,
+                         int32_t* idx_out, void* workspace, size_t workspace_bytes,
+                         dsa_stream_t stream)
+{
+    return logged(dsa_prefill_impl(q8, q_scale, w, k8, k_scale, q, kv, T, L, H_I, H, k, q_pos0,
+                  score_scale, sm_scale, out, lse, idx_out, workspace, workspace_bytes, stream),
+                  "dsa_prefill T=%d L=%d H_I=%d H=%d k=%d q_pos0=%d", T, L, H_I, H, k, q_pos0);
+}
+
+dsa_status_t dsa_prefill_varlen(int B, const int64_t* cu_seqlens_q, const int64_t* cu_seqlens_k,
+                                const uint8_t* q8, const float* q_scale, const float* w,
+                                const uint8_t* k8, const float* k_scale, const uint16_t* q,
+                                const uint16_t* kv, int H_I, int H, int k, float score_scale,
+                                float sm_scale, uint16_t* out, float* lse, int32_t* idx_out,
+                                void* workspace, size_t workspace_bytes, dsa_stream_t stream)
+{
+    return logged(dsa_prefill_varlen_impl(B, cu_seqlens_q, cu_seqlens_k, q8, q_scale, w, k8,
+                  k_scale, q, kv, H_I, H, k, score_scale, sm_scale, out, lse, idx_out,
+                  workspace, workspace_bytes, stream),
+                  "dsa_prefill_varlen B=%d H_I=%d H=%d k=%d", B, H_I, H, k);
+}
+
+dsa_status_t dsa_attention_lse(const uint16_t* q, const uint16_t* kv, int T, int L, int H,
+                               int q_pos0, float sm_scale, float* lse, dsa_stream_t stream)
+{
+    return logged(dsa_attention_lse_impl(q, kv, T, L, H, q_pos0, sm_scale, lse, stream),
+                  "dsa_attention_lse T=%d L=%d H=%d q_pos0=%d", T, L, H, q_pos0);
+}
+
+dsa_status_t dsa_attention_distribution(const uint16_t* q, const uint16_t* kv, const float* lse,
+                                        int T, int L, int H, int q_pos0, float sm_scale,
+                                        float* P, int64_t ld, dsa_stream_t stream)
+{
+    return logged(dsa_attention_distribution_impl(q, kv, lse, T, L, H, q_pos0, sm_scale, P, ld,
+                  stream),
+                  "dsa_attention_distribution T=%d L=%d H=%d q_pos0=%d", T, L, H, q_pos0);
+}
+
+dsa_status_t dsa_indexer_warmup(const uint8_t* q8, const float* q_scale, const float* w,
+                                const uint8_t* k8, const float* k_scale, const uint16_t* q,
+                                const uint16_t* kv, int T, int L, int H_I, int H, int q_pos0,
+                                float score_scale, float sm_scale, float* kl, float* dq,
+                                float* dw, float* dk, float* lse_teacher, float* lse_index,
+                                void* workspace, size_t workspace_bytes, dsa_stream_t stream)
+{
+    return logged(dsa_indexer_warmup_impl(q8, q_scale, w, k8, k_scale, q, kv, T, L, H_I, H, q_pos0,
+                  score_scale, sm_scale, kl, dq, dw, dk, lse_teacher, lse_index, workspace,
+                  workspace_bytes, stream),
+                  "dsa_indexer_warmup T=%d L=%d H_I=%d H=%d q_pos0=%d", T, L, H_I, H, q_pos0);
+}
+
+dsa_status_t dsa_decode(int B, const int64_t* seq_start, int max_len, int64_t total_tokens,
+                        const uint8_t* q8, const float* q_scale, const float* w,
+                        const uint8_t* k8_cache, const float* k_scale_cache,
+                        const uint16_t* q, const uint16_t* kv_cache, int H_I, int H, int k,
+                        float score_scale, float sm_scale, uint16_t* out, float* lse,
+                        int32_t* idx_out, void* workspace, size_t workspace_bytes,
+                        dsa_stream_t stream)
+{
+    return logged(dsa_decode_impl(B, seq_start, max_len, total_tokens, q8, q_scale, w, k8_cache,
+                  k_scale_cache, q, kv_cache, H_I, H, k, score_scale, sm_scale, out, lse,
+                  idx_out, workspace, workspace_bytes, stream),
+                  "dsa_decode B=%d max_len=%d total_tokens=%lld H_I=%d H=%d k=%d", B, max_len,
+                  (long long)total_tokens, H_I, H, k);
+}
+
+dsa_status_t dsa_quantize_fp8(const void* x, int x_is_bf16, int64_t n, uint8_t* q8,
+                              float* scale, dsa_stream_t stream)
+{
+    return logged(dsa_quantize_fp8_impl(x, x_is_bf16, n, q8, scale, stream),
+                  "dsa_quantize_fp8 n=%lld", (long long)n);
+}
+
+dsa_status_t dsa_decode_append(int B, const int64_t* seq_start, const void* k_new, int k_is_bf16,
+                               const uint16_t* kv_new, uint8_t* k8_cache, float* k_scale_cache,
+                               uint16_t* kv_cache, dsa_stream_t stream)
+{
+    return logged(dsa_decode_append_impl(B, seq_start, k_new, k_is_bf16, kv_new, k8_cache,
+                  k_scale_cache, kv_cache, stream),
+                  "dsa_decode_append B=%d", B);
+}
+
+dsa_status_t dsa_window_indices(int T, int L, int q_pos0, int window, int32_t* idx,
+                                dsa_stream_t stream)
+{
+    return logged(dsa_window_indices_impl(T, L, q_pos0, window, idx, stream),
+                  "dsa_window_indices T=%d L=%d q_pos0=%d window=%d", T, L, q_pos0, window);
+}
+
+dsa_status_t dsa_local_selected_indices(const int32_t* sel, int T, int L, int q_pos0, int k,
+                                        int window, int32_t* out, dsa_stream_t stream)
+{
+    return logged(dsa_local_selected_indices_impl(sel, T, L, q_pos0, k, window, out, stream),
+                  "dsa_local_selected_indices T=%d L=%d q_pos0=%d k=%d window=%d", T, L, q_pos0,
+                  k, window);
 }
 
 }  // extern "C"

@@ -30,7 +30,7 @@ bool indexer_supports(int H_I);
 hipError_t launch_topk_prefill(const float* scores, int64_t ld, int T, int L, int q_pos0,
                                int k, int32_t* idx, hipStream_t stream);
 // Decode rows: row b at scores + seq_start[b] with seq_start[b+1] - seq_start[b] <= max_len
-// scores.  Long rows are split over several workgroups when ws (at least
+// scores (a row longer than max_len, outside that contract, selects nothing: all -1).  Long rows are split over several workgroups when ws (at least
 // topk_decode_workspace_bytes(B, max_len) bytes, 16-byte aligned; may be null when that is
 // 0) is given; otherwise each row is selected by one workgroup.
 size_t topk_decode_workspace_bytes(int B, int max_len);

@@ -458,6 +458,10 @@ __global__ __launch_bounds__(TK_THREADS) void topk_kernel(
     const int n = rr.n;
     int32_t* out = idx + (int64_t)row * k;
 
+    if (DECODE && n > L) {                        // longer than the scored range (L = max_len):
+        for (int j = tid; j < k; j += TK_THREADS) out[j] = -1;   // no selection at all
+        return;
+    }
     if (n <= k) {                                 // short row: every visible position
         for (int j = tid; j < k; j += TK_THREADS) out[j] = j < n ? j : -1;
         return;
@@ -774,7 +778,7 @@ hipError_t launch_topk_decode(const float* scores, const int64_t* seq_start, int
         seg = SegCands{key, pos, cnt, nseg};
     }
     hipLaunchKernelGGL(topk_kernel<true>, dim3(B), dim3(TK_THREADS), 0, stream, scores,
-                       (int64_t)0, seq_start, 0, 0, k, idx, seg);
+                       (int64_t)0, seq_start, max_len, 0, k, idx, seg);
     return hipGetLastError();
 }
 

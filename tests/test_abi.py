@@ -241,3 +241,26 @@ def test_binding_refuses_host_score_matrices(lib):
     import torch
     with pytest.raises(TypeError):
         dsa.dsa_topk(torch.zeros((4, 8)), 8, 0, 2)
+
+
+def test_launch_log_prints_one_line_per_call():
+    """DSA_LOG=1: each entry-point call prints its name, sizes and status to stderr (checked
+    on calls that validation rejects, so no GPU is needed)."""
+    import subprocess
+    import sys
+    code = ("import ctypes, sparse_attention_05_amd as d; lib = d.load(); "
+            "lib.dsa_topk(None, 4, -1, 4, 0, 2, None, None, 0, None); "
+            "lib.dsa_decode(4, None, 100, 300, *([None] * 7), 64, 128, 64, 0.1, 0.05, None, None, "
+            "None, None, 0, None)")
+    env = dict(os.environ, DSA_LOG="1")
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, env=env,
+                       cwd=ROOT)
+    assert r.returncode == 0, r.stderr
+    lines = [l for l in r.stderr.splitlines() if l.startswith("[dsa] ")]
+    assert lines == ["[dsa] dsa_topk T=-1 L=4 q_pos0=0 k=2 -> DSA_ERR_INVALID_ARGUMENT",
+                     "[dsa] dsa_decode B=4 max_len=100 total_tokens=300 H_I=64 H=128 k=64 -> "
+                     "DSA_ERR_INVALID_ARGUMENT"], r.stderr
+    env["DSA_LOG"] = "0"
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, env=env,
+                       cwd=ROOT)
+    assert "[dsa]" not in r.stderr

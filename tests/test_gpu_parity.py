@@ -407,6 +407,32 @@ def test_decode_64_sequences_to_128k_every_sequence(dsa):
     report(cfg.name, **stats)
 
 
+def test_decode_sequence_longer_than_max_len_selects_nothing(dsa):
+    """A sequence longer than the max_len the caller passes is outside the contract: it gets
+    no selection (indices -1, output 0, lse -inf) instead of reading unscored positions, and
+    the other sequences are unaffected."""
+    cfg = DecodeCfg("case", B=4, len_lo=300, len_hi=3000, k=256, H_I=64, H=32, w_std=1 / 8,
+                    seed=77)
+    inp = make_decode(cfg)
+    d = to_device(inp)
+    lens = _np(inp["lens"])
+    long_b = int(np.argmax(lens))
+    short_max = int(np.sort(lens)[-2])                  # every other sequence still fits
+    assert lens[long_b] > short_max
+    args = lambda ml: (d["seq_start"], ml, d["q8"], d["qs"], d["w"], d["k8"], d["ks"], d["q"],
+                       d["kv"], cfg.k, cfg.score_scale, cfg.sm_scale)
+    idx_ok = torch.empty((cfg.B, cfg.k), dtype=torch.int32, device="cuda")
+    out_ok, lse_ok, _ = dsa.dsa_decode(*args(inp["max_len"]), idx_out=idx_ok)
+    idx = torch.empty((cfg.B, cfg.k), dtype=torch.int32, device="cuda")
+    out, lse, _ = dsa.dsa_decode(*args(short_max), idx_out=idx)
+    torch.cuda.synchronize()
+    assert torch.all(idx[long_b] == -1)
+    assert torch.all(out[long_b].float() == 0) and torch.all(torch.isneginf(lse[long_b]))
+    others = [b for b in range(cfg.B) if b != long_b]
+    assert torch.equal(idx[others], idx_ok[others])
+    assert torch.equal(out[others], out_ok[others]) and torch.equal(lse[others], lse_ok[others])
+
+
 def _decode_integer_scores(vals_per_seq, k, H=8, seed=0):
     """Decode inputs whose indexer scores are exact small integers in any summation order:
     H_I = 1, a one-hot fp8 query (1.0 in dimension 0), key dimension 0 = the integer value
