@@ -34,7 +34,8 @@
  *   - Every call only enqueues work on `stream` (a hipStream_t; NULL = the default stream)
  *     and returns.  Arguments are validated before any HIP call: an invalid call returns
  *     its status and launches nothing.  Launch failures return DSA_ERR_HIP.  The library
- *     allocates no memory and keeps no global state; calls are thread-safe.  The caller
+ *     allocates no memory; it keeps no global state except the fixed scratch array of
+ *     dsa_decode_noalloc (one per GPU, see there).  Calls are thread-safe.  The caller
  *     keeps every buffer alive until the stream has reached the call.
  *   - DSA_LOG=1 in the environment prints one line per call (entry point, sizes, status)
  *     to stderr.
@@ -70,7 +71,8 @@ const char* dsa_status_string(dsa_status_t status);
 /* ABI version: major * 100 + minor (1.02: + dsa_quantize_fp8, dsa_decode_append, dsa_window_indices,
  * dsa_local_selected_indices; 1.03: + dsa_prefill_varlen, dsa_prefill_varlen_workspace_bytes;
  * 1.04: + dsa_attention_lse, dsa_attention_distribution, dsa_indexer_warmup,
- * dsa_indexer_warmup_workspace_bytes). */
+ * dsa_indexer_warmup_workspace_bytes; 1.05: + dsa_decode_noalloc,
+ * dsa_decode_noalloc_scratch_bytes). */
 int dsa_version(void);
 
 /* Lightning-indexer scores ([csdn-workflow] §4 步骤二, [devpress-dsa] §三 第二步):
@@ -207,6 +209,28 @@ dsa_status_t dsa_decode(int B, const int64_t* seq_start, int max_len, int64_t to
 size_t dsa_decode_workspace_bytes(int B, int max_len, int64_t total_tokens, int H_I, int H,
                                   int k);
 
+/* dsa_decode for callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): the same arguments without a
+ * workspace, the same kernels and results.  Its workspace is a fixed array of
+ * DSA_DECODE_NOALLOC_SCRATCH_BYTES inside the library, one copy per GPU, held by each GPU the
+ * library runs on until the process ends; the call allocates nothing and needs no prior
+ * set-up (the array's device address is looked up on the first call on a device).
+ *   - A call whose workspace, dsa_decode_workspace_bytes(B, max_len, total_tokens, H_I, H, k),
+ *     exceeds the array returns DSA_ERR_WORKSPACE_TOO_SMALL and launches nothing (128 MiB
+ *     covers, e.g., 64 sequences of up to 131,072 tokens and 4.2M cached tokens at k = 2048,
+ *     H = 128).  Other errors as dsa_decode.
+ *   - Every call on a GPU uses that GPU's one array, which keeps the last call's contents:
+ *     calls that overlap on one GPU (other streams, other threads) race and must be
+ *     serialised by the caller.  Nothing in the array needs clearing between calls. */
+#define DSA_DECODE_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+dsa_status_t dsa_decode_noalloc(int B, const int64_t* seq_start, int max_len,
+                                int64_t total_tokens, const uint8_t* q8, const float* q_scale,
+                                const float* w, const uint8_t* k8_cache,
+                                const float* k_scale_cache, const uint16_t* q,
+                                const uint16_t* kv_cache, int H_I, int H, int k,
+                                float score_scale, float sm_scale, uint16_t* out, float* lse,
+                                int32_t* idx_out, dsa_stream_t stream);
+size_t dsa_decode_noalloc_scratch_bytes(void);
 
 /* fp8 preparation of the indexer's inputs, the step upstream of dsa_index_scores (the
  * indexer runs in FP8: [gxzdkb-dsa] 秘密武器：DSA, [csdn-workflow] §3 两大核心组件).  Each

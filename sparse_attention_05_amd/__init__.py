@@ -32,7 +32,8 @@ EXPORTS = ("dsa_status_string", "dsa_version", "dsa_index_scores", "dsa_topk",
            "dsa_decode_workspace_bytes", "dsa_quantize_fp8", "dsa_decode_append",
            "dsa_window_indices", "dsa_local_selected_indices", "dsa_prefill_varlen",
            "dsa_prefill_varlen_workspace_bytes", "dsa_attention_lse",
-           "dsa_attention_distribution", "dsa_indexer_warmup", "dsa_indexer_warmup_workspace_bytes")
+           "dsa_attention_distribution", "dsa_indexer_warmup", "dsa_indexer_warmup_workspace_bytes",
+           "dsa_decode_noalloc", "dsa_decode_noalloc_scratch_bytes")
 
 
 class DSAError(RuntimeError):
@@ -69,6 +70,10 @@ def load(path: str = LIB_PATH):
                                        f32, P, P, P, P, sz, P]
             lib.dsa_decode_workspace_bytes.restype = sz
             lib.dsa_decode_workspace_bytes.argtypes = [i32, i32, i64, i32, i32, i32]
+            lib.dsa_decode_noalloc.argtypes = [i32, P, i32, i64, P, P, P, P, P, P, P, i32, i32,
+                                               i32, f32, f32, P, P, P, P]
+            lib.dsa_decode_noalloc_scratch_bytes.restype = sz
+            lib.dsa_decode_noalloc_scratch_bytes.argtypes = []
             lib.dsa_quantize_fp8.argtypes = [P, i32, i64, P, P, P]
             lib.dsa_decode_append.argtypes = [i32, P, P, i32, P, P, P, P, P]
             lib.dsa_window_indices.argtypes = [i32, i32, i32, i32, P, P]
@@ -86,7 +91,7 @@ def load(path: str = LIB_PATH):
             # entry points that return a dsa_status_t (the *_workspace_bytes queries return
             # size_t and are set above)
             for fn in ("dsa_index_scores", "dsa_topk", "dsa_sparse_mla", "dsa_prefill",
-                       "dsa_decode", "dsa_quantize_fp8", "dsa_decode_append",
+                       "dsa_decode", "dsa_decode_noalloc", "dsa_quantize_fp8", "dsa_decode_append",
                        "dsa_window_indices", "dsa_local_selected_indices", "dsa_prefill_varlen",
                        "dsa_attention_lse", "dsa_attention_distribution", "dsa_indexer_warmup"):
                 getattr(lib, fn).restype = i32
@@ -410,6 +415,43 @@ def dsa_decode(seq_start, max_len: int, q8, q_scale, w, k8, k_scale, q, kv, k: i
                           _ptr(k8), _ptr(k_scale), _ptr(q), _ptr(kv), H_I, H, k, score_scale,
                           sm_scale, _ptr(out), _ptr(lse), _ptr(idx_out), _ptr(workspace),
                           _nbytes(workspace), _stream()), "dsa_decode")
+    return out, lse, idx_out
+
+
+def dsa_decode_noalloc_scratch_bytes() -> int:
+    return int(load().dsa_decode_noalloc_scratch_bytes())
+
+
+def dsa_decode_noalloc(seq_start, max_len: int, q8, q_scale, w, k8, k_scale, q, kv, k: int,
+                       score_scale: float, sm_scale: float, out=None, lse=None, idx_out=None):
+    """dsa_decode on the library's fixed per-GPU scratch array instead of a workspace (for
+    callers that cannot allocate; pass `out`, `lse` and `idx_out` to allocate nothing here
+    either).  Calls that overlap on one GPU race on that array."""
+    lib = load()
+    q8, k8 = _u8(q8), _u8(k8)
+    B, H_I = q8.shape[0], q8.shape[1]
+    N, H = k8.shape[0], q.shape[1]
+    _req(seq_start, torch.int64, (B + 1,), "seq_start")
+    _req(q8, torch.uint8, (B, H_I, 128), "q8")
+    _req(q_scale, torch.float32, (B, H_I), "q_scale")
+    _req(w, torch.float32, (B, H_I), "w")
+    _req(k8, torch.uint8, (N, 128), "k8")
+    _req(k_scale, torch.float32, (N,), "k_scale")
+    _req(q, torch.bfloat16, (B, H, 576), "q")
+    _req(kv, torch.bfloat16, (N, 576), "kv")
+    dev = q.device
+    if out is None:
+        out = torch.empty((B, H, 512), dtype=torch.bfloat16, device=dev)
+    if lse is None:
+        lse = torch.empty((B, H), dtype=torch.float32, device=dev)
+    _req(out, torch.bfloat16, (B, H, 512), "out")
+    _req(lse, torch.float32, (B, H), "lse")
+    if idx_out is not None:
+        _req(idx_out, torch.int32, (B, k), "idx_out")
+    _check(lib.dsa_decode_noalloc(B, _ptr(seq_start), max_len, N, _ptr(q8), _ptr(q_scale),
+                                  _ptr(w), _ptr(k8), _ptr(k_scale), _ptr(q), _ptr(kv), H_I, H, k,
+                                  score_scale, sm_scale, _ptr(out), _ptr(lse), _ptr(idx_out),
+                                  _stream()), "dsa_decode_noalloc")
     return out, lse, idx_out
 
 

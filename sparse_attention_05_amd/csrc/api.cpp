@@ -12,6 +12,7 @@
 #include <cstdint>
 #include <cstdio>
 #include <cstdlib>
+#include <mutex>
 
 #include "kernels.h"
 
@@ -126,7 +127,7 @@ const char* dsa_status_string(dsa_status_t status)
     return "DSA_ERR_UNKNOWN";
 }
 
-int dsa_version(void) { return 104; }
+int dsa_version(void) { return 105; }
 
 static dsa_status_t dsa_index_scores_impl(const uint8_t* q8, const float* q_scale, const float* w,
                                           const uint8_t* k8, const float* k_scale, int T, int L,
@@ -524,6 +525,59 @@ static dsa_status_t dsa_decode_impl(int B, const int64_t* seq_start, int max_len
                       static_cast<uint8_t*>(workspace), ws, as_hip(stream));
 }
 
+// ---- decode without a caller workspace: the same kernels on a scratch array of this file,
+// one copy per GPU (a static device array; the loader places it in each GPU's memory when
+// the library's code is loaded there), for callers that cannot allocate.  Host code never
+// passes the array's name to a kernel (that is a host-side stand-in, not a device address):
+// it asks the runtime for each device's address once, with that device current, and keeps it.
+static __device__ __align__(256) uint8_t scratch[DSA_DECODE_NOALLOC_SCRATCH_BYTES];
+
+static constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[kMaxDevices];
+
+// this device's scratch address, looked up on its first use (nullptr on failure)
+static void* scratch_on(int dev)
+{
+    if (dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        int cur = -1;
+        if (hipGetDevice(&cur) != hipSuccess) return nullptr;
+        if (cur != dev && hipSetDevice(dev) != hipSuccess) return nullptr;
+        void* p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (cur != dev) (void)hipSetDevice(cur);
+        if (e != hipSuccess || !p) return nullptr;
+        g_scratch_ptr[dev] = p;
+    }
+    return g_scratch_ptr[dev];
+}
+
+static dsa_status_t dsa_decode_noalloc_impl(int B, const int64_t* seq_start, int max_len,
+                                            int64_t total_tokens, const uint8_t* q8,
+                                            const float* q_scale, const float* w,
+                                            const uint8_t* k8_cache, const float* k_scale_cache,
+                                            const uint16_t* q, const uint16_t* kv_cache, int H_I,
+                                            int H, int k, float score_scale, float sm_scale,
+                                            uint16_t* out, float* lse, int32_t* idx_out,
+                                            dsa_stream_t stream)
+{
+    if (dsa_status_t st = decode_check(B, seq_start, max_len, total_tokens, q8, q_scale, w,
+                                       k8_cache, k_scale_cache, q, kv_cache, H_I, H, k,
+                                       score_scale, sm_scale, out))
+        return st;
+    if (B == 0) return DSA_OK;
+    const DecodeWs ws = decode_ws(B, max_len, total_tokens, H, k);
+    if (ws.total > (size_t)DSA_DECODE_NOALLOC_SCRATCH_BYTES) return DSA_ERR_WORKSPACE_TOO_SMALL;
+    hipStream_t s = as_hip(stream);
+    int dev = -1;
+    if ((s ? hipStreamGetDevice(s, &dev) : hipGetDevice(&dev)) != hipSuccess) return DSA_ERR_HIP;
+    uint8_t* base = static_cast<uint8_t*>(scratch_on(dev));
+    if (!base) return DSA_ERR_HIP;
+    return decode_run(B, seq_start, max_len, q8, q_scale, w, k8_cache, k_scale_cache, q,
+                      kv_cache, H_I, H, k, score_scale, sm_scale, out, lse, idx_out, base, ws, s);
+}
 
 static dsa_status_t dsa_quantize_fp8_impl(const void* x, int x_is_bf16, int64_t n, uint8_t* q8,
                                           float* scale, dsa_stream_t stream)
@@ -675,6 +729,23 @@ dsa_status_t dsa_decode(int B, const int64_t* seq_start, int max_len, int64_t to
                   "dsa_decode B=%d max_len=%d total_tokens=%lld H_I=%d H=%d k=%d", B, max_len,
                   (long long)total_tokens, H_I, H, k);
 }
+
+dsa_status_t dsa_decode_noalloc(int B, const int64_t* seq_start, int max_len,
+                                int64_t total_tokens, const uint8_t* q8, const float* q_scale,
+                                const float* w, const uint8_t* k8_cache,
+                                const float* k_scale_cache, const uint16_t* q,
+                                const uint16_t* kv_cache, int H_I, int H, int k,
+                                float score_scale, float sm_scale, uint16_t* out, float* lse,
+                                int32_t* idx_out, dsa_stream_t stream)
+{
+    return logged(dsa_decode_noalloc_impl(B, seq_start, max_len, total_tokens, q8, q_scale, w,
+                                          k8_cache, k_scale_cache, q, kv_cache, H_I, H, k,
+                                          score_scale, sm_scale, out, lse, idx_out, stream),
+                  "dsa_decode_noalloc B=%d max_len=%d total_tokens=%lld H_I=%d H=%d k=%d", B,
+                  max_len, (long long)total_tokens, H_I, H, k);
+}
+
+size_t dsa_decode_noalloc_scratch_bytes(void) { return DSA_DECODE_NOALLOC_SCRATCH_BYTES; }
 
 dsa_status_t dsa_quantize_fp8(const void* x, int x_is_bf16, int64_t n, uint8_t* q8,
                               float* scale, dsa_stream_t stream)

@@ -35,7 +35,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_status_strings_and_version(lib):
-    assert lib.dsa_version() == 104
+    assert lib.dsa_version() == 105
     for code, name in [(0, b"DSA_OK"), (1, b"DSA_ERR_INVALID_ARGUMENT"),
                        (2, b"DSA_ERR_UNSUPPORTED"), (3, b"DSA_ERR_WORKSPACE_TOO_SMALL"),
                        (4, b"DSA_ERR_HIP")]:
@@ -120,6 +120,27 @@ def test_decode_validation_and_workspace(lib):
     assert f(ws=NULL) == dsa.DSA_ERR_WORKSPACE_TOO_SMALL
     assert f(wsb=need - 1) == dsa.DSA_ERR_WORKSPACE_TOO_SMALL
     assert f(B=0, p=NULL) == dsa.DSA_OK
+
+
+def test_decode_noalloc_validation_and_scratch_limit(lib):
+    """The allocation-free decode validates like dsa_decode, and refuses (before any HIP call)
+    a batch whose workspace exceeds the library's fixed per-GPU scratch array."""
+    cap = lib.dsa_decode_noalloc_scratch_bytes()
+    assert cap == 128 << 20
+
+    def f(B=4, ml=100, N=300, H_I=64, H=128, k=64, p=FAKE):
+        return lib.dsa_decode_noalloc(B, p, ml, N, p, p, p, p, p, p, p, H_I, H, k, 0.1, 0.05,
+                                      p, p, NULL, NULL)
+    assert f(p=NULL) == dsa.DSA_ERR_INVALID_ARGUMENT
+    assert f(N=401) == dsa.DSA_ERR_INVALID_ARGUMENT
+    assert f(H_I=48) == dsa.DSA_ERR_UNSUPPORTED
+    assert f(B=0, p=NULL) == dsa.DSA_OK
+    # the 64-sequence decode batch at 128K fits; four times as many sequences do not
+    big = dict(B=64, ml=131072, N=4_199_844, H_I=64, H=128, k=2048)
+    assert lib.dsa_decode_workspace_bytes(64, 131072, 4_199_844, 64, 128, 2048) <= cap
+    over = dict(big, B=256, N=4 * 4_199_844)
+    assert lib.dsa_decode_workspace_bytes(256, 131072, 4 * 4_199_844, 64, 128, 2048) > cap
+    assert f(**over) == dsa.DSA_ERR_WORKSPACE_TOO_SMALL
 
 
 def test_quantize_and_append_validation(lib):

@@ -21,7 +21,7 @@ static int failures = 0;
 
 int main(void)
 {
-    EXPECT(dsa_version() == 104);
+    EXPECT(dsa_version() == 105);
     EXPECT(strcmp(dsa_status_string(DSA_OK), "DSA_OK") == 0);
     EXPECT(strcmp(dsa_status_string(DSA_ERR_WORKSPACE_TOO_SMALL), "DSA_ERR_WORKSPACE_TOO_SMALL") == 0);
 
@@ -30,6 +30,7 @@ int main(void)
     EXPECT(dsa_prefill_workspace_bytes(131072, 131072, 64, 128, 2048) > ((size_t)1 << 31));
     EXPECT(dsa_prefill_workspace_bytes(0, 10, 64, 128, 16) == 0);
     EXPECT(dsa_topk_workspace_bytes(4, 100, 8) == 0);
+    EXPECT(dsa_decode_noalloc_scratch_bytes() == DSA_DECODE_NOALLOC_SCRATCH_BYTES);
 
     /* rejected before any HIP call: nothing is launched, nothing written */
     float sc[4] = {1.f, 2.f, 3.f, 4.f};
@@ -43,6 +44,8 @@ int main(void)
     EXPECT(dsa_sparse_mla(NULL, NULL, NULL, 1, 1, 129, 1, 1.f, NULL, NULL, NULL)
            != DSA_OK);
     EXPECT(dsa_window_indices(1, 1, 0, 0, idx, NULL) == DSA_ERR_INVALID_ARGUMENT);
+    EXPECT(dsa_decode_noalloc(1, NULL, 1, 1, NULL, NULL, NULL, NULL, NULL, NULL, NULL, 64, 128,
+                              16, 1.f, 1.f, NULL, NULL, NULL, NULL) == DSA_ERR_INVALID_ARGUMENT);
     EXPECT(idx[0] == 7 && idx[3] == 7);
     printf(failures ? "c consumer: %d failures\n" : "c consumer ok\n", failures);
     return failures != 0;
