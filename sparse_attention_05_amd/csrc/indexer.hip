@@ -24,11 +24,16 @@ template <int HI> constexpr int ip_waves_per_simd() { return (HI >= 128 || HI <=
 constexpr int IP_KT = 128;                 // keys per LDS tile
 constexpr int IP_KSPLIT = 4096;            // keys per workgroup (grid.y)
 
-// LDS key tile: 128 keys x 128 B.  16-byte chunk c of key r lives at chunk c ^ (r & 7), so
-// the 16 keys one MFMA reads at equal chunk index fall on distinct banks.
+// LDS key tile: 128 keys x 128 B.  16-byte chunk c of key r lives at chunk
+// c ^ (r & 7) ^ ((r >> 3) & 1).  A 16-byte LDS read is served 16 lanes at a time, in the lane
+// groups {0-7, 24-31} and {8-15, 16-23} (and the same in the upper half-wave), 256 B per clock
+// when the group's 16-byte slots (address / 16 mod 16) are distinct.  A B-operand read gives
+// lane (g, c16) chunk 2g (or 2g + 1) of key c16 of a 16-key block, so a group pairs keys 0-7
+// at chunk 2g with keys 8-15 at chunk 2g + 2; the extra XOR by key bit 3 moves the second
+// half to the other chunk parity, and the group's slots are then all distinct.
 __device__ __forceinline__ int ktile_off(int key, int chunk)
 {
-    return key * 128 + ((chunk ^ (key & 7)) << 4);
+    return key * 128 + ((chunk ^ (key & 7) ^ ((key >> 3) & 1)) << 4);
 }
 
 // Head reduction of one 32-key step.  acc[kb][j][r] holds D for tile row 4g + r of tile j
