@@ -86,6 +86,12 @@ def parse():
                     help="skip timing the indexer warm-up loss and gradient")
     ap.add_argument("--no-prefill", action="store_true",
                     help="decode only (for profiling runs; prints no prefill value)")
+    ap.add_argument("--no-peaks", action="store_true",
+                    help="skip measuring the chip's MFMA and HBM-read peaks")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip timing the other prefill configurations (dense fallback, 32K)")
+    ap.add_argument("--configs", default="prefill-L2048-k2048-dense,prefill-L32768-k2048",
+                    help="comma-separated further prefill workloads timed beside the main one")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run a plain 1 GiB device copy 5 times and exit (the known-size "
                          "reference for FETCH_SIZE / WRITE_SIZE counter scaling)")
@@ -135,6 +141,7 @@ def main():
         decode = run_decode(args, WORKLOADS[args.decode_workload], dev)
         print(json.dumps({"decode": decode}), flush=True)
         return
+    peaks = None if args.no_peaks else run_peaks(dev)
     log("generating", cfg.name)
     inp = make_prefill(cfg, device=dev)
     out = torch.empty((T, H, D_V), dtype=torch.bfloat16, device=dev)
@@ -221,17 +228,32 @@ def main():
                           achieved=round(ach, 2), unit=unit, peak=peak,
                           frac=round(ach / peak, 4), bound=bound,
                           traffic=measured_traffic(cfg.name, name, chunk))
+        mp = measured_peak_for(peaks, bound, name)
+        if mp:
+            kern[name]["measured_peak"] = mp
+            kern[name]["frac_of_measured"] = round(ach / mp, 4)
+        if name == "sparse_mla":
+            # the selected rows it gathers (1152 B each) from L2 / the last-level cache / HBM
+            kern[name]["gather_GBps"] = round(kunits[name] * D_QK * 2 / sec / 1e9, 1)
     dom = max(kern, key=lambda n: kern[n]["total_ms"])
     log("kernels:", json.dumps(kern))
     roofline = dict(bound=kern[dom]["bound"], achieved=kern[dom]["achieved"],
                     peak=kern[dom]["peak"], unit=kern[dom]["unit"], frac=kern[dom]["frac"],
                     traffic=kern[dom]["traffic"], kernel=dom, avg_launch_ms=kern[dom]["avg_launch_ms"])
+    if "frac_of_measured" in kern[dom]:
+        roofline["measured_peak"] = kern[dom]["measured_peak"]
+        roofline["frac_of_measured"] = kern[dom]["frac_of_measured"]
     sum_pairs, sum_sel = prefill_units(L, T, cfg.q_pos0, k, 0, T)
     prefill_flops = sum_pairs * idx_flop + sum_sel * mla_flop
     del sc, idx
 
+    # ---- the other prefill configurations (dense fallback, 32K), after the main one is freed
+    main_inputs = (inp, out, lse, ws)
+
     # ---- decode
-    decode = None if args.no_decode else run_decode(args, WORKLOADS[args.decode_workload], dev)
+    decode = None if args.no_decode else run_decode(args, WORKLOADS[args.decode_workload], dev,
+                                                    peaks, want_host=not args.no_cpu_baseline)
+    dec_host = decode.pop("_host", None) if decode else None
 
     # ---- sliding-window attention through the same sparse MLA (an alternative index rule)
     window = None if args.no_window else run_window(args, cfg, inp, out, lse, chunk, dev)
@@ -246,10 +268,18 @@ def main():
     # ---- indexer warm-up: KL to the dense attention distribution and its gradient
     warm = None if args.no_warmup_kl else run_warmup_kl(args, WORKLOADS[args.warmup_workload], dev)
 
-    # ---- CPU oracle baseline on sampled rows of the same prefill workload
+    # ---- CPU oracle baseline on sampled rows of the same prefill workload, and the whole
+    # decode step of the decode workload
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(inp, cfg, args.cpu_seconds)
+        if dec_host is not None:
+            cpu["decode"] = cpu_baseline_decode(dec_host)
+        del dec_host
+    del main_inputs, inp, out, lse, ws
+    torch.cuda.empty_cache()
+    configs = None if args.no_configs else [run_prefill_config(args, WORKLOADS[w], dev, peaks)
+                                            for w in args.configs.split(",") if w]
 
     res = {
         "metric": "DSA prefill tokens/s at L=128K (k=2048); decode tokens/s; % MFMA/HBM peak",
@@ -268,7 +298,9 @@ def main():
                    "batch": 1, "chunk_rows": chunk,
                    "algorithmic_tflop_per_step": round(prefill_flops / 1e12, 3)},
         "roofline": roofline,
+        "measured_peaks": peaks,
         "kernels": kern,
+        "prefill_configs": configs,
         "decode": decode,
         "input_prep": prep,
         "window_attention": window,
@@ -279,8 +311,9 @@ def main():
     print(json.dumps(res), flush=True)
 
 
-def run_decode(args, dcfg, dev):
-    """Time dsa_decode on one batch of the decode workload; returns its result object."""
+def run_decode(args, dcfg, dev, peaks=None, want_host=False):
+    """Time dsa_decode on one batch of the decode workload; returns its result object (with
+    the inputs as host arrays under "_host" when want_host, for the CPU oracle's timing)."""
     import numpy as np
     import torch
 
@@ -336,12 +369,142 @@ def run_decode(args, dcfg, dev):
     torch.cuda.synchronize()
     app_us = d0.elapsed_time(d1) / 50 * 1e3
     log("decode cache append %.2f us" % app_us)
-    return dict(workload=dcfg.name, ms_per_step=round(dms, 4),
-                tokens_per_s=round(B / (dms / 1e3), 1), sequences=B, context_tokens=int(N),
-                steps=dsteps, append_us=round(app_us, 2),
-                roofline=dict(bound="hbm", achieved=round(gbs, 1), peak=HBM_PEAK_GBS,
-                              unit="GB/s", frac=round(gbs / HBM_PEAK_GBS, 4),
-                              algorithmic_bytes=int(hbm)))
+    res = dict(workload=dcfg.name, ms_per_step=round(dms, 4),
+               tokens_per_s=round(B / (dms / 1e3), 1), sequences=B, context_tokens=int(N),
+               steps=dsteps, append_us=round(app_us, 2),
+               roofline=dict(bound="hbm", achieved=round(gbs, 1), peak=HBM_PEAK_GBS,
+                             unit="GB/s", frac=round(gbs / HBM_PEAK_GBS, 4),
+                             algorithmic_bytes=int(hbm)))
+    mp = measured_peak_for(peaks, "hbm", "decode")
+    if mp:
+        res["roofline"]["measured_peak"] = mp
+        res["roofline"]["frac_of_measured"] = round(gbs / mp, 4)
+    if want_host:
+        from synth import host_arrays
+        res["_host"] = host_arrays(dinp)
+    del dinp, dout, dlse, dws
+    torch.cuda.empty_cache()
+    return res
+
+
+def measured_peak_for(peaks, bound, name):
+    """The measured peak a kernel's roofline is also compared with (None when not measured)."""
+    if not peaks:
+        return None
+    if bound == "hbm":
+        return peaks["hbm_read_GBps"]
+    return peaks["fp8_tflops"] if name == "indexer" else peaks["bf16_tflops"]
+
+
+def run_peaks(dev):
+    """The chip's measured peaks: dependency-free fp8 and bf16 MFMA streams on random
+    operands (one and two waves per SIMD on all 256 CUs; the better of the two) and a plain
+    16-byte read of an 8 GiB buffer (libdsa_peaks.so).  Each timed with HIP events on the
+    launch stream, best of three."""
+    import ctypes
+
+    import torch
+
+    from sparse_attention_05_amd import build as hip_build
+
+    lib = ctypes.CDLL(hip_build.PEAKS_LIB)
+    lib.dsa_peak_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                  ctypes.c_void_p]
+    lib.dsa_peak_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p,
+                                  ctypes.c_void_p]
+    lib.dsa_peak_mfma.restype = lib.dsa_peak_read.restype = ctypes.c_int
+    stream = torch.cuda.current_stream()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    sink = torch.zeros(2 * cus * 256, dtype=torch.float32, device=dev)
+
+    def best(launch, reps=3):
+        launch()
+        torch.cuda.synchronize()
+        t = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            launch()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            t.append(e0.elapsed_time(e1))
+        return min(t)
+
+    res = {}
+    for kind, name, flop in ((0, "fp8_tflops", 2 * 16 * 16 * 128), (1, "bf16_tflops", 2 * 16 * 16 * 32)):
+        iters = 4000 if kind == 0 else 8000
+        rates = []
+        for per_simd in (1, 2):
+            blocks = cus * per_simd
+            ms = best(lambda: lib.dsa_peak_mfma(kind, blocks, iters, ctypes.c_void_p(sink.data_ptr()), sp))
+            rates.append(blocks * 4 * iters * 8 * flop / (ms / 1e3) / 1e12)
+        res[name] = round(max(rates), 1)
+    nbytes = 8 << 30
+    buf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    ms = best(lambda: lib.dsa_peak_read(ctypes.c_void_p(buf.data_ptr()), nbytes, cus * 16,
+                                        ctypes.c_void_p(sink.data_ptr()), sp), reps=5)
+    res["hbm_read_GBps"] = round(nbytes / (ms / 1e3) / 1e9, 1)
+    del buf, sink
+    torch.cuda.empty_cache()
+    res["method"] = ("dependency-free MFMA streams (8 independent accumulators per wave, random "
+                     "finite operands, 1 and 2 waves per SIMD on every CU) and one 16-byte-load "
+                     "read of an 8 GiB buffer; best of 3 / 5 runs")
+    res["published"] = {"fp8_tflops": PEAK["fp8"], "bf16_tflops": PEAK["bf16"],
+                        "hbm_GBps": HBM_PEAK_GBS}
+    log("measured peaks:", json.dumps({k: v for k, v in res.items() if k not in ("method",)}))
+    return res
+
+
+def run_prefill_config(args, pcfg, dev, peaks):
+    """One dsa_prefill call over a further prefill workload (every query row, inputs resident
+    in HBM): ms, tokens/s, and the fraction of the time its algorithmic work takes at peak
+    (indexer flops at the fp8 MFMA peak plus attention flops at the bf16 peak)."""
+    import torch
+
+    import sparse_attention_05_amd as dsa
+    from synth import make_prefill
+
+    log("generating", pcfg.name)
+    inp = make_prefill(pcfg, device=dev)
+    L, T, k, H_I, H = pcfg.L, pcfg.rows, pcfg.k, pcfg.H_I, pcfg.H
+    out = torch.empty((T, H, D_V), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((T, H), dtype=torch.float32, device=dev)
+    ws = torch.empty((max(1, dsa.dsa_prefill_workspace_bytes(T, L, H_I, H, k)),),
+                     dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        dsa.dsa_prefill(inp["q8"], inp["qs"], inp["w"], inp["k8"], inp["ks"], inp["q"],
+                        inp["kv"], k, pcfg.q_pos0, pcfg.score_scale, pcfg.sm_scale, out=out,
+                        lse=lse, workspace=ws)
+
+    for _ in range(2):
+        step()
+    torch.cuda.synchronize()
+    reps = 10 if L <= 4096 else 3
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    pairs, sel = prefill_units(L, T, pcfg.q_pos0, k, 0, T)
+    f_idx, f_mla = pairs * 2.0 * H_I * D_I, sel * 2.0 * H * (D_QK + D_V)
+    ideal = (f_idx / (PEAK["fp8"] * 1e12) + f_mla / (PEAK["bf16"] * 1e12)) * 1e3
+    res = dict(workload=pcfg.name, L=L, query_rows=T, k=k, H_I=H_I, H=H, ms=round(ms, 4),
+               tokens_per_s=round(T / (ms / 1e3), 1),
+               algorithmic_tflop=round((f_idx + f_mla) / 1e12, 4),
+               ms_at_peak=round(ideal, 4), frac_of_peak=round(ideal / ms, 4))
+    if peaks:
+        ideal_m = (f_idx / (peaks["fp8_tflops"] * 1e12) + f_mla / (peaks["bf16_tflops"] * 1e12)) * 1e3
+        res["frac_of_measured_peak"] = round(ideal_m / ms, 4)
+    log("prefill %s: %.3f ms, %.0f tokens/s, %.3f of peak" % (pcfg.name, ms, T / (ms / 1e3),
+                                                             ideal / ms))
+    del inp, out, lse, ws
+    torch.cuda.empty_cache()
+    return res
 
 
 def run_window(args, cfg, inp, out, lse, chunk, dev, W=2048):
@@ -555,10 +718,26 @@ def run_input_prep(args, cfg, dev):
                               frac=round(gbs / HBM_PEAK_GBS, 4), algorithmic_bytes=int(nbytes)))
 
 
+def host_info():
+    """The host the oracle ran on: the CPUs this process may use, OMP_NUM_THREADS, the model."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return dict(affinity_cpus=len(os.sched_getaffinity(0)),
+                omp_num_threads=os.environ.get("OMP_NUM_THREADS"), cpu_model=model)
+
+
 def cpu_baseline(inp, cfg, seconds):
-    """The oracle, as it is, on uniformly sampled query rows (indexer scores, top-k and
-    sparse MLA of each row).  Rows are sampled uniformly over the workload, so rows/s is an
-    unbiased estimate of the oracle's tokens/s on the whole workload."""
+    """The oracle, as it is, on uniformly sampled query rows of the workload (indexer scores,
+    top-k and sparse MLA of each row), all sampled rows in one call per step so that its
+    OpenMP loop over rows uses every thread it has.  Rows are drawn uniformly over the
+    workload, so rows/s is an unbiased estimate of the oracle's tokens/s on all of it."""
     import numpy as np
     import torch
 
@@ -567,33 +746,70 @@ def cpu_baseline(inp, cfg, seconds):
     k8 = inp["k8"].cpu().numpy()
     ks = inp["ks"].cpu().numpy()
     kv = inp["kv"].cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+    q8, qs, w = inp["q8"].cpu().numpy(), inp["qs"].cpu().numpy(), inp["w"].cpu().numpy()
     rng = np.random.default_rng(cfg.seed)
 
     def run(rows):
+        rows = np.sort(np.asarray(rows, np.int64))
+        dev_rows = torch.as_tensor(rows, device=inp["q"].device)
+        q = inp["q"][dev_rows].cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
         t0 = time.perf_counter()
-        for t in rows:
-            t = int(t)
-            p = cfg.q_pos0 + t
-            sc = oracle.index_scores(inp["q8"][t:t + 1].cpu().numpy(),
-                                     inp["qs"][t:t + 1].cpu().numpy(),
-                                     inp["w"][t:t + 1].cpu().numpy(), k8, ks, p,
-                                     cfg.score_scale)
-            idx = oracle.topk(sc, [p + 1], cfg.k)
-            q = inp["q"][t:t + 1].cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
-            oracle.sparse_mla(q, kv, idx, cfg.sm_scale)
+        sc = oracle.index_scores(q8, qs, w, k8, ks, cfg.q_pos0, cfg.score_scale, rows=rows)
+        idx = oracle.topk(sc, cfg.q_pos0 + rows + 1, cfg.k)
+        oracle.sparse_mla(q, kv, idx, cfg.sm_scale)
         return time.perf_counter() - t0
 
-    oracle.num_threads()
-    probe = rng.integers(0, cfg.rows, 4)
+    threads = oracle.num_threads()
+    probe = rng.integers(0, cfg.rows, max(8, threads))
     tp = run(probe)
-    n = int(min(4096, max(8, seconds / max(tp / len(probe), 1e-6))))
+    n = int(min(1024, max(len(probe), seconds / max(tp / len(probe), 1e-6))))
     rows = rng.integers(0, cfg.rows, n)
-    log("cpu oracle: %d sampled rows (probe %.2f s for 4)" % (n, tp))
+    log("cpu oracle: %d sampled rows (probe %.2f s for %d)" % (n, tp, len(probe)))
     sec = run(rows)
-    return dict(value=round(n / sec, 3), unit="tokens/s", cores=oracle.num_threads(),
-                kind="oracle", seconds=round(sec, 2),
-                sample="%d query rows drawn uniformly from the %d rows of %s "
-                       "(indexer scores + top-k + sparse MLA per row)" % (n, cfg.rows, cfg.name))
+    res = dict(value=round(n / sec, 3), unit="tokens/s", cores=threads, kind="oracle",
+               seconds=round(sec, 2),
+               sample="%d query rows drawn uniformly from the %d rows of %s (indexer scores + "
+                      "top-k + sparse MLA per row, rows spread over %d host threads)"
+                      % (n, cfg.rows, cfg.name, threads))
+    res.update(host_info())
+    return res
+
+
+def cpu_baseline_decode(h):
+    """The oracle on the whole decode step of the decode workload (every sequence: indexer
+    scores over its cache, top-k, sparse MLA), sequences spread over the host threads."""
+    from concurrent.futures import ThreadPoolExecutor
+    import ctypes
+
+    import numpy as np
+
+    import oracle
+
+    st = np.asarray(h["seq_start"], np.int64)
+    B, k = h["B"], h["k"]
+    threads = oracle.num_threads()
+
+    def one(b):
+        try:
+            ctypes.CDLL("libgomp.so.1").omp_set_num_threads(1)
+        except OSError:
+            pass
+        a, e = int(st[b]), int(st[b + 1])
+        sc = oracle.index_scores(h["q8"][b:b + 1], h["qs"][b:b + 1], h["w"][b:b + 1],
+                                 h["k8"][a:e], h["ks"][a:e], e - a - 1, h["score_scale"])
+        idx = oracle.topk(sc, [e - a], k)
+        oracle.sparse_mla(h["q"][b:b + 1], h["kv"][a:e], idx, h["sm_scale"])
+
+    t0 = time.perf_counter()
+    with ThreadPoolExecutor(max_workers=threads) as ex:
+        list(ex.map(one, range(B)))
+    sec = time.perf_counter() - t0
+    log("cpu oracle decode: %d sequences in %.2f s" % (B, sec))
+    res = dict(value=round(B / sec, 3), unit="tokens/s", cores=threads, kind="oracle",
+               seconds=round(sec, 2),
+               sample="the whole decode step: %d sequences, %d cached tokens" % (B, int(st[-1])))
+    res.update(host_info())
+    return res
 
 
 if __name__ == "__main__":

@@ -11,7 +11,7 @@ import pytest
 
 from sparse_attention_05_amd import build as hip_build
 
-KERNEL_SOURCES = [s for s in hip_build.SOURCES if s.endswith(".hip")]
+KERNEL_SOURCES = [s for s in hip_build.SOURCES + hip_build.PEAKS_SOURCES if s.endswith(".hip")]
 
 
 def _report(src):
