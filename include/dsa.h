@@ -111,7 +111,14 @@ dsa_status_t dsa_sparse_mla(const uint16_t* q, const uint16_t* kv, const int32_t
  * query chunks so the fp32 score rows of one chunk live in the workspace.  Arguments are
  * those of the three calls above; idx_out [T,k] (nullable) receives the selected indices.
  * workspace must be at least dsa_prefill_workspace_bytes(T, L, H_I, H, k) bytes,
- * 256-byte aligned. */
+ * 256-byte aligned.
+ * With H_I in {64, 128}, 11776 <= L <= 188416 and 2k <= 5888 the scores do not make a round
+ * trip through memory: each row's threshold comes from the scores of every 32nd key (every
+ * ceil(L/4096)-th beyond L = 131072), the indexer keeps only the (key, position) pairs at
+ * or above it, and an exact select over those gives the row's top-k; a row whose pairs
+ * cannot decide it (fewer than k, or more than 5888) is scored in full and selected by the
+ * exact top-k.  The indices are the same as the two-pass path's.  DSA_PREFILL_UNFUSED=1 in
+ * the environment (read once) keeps the two-pass path for every shape. */
 dsa_status_t dsa_prefill(const uint8_t* q8, const float* q_scale, const float* w,
                          const uint8_t* k8, const float* k_scale, const uint16_t* q,
                          const uint16_t* kv, int T, int L, int H_I, int H, int k, int q_pos0,
@@ -121,7 +128,7 @@ dsa_status_t dsa_prefill(const uint8_t* q8, const float* q_scale, const float* w
 size_t dsa_prefill_workspace_bytes(int T, int L, int H_I, int H, int k);
 
 /* Query rows per chunk that dsa_prefill uses for (T, L): chunk c covers rows
- * [c * rows, min(T, (c + 1) * rows)), and within a chunk the path is exactly
+ * [c * rows, min(T, (c + 1) * rows)), and within a chunk the result is exactly that of
  * dsa_index_scores (write_masked = 0, rows that see more than k tokens only) ->
  * dsa_topk -> dsa_sparse_mla on that chunk.  Returns 0 for invalid sizes. */
 int dsa_prefill_chunk_rows(int T, int L);

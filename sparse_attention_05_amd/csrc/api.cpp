@@ -74,9 +74,12 @@ int prefill_chunk_rows(int T, int L)
     return (int)std::min<int64_t>(std::max(T, 1), rows);
 }
 
+// Workspace of one prefill call: a chunk's fp32 score rows (also the home of the fused
+// selection's key sample and candidate arrays, which never need more room), its indices and
+// the fused selection's per-row threshold, candidate count and fallback flag.
 struct PrefillWs {
     int chunk;
-    size_t scores_off, idx_off, total;
+    size_t scores_off, idx_off, sel_off, total;
 };
 
 PrefillWs prefill_ws(int T, int L, int k)
@@ -85,8 +88,19 @@ PrefillWs prefill_ws(int T, int L, int k)
     w.chunk = prefill_chunk_rows(T, L);
     w.scores_off = 0;
     w.idx_off = align_up(size_t(w.chunk) * size_t(L) * 4);
-    w.total = w.idx_off + align_up(size_t(w.chunk) * size_t(k) * 4);
+    w.sel_off = w.idx_off + align_up(size_t(w.chunk) * size_t(k) * 4);
+    w.total = w.sel_off + 3 * align_up(size_t(w.chunk) * 4);
     return w;
+}
+
+// The fused selection applies (candidates instead of a score round trip through memory).
+bool prefill_fused(int L, int H_I, int k)
+{
+    static const bool off = [] {
+        const char* v = std::getenv("DSA_PREFILL_UNFUSED");
+        return v && v[0] == '1';
+    }();
+    return !off && dsa::indexer_fused_supports(H_I) && dsa::fused_select_supports(L, k);
 }
 
 // ---- decode workspace: packed scores, indices, split-K partials
@@ -207,6 +221,10 @@ static dsa_status_t prefill_run(const uint8_t* q8, const float* q_scale, const f
     uint8_t* base = static_cast<uint8_t*>(workspace);
     float* scores = reinterpret_cast<float*>(base + ws.scores_off);
     int32_t* idx_ws = reinterpret_cast<int32_t*>(base + ws.idx_off);
+    uint32_t* tau = reinterpret_cast<uint32_t*>(base + ws.sel_off);
+    int* fill = reinterpret_cast<int*>(base + ws.sel_off + align_up(size_t(ws.chunk) * 4));
+    int* fb = reinterpret_cast<int*>(base + ws.sel_off + 2 * align_up(size_t(ws.chunk) * 4));
+    const bool fused = prefill_fused(L, H_I, k);
     // first row that sees more than k tokens (earlier rows select all without scores)
     const int t_sel = std::max(0, k - q_pos0);
     for (int r0 = 0; r0 < T; r0 += ws.chunk) {
@@ -214,15 +232,51 @@ static dsa_status_t prefill_run(const uint8_t* q8, const float* q_scale, const f
         const int qp = q_pos0 + r0;
         int32_t* idx = idx_out ? idx_out + (int64_t)r0 * k : idx_ws;
         const int s0 = std::max(r0, t_sel);           // rows needing scores in this chunk
+        const int off = std::min(rows, s0 - r0);
+        const int nsel = rows - off;
+        const uint8_t* q8s = q8 + (int64_t)s0 * H_I * 128;
+        const float* qss = q_scale + (int64_t)s0 * H_I;
+        const float* ws_ = w + (int64_t)s0 * H_I;
         hipError_t e = hipSuccess;
-        if (s0 < r0 + rows) {
-            const int off = s0 - r0;
-            e = dsa::launch_indexer_prefill(q8 + (int64_t)s0 * H_I * 128,
-                                            q_scale + (int64_t)s0 * H_I, w + (int64_t)s0 * H_I,
-                                            k8, k_scale, rows - off, L, H_I, q_pos0 + s0,
-                                            score_scale, scores + (int64_t)off * L, L, s);
+        if (fused) {
+            // threshold sample -> candidates -> resolve; rows the candidates cannot decide
+            // are scored and selected exactly (their launches skip every other row)
+            dsa::IdxExtra ex;
+            ex.kstride = dsa::fused_sample_stride(L);
+            ex.ksplit = 512;                  // a short pass: spread it over more workgroups
+            const int nsamp = dsa::fused_sample_count(L);
+            if (nsel > 0)
+                e = dsa::launch_indexer_prefill(q8s, qss, ws_, k8, k_scale, nsel, L, H_I,
+                                                q_pos0 + s0, score_scale, scores, nsamp, s, ex);
+            if (e == hipSuccess)
+                e = dsa::launch_topk_threshold(scores, nsamp, nsel, L, q_pos0 + s0, k, tau,
+                                               fill, fb, s);
+            ex = dsa::IdxExtra{};
+            ex.tau = tau;
+            ex.fill = fill;
+            ex.cand = reinterpret_cast<uint2*>(scores);
+            ex.capr = dsa::fused_cand_cap();
+            if (e == hipSuccess && nsel > 0)
+                e = dsa::launch_indexer_candidates(q8s, qss, ws_, k8, k_scale, nsel, L, H_I,
+                                                   q_pos0 + s0, score_scale, ex, s);
+            if (e == hipSuccess)
+                e = dsa::launch_topk_resolve(ex.cand, ex.capr, fill, rows, L, qp, k, off, idx,
+                                             fb, s);
+            ex = dsa::IdxExtra{};
+            ex.only = fb;
+            if (e == hipSuccess && nsel > 0)
+                e = dsa::launch_indexer_prefill(q8s, qss, ws_, k8, k_scale, nsel, L, H_I,
+                                                q_pos0 + s0, score_scale,
+                                                scores + (int64_t)off * L, L, s, ex);
+            if (e == hipSuccess)
+                e = dsa::launch_topk_prefill_only(scores, L, rows, L, qp, k, idx, fb, off, s);
+        } else {
+            if (nsel > 0)
+                e = dsa::launch_indexer_prefill(q8s, qss, ws_, k8, k_scale, nsel, L, H_I,
+                                                q_pos0 + s0, score_scale,
+                                                scores + (int64_t)off * L, L, s);
+            if (e == hipSuccess) e = dsa::launch_topk_prefill(scores, L, rows, L, qp, k, idx, s);
         }
-        if (e == hipSuccess) e = dsa::launch_topk_prefill(scores, L, rows, L, qp, k, idx, s);
         if (e == hipSuccess)
             e = dsa::launch_sparse_mla(q + (int64_t)r0 * H * 576, kv, idx, nullptr, rows, L, H,
                                        k, sm_scale, 1, out + (int64_t)r0 * H * 512,

@@ -23,6 +23,7 @@ template <int HI> constexpr int ip_rows() { return HI >= 128 ? 128 : 64; }
 template <int HI> constexpr int ip_waves_per_simd() { return (HI >= 128 || HI <= 2) ? 2 : 4; }
 constexpr int IP_KT = 128;                 // keys per LDS tile
 constexpr int IP_KSPLIT = 4096;            // keys per workgroup (grid.y)
+constexpr int IP_CSTAGE = 256;             // candidates staged per wave (MODE 1)
 
 // LDS key tile: 128 keys x 128 B.  16-byte chunk c of key r lives at chunk
 // c ^ (r & 7) ^ ((r >> 3) & 1).  A 16-byte LDS read is served 16 lanes at a time, in the lane
@@ -119,32 +120,47 @@ __device__ __forceinline__ void reduce_heads(const v4f (&acc)[2][NT],
 //       y = key ranges of IP_KSPLIT keys.  Each wave keeps 128 (token, head) query rows
 // in registers as MFMA A operands; the workgroup streams 128-key tiles through a
 // double-buffered LDS ring that all eight waves read as B operands.
-template <int HI>
+// MODE 0 writes the scores.  One token per wave (HI >= 64) also allows a key stride (key
+// index s reads cache row kstride * s, visible when kstride * s <= the token's position:
+// the threshold sample) and a row filter (only[t] == 0: row t is skipped).  MODE 1 (one
+// token per wave) keeps, per row, the keys of score >= tau[t] as candidates.
+template <int HI, int MODE>
 __global__ __launch_bounds__(IP_WAVES * 64, ip_waves_per_simd<HI>()) void indexer_prefill_kernel(
     const uint8_t* __restrict__ q8, const float* __restrict__ qs, const float* __restrict__ w,
     const uint8_t* __restrict__ k8, const float* __restrict__ ks, int T, int q_pos0, float c,
-    float* __restrict__ scores, int64_t ld)
+    float* __restrict__ scores, int64_t ld, IdxExtra ex)
 {
     constexpr int IP_ROWS = ip_rows<HI>();
     constexpr int IP_NT = IP_ROWS / 16;        // 16-row MFMA tiles per wave
     constexpr int TPW = IP_ROWS / HI;
     constexpr int TB = IP_WAVES * TPW;
+    static_assert(MODE == 0 || TPW == 1, "candidates need one token per wave");
     __shared__ __attribute__((aligned(16))) uint8_t s_key[2][IP_KT * 128];
     __shared__ float s_ks[2][IP_KT];
+    // MODE 1: each wave stages its row's candidates here and appends them to the row's
+    // array a batch at a time (one atomic per batch)
+    __shared__ uint2 s_cand[IP_WAVES][MODE == 1 ? IP_CSTAGE : 1];
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int g = lane >> 4, c16 = lane & 15;
     const int blk = gridDim.x - 1 - blockIdx.x;
     const int t0 = blk * TB;
     const int t_end = min(T, t0 + TB);
-    const int p_last = q_pos0 + t_end - 1;            // last key any row here sees
-    const int kbeg = blockIdx.y * IP_KSPLIT;
+    const int kstride = TPW == 1 ? ex.kstride : 1;
+    const int p_last = (q_pos0 + t_end - 1) / kstride;   // last key any row here sees
+    const int ksplit = ex.ksplit > 0 ? ex.ksplit : IP_KSPLIT;
+    const int kbeg = blockIdx.y * ksplit;
     if (kbeg > p_last) return;                         // uniform over the workgroup
-    const int kend = min(kbeg + IP_KSPLIT, p_last + 1);
+    const int kend = min(kbeg + ksplit, p_last + 1);
+    if (TPW == 1 && ex.only) {                         // rows of this block still to score
+        bool any = false;
+        for (int t = t0; t < t_end; ++t) any |= ex.only[t] != 0;
+        if (!any) return;                              // uniform
+    }
 
     const int tw0 = t0 + wave * TPW;                   // first token row of this wave
-    const bool wave_active = tw0 < T;
-    const int pw_last = q_pos0 + min(T, tw0 + TPW) - 1;
+    const bool wave_active = tw0 < T && (TPW > 1 || !ex.only || ex.only[tw0] != 0);
+    const int pw_last = (q_pos0 + min(T, tw0 + TPW) - 1) / kstride;
     const int64_t nrows = (int64_t)T * HI;
 
     // A operands: row 16j + c16 of the wave's (token, head) rows, bytes [32g, 32g + 32)
@@ -174,7 +190,7 @@ __global__ __launch_bounds__(IP_WAVES * 64, ip_waves_per_simd<HI>()) void indexe
     auto gload = [&](int tile) {
         const int s = kbeg + tile * IP_KT + lkey;
         if (s < kend) {
-            const u32x4* src = reinterpret_cast<const u32x4*>(k8 + (int64_t)s * 128 + 32 * lpart);
+            const u32x4* src = reinterpret_cast<const u32x4*>(k8 + (int64_t)s * kstride * 128 + 32 * lpart);
             pre0 = src[0];
             pre1 = src[1];
         } else {
@@ -183,8 +199,20 @@ __global__ __launch_bounds__(IP_WAVES * 64, ip_waves_per_simd<HI>()) void indexe
         }
         if (tid < IP_KT) {
             const int s2 = kbeg + tile * IP_KT + tid;
-            pre_s = s2 < kend ? ks[s2] : 0.f;
+            pre_s = s2 < kend ? ks[(int64_t)s2 * kstride] : 0.f;
         }
+    };
+    // MODE 1: the wave's staged candidates (a wave-uniform count) and its row's threshold
+    int nst = 0;
+    const uint32_t tau_w = MODE == 1 && wave_active ? ex.tau[tw0] : 0u;
+    auto flush = [&]() {
+        int base = 0;
+        if (lane == 0) base = atomicAdd(&ex.fill[tw0], nst);
+        base = __shfl(base, 0, 64);
+        uint2* dst = ex.cand + (int64_t)tw0 * ex.capr;
+        for (int i = lane; i < nst; i += 64)
+            if (base + i < ex.capr) dst[base + i] = s_cand[wave][i];
+        nst = 0;
     };
     auto sstore = [&](int buf) {
         *reinterpret_cast<u32x4*>(&s_key[buf][ktile_off(lkey, 2 * lpart)]) = pre0;
@@ -238,8 +266,23 @@ __global__ __launch_bounds__(IP_WAVES * 64, ip_waves_per_simd<HI>()) void indexe
                     }
                     const float v = fold16(fold32(P[0], P[2]), fold32(P[1], P[3]));
                     const int sl = step * 64 + 16 * g + c16;          // key within the tile
-                    if (tbase + sl <= pw_last && tbase + sl < kend)
-                        srow[sl] = v * s_ks[buf][sl];
+                    const bool vis = tbase + sl <= pw_last && tbase + sl < kend;
+                    if constexpr (MODE == 0) {
+                        if (vis) srow[sl] = v * s_ks[buf][sl];
+                    } else {
+                        // lanes hold consecutive keys, so ballot order is position order
+                        const uint32_t key = score_key(v * s_ks[buf][sl]);
+                        const bool take = vis && key >= tau_w;
+                        const uint64_t m = __ballot(take);
+                        if (m) {
+                            const int nm = __popcll(m);
+                            if (nst + nm > IP_CSTAGE) flush();
+                            const int rk = __builtin_amdgcn_mbcnt_hi(
+                                (uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
+                            if (take) s_cand[wave][nst + rk] = make_uint2(key, tbase + sl);
+                            nst += nm;
+                        }
+                    }
                 }
             }
         } else if (wave_active && tbase <= pw_last) {
@@ -272,6 +315,8 @@ __global__ __launch_bounds__(IP_WAVES * 64, ip_waves_per_simd<HI>()) void indexe
         if (it + 1 < ntiles) sstore(buf ^ 1);
         __syncthreads();
     }
+    if constexpr (MODE == 1)
+        if (wave_active && nst > 0) flush();
 }
 
 __global__ __launch_bounds__(256) void mask_fill_kernel(int L, int q_pos0, float* scores,
@@ -374,16 +419,20 @@ __global__ __launch_bounds__(ID_WAVES * 64) void indexer_decode_kernel(
     }
 }
 
-template <int HI>
+template <int HI, int MODE>
 hipError_t launch_prefill_hi(const uint8_t* q8, const float* qs, const float* w,
                              const uint8_t* k8, const float* ks, int T, int L, int q_pos0,
-                             float c, float* scores, int64_t ld, hipStream_t stream)
+                             float c, float* scores, int64_t ld, const IdxExtra& ex,
+                             hipStream_t stream)
 {
     constexpr int TB = IP_WAVES * (ip_rows<HI>() / HI);
-    const int keys = min(L, q_pos0 + T);               // keys any row can see
-    dim3 grid((T + TB - 1) / TB, (keys + IP_KSPLIT - 1) / IP_KSPLIT);
-    hipLaunchKernelGGL(indexer_prefill_kernel<HI>, grid, dim3(IP_WAVES * 64), 0, stream, q8,
-                       qs, w, k8, ks, T, q_pos0, c, scores, ld);
+    const int kstride = ex.kstride > 1 ? ex.kstride : 1;
+    // key indices any row can see: s with kstride * s <= q_pos0 + T - 1 (and < L)
+    const int keys = min((L - 1) / kstride, (q_pos0 + T - 1) / kstride) + 1;
+    const int ksplit = ex.ksplit > 0 ? ex.ksplit : IP_KSPLIT;
+    dim3 grid((T + TB - 1) / TB, (keys + ksplit - 1) / ksplit);
+    hipLaunchKernelGGL((indexer_prefill_kernel<HI, MODE>), grid, dim3(IP_WAVES * 64), 0,
+                       stream, q8, qs, w, k8, ks, T, q_pos0, c, scores, ld, ex);
     return hipGetLastError();
 }
 
@@ -406,20 +455,39 @@ bool indexer_supports(int H_I)
            H_I == 64 || H_I == 128;
 }
 
+bool indexer_fused_supports(int H_I) { return H_I == 64 || H_I == 128; }
+
 hipError_t launch_indexer_prefill(const uint8_t* q8, const float* qs, const float* w,
                                   const uint8_t* k8, const float* ks, int T, int L, int H_I,
                                   int q_pos0, float c, float* scores, int64_t ld,
-                                  hipStream_t stream)
+                                  hipStream_t stream, const IdxExtra& ex)
 {
     if (T <= 0) return hipSuccess;
+    if ((ex.kstride > 1 || ex.only) && !indexer_fused_supports(H_I)) return hipErrorInvalidValue;
 #define DSA_IDX_CASE(HI) \
-    case HI: return launch_prefill_hi<HI>(q8, qs, w, k8, ks, T, L, q_pos0, c, scores, ld, stream);
+    case HI: return launch_prefill_hi<HI, 0>(q8, qs, w, k8, ks, T, L, q_pos0, c, scores, ld, ex, stream);
     switch (H_I) {
         DSA_IDX_CASE(1) DSA_IDX_CASE(2) DSA_IDX_CASE(4) DSA_IDX_CASE(8)
         DSA_IDX_CASE(16) DSA_IDX_CASE(32) DSA_IDX_CASE(64) DSA_IDX_CASE(128)
         default: return hipErrorInvalidValue;
     }
 #undef DSA_IDX_CASE
+}
+
+hipError_t launch_indexer_candidates(const uint8_t* q8, const float* qs, const float* w,
+                                     const uint8_t* k8, const float* ks, int T, int L, int H_I,
+                                     int q_pos0, float c, const IdxExtra& ex,
+                                     hipStream_t stream)
+{
+    if (T <= 0) return hipSuccess;
+    IdxExtra e = ex;
+    e.kstride = 1;
+    e.only = nullptr;
+    if (H_I == 64)
+        return launch_prefill_hi<64, 1>(q8, qs, w, k8, ks, T, L, q_pos0, c, nullptr, 0, e, stream);
+    if (H_I == 128)
+        return launch_prefill_hi<128, 1>(q8, qs, w, k8, ks, T, L, q_pos0, c, nullptr, 0, e, stream);
+    return hipErrorInvalidValue;
 }
 
 hipError_t launch_mask_fill(int T, int L, int q_pos0, float* scores, int64_t ld,

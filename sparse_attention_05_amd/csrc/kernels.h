@@ -8,12 +8,32 @@
 namespace dsa {
 
 // ---- lightning indexer --------------------------------------------------------------
+// Extra inputs of the prefill indexer passes; the defaults give plain scores.
+struct IdxExtra {
+    int kstride = 1;                 // key index s reads cache row kstride * s (visible when
+                                     // kstride * s <= the row's position): a strided sample
+    int ksplit = 0;                  // keys per workgroup (a multiple of 128; 0: the default)
+    const int* only = nullptr;       // rows t with only[t] == 0 are not scored
+    const uint32_t* tau = nullptr;   // candidates: per-row thresholds (score_key images)
+    int* fill = nullptr;             // candidates: per-row counts, 0 before the launch
+    uint2* cand = nullptr;           // candidates: (key, position) arrays of capr per row
+    int capr = 0;
+};
 // Scores of T query rows (positions q_pos0 + t) against keys 0..L-1; writes only the
-// visible entries s <= q_pos0 + t of each row (row t at scores + t * ld).
+// visible entries s <= q_pos0 + t of each row (row t at scores + t * ld).  kstride > 1 and
+// only need indexer_fused_supports(H_I).
 hipError_t launch_indexer_prefill(const uint8_t* q8, const float* qs, const float* w,
                                   const uint8_t* k8, const float* ks, int T, int L, int H_I,
                                   int q_pos0, float c, float* scores, int64_t ld,
-                                  hipStream_t stream);
+                                  hipStream_t stream, const IdxExtra& ex = IdxExtra{});
+// Candidates instead of scores: row t's visible keys with score_key(score) >= tau[t] are
+// appended to cand + t * capr as (key, position) in no particular order; fill[t] counts all
+// of them (entries past capr are counted, not stored).
+bool indexer_fused_supports(int H_I);
+hipError_t launch_indexer_candidates(const uint8_t* q8, const float* qs, const float* w,
+                                     const uint8_t* k8, const float* ks, int T, int L, int H_I,
+                                     int q_pos0, float c, const IdxExtra& ex,
+                                     hipStream_t stream);
 // Writes -inf to the masked entries q_pos0 + t < s < L of every row.
 hipError_t launch_mask_fill(int T, int L, int q_pos0, float* scores, int64_t ld,
                             hipStream_t stream);
@@ -29,6 +49,30 @@ bool indexer_supports(int H_I);
 // Prefill rows: row t at scores + t * ld with n_t = min(L, q_pos0 + t + 1) visible scores.
 hipError_t launch_topk_prefill(const float* scores, int64_t ld, int T, int L, int q_pos0,
                                int k, int32_t* idx, hipStream_t stream);
+// The fused prefill selection (the indexer writes candidates, not scores):
+//  1. launch_indexer_prefill with kstride = fused_sample_stride(L) scores the keys 0, S, 2S,
+//     .. (fused_sample_count(L) per row at most) into samp;
+//  2. launch_topk_threshold derives each row's threshold tau from them and clears fill, fb;
+//  3. launch_indexer_candidates keeps the keys at or above tau (capr = fused_cand_cap());
+//  4. launch_topk_resolve selects from the candidates, flagging in fb the rows whose
+//     candidates cannot decide (fewer than k, or more than the capacity);
+//  5. the flagged rows are scored (launch_indexer_prefill with only = fb) and selected by
+//     launch_topk_prefill_only.
+// Rows are relative to the chunk for the resolve (T rows from q_pos0, the first `off` of
+// them seeing at most k keys) and to the first scored row for tau, fill and fb.
+// Applies when fused_select_supports(L, k) and indexer_fused_supports(H_I).
+bool fused_select_supports(int L, int k);
+int fused_sample_stride(int L);
+int fused_sample_count(int L);
+int fused_cand_cap();
+hipError_t launch_topk_threshold(const float* samp, int64_t ld, int T, int L, int q_pos0,
+                                 int k, uint32_t* tau, int* fill, int* fb, hipStream_t stream);
+hipError_t launch_topk_resolve(const uint2* cand, int capr, const int* fill, int T, int L,
+                               int q_pos0, int k, int off, int32_t* idx, int* fb,
+                               hipStream_t stream);
+hipError_t launch_topk_prefill_only(const float* scores, int64_t ld, int T, int L, int q_pos0,
+                                    int k, int32_t* idx, const int* only, int only_off,
+                                    hipStream_t stream);
 // Decode rows: row b at scores + seq_start[b] with seq_start[b+1] - seq_start[b] <= max_len
 // scores (a row longer than max_len, outside that contract, selects nothing: all -1).  Long rows are split over several workgroups when ws (at least
 // topk_decode_workspace_bytes(B, max_len) bytes, 16-byte aligned; may be null when that is

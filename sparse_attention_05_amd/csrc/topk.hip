@@ -16,6 +16,16 @@
 // to the exact path: a 4096-bin histogram pass, an ordered pass keeping the positions above
 // the boundary bin and the boundary bin's candidates, an LDS radix resolve and a co-rank
 // merge (two reads of the row; a global multi-level pass if even that bin overflows).
+//
+// The fused prefill selection replaces the score row by candidates: a threshold per row
+// from the scores of its every 32nd key (topk_threshold_kernel, a lower bound of the key
+// with about 1.75k keys above it), the indexer keeping the keys at or above it, and
+// topk_resolve_kernel deciding the row from those alone.  Any candidate set holding at least
+// k keys contains every key at or above the row's k-th largest, ties included, so the exact
+// select over it gives the same top-k as the full row; rows short of k candidates, or with
+// more than fit, are flagged and go through the full scores and topk_kernel instead.
+#include <algorithm>
+
 #include "dsa_device.h"
 #include "kernels.h"
 
@@ -444,7 +454,8 @@ struct SegCands {
 template <bool DECODE>
 __global__ __launch_bounds__(TK_THREADS) void topk_kernel(
     const float* __restrict__ scores, int64_t ld, const int64_t* __restrict__ seq_start, int L,
-    int q_pos0, int k, int32_t* __restrict__ idx, SegCands seg)
+    int q_pos0, int k, int32_t* __restrict__ idx, SegCands seg, const int* __restrict__ only,
+    int only_off)
 {
     __shared__ __attribute__((aligned(16))) uint8_t s_buf[LDS_BYTES];
     __shared__ int s_wave_mem[2 * TK_WAVES];
@@ -454,6 +465,7 @@ __global__ __launch_bounds__(TK_THREADS) void topk_kernel(
 
     const int row = blockIdx.x;
     const int tid = threadIdx.x;
+    if (only && (row < only_off || only[row - only_off] == 0)) return;   // uniform
     const RowRef rr = row_of<DECODE>(row, scores, ld, seq_start, L, q_pos0);
     const int n = rr.n;
     int32_t* out = idx + (int64_t)row * k;
@@ -735,14 +747,192 @@ __global__ __launch_bounds__(TK_THREADS) void topk_segment_kernel(
     }
 }
 
+// ---- the fused prefill selection: threshold, then resolve over the indexer's candidates
+
+// Candidates a row aims for: about 1.75k keys above its threshold (on the 128K workload,
+// sampling every 32nd key, rows then keep 0.65k .. 1.4k above the k they need, within the
+// LDS capacity).
+__device__ __forceinline__ int fused_target(int k) { return min(7 * k / 4, (k + CAND_CAP) / 2); }
+
+// Row t (position q_pos0 + t, n = min(L, q_pos0 + t + 1) visible keys): its threshold from
+// the scores of the sampled keys 0, S, 2S, .. (samp + t * ld); 0 (every key) when the whole
+// row fits the candidate capacity.  Also clears the row's candidate count and fallback flag.
+__global__ __launch_bounds__(TK_THREADS) void topk_threshold_kernel(
+    const float* __restrict__ samp, int64_t ld, int S, int L, int q_pos0, int k,
+    uint32_t* __restrict__ tau, int* __restrict__ fill, int* __restrict__ fb)
+{
+    __shared__ __attribute__((aligned(16))) uint32_t s_keys[SAMPLE];
+    __shared__ int s_hist[4096];
+    __shared__ int s_wave_mem[2 * TK_WAVES];
+    ScanBuf s_wave{s_wave_mem, 0};
+    __shared__ uint32_t s_mm[2 * TK_WAVES];
+    const int row = blockIdx.x, tid = threadIdx.x;
+    const int n = min(L, q_pos0 + row + 1);
+    if (tid == 0) {
+        fill[row] = 0;
+        fb[row] = 0;
+    }
+    if (n <= CAND_CAP) {
+        if (tid == 0) tau[row] = 0u;
+        return;
+    }
+    const int ns = (n - 1) / S + 1;                     // sampled keys this row sees (<= SAMPLE)
+    for (int i = tid; i < ns; i += TK_THREADS) s_keys[i] = score_key(samp[(int64_t)row * ld + i]);
+    __syncthreads();
+    const int rs = (int)max<int64_t>(1, min<int64_t>(ns, ((int64_t)fused_target(k) * ns + n - 1) / n));
+    int unused_eq;
+    const uint32_t t = lds_select(s_keys, ns, rs, s_hist, s_wave, s_mm, &unused_eq, false);
+    if (tid == 0) tau[row] = t;
+}
+
+// Row t's top-k from its candidates (fill[t - off] of them, unordered, at cand + (t - off) *
+// capr): an exact radix select finds the k-th key tau and the ties to keep, two LDS bitmaps
+// over the row's positions (above tau; equal to tau) give the selection in position order.
+// Rows seeing at most k keys take every position.  A row whose candidates are fewer than k
+// (the threshold was too high) or more than fit is flagged in fb for the exact path.
+__global__ __launch_bounds__(TK_THREADS) void topk_resolve_kernel(
+    const uint2* __restrict__ cand, int capr, const int* __restrict__ fill, int L, int q_pos0,
+    int k, int off, int32_t* __restrict__ idx, int* __restrict__ fb)
+{
+    __shared__ __attribute__((aligned(16))) uint8_t s_buf[LDS_BYTES];
+    __shared__ int s_wave_mem[2 * TK_WAVES];
+    ScanBuf s_wave{s_wave_mem, 0};
+    __shared__ uint32_t s_mm[2 * TK_WAVES];
+    int* hist = reinterpret_cast<int*>(s_buf + OFF_HIST);
+    uint32_t* ckey = reinterpret_cast<uint32_t*>(s_buf + OFF_A);
+    int* cpos = reinterpret_cast<int*>(s_buf + OFF_A + 4 * CAND_CAP);
+
+    const int row = blockIdx.x, tid = threadIdx.x;
+    const int n = min(L, q_pos0 + row + 1);
+    int32_t* out = idx + (int64_t)row * k;
+    if (n <= k) {                                       // every visible position
+        for (int j = tid; j < k; j += TK_THREADS) out[j] = j < n ? j : -1;
+        return;
+    }
+    const int cr = row - off;
+    const int nc = fill[cr];
+    if (nc < k || nc > min(capr, CAND_CAP)) {           // uniform
+        if (tid == 0) fb[cr] = 1;
+        return;
+    }
+    const uint2* src = cand + (int64_t)cr * capr;
+    for (int i = tid; i < nc; i += TK_THREADS) {
+        const uint2 e = src[i];
+        ckey[i] = e.x;
+        cpos[i] = (int)e.y;
+    }
+    __syncthreads();
+    uint32_t kr[SEL_PT];
+    int pr[SEL_PT];
+    const int cnt = load_own(ckey, nc, kr);
+    load_own(cpos, nc, pr);
+    int need_eq;
+    const uint32_t tau = lds_select(ckey, nc, k, hist, s_wave, s_mm, &need_eq);
+
+    // bitmaps over positions 0 .. n-1 (nw words each) in the candidate area, now free
+    const int nw = (n + 31) >> 5;
+    uint32_t* gt = reinterpret_cast<uint32_t*>(s_buf + OFF_A);
+    uint32_t* eq = gt + nw;
+    __syncthreads();                                    // every candidate read
+    for (int i = tid; i < 2 * nw; i += TK_THREADS) gt[i] = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < SEL_PT; ++j) {
+        if (j < cnt && kr[j] >= tau) {
+            const int p = pr[j];
+            atomicOr(&(kr[j] > tau ? gt : eq)[p >> 5], 1u << (p & 31));
+        }
+    }
+    __syncthreads();
+    // thread t owns words [wpt t, wpt t + wpt)
+    const int wpt = (nw + TK_THREADS - 1) / TK_THREADS;
+    const int w0 = min(nw, wpt * tid), w1 = min(nw, w0 + wpt);
+    // the first need_eq ties in position order join the selection
+    int ne = 0;
+    for (int i = w0; i < w1; ++i) ne += __popc(eq[i]);
+    int tot;
+    int before = block_excl_scan(ne, s_wave, &tot);
+    for (int i = w0; i < w1 && before < need_eq; ++i) {
+        uint32_t m = eq[i];
+        uint32_t keep = 0u;
+        while (m && before < need_eq) {
+            const uint32_t b = m & (0u - m);
+            keep |= b;
+            m ^= b;
+            ++before;
+        }
+        gt[i] |= keep;
+    }
+    __syncthreads();
+    // emit in position order
+    int ns = 0;
+    for (int i = w0; i < w1; ++i) ns += __popc(gt[i]);
+    int slot = block_excl_scan(ns, s_wave, &tot);
+    for (int i = w0; i < w1; ++i) {
+        uint32_t m = gt[i];
+        while (m) {
+            const int b = __builtin_ctz(m);
+            m &= m - 1u;
+            if (slot < k) out[slot] = 32 * i + b;
+            ++slot;
+        }
+    }
+}
+
 }  // namespace
+
+// Every 32nd key (at most SAMPLE of them)
+int fused_sample_stride(int L) { return std::max(32, (L + SAMPLE - 1) / SAMPLE); }
+
+bool fused_select_supports(int L, int k)
+{
+    // candidates aim at 2k within CAND_CAP; a row's candidate array (8 bytes each) takes no
+    // more room than its fp32 scores would; both bitmaps of a row fit the candidate area
+    return 2 * k <= CAND_CAP && L >= 2 * CAND_CAP &&
+           2 * ((L + 31) / 32) * 4 <= 8 * CAND_CAP + 4 * SAMPLE;
+}
+
+int fused_cand_cap() { return CAND_CAP; }
+
+int fused_sample_count(int L) { return (L - 1) / fused_sample_stride(L) + 1; }
+
+hipError_t launch_topk_threshold(const float* samp, int64_t ld, int T, int L, int q_pos0,
+                                 int k, uint32_t* tau, int* fill, int* fb, hipStream_t stream)
+{
+    if (T <= 0) return hipSuccess;
+    hipLaunchKernelGGL(topk_threshold_kernel, dim3(T), dim3(TK_THREADS), 0, stream, samp, ld,
+                       fused_sample_stride(L), L, q_pos0, k, tau, fill, fb);
+    return hipGetLastError();
+}
+
+hipError_t launch_topk_resolve(const uint2* cand, int capr, const int* fill, int T, int L,
+                               int q_pos0, int k, int off, int32_t* idx, int* fb,
+                               hipStream_t stream)
+{
+    if (T <= 0) return hipSuccess;
+    hipLaunchKernelGGL(topk_resolve_kernel, dim3(T), dim3(TK_THREADS), 0, stream, cand, capr,
+                       fill, L, q_pos0, k, off, idx, fb);
+    return hipGetLastError();
+}
+
+hipError_t launch_topk_prefill_only(const float* scores, int64_t ld, int T, int L, int q_pos0,
+                                    int k, int32_t* idx, const int* only, int only_off,
+                                    hipStream_t stream)
+{
+    if (T <= 0) return hipSuccess;
+    hipLaunchKernelGGL(topk_kernel<false>, dim3(T), dim3(TK_THREADS), 0, stream, scores, ld,
+                       (const int64_t*)nullptr, L, q_pos0, k, idx,
+                       SegCands{nullptr, nullptr, nullptr, 0}, only, only_off);
+    return hipGetLastError();
+}
 
 hipError_t launch_topk_prefill(const float* scores, int64_t ld, int T, int L, int q_pos0,
                                int k, int32_t* idx, hipStream_t stream)
 {
     if (T <= 0) return hipSuccess;
     hipLaunchKernelGGL(topk_kernel<false>, dim3(T), dim3(TK_THREADS), 0, stream, scores, ld,
-                       (const int64_t*)nullptr, L, q_pos0, k, idx, SegCands{nullptr, nullptr, nullptr, 0});
+                       (const int64_t*)nullptr, L, q_pos0, k, idx, SegCands{nullptr, nullptr, nullptr, 0},
+                       (const int*)nullptr, 0);
     return hipGetLastError();
 }
 
@@ -778,7 +968,7 @@ hipError_t launch_topk_decode(const float* scores, const int64_t* seq_start, int
         seg = SegCands{key, pos, cnt, nseg};
     }
     hipLaunchKernelGGL(topk_kernel<true>, dim3(B), dim3(TK_THREADS), 0, stream, scores,
-                       (int64_t)0, seq_start, max_len, 0, k, idx, seg);
+                       (int64_t)0, seq_start, max_len, 0, k, idx, seg, (const int*)nullptr, 0);
     return hipGetLastError();
 }
 
