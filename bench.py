@@ -88,6 +88,8 @@ def parse():
                     help="decode only (for profiling runs; prints no prefill value)")
     ap.add_argument("--no-peaks", action="store_true",
                     help="skip measuring the chip's MFMA and HBM-read peaks")
+    ap.add_argument("--no-two-pass", action="store_true",
+                    help="skip timing the prefill step with the two-pass selection")
     ap.add_argument("--no-configs", action="store_true",
                     help="skip timing the other prefill configurations (dense fallback, 32K)")
     ap.add_argument("--configs", default="prefill-L2048-k2048-dense,prefill-L32768-k2048",
@@ -169,6 +171,26 @@ def main():
     ms = e0.elapsed_time(e1) / args.steps
     tok_s = T / (ms / 1e3)
     log("prefill %.3f ms/step, %.0f tokens/s" % (ms, tok_s))
+
+    # ---- the same step with the two-pass selection (every row's fp32 scores written by the
+    # indexer and read back by top-k), for comparison with the candidate selection above
+    two_pass = None
+    if not args.no_two_pass:
+        os.environ["DSA_PREFILL_UNFUSED"] = "1"
+        try:
+            step()
+            torch.cuda.synchronize()
+            e0.record(stream)
+            for _ in range(args.steps):
+                step()
+            e1.record(stream)
+            torch.cuda.synchronize()
+        finally:
+            del os.environ["DSA_PREFILL_UNFUSED"]
+        ms2 = e0.elapsed_time(e1) / args.steps
+        two_pass = dict(ms_per_step=round(ms2, 4), tokens_per_s=round(T / (ms2 / 1e3), 1),
+                        steps=args.steps, candidate_selection_saves_ms=round(ms2 - ms, 3))
+        log("prefill, two-pass selection: %.3f ms/step" % ms2)
 
     # ---- per-kernel pass: the fused call's chunks replayed through the single-kernel
     # entry points, HIP events around each launch on the same stream
@@ -300,6 +322,7 @@ def main():
         "roofline": roofline,
         "measured_peaks": peaks,
         "kernels": kern,
+        "prefill_two_pass": two_pass,
         "prefill_configs": configs,
         "decode": decode,
         "input_prep": prep,

@@ -93,13 +93,12 @@ PrefillWs prefill_ws(int T, int L, int k)
     return w;
 }
 
-// The fused selection applies (candidates instead of a score round trip through memory).
+// The fused selection applies (candidates instead of a score round trip through memory);
+// DSA_PREFILL_UNFUSED=1, read at every call, keeps the two-pass path.
 bool prefill_fused(int L, int H_I, int k)
 {
-    static const bool off = [] {
-        const char* v = std::getenv("DSA_PREFILL_UNFUSED");
-        return v && v[0] == '1';
-    }();
+    const char* v = std::getenv("DSA_PREFILL_UNFUSED");
+    const bool off = v && v[0] == '1';
     return !off && dsa::indexer_fused_supports(H_I) && dsa::fused_select_supports(L, k);
 }
 
