@@ -22,7 +22,10 @@ constexpr int IP_WAVES = 8;                // waves per workgroup
 template <int HI> constexpr int ip_rows() { return HI >= 128 ? 128 : 64; }
 template <int HI> constexpr int ip_waves_per_simd() { return (HI >= 128 || HI <= 2) ? 2 : 4; }
 constexpr int IP_KT = 128;                 // keys per LDS tile
-constexpr int IP_KSPLIT = 4096;            // keys per workgroup (grid.y)
+// keys per workgroup (grid.y): each workgroup loads its rows' queries once per key range, so
+// longer ranges fetch them fewer times (16,384: a quarter of the fetches of 4,096, and 1.5%
+// faster on a 128K chunk)
+constexpr int IP_KSPLIT = 16384;
 constexpr int IP_CSTAGE = 256;             // candidates staged per wave (MODE 1)
 
 // LDS key tile: 128 keys x 128 B.  16-byte chunk c of key r lives at chunk
