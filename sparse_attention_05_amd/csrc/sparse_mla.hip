@@ -365,38 +365,77 @@ __global__ __launch_bounds__(NW * 64) void sparse_mla_kernel(
     }
 }
 
-// Merge split partials: out = sum_s exp(lse_s - lse) o_s with lse = log sum_s exp(lse_s).
-__global__ __launch_bounds__(128) void mla_combine_kernel(const float* __restrict__ part_o,
-                                                          const float* __restrict__ part_lse,
-                                                          int H, int splits,
-                                                          uint16_t* __restrict__ out,
-                                                          float* __restrict__ lse)
+// Merge split partials: out = sum_s w_s o_s / sum_s w_s, w_s = exp(lse_s - M), M = max_s lse_s,
+// lse = M + log sum_s w_s.  One workgroup per (row, 16-head group): its 16 heads' weights go
+// to LDS first, then thread i of 256 takes the 16-byte words i, i + 256, .. of the group's
+// 16 x 512 fp32 block (head 16 grp + w / 128, dims 4 (w % 128) .. +3) of every split, all of a
+// split's loads in flight at once, and writes 8 bytes of bf16 output per word.
+constexpr int CB_THREADS = 256;
+constexpr int CB_WORDS = 16 * 128 / CB_THREADS;      // 16-byte words per thread and split
+constexpr int CB_SMAX = 8;                           // splits at most
+
+__global__ __launch_bounds__(CB_THREADS) void mla_combine_kernel(const float* __restrict__ part_o,
+                                                                 const float* __restrict__ part_lse,
+                                                                 int H, int splits,
+                                                                 uint16_t* __restrict__ out,
+                                                                 float* __restrict__ lse)
 {
-    const int row = blockIdx.x / H, hh = blockIdx.x % H;
-    const int tid = threadIdx.x;                     // 4 dims per thread
-    float mx = -__builtin_huge_valf();
-    for (int s = 0; s < splits; ++s)
-        mx = fmaxf(mx, part_lse[((int64_t)row * splits + s) * H + hh]);
-    float acc[4] = {0.f, 0.f, 0.f, 0.f}, den = 0.f;
-    if (mx != -__builtin_huge_valf()) {
-        for (int s = 0; s < splits; ++s) {
-            const int64_t pb = ((int64_t)row * splits + s) * H + hh;
-            const float ls = part_lse[pb];
-            if (ls == -__builtin_huge_valf()) continue;
-            const float wgt = expf(ls - mx);
-            den += wgt;
-            const v4f o = *reinterpret_cast<const v4f*>(part_o + pb * 512 + 4 * tid);
+    __shared__ float s_w[CB_SMAX][16];               // weight of split s for head 16 grp + h
+    __shared__ float s_inv[16];                      // 1 / sum of the weights
+    const int ng = (H + 15) >> 4;
+    const int row = blockIdx.x / ng, grp = blockIdx.x % ng;
+    const int tid = threadIdx.x;
+    if (tid < 16) {
+        const int hh = grp * 16 + tid;
+        float l[CB_SMAX], M = -__builtin_huge_valf();
 #pragma unroll
-            for (int e = 0; e < 4; ++e) acc[e] += wgt * o[e];
+        for (int sp = 0; sp < CB_SMAX; ++sp) {
+            l[sp] = sp < splits && hh < H ? part_lse[((int64_t)row * splits + sp) * H + hh]
+                                          : -__builtin_huge_valf();
+            M = fmaxf(M, l[sp]);
+        }
+        const float Mf = M == -__builtin_huge_valf() ? 0.f : M;   // no split has a valid entry
+        float den = 0.f;
+#pragma unroll
+        for (int sp = 0; sp < CB_SMAX; ++sp) {
+            const float wgt = expf(l[sp] - Mf);      // 0 for an empty split
+            s_w[sp][tid] = wgt;
+            den += wgt;
+        }
+        s_inv[tid] = den > 0.f ? 1.f / den : 0.f;
+        if (lse && hh < H) lse[(int64_t)row * H + hh] = den > 0.f ? Mf + logf(den) : -__builtin_huge_valf();
+    }
+    __syncthreads();
+    const int hl0 = tid >> 7;                        // word j: head hl0 + 2j, dims 4 (tid % 128)
+    const v4f* src = reinterpret_cast<const v4f*>(part_o) +
+                     ((int64_t)row * splits * H + grp * 16) * 128 + (tid & 127);
+    v4f acc[CB_WORDS];
+#pragma unroll
+    for (int j = 0; j < CB_WORDS; ++j) acc[j] = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int sp = 0; sp < splits; ++sp) {
+        v4f o[CB_WORDS];
+#pragma unroll
+        for (int j = 0; j < CB_WORDS; ++j) {
+            const int hl = hl0 + 2 * j;
+            o[j] = grp * 16 + hl < H ? src[((int64_t)sp * H + hl) * 128] : v4f{0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+        for (int j = 0; j < CB_WORDS; ++j) {
+            const float wgt = s_w[sp][hl0 + 2 * j];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[j][e] = fmaf(wgt, o[j][e], acc[j][e]);
         }
     }
-    const float inv = den > 0.f ? 1.f / den : 0.f;
-    u32x2 packed;
-    packed[0] = pack_bf16x2(acc[0] * inv, acc[1] * inv);
-    packed[1] = pack_bf16x2(acc[2] * inv, acc[3] * inv);
-    *reinterpret_cast<u32x2*>(out + ((int64_t)row * H + hh) * 512 + 4 * tid) = packed;
-    if (lse && tid == 0)
-        lse[(int64_t)row * H + hh] = den > 0.f ? mx + logf(den) : -__builtin_huge_valf();
+#pragma unroll
+    for (int j = 0; j < CB_WORDS; ++j) {
+        const int hl = hl0 + 2 * j, hh = grp * 16 + hl;
+        if (hh >= H) continue;
+        const float inv = s_inv[hl];
+        u32x2 packed;
+        packed[0] = pack_bf16x2(acc[j][0] * inv, acc[j][1] * inv);
+        packed[1] = pack_bf16x2(acc[j][2] * inv, acc[j][3] * inv);
+        *reinterpret_cast<u32x2*>(out + ((int64_t)row * H + hh) * 512 + 4 * (tid & 127)) = packed;
+    }
 }
 
 template <int NW>
@@ -432,8 +471,9 @@ hipError_t launch_mla_combine(const float* part_o, const float* part_lse, int T,
                               int splits, uint16_t* out, float* lse, hipStream_t stream)
 {
     if (T <= 0) return hipSuccess;
-    hipLaunchKernelGGL(mla_combine_kernel, dim3(T * H), dim3(128), 0, stream, part_o, part_lse,
-                       H, splits, out, lse);
+    if (splits > CB_SMAX) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(mla_combine_kernel, dim3(T * ((H + 15) / 16)), dim3(CB_THREADS), 0, stream,
+                       part_o, part_lse, H, splits, out, lse);
     return hipGetLastError();
 }
 
