@@ -62,6 +62,8 @@ def _cfg(L, k, H_I, H, seed, q_pos0=0, T=None, planted=0.0):
     # a chunk further in, H_I = 128, ragged sizes
     (20001, 2048, 128, 8, 20001 - 3001, 3001, 0.01),
     (16384, 2944, 64, 8, 5000, 7000, 0.0),
+    # k = 1: one candidate suffices; the smallest cache the candidate selection takes
+    (11776, 1, 64, 8, 0, None, 0.0),
 ])
 def test_fused_selection_equals_two_pass(dsa, L, k, H_I, H, q_pos0, T, planted):
     cfg = _cfg(L, k, H_I, H, seed=L + k + H_I, q_pos0=q_pos0, T=T, planted=planted)

@@ -81,26 +81,29 @@ def test_indexer_dense_heads_sampled_rows(dsa):
 
 
 @pytest.mark.parametrize("H_I", [4, 64])
-def test_indexer_many_key_ranges(dsa, H_I):
-    """Rows of 12,801 keys and more, split by the kernel over several 4096-key ranges (grid.y)
-    with 128-key tiles and causal early exit: full score rows compared element by element on
-    rows whose visible ends straddle the range and tile boundaries, with q_pos0 > 0."""
-    L, q_pos0 = 12800, 4000
-    cfg = _cfg(L, 16, H_I, 16, seed=300 + H_I, q_pos0=q_pos0)
+@pytest.mark.parametrize("q_pos0,T", [(16000, 1000), (32500, 7500)])
+def test_indexer_many_key_ranges(dsa, H_I, q_pos0, T):
+    """Rows of 16,001 keys and more against a 40,000-key cache, split by the kernel over
+    16,384-key ranges (grid.y) with 128-key tiles and causal early exit: full score rows
+    compared element by element on rows whose visible ends straddle the range and tile
+    boundaries (16,384 and 32,768), with q_pos0 > 0."""
+    L = 40000
+    cfg = _cfg(L, 16, H_I, 16, seed=300 + H_I + q_pos0, q_pos0=q_pos0, T=T)
     inp = make_prefill(cfg)
     h, d = host_arrays(inp), to_device(inp)
     g = dsa.dsa_index_scores(d["q8"], d["qs"], d["w"], d["k8"], d["ks"], q_pos0, cfg.score_scale)
     torch.cuda.synchronize()
-    pos = [4000, 4001, 4095, 4096, 4097, 4223, 4224, 4225, 5119, 5120, 6143, 6144, 8063, 8064,
-           8191, 8192, 8193, 8319, 8320, 12159, 12160, 12287, 12288, 12289, 12415, 12416,
-           12798, 12799]
-    rng = np.random.default_rng(H_I)
-    rows = np.unique(np.array(pos + rng.integers(q_pos0, L, 24).tolist()) - q_pos0)
-    rows = np.unique(np.concatenate([rows, [7, 8, 127, 128, 255, 256]]))
+    edges = [16255, 16256, 16383, 16384, 16385, 16511, 16512, 32639, 32640, 32767, 32768,
+             32769, 32895, 32896, 39998, 39999]
+    pos = [p for p in edges if q_pos0 <= p < q_pos0 + T] + [q_pos0, q_pos0 + 1, q_pos0 + T - 1]
+    rng = np.random.default_rng(H_I + q_pos0)
+    rows = np.unique(np.array(pos + rng.integers(q_pos0, q_pos0 + T, 24).tolist()) - q_pos0)
     o, bound = oracle.index_scores(h["q8"], h["qs"], h["w"], h["k8"], h["ks"], q_pos0,
                                    cfg.score_scale, rows=rows, with_bound=True)
-    err = check_scores(_np(g)[rows], o, bound, "indexer L=%d H_I=%d" % (L, H_I))
-    report("indexer-L12800-q_pos0-4000-H_I%d" % H_I, rows_checked=int(len(rows)), max_dscore=err)
+    err = check_scores(_np(g[torch.from_numpy(rows).cuda()]), o, bound,
+                       "indexer L=%d q_pos0=%d H_I=%d" % (L, q_pos0, H_I))
+    report("indexer-L40000-q_pos0-%d-H_I%d" % (q_pos0, H_I), rows_checked=int(len(rows)),
+           max_dscore=err)
 
 
 # ----------------------------------------------------------------------------- top-k
