@@ -215,13 +215,13 @@ __device__ __forceinline__ int load_own(const T* a, int n, T (&r)[SEL_PT])
 // returns the lowest key of the bin reached: a lower bound of the kth-largest key that at
 // most the keys of one 22-bit-resolved bin exceed beyond it.
 // hist: 4096 ints (levels alternate between its halves); s_mm: 2 * TK_WAVES ints.
-__device__ __forceinline__ uint32_t lds_select(const uint32_t* keys, int nk, int kth, int* hist,
-                                               ScanBuf& s_wave, uint32_t* s_mm, int* need_eq,
-                                               bool exact = true)
+// select_own takes the keys already in registers: each thread's kr[0 .. cnt), the keys of all
+// threads together being the nk keys selected from.
+__device__ __forceinline__ uint32_t select_own(const uint32_t (&kr)[SEL_PT], int cnt, int kth,
+                                               int* hist, ScanBuf& s_wave, uint32_t* s_mm,
+                                               int* need_eq, bool exact = true)
 {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    uint32_t kr[SEL_PT];
-    const int cnt = load_own(keys, nk, kr);
     uint32_t lmax = 0, lnmin = 0;                 // max of the keys and of their complements
 #pragma unroll
     for (int j = 0; j < SEL_PT; ++j) {
@@ -280,6 +280,15 @@ __device__ __forceinline__ uint32_t lds_select(const uint32_t* keys, int nk, int
     }
     *need_eq = need;
     return prefix;
+}
+
+__device__ __forceinline__ uint32_t lds_select(const uint32_t* keys, int nk, int kth, int* hist,
+                                               ScanBuf& s_wave, uint32_t* s_mm, int* need_eq,
+                                               bool exact = true)
+{
+    uint32_t kr[SEL_PT];
+    const int cnt = load_own(keys, nk, kr);
+    return select_own(kr, cnt, kth, hist, s_wave, s_mm, need_eq, exact);
 }
 
 // Visit the row in position order.  The 16-byte-aligned body goes in super-rounds of
@@ -761,7 +770,6 @@ __global__ __launch_bounds__(TK_THREADS) void topk_threshold_kernel(
     const float* __restrict__ samp, int64_t ld, int S, int L, int q_pos0, int k,
     uint32_t* __restrict__ tau, int* __restrict__ fill, int* __restrict__ fb)
 {
-    __shared__ __attribute__((aligned(16))) uint32_t s_keys[SAMPLE];
     __shared__ int s_hist[4096];
     __shared__ int s_wave_mem[2 * TK_WAVES];
     ScanBuf s_wave{s_wave_mem, 0};
@@ -777,30 +785,41 @@ __global__ __launch_bounds__(TK_THREADS) void topk_threshold_kernel(
         return;
     }
     const int ns = (n - 1) / S + 1;                     // sampled keys this row sees (<= SAMPLE)
-    for (int i = tid; i < ns; i += TK_THREADS) s_keys[i] = score_key(samp[(int64_t)row * ld + i]);
-    __syncthreads();
+    // this thread's sampled keys [SEL_PT tid, SEL_PT tid + SEL_PT), straight into registers
+    const float* sr = samp + (int64_t)row * ld + SEL_PT * tid;
+    const int cnt = max(0, min(SEL_PT, ns - SEL_PT * tid));
+    uint32_t kr[SEL_PT];
+#pragma unroll
+    for (int j = 0; j < SEL_PT; ++j) kr[j] = j < cnt ? score_key(sr[j]) : 0u;
     const int rs = (int)max<int64_t>(1, min<int64_t>(ns, ((int64_t)fused_target(k) * ns + n - 1) / n));
     int unused_eq;
-    const uint32_t t = lds_select(s_keys, ns, rs, s_hist, s_wave, s_mm, &unused_eq, false);
+    const uint32_t t = select_own(kr, cnt, rs, s_hist, s_wave, s_mm, &unused_eq, false);
     if (tid == 0) tau[row] = t;
 }
 
 // Row t's top-k from its candidates (fill[t - off] of them, unordered, at cand + (t - off) *
-// capr): an exact radix select finds the k-th key tau and the ties to keep, two LDS bitmaps
-// over the row's positions (above tau; equal to tau) give the selection in position order.
-// Rows seeing at most k keys take every position.  A row whose candidates are fewer than k
-// (the threshold was too high) or more than fit is flagged in fb for the exact path.
+// capr): an exact radix select finds the k-th key tau and how many keys equal to it to keep;
+// an LDS bitmap over the row's positions marks the keys above tau and the kept ties (the
+// lowest positions among the keys equal to tau), and the selection is emitted in position
+// order.  Rows seeing at most k keys take every position.  A row whose candidates are fewer
+// than k (the threshold was too high) or more than fit, or that holds more than TIE_CAP keys
+// equal to tau, is flagged in fb for the exact path.  The candidates go straight from memory
+// to registers (thread t: entries [SEL_PT t, +SEL_PT)), so LDS holds only the histogram, the
+// bitmap and the tie list (dynamic: RES_HIST_BYTES + 4 bytes per 32 positions of the longest
+// row + RES_TIE_BYTES), and four workgroups share a CU on rows of up to 128K keys.
+constexpr int RES_HIST_BYTES = 4 * 4096;
+constexpr int TIE_CAP = 256;
+constexpr int RES_TIE_BYTES = 4 * TIE_CAP;
 __global__ __launch_bounds__(TK_THREADS) void topk_resolve_kernel(
     const uint2* __restrict__ cand, int capr, const int* __restrict__ fill, int L, int q_pos0,
     int k, int off, int32_t* __restrict__ idx, int* __restrict__ fb)
 {
-    __shared__ __attribute__((aligned(16))) uint8_t s_buf[LDS_BYTES];
+    extern __shared__ __attribute__((aligned(16))) uint8_t s_dyn[];
     __shared__ int s_wave_mem[2 * TK_WAVES];
     ScanBuf s_wave{s_wave_mem, 0};
     __shared__ uint32_t s_mm[2 * TK_WAVES];
-    int* hist = reinterpret_cast<int*>(s_buf + OFF_HIST);
-    uint32_t* ckey = reinterpret_cast<uint32_t*>(s_buf + OFF_A);
-    int* cpos = reinterpret_cast<int*>(s_buf + OFF_A + 4 * CAND_CAP);
+    __shared__ int s_ntie;
+    int* hist = reinterpret_cast<int*>(s_dyn);
 
     const int row = blockIdx.x, tid = threadIdx.x;
     const int n = min(L, q_pos0 + row + 1);
@@ -815,61 +834,69 @@ __global__ __launch_bounds__(TK_THREADS) void topk_resolve_kernel(
         if (tid == 0) fb[cr] = 1;
         return;
     }
-    const uint2* src = cand + (int64_t)cr * capr;
-    for (int i = tid; i < nc; i += TK_THREADS) {
-        const uint2 e = src[i];
-        ckey[i] = e.x;
-        cpos[i] = (int)e.y;
-    }
-    __syncthreads();
+    const uint2* src = cand + (int64_t)cr * capr + SEL_PT * tid;
+    const int cnt = max(0, min(SEL_PT, nc - SEL_PT * tid));
     uint32_t kr[SEL_PT];
     int pr[SEL_PT];
-    const int cnt = load_own(ckey, nc, kr);
-    load_own(cpos, nc, pr);
-    int need_eq;
-    const uint32_t tau = lds_select(ckey, nc, k, hist, s_wave, s_mm, &need_eq);
-
-    // bitmaps over positions 0 .. n-1 (nw words each) in the candidate area, now free
+    if (cnt == SEL_PT) {                                // 16-byte aligned: capr and SEL_PT even
+#pragma unroll
+        for (int q = 0; q < SEL_PT / 2; ++q) {
+            const u32x4 v = *reinterpret_cast<const u32x4*>(src + 2 * q);
+            kr[2 * q] = v[0];
+            pr[2 * q] = (int)v[1];
+            kr[2 * q + 1] = v[2];
+            pr[2 * q + 1] = (int)v[3];
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < SEL_PT; ++j) {
+            const uint2 e = j < cnt ? src[j] : make_uint2(0u, 0u);
+            kr[j] = e.x;
+            pr[j] = (int)e.y;
+        }
+    }
+    // bitmap over positions 0 .. n-1 (nw words) and tie list after the histogram, cleared
+    // here: the selection's barriers order the clearing before the marking
     const int nw = (n + 31) >> 5;
-    uint32_t* gt = reinterpret_cast<uint32_t*>(s_buf + OFF_A);
-    uint32_t* eq = gt + nw;
-    __syncthreads();                                    // every candidate read
-    for (int i = tid; i < 2 * nw; i += TK_THREADS) gt[i] = 0u;
-    __syncthreads();
+    uint32_t* sel = reinterpret_cast<uint32_t*>(s_dyn + RES_HIST_BYTES);
+    int* ties = reinterpret_cast<int*>(sel + nw);
+    for (int i = tid; i < nw; i += TK_THREADS) sel[i] = 0u;
+    if (tid == 0) s_ntie = 0;
+    int need_eq;
+    const uint32_t tau = select_own(kr, cnt, k, hist, s_wave, s_mm, &need_eq);
 #pragma unroll
     for (int j = 0; j < SEL_PT; ++j) {
-        if (j < cnt && kr[j] >= tau) {
-            const int p = pr[j];
-            atomicOr(&(kr[j] > tau ? gt : eq)[p >> 5], 1u << (p & 31));
+        if (j < cnt && kr[j] > tau) {
+            atomicOr(&sel[pr[j] >> 5], 1u << (pr[j] & 31));
+        } else if (j < cnt && kr[j] == tau) {
+            const int t = atomicAdd(&s_ntie, 1);
+            if (t < TIE_CAP) ties[t] = pr[j];
         }
     }
     __syncthreads();
-    // thread t owns words [wpt t, wpt t + wpt)
+    const int nt = s_ntie;                              // >= need_eq >= 1
+    if (nt > TIE_CAP) {                                 // uniform
+        if (tid == 0) fb[cr] = 1;
+        return;
+    }
+    // the need_eq ties of lowest position join the selection (positions are distinct)
+    for (int i = tid; i < nt; i += TK_THREADS) {
+        const int p = ties[i];
+        int rank = 0;
+        if (nt > need_eq)
+            for (int j = 0; j < nt; ++j) rank += ties[j] < p ? 1 : 0;
+        if (rank < need_eq) atomicOr(&sel[p >> 5], 1u << (p & 31));
+    }
+    __syncthreads();
+    // emit in position order: thread t owns words [wpt t, wpt t + wpt)
     const int wpt = (nw + TK_THREADS - 1) / TK_THREADS;
     const int w0 = min(nw, wpt * tid), w1 = min(nw, w0 + wpt);
-    // the first need_eq ties in position order join the selection
-    int ne = 0;
-    for (int i = w0; i < w1; ++i) ne += __popc(eq[i]);
-    int tot;
-    int before = block_excl_scan(ne, s_wave, &tot);
-    for (int i = w0; i < w1 && before < need_eq; ++i) {
-        uint32_t m = eq[i];
-        uint32_t keep = 0u;
-        while (m && before < need_eq) {
-            const uint32_t b = m & (0u - m);
-            keep |= b;
-            m ^= b;
-            ++before;
-        }
-        gt[i] |= keep;
-    }
-    __syncthreads();
-    // emit in position order
     int ns = 0;
-    for (int i = w0; i < w1; ++i) ns += __popc(gt[i]);
+    for (int i = w0; i < w1; ++i) ns += __popc(sel[i]);
+    int tot;
     int slot = block_excl_scan(ns, s_wave, &tot);
     for (int i = w0; i < w1; ++i) {
-        uint32_t m = gt[i];
+        uint32_t m = sel[i];
         while (m) {
             const int b = __builtin_ctz(m);
             m &= m - 1u;
@@ -887,9 +914,11 @@ int fused_sample_stride(int L) { return std::max(32, (L + SAMPLE - 1) / SAMPLE);
 bool fused_select_supports(int L, int k)
 {
     // candidates aim at 2k within CAND_CAP; a row's candidate array (8 bytes each) takes no
-    // more room than its fp32 scores would; both bitmaps of a row fit the candidate area
-    return 2 * k <= CAND_CAP && L >= 2 * CAND_CAP &&
-           2 * ((L + 31) / 32) * 4 <= 8 * CAND_CAP + 4 * SAMPLE;
+    // more room than its fp32 scores would; the resolve's histogram, position bitmap and tie
+    // list fit 64 KB of LDS
+    static_assert(RES_HIST_BYTES + 4 * CAND_CAP + RES_TIE_BYTES <= 65536,
+                  "resolve LDS at the longest row");
+    return 2 * k <= CAND_CAP && L >= 2 * CAND_CAP && L <= 32 * CAND_CAP;
 }
 
 int fused_cand_cap() { return CAND_CAP; }
@@ -910,7 +939,10 @@ hipError_t launch_topk_resolve(const uint2* cand, int capr, const int* fill, int
                                hipStream_t stream)
 {
     if (T <= 0) return hipSuccess;
-    hipLaunchKernelGGL(topk_resolve_kernel, dim3(T), dim3(TK_THREADS), 0, stream, cand, capr,
+    const int64_t nmax = std::min<int64_t>(L, (int64_t)q_pos0 + T);
+    const size_t lds = RES_HIST_BYTES + 4 * (size_t)((nmax + 31) / 32) + RES_TIE_BYTES;
+    if (lds > 65536) return hipErrorInvalidValue;       // rows longer than the candidate path takes
+    hipLaunchKernelGGL(topk_resolve_kernel, dim3(T), dim3(TK_THREADS), lds, stream, cand, capr,
                        fill, L, q_pos0, k, off, idx, fb);
     return hipGetLastError();
 }

@@ -117,3 +117,33 @@ def test_fused_selection_falls_back_when_candidates_cannot_decide(dsa):
     bad = _unfused_equal(dsa, boosted, k, idx)
     assert not bad, "sparse sample: %d rows differ, first %s" % (len(bad), bad[:8])
     report("fused fallbacks", rows_compared=2 * L, rows_differing=0)
+
+
+@pytest.mark.parametrize("group", [200, 300])
+def test_fused_selection_ties_at_the_boundary(dsa, group):
+    """Keys tied at the k-th score.  `group` positions, spread over the cache, hold the same
+    boosted key (same fp8 row, same scale) and the weights are positive, so for every row that
+    sees more than k of them the k-th largest score is the group's and the selection must keep
+    the k group positions of lowest index.  With 200 tied candidates the resolve ranks the
+    ties itself; with 300 (more than its tie list holds) the row takes the exact path."""
+    L, k, H_I, H = 16384, 64, 64, 8
+    cfg = _cfg(L, k, H_I, H, seed=91 + group)
+    d = to_device(make_prefill(cfg))
+    d["w"] = d["w"].abs()
+    g = torch.Generator().manual_seed(group)
+    pos = torch.randperm(L, generator=g)[:group].sort().values.to("cuda")
+    k8 = d["k8"].clone()
+    k8[pos] = k8[pos[0]].clone()
+    ks = d["ks"].clone()
+    ks[pos] = float(ks.max()) * 8.0
+    d["k8"], d["ks"] = k8, ks
+    idx = _fused_idx(dsa, d, k)
+    bad = _unfused_equal(dsa, d, k, idx)
+    assert not bad, "ties: %d rows differ, first %s" % (len(bad), bad[:8])
+    # the last row sees every group position; whatever tau is, the group positions it keeps
+    # are the lowest ones of the group
+    sel = set(idx[-1].tolist())
+    kept = [p for p in pos.tolist() if p in sel]
+    assert kept == pos.tolist()[:len(kept)], "tied positions kept out of order"
+    report("fused ties group=%d" % group, rows_compared=L, rows_differing=0,
+           last_row_group_kept=len(kept))
