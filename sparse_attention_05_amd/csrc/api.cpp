@@ -55,6 +55,10 @@ bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
 
 bool heads_ok(int H) { return H >= 1 && H <= 128; }
 bool k_ok(int k) { return k >= 1 && k <= 8192; }
+// latent-cache rows one attention call may address: the sparse MLA finds a gathered row by a
+// 32-bit byte offset (1152 bytes per row) within the call's (or sequence's) cache
+constexpr int64_t kMaxCacheRows = 0xFFFFFFFFll / 1152;   // 3,728,270
+bool cache_ok(int64_t L) { return L <= kMaxCacheRows; }
 
 // rows of the causal triangle: (T, L, q_pos0) consistency shared by the prefill calls
 dsa_status_t check_rows(int T, int L, int q_pos0)
@@ -187,7 +191,7 @@ static dsa_status_t dsa_sparse_mla_impl(const uint16_t* q, const uint16_t* kv, c
     if (T > 0 && (!q || !kv || !idx || !out)) return DSA_ERR_INVALID_ARGUMENT;
     if (!heads_ok(H)) return H < 1 ? DSA_ERR_INVALID_ARGUMENT : DSA_ERR_UNSUPPORTED;
     if (!(sm_scale > 0.f)) return DSA_ERR_INVALID_ARGUMENT;
-    if ((int64_t)T * std::max(L, k) > kMaxElems) return DSA_ERR_UNSUPPORTED;
+    if ((int64_t)T * std::max(L, k) > kMaxElems || !cache_ok(L)) return DSA_ERR_UNSUPPORTED;
     if (!aligned(q, 16) || !aligned(kv, 16) || !aligned(out, 4)) return DSA_ERR_INVALID_ARGUMENT;
     if (T == 0) return DSA_OK;
     return from_hip(dsa::launch_sparse_mla(q, kv, idx, nullptr, T, L, H, k, sm_scale, 1, out,
@@ -299,7 +303,7 @@ static dsa_status_t dsa_prefill_impl(const uint8_t* q8, const float* q_scale, co
     if (k < 1 || H < 1) return DSA_ERR_INVALID_ARGUMENT;
     if (!(score_scale > 0.f) || !(sm_scale > 0.f)) return DSA_ERR_INVALID_ARGUMENT;
     if (!dsa::indexer_supports(H_I) || !heads_ok(H) || !k_ok(k)) return DSA_ERR_UNSUPPORTED;
-    if ((int64_t)T * std::max(L, k) > kMaxElems) return DSA_ERR_UNSUPPORTED;
+    if ((int64_t)T * std::max(L, k) > kMaxElems || !cache_ok(L)) return DSA_ERR_UNSUPPORTED;
     if (!aligned(q8, 16) || !aligned(k8, 16) || !aligned(q, 16) || !aligned(kv, 16) ||
         !aligned(out, 4))
         return DSA_ERR_INVALID_ARGUMENT;
@@ -323,7 +327,7 @@ static int64_t varlen_ws(int B, const int64_t* cu_q, const int64_t* cu_k, int k)
         const int64_t T = cu_q[b + 1] - cu_q[b], L = cu_k[b + 1] - cu_k[b];
         if (T < 0 || L < T || L > INT32_MAX) return -1;
         if (T == 0) continue;
-        if (T * std::max<int64_t>(L, k) > kMaxElems) return -1;
+        if (T * std::max<int64_t>(L, k) > kMaxElems || !cache_ok(L)) return -1;
         need = std::max(need, prefill_ws((int)T, (int)L, k).total);
     }
     return (int64_t)need;
@@ -523,7 +527,8 @@ static dsa_status_t decode_check(int B, const int64_t* seq_start, int max_len,
         return DSA_ERR_INVALID_ARGUMENT;
     if (!(score_scale > 0.f) || !(sm_scale > 0.f)) return DSA_ERR_INVALID_ARGUMENT;
     if (!dsa::indexer_supports(H_I) || !heads_ok(H) || !k_ok(k)) return DSA_ERR_UNSUPPORTED;
-    if (total_tokens >= (int64_t(1) << 31) || B > 65535) return DSA_ERR_UNSUPPORTED;
+    if (total_tokens >= (int64_t(1) << 31) || B > 65535 || !cache_ok(max_len))
+        return DSA_ERR_UNSUPPORTED;
     if (!aligned(q8, 16) || !aligned(k8_cache, 16) || !aligned(q, 16) ||
         !aligned(kv_cache, 16) || !aligned(out, 8))
         return DSA_ERR_INVALID_ARGUMENT;

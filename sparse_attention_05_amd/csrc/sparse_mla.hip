@@ -130,22 +130,25 @@ __global__ __launch_bounds__(NW * 64) void sparse_mla_kernel(
     const uint32_t rope_src[2] = {16u * (64u + (uint32_t)((lane & 7) ^ (lane >> 4))),
                                   16u * (64u + (uint32_t)((lane & 7) ^ (4 + (lane >> 4))))};
     const uint32_t lds_tiles = __builtin_amdgcn_readfirstlane(lds_addr(s_tile[0]));
+    // a gathered row is a 32-bit byte offset from the row's cache (its index times 1152; the
+    // launch keeps every cache below 4 GB), added to the lane's chunk offset: a row's load costs
+    // a lane read, one add and the load rather than 64-bit address arithmetic
     auto issue = [&](int buf, int tidx) {
         const uint32_t dst = lds_tiles + (uint32_t)buf * TILE_BYTES;
+        const uint32_t roff = (uint32_t)max(tidx, 0) * 1152u;   // lane r: row r's byte offset
 #pragma unroll 2
         for (int i0 = 0; i0 < RPW; i0 += 8)
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 const int r = wave * RPW + i0 + i;         // r & 7 == i: lat_x(r) = 2 i
-                const int sx = max(__builtin_amdgcn_readlane(tidx, r), 0);
-                dma16_s(16u * (uint32_t)(lane ^ (2 * i)), kvr + (int64_t)sx * 576, dst + r * LROW);
+                dma16_s((uint32_t)__builtin_amdgcn_readlane((int)roff, r) +
+                            16u * (uint32_t)(lane ^ (2 * i)), kvr, dst + r * LROW);
             }
 #pragma unroll
         for (int jj = 0; jj < JPW; ++jj) {
             const int j = wave * JPW + jj;
-            const int sx = max(__builtin_amdgcn_ds_bpermute((8 * j + (lane >> 3)) * 4, tidx), 0);
-            dma16(reinterpret_cast<const uint8_t*>(kvr + (int64_t)sx * 576) + rope_src[jj & 1],
-                  dst + ROPE_OFF + j * 1024);
+            const uint32_t ro = (uint32_t)__builtin_amdgcn_ds_bpermute((8 * j + (lane >> 3)) * 4, (int)roff);
+            dma16_s(ro + rope_src[jj & 1], kvr, dst + ROPE_OFF + j * 1024);
         }
     };
 
@@ -313,6 +316,12 @@ __global__ __launch_bounds__(NW * 64) void sparse_mla_kernel(
         if (!redo) break;
     }
 
+    // lane coordinates taken afresh, so that no address of the stores below is formed before
+    // the loop and held across it
+    int lane_e = lane;
+    asm volatile("" : "+v"(lane_e));
+    const int ge = lane_e >> 4, ce = lane_e & 15;
+
     // totals per head (lanes c16 of head group hq), then 1/total for the heads of O's rows
     // (head 16 hq + 4g + r sits in lane 4g + r's column)
     float my_lse[2], inv[2];
@@ -329,18 +338,18 @@ __global__ __launch_bounds__(NW * 64) void sparse_mla_kernel(
         for (int hq = 0; hq < 2; ++hq)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int hh = wave * 32 + hq * 16 + 4 * g + r;
-                const float ir = __shfl(inv[hq], 4 * g + r, 64);
+                const int hh = wave * 32 + hq * 16 + 4 * ge + r;
+                const float ir = __shfl(inv[hq], 4 * ge + r, 64);
                 if (hh >= H) continue;
                 uint16_t* orow = out + ((int64_t)row * H + hh) * 512;
 #pragma unroll
                 for (int n = 0; n < 32; ++n)
-                    orow[16 * n + c16] = (uint16_t)bf16_bits(O[hq][n][r] * ir);
+                    orow[16 * n + ce] = (uint16_t)bf16_bits(O[hq][n][r] * ir);
             }
-        if (lse && g == 0)
+        if (lse && ge == 0)
 #pragma unroll
             for (int hq = 0; hq < 2; ++hq) {
-                const int hh = wave * 32 + hq * 16 + c16;
+                const int hh = wave * 32 + hq * 16 + ce;
                 if (hh < H) lse[(int64_t)row * H + hh] = my_lse[hq];
             }
     } else {
@@ -349,17 +358,17 @@ __global__ __launch_bounds__(NW * 64) void sparse_mla_kernel(
         for (int hq = 0; hq < 2; ++hq)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int hh = wave * 32 + hq * 16 + 4 * g + r;
-                const float ir = __shfl(inv[hq], 4 * g + r, 64);
+                const int hh = wave * 32 + hq * 16 + 4 * ge + r;
+                const float ir = __shfl(inv[hq], 4 * ge + r, 64);
                 if (hh >= H) continue;
                 float* orow = part_o + (pb + hh) * 512;
 #pragma unroll
-                for (int n = 0; n < 32; ++n) orow[16 * n + c16] = O[hq][n][r] * ir;
+                for (int n = 0; n < 32; ++n) orow[16 * n + ce] = O[hq][n][r] * ir;
             }
-        if (g == 0)
+        if (ge == 0)
 #pragma unroll
             for (int hq = 0; hq < 2; ++hq) {
-                const int hh = wave * 32 + hq * 16 + c16;
+                const int hh = wave * 32 + hq * 16 + ce;
                 if (hh < H) part_lse[pb + hh] = my_lse[hq];
             }
     }
@@ -458,6 +467,8 @@ hipError_t launch_sparse_mla(const uint16_t* q, const uint16_t* kv, const int32_
                              float* part_o, float* part_lse, int valid_pos0, hipStream_t stream)
 {
     if (T <= 0) return hipSuccess;
+    // gathered rows are addressed by 32-bit byte offsets within a sequence's cache
+    if ((int64_t)L * 1152 > 0xFFFFFFFFll) return hipErrorInvalidValue;
     // four waves of 32 head slots; fewer heads leave slots empty (their queries read as zero
     // and their outputs are not written): one shape, which fits its 512 registers without
     // spilling to scratch (checked by the CPU tests on the compiler's resource report)
