@@ -246,7 +246,7 @@ static dsa_status_t prefill_run(const uint8_t* q8, const float* q_scale, const f
             // are scored and selected exactly (their launches skip every other row)
             dsa::IdxExtra ex;
             ex.kstride = dsa::fused_sample_stride(L);
-            ex.ksplit = 512;                  // a short pass: spread it over more workgroups
+            ex.ksplit = 2048;                 // sampled keys per workgroup (of at most 4096)
             const int nsamp = dsa::fused_sample_count(L);
             if (nsel > 0)
                 e = dsa::launch_indexer_prefill(q8s, qss, ws_, k8, k_scale, nsel, L, H_I,

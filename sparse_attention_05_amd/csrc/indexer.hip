@@ -24,8 +24,9 @@ template <int HI> constexpr int ip_waves_per_simd() { return (HI >= 128 || HI <=
 constexpr int IP_KT = 128;                 // keys per LDS tile
 // keys per workgroup (grid.y): each workgroup loads its rows' queries once per key range, so
 // longer ranges fetch them fewer times (16,384: a quarter of the fetches of 4,096, and 1.5%
-// faster on a 128K chunk)
-constexpr int IP_KSPLIT = 16384;
+// faster on a 128K chunk; 32,768 halves them again at the same speed within the spread
+// between runs; 65,536 leaves too few workgroups per launch and is slower)
+constexpr int IP_KSPLIT = 32768;
 constexpr int IP_CSTAGE = 256;             // candidates staged per wave (MODE 1)
 
 // LDS key tile: 128 keys x 128 B.  16-byte chunk c of key r lives at chunk

@@ -84,8 +84,8 @@ def test_indexer_dense_heads_sampled_rows(dsa):
 @pytest.mark.parametrize("q_pos0,T", [(16000, 1000), (32500, 7500)])
 def test_indexer_many_key_ranges(dsa, H_I, q_pos0, T):
     """Rows of 16,001 keys and more against a 40,000-key cache, split by the kernel over
-    16,384-key ranges (grid.y) with 128-key tiles and causal early exit: full score rows
-    compared element by element on rows whose visible ends straddle the range and tile
+    32,768-key ranges (grid.y) with 128-key tiles and causal early exit: full score rows
+    compared element by element on rows whose visible ends straddle tile and range
     boundaries (16,384 and 32,768), with q_pos0 > 0."""
     L = 40000
     cfg = _cfg(L, 16, H_I, 16, seed=300 + H_I + q_pos0, q_pos0=q_pos0, T=T)
