@@ -118,8 +118,8 @@ dsa_status_t dsa_sparse_mla(const uint16_t* q, const uint16_t* kv, const int32_t
  * trip through memory: each row's threshold comes from the scores of every 32nd key (every
  * ceil(L/4096)-th beyond L = 131072), the indexer keeps only the (key, position) pairs at
  * or above it, and an exact select over those gives the row's top-k; a row whose pairs
- * cannot decide it (fewer than k, or more than 5888) is scored in full and selected by the
- * exact top-k.  The indices are the same as the two-pass path's.  DSA_PREFILL_UNFUSED=1 in
+ * cannot decide it (fewer than k, more than 5888, or more than 256 tied at the k-th score)
+ * is scored in full and selected by the exact top-k.  The indices are the same as the two-pass path's.  DSA_PREFILL_UNFUSED=1 in
  * the environment (read at each call) keeps the two-pass path for every shape. */
 dsa_status_t dsa_prefill(const uint8_t* q8, const float* q_scale, const float* w,
                          const uint8_t* k8, const float* k_scale, const uint16_t* q,
