@@ -9,7 +9,10 @@
 // 原始 Attention 的计算逻辑: the cache is updated, then the step attends).
 //
 // Memory-bound: 16 lanes per vector, each lane 8 consecutive elements (32 or 16 bytes in,
-// 8 bytes of codes out, coalesced across the wave); the amax is reduced across the 16 lanes.
+// 8 bytes of codes out, coalesced across the wave); the amax is reduced across the 16 lanes by
+// rotations within the lane row, and the codes come from gfx950's pack conversion to OCP
+// e4m3fn (round to nearest even), checked against the format's rounding on every fp32 value
+// of magnitude at most 448.
 #include "dsa_device.h"
 #include "kernels.h"
 
@@ -18,21 +21,15 @@ namespace {
 
 constexpr int QT = 256;                        // threads per workgroup: 16 vectors
 
-// e4m3fn code of y, |y| <= 448, rounded to nearest even.  Normal range (|y| >= 2^-6): the
-// fp32 mantissa rounded to 3 bits by add-and-shift (a carry moves into the exponent), the
-// exponent re-biased from 127 to 7.  Below it the e4m3fn values are the multiples of 2^-9,
-// so |y| * 512 (exact) rounded half-to-even to an integer is the code (8: the smallest
-// normal).  The sign of y, zero included, is the code's top bit.
-__device__ __forceinline__ uint32_t e4m3fn_rne(float y)
+// maximum over the 16 lanes of a lane row (lanes 16r .. 16r + 15): rotations by 8, 4, 2 and 1
+// lanes within the row (data-parallel-primitive moves, no LDS)
+__device__ __forceinline__ float row16_max(float v)
 {
-    const uint32_t b = __float_as_uint(y);
-    const uint32_t a = b & 0x7FFFFFFFu;
-    uint32_t code;
-    if (a >= 0x3C800000u)
-        code = ((a + 0x7FFFFu + ((a >> 20) & 1u)) >> 20) - (120u << 3);
-    else
-        code = (uint32_t)__builtin_rintf(__uint_as_float(a) * 512.0f);
-    return ((b >> 24) & 0x80u) | code;
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xf, 0xf, false)));
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x124, 0xf, 0xf, false)));
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x122, 0xf, 0xf, false)));
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x121, 0xf, 0xf, false)));
+    return v;
 }
 
 struct Quant8 {
@@ -47,14 +44,17 @@ __device__ __forceinline__ Quant8 quantize8(const float (&x)[8])
     float amax = 0.f;
 #pragma unroll
     for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(x[j]));
-#pragma unroll
-    for (int o = 8; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 16));
+    amax = row16_max(amax);
     const float s = amax > 0.f ? amax / 448.0f : 1.0f;
-    uint32_t w[2] = {0u, 0u};
+    float y[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        const float y = fminf(fmaxf(x[j] / s, -448.0f), 448.0f);
-        w[j >> 2] |= e4m3fn_rne(y) << (8 * (j & 3));
+    for (int j = 0; j < 8; ++j) y[j] = fminf(fmaxf(x[j] / s, -448.0f), 448.0f);
+    // codes of elements 4i .. 4i + 3 in word i, element 4i + m in byte m
+    uint32_t w[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(y[4 * i], y[4 * i + 1], 0, false);
+        w[i] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y[4 * i + 2], y[4 * i + 3], lo, true);
     }
     return Quant8{u32x2{w[0], w[1]}, s};
 }

@@ -51,6 +51,34 @@ def test_quantize_fp8_matches_oracle(dsa, dtype, n):
     assert np.array_equal(_np(q8), oq)
 
 
+def test_quantize_fp8_every_fp32_value_of_magnitude_at_most_448(dsa):
+    """Each fp32 value with |x| <= 448, both signs, zero and the subnormals included (2.28e9
+    values), quantised at scale 1 (every vector also holds 448, its amax, so x / scale = x):
+    the codes equal torch's e4m3fn cast (round to nearest even) on the same values.  This pins
+    the rounding of a quotient to a code exhaustively; the other tests pin the scale and the
+    quotient against the oracle."""
+    top = 0x43E00000                                 # 448.0
+    batch = 127 << 20                                # values per call (127 per vector)
+    for start in range(0, top + 1, batch):
+        n = min(batch, top + 1 - start)
+        bits = torch.arange(start, start + n, dtype=torch.int32, device="cuda")
+        for sign in (0, -(1 << 31)):
+            nv = (n + 126) // 127
+            flat = torch.zeros(nv * 127, dtype=torch.int32, device="cuda")
+            flat[:n] = bits | sign
+            x = torch.cat([torch.full((nv, 1), 448.0, device="cuda"),
+                           flat.view(torch.float32).view(nv, 127)], dim=1).contiguous()
+            q8, sc = dsa.dsa_quantize_fp8(x)
+            want = x.to(torch.float8_e4m3fn).view(torch.uint8)
+            assert bool((sc == 1.0).all()), "scale of a vector whose amax is 448"
+            bad = (q8.view(torch.uint8) != want).nonzero()
+            assert bad.numel() == 0, "first mismatch at value bits %#x" % (
+                int(x[bad[0, 0], bad[0, 1]].view(torch.int32)) & 0xFFFFFFFF)
+            del flat, x, q8, sc, want
+        del bits
+        torch.cuda.empty_cache()
+
+
 def test_quantize_fp8_prefill_inputs_sampled(dsa):
     """The indexer inputs of the 128K prefill (131072 x 64 query vectors and 131072 key
     vectors, bf16), quantised in one call; sampled vectors against the oracle."""
