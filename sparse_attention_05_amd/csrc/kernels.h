@@ -55,7 +55,8 @@ hipError_t launch_topk_prefill(const float* scores, int64_t ld, int T, int L, in
 //  2. launch_topk_threshold derives each row's threshold tau from them and clears fill, fb;
 //  3. launch_indexer_candidates keeps the keys at or above tau (capr = fused_cand_cap());
 //  4. launch_topk_resolve selects from the candidates, flagging in fb the rows whose
-//     candidates cannot decide (fewer than k, or more than the capacity);
+//     candidates cannot decide (fewer than k, more than the capacity, or more ties at the
+//     k-th key than its tie list holds);
 //  5. the flagged rows are scored (launch_indexer_prefill with only = fb) and selected by
 //     launch_topk_prefill_only.
 // Rows are relative to the chunk for the resolve (T rows from q_pos0, the first `off` of
@@ -74,7 +75,8 @@ hipError_t launch_topk_prefill_only(const float* scores, int64_t ld, int T, int 
                                     int k, int32_t* idx, const int* only, int only_off,
                                     hipStream_t stream);
 // Decode rows: row b at scores + seq_start[b] with seq_start[b+1] - seq_start[b] <= max_len
-// scores (a row longer than max_len, outside that contract, selects nothing: all -1).  Long rows are split over several workgroups when ws (at least
+// scores (a row longer than max_len, outside that contract, selects nothing: all -1).  Long
+// rows are split over several workgroups when ws (at least
 // topk_decode_workspace_bytes(B, max_len) bytes, 16-byte aligned; may be null when that is
 // 0) is given; otherwise each row is selected by one workgroup.
 size_t topk_decode_workspace_bytes(int B, int max_len);
