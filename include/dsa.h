@@ -44,7 +44,7 @@
  *   - Supported shapes: H_I in {1,2,4,8,16,32,64,128}; 1 <= H <= 128;
  *     1 <= k <= 8192 (index lists of dsa_sparse_mla: any k >= 1); L < 2^31;
  *     T * max(L, k) < 2^40; a latent cache an attention call (or a sequence of a batch)
- *     addresses holds at most 3,728,270 rows (4 GiB of 1152-byte rows: L, each varlen
+ *     addresses holds at most 1,864,135 rows (2 GiB of 1152-byte rows: L, each varlen
  *     sequence's keys, decode's max_len).  Other shapes return DSA_ERR_UNSUPPORTED.
  */
 #ifndef DSA_H

@@ -56,8 +56,8 @@ bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
 bool heads_ok(int H) { return H >= 1 && H <= 128; }
 bool k_ok(int k) { return k >= 1 && k <= 8192; }
 // latent-cache rows one attention call may address: the sparse MLA finds a gathered row by a
-// 32-bit byte offset (1152 bytes per row) within the call's (or sequence's) cache
-constexpr int64_t kMaxCacheRows = 0xFFFFFFFFll / 1152;   // 3,728,270
+// byte offset (1152 bytes per row) below 2^31 within the call's (or sequence's) cache
+constexpr int64_t kMaxCacheRows = 0x7FFFFFFFll / 1152;   // 1,864,135
 bool cache_ok(int64_t L) { return L <= kMaxCacheRows; }
 
 // rows of the causal triangle: (T, L, q_pos0) consistency shared by the prefill calls

@@ -131,8 +131,9 @@ __global__ __launch_bounds__(NW * 64) void sparse_mla_kernel(
                                   16u * (64u + (uint32_t)((lane & 7) ^ (4 + (lane >> 4))))};
     const uint32_t lds_tiles = __builtin_amdgcn_readfirstlane(lds_addr(s_tile[0]));
     // a gathered row is a 32-bit byte offset from the row's cache (its index times 1152; the
-    // launch keeps every cache below 4 GB), added to the lane's chunk offset: a row's load costs
-    // a lane read, one add and the load rather than 64-bit address arithmetic
+    // launch keeps every cache below 2 GiB, so the offset stays below 2^31), added to the
+    // lane's chunk offset: a row's load costs a lane read, one add and the load rather than
+    // 64-bit address arithmetic
     auto issue = [&](int buf, int tidx) {
         const uint32_t dst = lds_tiles + (uint32_t)buf * TILE_BYTES;
         const uint32_t roff = (uint32_t)max(tidx, 0) * 1152u;   // lane r: row r's byte offset
@@ -467,8 +468,8 @@ hipError_t launch_sparse_mla(const uint16_t* q, const uint16_t* kv, const int32_
                              float* part_o, float* part_lse, int valid_pos0, hipStream_t stream)
 {
     if (T <= 0) return hipSuccess;
-    // gathered rows are addressed by 32-bit byte offsets within a sequence's cache
-    if ((int64_t)L * 1152 > 0xFFFFFFFFll) return hipErrorInvalidValue;
+    // gathered rows are addressed by byte offsets below 2^31 within a sequence's cache
+    if ((int64_t)L * 1152 > 0x7FFFFFFFll) return hipErrorInvalidValue;
     // four waves of 32 head slots; fewer heads leave slots empty (their queries read as zero
     // and their outputs are not written): one shape, which fits its 512 registers without
     // spilling to scratch (checked by the CPU tests on the compiler's resource report)

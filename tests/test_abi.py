@@ -82,8 +82,8 @@ def test_sparse_mla_validation(lib):
     assert f(s=-1.0) == dsa.DSA_ERR_INVALID_ARGUMENT
     assert f(L=0) == dsa.DSA_ERR_INVALID_ARGUMENT
     assert f(T=0, p=NULL) == dsa.DSA_OK
-    # a cache of more than 4 GiB of 1152-byte rows is beyond the gather's 32-bit row offsets
-    assert f(T=1, L=3728271) == dsa.DSA_ERR_UNSUPPORTED
+    # a cache of more than 2 GiB of 1152-byte rows is beyond the gather's row offsets
+    assert f(T=1, L=1864136) == dsa.DSA_ERR_UNSUPPORTED
 
 
 def test_prefill_validation_and_workspace(lib):
@@ -105,7 +105,7 @@ def test_prefill_validation_and_workspace(lib):
     assert f(ws=NULL) == dsa.DSA_ERR_WORKSPACE_TOO_SMALL
     assert f(wsb=1) == dsa.DSA_ERR_WORKSPACE_TOO_SMALL
     assert f(ws=ctypes.c_void_p((1 << 20) + 128)) == dsa.DSA_ERR_INVALID_ARGUMENT  # alignment
-    assert f(L=3728271) == dsa.DSA_ERR_UNSUPPORTED                  # cache beyond 4 GiB
+    assert f(L=1864136) == dsa.DSA_ERR_UNSUPPORTED                  # cache beyond 2 GiB
 
 
 def test_decode_validation_and_workspace(lib):
@@ -120,7 +120,7 @@ def test_decode_validation_and_workspace(lib):
     assert f(N=401) == dsa.DSA_ERR_INVALID_ARGUMENT       # more tokens than B * max_len
     assert f(ml=0) == dsa.DSA_ERR_INVALID_ARGUMENT
     assert f(H_I=48) == dsa.DSA_ERR_UNSUPPORTED
-    assert f(ml=3728271) == dsa.DSA_ERR_UNSUPPORTED                 # a sequence beyond 4 GiB
+    assert f(ml=1864136) == dsa.DSA_ERR_UNSUPPORTED                 # a sequence beyond 2 GiB
     assert f(ws=NULL) == dsa.DSA_ERR_WORKSPACE_TOO_SMALL
     assert f(wsb=need - 1) == dsa.DSA_ERR_WORKSPACE_TOO_SMALL
     assert f(B=0, p=NULL) == dsa.DSA_OK

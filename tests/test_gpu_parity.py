@@ -210,6 +210,31 @@ def test_sparse_mla_long_index_lists(dsa, L, k):
     check_mla(bf16_to_f64(out), _np(lse), oo, ol, "mla long L=%d k=%d" % (L, k))
 
 
+def test_sparse_mla_rows_at_the_cache_limit(dsa):
+    """The gather finds a row by its byte offset in the cache: a cache of 1,864,135 rows (the
+    2 GiB the entry points accept), index lists drawn from its last rows and from across it,
+    against the oracle on a compact copy of the selected rows (indices remapped)."""
+    L, T, H, k = 1864135, 3, 16, 96
+    g = torch.Generator(device="cuda").manual_seed(41)
+    kv = (torch.randn((L, 576), generator=g, device="cuda") * 0.5).to(torch.bfloat16)
+    q = (torch.randn((T, H, 576), generator=g, device="cuda") * 0.5).to(torch.bfloat16)
+    rng = np.random.default_rng(41)
+    idx = np.empty((T, k), np.int32)
+    idx[0] = np.arange(L - k, L)                               # the last rows
+    idx[1] = rng.choice(L, k, replace=False)                   # across the cache
+    idx[2] = np.concatenate([np.arange(L - 32, L), rng.choice(L - 32, k - 32, replace=False)])
+    sm_scale = 576 ** -0.5
+    out, lse = dsa.dsa_sparse_mla(q, kv, torch.from_numpy(idx).cuda(), sm_scale)
+    torch.cuda.synchronize()
+    uniq, inv = np.unique(idx, return_inverse=True)
+    kv_c = _u16(kv[torch.from_numpy(uniq).long().cuda()])
+    idx_c = inv.reshape(idx.shape).astype(np.int32)
+    oo, ol = oracle.sparse_mla(_u16(q), kv_c, idx_c, sm_scale)
+    check_mla(bf16_to_f64(out), _np(lse), oo, ol, "mla rows at the cache limit")
+    del kv
+    torch.cuda.empty_cache()
+
+
 def test_sparse_mla_late_dominant_logit_recomputes(dsa):
     """The kernel fixes each head's softmax reference from the first valid logits and
     recomputes the row with the exact maximum when a later logit exceeds that reference by
