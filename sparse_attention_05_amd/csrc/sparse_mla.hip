@@ -23,12 +23,23 @@
 // Softmax runs in the exp2 domain with fp32 statistics against a per-head reference max
 // fixed by the first valid logits of the row, so O is never rescaled.  Should a later logit
 // exceed the reference by more than 2^OVF_SLACK (a logit spread no real attention row
-// reaches), the row is recomputed once with the exact per-head max as the reference.
+// reaches), the row is recomputed once with the exact per-head max as the reference; the test
+// uses each lane's running maximum of its raw logits, reduced across lanes once per pass.
+// Once the references are fixed, a tile whose 64 keys are all valid runs software-pipelined
+// within the wave: the softmax of its first 32 keys is spread over the QK MFMAs of the second
+// 32, the softmax of the second over the P V MFMAs of the first (one wave per SIMD keeps
+// issuing a few vector instructions under each MFMA), with the arithmetic of each head in
+// the same order as the unsplit form, so the results are the same bits.
+#include <type_traits>
+
 #include "dsa_device.h"
 #include "kernels.h"
 
 namespace dsa {
 namespace {
+
+typedef float v2f __attribute__((ext_vector_type(2)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 
 constexpr int MT = 64;                       // keys per tile
 constexpr int CH = 72;                       // 16-byte chunks per 1152-byte row
@@ -135,6 +146,9 @@ __global__ __launch_bounds__(NW * 64) void sparse_mla_kernel(
     // lane's chunk offset: a row's load costs a lane read, one add and the load rather than
     // 64-bit address arithmetic
     auto issue = [&](int buf, int tidx) {
+        // the lane's chunk offsets are formed here rather than held across the tile loop
+        int ln = lane;
+        asm volatile("" : "+v"(ln));
         const uint32_t dst = lds_tiles + (uint32_t)buf * TILE_BYTES;
         const uint32_t roff = (uint32_t)max(tidx, 0) * 1152u;   // lane r: row r's byte offset
 #pragma unroll 2
@@ -143,7 +157,7 @@ __global__ __launch_bounds__(NW * 64) void sparse_mla_kernel(
             for (int i = 0; i < 8; ++i) {
                 const int r = wave * RPW + i0 + i;         // r & 7 == i: lat_x(r) = 2 i
                 dma16_s((uint32_t)__builtin_amdgcn_readlane((int)roff, r) +
-                            16u * (uint32_t)(lane ^ (2 * i)), kvr, dst + r * LROW);
+                            16u * (uint32_t)(ln ^ (2 * i)), kvr, dst + r * LROW);
             }
 #pragma unroll
         for (int jj = 0; jj < JPW; ++jj) {
@@ -171,28 +185,166 @@ __global__ __launch_bounds__(NW * 64) void sparse_mla_kernel(
     for (int j = 0; j < 4; ++j) vo[j] = 32 * (j ^ (rv & 3)) + 16 * ((c16 & 3) >> 1);
 
     v4f O[2][32];                      // O[hq][n]: heads 32 wave + 16 hq + 4g + r, dims 16n + c16
-    float m_ref[2], m_max[2] = {-__builtin_huge_valf(), -__builtin_huge_valf()}, l_run[2];
+    // m_ref: -inf for the first pass (then fixed by the row's first valid logits); a
+    // recomputation pass takes the exact per-head maximum the first pass found
+    float m_ref[2] = {-__builtin_huge_valf(), -__builtin_huge_valf()}, l_run[2];
+    // each lane's running maximum of its own raw logits (reduced across lanes once per pass)
+    float m_lane[2];
+
+    // S^T[key][head] of one half tile (keys 32 half + 16 kt + (4g + r), heads 16 hq + c16):
+    // A = row 32 half + 16 kt + c16, dims [32s + 8g, +8) (chunk 4s + g), each A read feeding
+    // both head groups, read QD steps ahead; B = Q^T.  The accumulators are pinned in VGPRs
+    // (the compiler would place them in AGPRs beside O and shuffle part of O out and back
+    // around every half).  between(s) runs inside step s's scheduling region.
+    auto qk_half = [&](const uint8_t* tb, int half, v4f (&S)[2][2], auto&& between) {
+        const uint8_t* rb = tb + row_base(half * 32 + c16);    // kt adds 16 rows
+        const uint8_t* rr = tb + ROPE_OFF + RROW * (half * 32 + c16);
+        constexpr int QD = 2;
+        u32x4 abuf[QD][2];
+#pragma unroll
+        for (int s = 0; s < QD; ++s)
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt)
+                abuf[s][kt] = *reinterpret_cast<const u32x4*>(rb + kt * 16 * LROW + 256 * (s >> 2) + qo[s & 3]);
+#pragma unroll
+        for (int s = 0; s < 18; ++s) {
+            __builtin_amdgcn_sched_barrier(0);
+            const u32x4 a[2] = {abuf[s % QD][0], abuf[s % QD][1]};
+            if (s + QD < 18) {
+                const int m = s + QD;
+#pragma unroll
+                for (int kt = 0; kt < 2; ++kt)
+                    abuf[s % QD][kt] = *reinterpret_cast<const u32x4*>(
+                        m < 16 ? rb + kt * 16 * LROW + 256 * (m >> 2) + qo[m & 3]
+                               : rr + kt * 16 * RROW + ro[m & 1]);
+            }
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                for (int hq = 0; hq < 2; ++hq) {
+                    if (s == 0)
+                        asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, 0"
+                                     : "=&v"(S[kt][hq]) : "v"(a[kt]), "v"(qreg[hq][s]));
+                    else
+                        asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0"
+                                     : "+v"(S[kt][hq]) : "v"(a[kt]), "v"(qreg[hq][s]));
+                }
+            between(s);
+        }
+        // no VALU read of the accumulators before the last MFMA has written them: 19 wait
+        // states, enough for any MFMA pass count
+        asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 2"
+                     : "+v"(S[0][0]), "+v"(S[0][1]), "+v"(S[1][0]), "+v"(S[1][1]));
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    // O[hq][n] += P[hq] V[:, 16n .. 16n + 15] over one half's 32 keys, the V operands read VD
+    // blocks ahead; between(n) runs inside step n's scheduling region
+    auto pv_half = [&](const uint8_t* tb, int half, const u32x4 (&pa)[2], auto&& between) {
+        const uint8_t* vb = tb + half * 32 * LROW + vbase;
+        constexpr int VD = 4;
+        u32x4 vbuf[VD];
+        auto vread = [&](int n) -> u32x4 {
+            const int o = 128 * ((n >> 2) ^ vq) + vo[n & 3];
+            const u32x2 lo = ds_read_tr(vb + o);
+            const u32x2 hi = ds_read_tr(vb + o + 16 * LROW);
+            return u32x4{lo[0], lo[1], hi[0], hi[1]};
+        };
+#pragma unroll
+        for (int n = 0; n < VD; ++n) vbuf[n] = vread(n);
+#pragma unroll
+        for (int n = 0; n < 32; ++n) {
+            __builtin_amdgcn_sched_barrier(0);
+            const u32x4 v = vbuf[n % VD];
+            if (n + VD < 32) vbuf[n % VD] = vread(n + VD);
+#pragma unroll
+            for (int hq = 0; hq < 2; ++hq)
+                O[hq][n] = mfma_bf16(as_bf16x8(pa[hq]), as_bf16x8(v), O[hq][n]);
+            between(n);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    // Softmax of one half for heads 16 hq + c16; the bf16 probabilities come out in the A
+    // layout of P V (head c16, keys {4g..4g+3} of each 16-key group).  Raw logits, masked to
+    // -inf where hbits (the half's 32 key-validity bits) says so; the scale is applied inside
+    // the exponent's fma, and to a maximum once: scale2 > 0 and rounding is monotonic, so
+    // max(x) * scale2 is exactly the maximum of the rounded x * scale2.
+    // FIX: some head still lacks its reference -- the half's per-head maxima across the lanes
+    // fix it (the first valid logits; O and l are still zero then).
+    auto softmax_half = [&](const v4f (&S)[2][2], uint32_t hbits, bool fix, u32x4 (&pa)[2]) {
+#pragma unroll
+        for (int hq = 0; hq < 2; ++hq) {
+            float x[2][4];
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    x[kt][r] = ((hbits >> (kt * 16 + 4 * g + r)) & 1u) ? S[kt][hq][r]
+                                                                     : -__builtin_huge_valf();
+            const float mx = fmaxf(fmaxf(fmaxf(x[0][0], x[0][1]), fmaxf(x[0][2], x[0][3])),
+                                   fmaxf(fmaxf(x[1][0], x[1][1]), fmaxf(x[1][2], x[1][3])));
+            m_lane[hq] = fmaxf(m_lane[hq], mx);
+            if (fix) {
+                const float mh = max_xor32(max_xor16(mx)) * scale2;   // all lanes take part
+                if (m_ref[hq] == -__builtin_huge_valf()) m_ref[hq] = mh;
+            }
+            // no valid logit yet: keep exp2(-inf - m) = 0 rather than exp2(-inf + inf)
+            const float m_sub = m_ref[hq] == -__builtin_huge_valf() ? 0.f : m_ref[hq];
+            float p[2][4];
+            float psum = 0.f;
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    p[kt][r] = __builtin_amdgcn_exp2f(fmaf(x[kt][r], scale2, -m_sub));
+                    psum += p[kt][r];
+                }
+            l_run[hq] += psum;
+            pa[hq] = __builtin_bit_cast(u32x4, __builtin_convertvector(
+                (v8f){p[0][0], p[0][1], p[0][2], p[0][3], p[1][0], p[1][1], p[1][2], p[1][3]}, v8bf));
+        }
+    };
+    // Element e of a half's softmax when every key is valid and the references are fixed
+    // (head group e / 8, key group e / 4 % 2, element e % 4): per head the same operations in
+    // the same order as softmax_half, so the results are bitwise those of the unsplit form.
+    auto softmax_elem = [&](const v4f (&S)[2][2], int e, float (&pb)[2], float (&psum)[2],
+                            u32x4 (&pa)[2]) {
+        const int hq = e >> 3, kt = (e >> 2) & 1, r = e & 3;
+        const float x = S[kt][hq][r];
+        m_lane[hq] = fmaxf(m_lane[hq], x);
+        const float p = __builtin_amdgcn_exp2f(fmaf(x, scale2, -m_ref[hq]));
+        psum[hq] = (e & 7) == 0 ? p : psum[hq] + p;
+        if (r & 1)
+            pa[hq][(kt * 4 + r) >> 1] =
+                __builtin_bit_cast(uint32_t, __builtin_convertvector((v2f){pb[hq], p}, v2bf));
+        else
+            pb[hq] = p;
+        if ((e & 7) == 7) l_run[hq] += psum[hq];
+    };
 
 #pragma unroll 1
     for (int pass = 0; pass < 2; ++pass) {
 #pragma unroll
-        for (int hq = 0; hq < 2; ++hq)
+        for (int hq = 0; hq < 2; ++hq) {
 #pragma unroll
             for (int n = 0; n < 32; ++n) O[hq][n] = v4f{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int hq = 0; hq < 2; ++hq) {
             l_run[hq] = 0.f;
-            m_ref[hq] = pass ? m_max[hq] : -__builtin_huge_valf();
+            m_lane[hq] = -__builtin_huge_valf();
         }
-        bool over = false;
+        // a recomputation pass starts with every reference set (-inf only for a head that saw
+        // no valid key)
+        bool have_ref = __all(m_ref[0] != -__builtin_huge_valf() && m_ref[1] != -__builtin_huge_valf());
         int idx_cur = 0, idx_nxt = 0;
         if (ntile > 0) {
             idx_cur = check_idx(0, load_idx(0));
             idx_nxt = load_idx(1);
             issue(0, idx_cur);
         }
-        // one tile: tb holds it, the other buffer receives the next one
-        auto step = [&](int t, const uint8_t* tb) {
+        // One tile: tb holds it, the other buffer receives the next one.  KIND 2: every key
+        // valid and the references fixed -- the softmax of the first half runs between the QK
+        // MFMAs of the second, that of the second between the P V MFMAs of the first.  KIND 1:
+        // references fixed, keys may be masked; KIND 0: some head still lacks its reference.
+        auto step = [&](int t, const uint8_t* tb, auto kind_tag) {
+            constexpr int KIND = decltype(kind_tag)::value;
             __builtin_amdgcn_s_waitcnt(0);             // this wave's part of tile t landed
             __syncthreads();                           // everyone's part; tile t-1 consumed
             const uint64_t vmask = __ballot(idx_cur >= 0);
@@ -200,112 +352,50 @@ __global__ __launch_bounds__(NW * 64) void sparse_mla_kernel(
             if (t + 1 < ntile) issue((t + 1) & 1, idx_nxt);
             idx_cur = idx_nxt;
             idx_nxt = load_idx(t + 2);
+            if constexpr (KIND == 2) {
+                v4f S0[2][2], S1[2][2];
+                u32x4 pa0[2], pa1[2];
+                float pb[2], psum[2];
+                qk_half(tb, 0, S0, [](int) {});
+                qk_half(tb, 1, S1, [&](int s) {
+                    if (s < 16) softmax_elem(S0, s, pb, psum, pa0);
+                });
+                pv_half(tb, 0, pa0, [&](int n) {
+                    if ((n & 1) == 0) softmax_elem(S1, n >> 1, pb, psum, pa1);
+                });
+                pv_half(tb, 1, pa1, [](int) {});
+            } else {
 #pragma unroll 1
-            for (int half = 0; half < 2; ++half) {
-                // S^T[key][head] for keys 32 half + 16 kt + (4g + r), heads 16 hq + c16;
-                // A = row 32 half + 16 kt + c16, dims [32s + 8g, +8): chunk 4s + g, each A
-                // read feeding both head groups; A operands read QD steps ahead
-                v4f S[2][2];
-#pragma unroll
-                for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-                    for (int hq = 0; hq < 2; ++hq) S[kt][hq] = v4f{0.f, 0.f, 0.f, 0.f};
-                const uint8_t* rb = tb + row_base(half * 32 + c16);    // kt adds 16 rows
-                const uint8_t* rr = tb + ROPE_OFF + RROW * (half * 32 + c16);
-                constexpr int QD = 3;
-                u32x4 abuf[QD][2];
-#pragma unroll
-                for (int s = 0; s < QD; ++s)
-#pragma unroll
-                    for (int kt = 0; kt < 2; ++kt)
-                        abuf[s][kt] = *reinterpret_cast<const u32x4*>(rb + kt * 16 * LROW + 256 * (s >> 2) + qo[s & 3]);
-#pragma unroll
-                for (int s = 0; s < 18; ++s) {
-                    __builtin_amdgcn_sched_barrier(0);
-                    u32x4 a[2] = {abuf[s % QD][0], abuf[s % QD][1]};
-                    if (s + QD < 18) {
-                        const int m = s + QD;
-#pragma unroll
-                        for (int kt = 0; kt < 2; ++kt)
-                            abuf[s % QD][kt] = *reinterpret_cast<const u32x4*>(
-                                m < 16 ? rb + kt * 16 * LROW + 256 * (m >> 2) + qo[m & 3]
-                                       : rr + kt * 16 * RROW + ro[m & 1]);
-                    }
-#pragma unroll
-                    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-                        for (int hq = 0; hq < 2; ++hq)
-                            S[kt][hq] = mfma_bf16(as_bf16x8(a[kt]), as_bf16x8(qreg[hq][s]), S[kt][hq]);
+                for (int half = 0; half < 2; ++half) {
+                    v4f S[2][2];
+                    u32x4 pa[2];
+                    qk_half(tb, half, S, [](int) {});
+                    softmax_half(S, (uint32_t)(vmask >> (half * 32)), KIND == 0, pa);
+                    if (KIND == 0)
+                        have_ref = __all(m_ref[0] != -__builtin_huge_valf() &&
+                                         m_ref[1] != -__builtin_huge_valf());
+                    pv_half(tb, half, pa, [](int) {});
                 }
-                __builtin_amdgcn_sched_barrier(0);
-                // softmax for heads 16 hq + c16 over this half's 32 keys; P stays in
-                // registers as the A operand of P V (head c16, keys {4g..4g+3} of each
-                // 16-key group)
-                u32x4 pa[2];
-#pragma unroll
-                for (int hq = 0; hq < 2; ++hq) {
-                    // raw logits (masked: -inf); the scale is applied inside the exponent's
-                    // fma, and to the maximum once: scale2 > 0 and rounding is monotonic, so
-                    // max(x) * scale2 is exactly the maximum of the rounded x * scale2
-                    float x[2][4];
-                    float mloc = -__builtin_huge_valf();
-#pragma unroll
-                    for (int kt = 0; kt < 2; ++kt) {
-                        const uint32_t bits = (uint32_t)(vmask >> (half * 32 + kt * 16 + 4 * g));
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) {
-                            x[kt][r] = ((bits >> r) & 1u) ? S[kt][hq][r] : -__builtin_huge_valf();
-                            mloc = fmaxf(mloc, x[kt][r]);
-                        }
-                    }
-                    mloc = max_xor32(max_xor16(mloc)) * scale2;
-                    m_max[hq] = fmaxf(m_max[hq], mloc);
-                    // the first valid logits fix the reference (O and l are still zero then)
-                    if (m_ref[hq] == -__builtin_huge_valf()) m_ref[hq] = mloc;
-                    over |= mloc > m_ref[hq] + OVF_SLACK;
-                    // no valid logit yet: keep exp2(-inf - m) = 0 rather than exp2(-inf + inf)
-                    const float m_sub = m_ref[hq] == -__builtin_huge_valf() ? 0.f : m_ref[hq];
-                    float p[2][4];
-                    float psum = 0.f;
-#pragma unroll
-                    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) {
-                            p[kt][r] = __builtin_amdgcn_exp2f(fmaf(x[kt][r], scale2, -m_sub));
-                            psum += p[kt][r];
-                        }
-                    l_run[hq] += psum;
-                    pa[hq] = __builtin_bit_cast(u32x4, __builtin_convertvector(
-                        (v8f){p[0][0], p[0][1], p[0][2], p[0][3], p[1][0], p[1][1], p[1][2], p[1][3]},
-                        v8bf));
-                }
-                // O[hq][n] += P[hq] V[:, 16n .. 16n + 15] over this half's 32 keys; the V
-                // operands are read VD blocks ahead of their MFMAs
-                const uint8_t* vb = tb + half * 32 * LROW + vbase;
-                constexpr int VD = 4;
-                u32x4 vbuf[VD];
-                auto vread = [&](int n) -> u32x4 {
-                    const int o = 128 * ((n >> 2) ^ vq) + vo[n & 3];
-                    const u32x2 lo = ds_read_tr(vb + o);
-                    const u32x2 hi = ds_read_tr(vb + o + 16 * LROW);
-                    return u32x4{lo[0], lo[1], hi[0], hi[1]};
-                };
-#pragma unroll
-                for (int n = 0; n < VD; ++n) vbuf[n] = vread(n);
-#pragma unroll
-                for (int n = 0; n < 32; ++n) {
-                    __builtin_amdgcn_sched_barrier(0);
-                    const u32x4 v = vbuf[n % VD];
-                    if (n + VD < 32) vbuf[n % VD] = vread(n + VD);
-#pragma unroll
-                    for (int hq = 0; hq < 2; ++hq)
-                        O[hq][n] = mfma_bf16(as_bf16x8(pa[hq]), as_bf16x8(v), O[hq][n]);
-                }
-                __builtin_amdgcn_sched_barrier(0);
             }
         };
+        int t = 0;
 #pragma unroll 1
-        for (int t = 0; t < ntile; ++t) step(t, s_tile[t & 1]);
+        for (; t < ntile && !have_ref; ++t) step(t, s_tile[t & 1], std::integral_constant<int, 0>{});
+#pragma unroll 1
+        for (; t < ntile && __ballot(idx_cur >= 0) == ~0ull; ++t)
+            step(t, s_tile[t & 1], std::integral_constant<int, 2>{});
+#pragma unroll 1
+        for (; t < ntile; ++t) step(t, s_tile[t & 1], std::integral_constant<int, 1>{});
+
+        // the heads' maxima over the pass and the overflow test (the halves before a head's
+        // reference was fixed held no valid logit, or fixed it, so none of them exceeds it)
+        bool over = false;
+        float m_max[2];
+#pragma unroll
+        for (int hq = 0; hq < 2; ++hq) {
+            m_max[hq] = max_xor32(max_xor16(m_lane[hq])) * scale2;
+            over |= m_max[hq] > m_ref[hq] + OVF_SLACK;
+        }
         // every wave must agree on a recomputation (the tile barriers pair up): flags through LDS
         const bool wave_over = __any(over);
         if (lane == 0) s_flag[wave] = wave_over ? 1 : 0;
@@ -315,8 +405,9 @@ __global__ __launch_bounds__(NW * 64) void sparse_mla_kernel(
         for (int w = 0; w < NW; ++w) redo |= s_flag[w] != 0;
         __syncthreads();                               // flags read before the next pass
         if (!redo) break;
+#pragma unroll
+        for (int hq = 0; hq < 2; ++hq) m_ref[hq] = m_max[hq];
     }
-
     // lane coordinates taken afresh, so that no address of the stores below is formed before
     // the loop and held across it
     int lane_e = lane;
