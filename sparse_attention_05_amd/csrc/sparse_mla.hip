@@ -44,26 +44,50 @@ typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 constexpr int MT = 64;                       // keys per tile
 constexpr int CH = 72;                       // 16-byte chunks per 1152-byte row
 constexpr int TILE_BYTES = MT * CH * 16;     // 73,728
-constexpr int LROW = 1024;                   // latent bytes per row (dims 0..511)
-constexpr int ROPE_OFF = MT * LROW;          // rope part of a tile: [MT rows][128 B]
-constexpr int RROW = 128;                    // rope bytes per row (dims 512..575)
+constexpr int GROW = 128;                    // bytes of a row in one chunk group
+constexpr int GRP = MT * GROW;               // bytes of one chunk group: 8,192
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
 // Headroom of the fixed softmax reference (log2 units): p = 2^(x - m_ref) <= 2^64, so the
 // row sum stays below 2^77 for k <= 8192 and fp32 keeps its relative precision throughout.
 constexpr float OVF_SLACK = 64.f;
 
-// Tile layout.  Latent dims [8c, 8c + 8) of row r (16-byte chunk c < 64) sit at byte
-// row_base(r) + 16 (c ^ lat_x(r)); rope chunk b < 8 (dims 512 + 8b ..) at
-// ROPE_OFF + RROW r + 16 (b ^ rope_x(r)).  lat_x only touches chunk bits 1-3, so for
-// c = 16a + b the offset is a per-lane part for b plus the immediate 256 a.  With these
-// permutations the reads below are free of LDS bank conflicts (measured on gfx950, where a
-// 16-byte read serves lanes {0-7, 24-31}, {8-15, 16-23} and likewise in the upper half
-// together): the K operand reads (16 rows at one chunk per instruction, latent and rope) and
-// the transposing V reads (8-byte pieces of 8 rows, a 32-byte chunk pair per row).
-__device__ __forceinline__ int row_base(int r) { return r * LROW; }
-__device__ __forceinline__ int lat_x(int r) { return (r & 7) << 1; }
-__device__ __forceinline__ int rope_x(int r) { return (r >> 1) & 7; }
+// Tile layout: nine groups of eight 16-byte chunks (group G < 8: latent dims
+// [64G, 64G + 64); group 8: the 64 rope dims), each group [64 rows][128 B].  Chunk c of row
+// r sits at byte GRP (c / 8) + GROW r + 16 ((c % 8) ^ swz(r)), swz(r) = 2 ((r / 2) % 4).
+// One gather instruction fills 1 KB of one group: rows 8j .. 8j + 7, lane l writing row
+// 8j + l/8, slot l % 8.  With swz the reads below are free of LDS bank conflicts (gfx950
+// serves a 16-byte read in the lane groups {0-7, 24-31}, {8-15, 16-23} and likewise in the
+// upper half, an 8-byte read in lanes 0-31 and 32-63): the K operand reads (16 rows at one
+// chunk, the four lane groups at chunks 4m .. 4m + 3) and the transposing V reads (8-byte
+// pieces of 8 rows, a 32-byte chunk pair per row).
+__device__ __forceinline__ int swz(int r) { return ((r >> 1) & 3) << 1; }
+
+// The nine gather instructions of rows 8j .. 8j + 7: lane l loads 16 bytes from sbase + voff
+// + 128 G (group G's chunks) into LDS byte lds_rows + GRP G + 16 l.  The instruction's
+// offset applies to the LDS address (M0 + offset + 16 l) as well as to the global one, so
+// M0 takes lds_rows + (GRP - 128) G; one wait state after each write of M0.
+#define DSA_GRP_LOAD(G) "s_add_u32 m0, %2, " #G " * 8064\n\ts_nop 0\n\t" \
+                        "global_load_lds_dwordx4 %0, %1 offset:" #G " * 128\n\t"
+__device__ __forceinline__ void dma_rows(uint32_t voff, const void* sbase, uint32_t lds_rows)
+{
+    static_assert(GRP - 128 == 8064, "group stride in the gather's immediates");
+    asm volatile(DSA_GRP_LOAD(0) DSA_GRP_LOAD(1) DSA_GRP_LOAD(2) DSA_GRP_LOAD(3) DSA_GRP_LOAD(4)
+                 DSA_GRP_LOAD(5) DSA_GRP_LOAD(6) DSA_GRP_LOAD(7) DSA_GRP_LOAD(8)
+                 :
+                 : "v"(voff), "s"(sbase), "s"(lds_rows)
+                 : "memory", "m0", "scc");
+}
+#undef DSA_GRP_LOAD
+// One of those instructions (group G), for issuing them one at a time between other work.
+template <int G>
+__device__ __forceinline__ void dma_row_group(uint32_t voff, const void* sbase, uint32_t lds_rows)
+{
+    asm volatile("s_add_u32 m0, %2, %3\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 offset:%4"
+                 :
+                 : "v"(voff), "s"(sbase), "s"(lds_rows), "i"(G * (GRP - 128)), "i"(128 * G)
+                 : "memory", "m0", "scc");
+}
 
 // NW = 4 waves; wave w owns heads [32w, 32w + 32) throughout: S^T = K Q^T for them, their
 // softmax, and O = P V over all 512 value dims, so P never leaves the wave's registers and
@@ -131,58 +155,68 @@ __global__ __launch_bounds__(NW * 64) void sparse_mla_kernel(
         return (t * MT + lane < nkeys && s >= 0 && s < Lr) ? s : -1;
     };
     // Gather of a tile into dst (tidx: lane r holds row r's index, -1 for padding, which loads
-    // row 0 and is masked later).  Latent parts: wave w moves rows [RPW w, RPW w + RPW), one
-    // instruction per row, lane l loading the source chunk stored in slot l (chunk
-    // l ^ lat_x(r)).  Rope parts: instruction j moves rows 8j .. 8j+7, lane l row 8j + l/8,
-    // slot l%8, i.e. source chunk 64 + ((l%8) ^ rope_x(8j + l/8)) = 64 + ((l%8) ^ (4 (j%2) + l/16)).
-    constexpr int RPW = MT / NW;                       // latent rows per wave
-    constexpr int JPW = 8 / NW;                        // rope instructions per wave
-    static_assert(JPW % 2 == 0 && RPW % 8 == 0, "rope instruction parity and row groups per wave");
-    const uint32_t rope_src[2] = {16u * (64u + (uint32_t)((lane & 7) ^ (lane >> 4))),
-                                  16u * (64u + (uint32_t)((lane & 7) ^ (4 + (lane >> 4))))};
+    // row 0 and is masked later).  Wave w moves rows 8j .. 8j + 7 for j = 2w, 2w + 1 in all
+    // nine groups: lane l loads row 8j + l/8's chunk 8G + ((l % 8) ^ swz(l / 8)) (swz(8j + x)
+    // = swz(x)).  A row is a 32-bit byte offset from the row's cache (its index times 1152;
+    // the launch keeps every cache below 2 GiB, so the offset stays below 2^31), fetched from
+    // the lane holding it; the group's chunk offset is the instruction's immediate.
     const uint32_t lds_tiles = __builtin_amdgcn_readfirstlane(lds_addr(s_tile[0]));
-    // a gathered row is a 32-bit byte offset from the row's cache (its index times 1152; the
-    // launch keeps every cache below 2 GiB, so the offset stays below 2^31), added to the
-    // lane's chunk offset: a row's load costs a lane read, one add and the load rather than
-    // 64-bit address arithmetic
-    auto issue = [&](int buf, int tidx) {
-        // the lane's chunk offsets are formed here rather than held across the tile loop
+    // gather operands of the wave's two row blocks: the lane's source offset v[jj] and the
+    // LDS address of the block's rows in group 0, rows[jj]
+    struct GatherOps {
+        uint32_t v[2];
+        uint32_t rows[2];
+    };
+    auto gather_ops = [&](int buf, int tidx) -> GatherOps {
+        // the lane's offsets are formed here rather than held across the tile loop
         int ln = lane;
         asm volatile("" : "+v"(ln));
         const uint32_t dst = lds_tiles + (uint32_t)buf * TILE_BYTES;
         const uint32_t roff = (uint32_t)max(tidx, 0) * 1152u;   // lane r: row r's byte offset
-#pragma unroll 2
-        for (int i0 = 0; i0 < RPW; i0 += 8)
+        const uint32_t part = 16u * (uint32_t)((ln & 7) ^ swz(ln >> 3));
+        GatherOps o;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const int r = wave * RPW + i0 + i;         // r & 7 == i: lat_x(r) = 2 i
-                dma16_s((uint32_t)__builtin_amdgcn_readlane((int)roff, r) +
-                            16u * (uint32_t)(ln ^ (2 * i)), kvr, dst + r * LROW);
-            }
-#pragma unroll
-        for (int jj = 0; jj < JPW; ++jj) {
-            const int j = wave * JPW + jj;
-            const uint32_t ro = (uint32_t)__builtin_amdgcn_ds_bpermute((8 * j + (lane >> 3)) * 4, (int)roff);
-            dma16_s(ro + rope_src[jj & 1], kvr, dst + ROPE_OFF + j * 1024);
+        for (int jj = 0; jj < 2; ++jj) {
+            const int j = 2 * wave + jj;
+            o.v[jj] = (uint32_t)__builtin_amdgcn_ds_bpermute((8 * j + (ln >> 3)) * 4, (int)roff) + part;
+            o.rows[jj] = dst + (uint32_t)j * 1024u;
+        }
+        return o;
+    };
+    auto issue = [&](int buf, int tidx) {
+        const GatherOps o = gather_ops(buf, tidx);
+        dma_rows(o.v[0], kvr, o.rows[0]);
+        dma_rows(o.v[1], kvr, o.rows[1]);
+    };
+    // the i-th of the wave's 18 gather instructions (row block i / 9, group i % 9)
+    auto issue_one = [&](const GatherOps& o, int i) {
+        const int jj = i / 9;
+        switch (i % 9) {
+        case 0: dma_row_group<0>(o.v[jj], kvr, o.rows[jj]); break;
+        case 1: dma_row_group<1>(o.v[jj], kvr, o.rows[jj]); break;
+        case 2: dma_row_group<2>(o.v[jj], kvr, o.rows[jj]); break;
+        case 3: dma_row_group<3>(o.v[jj], kvr, o.rows[jj]); break;
+        case 4: dma_row_group<4>(o.v[jj], kvr, o.rows[jj]); break;
+        case 5: dma_row_group<5>(o.v[jj], kvr, o.rows[jj]); break;
+        case 6: dma_row_group<6>(o.v[jj], kvr, o.rows[jj]); break;
+        case 7: dma_row_group<7>(o.v[jj], kvr, o.rows[jj]); break;
+        default: dma_row_group<8>(o.v[jj], kvr, o.rows[jj]); break;
         }
     };
 
-    // per-lane offsets of the operand reads (see the tile layout above)
-    int qo[4], ro[2];                  // S^T A operand: latent chunk 4m + g, rope chunk 4(m-16) + g
+    // per-lane offsets of the operand reads (see the tile layout above).  S^T A operand for
+    // step m (chunk 4m + g of rows 32 half + 16 kt + c16: group m / 2, slot 4 (m % 2) + g)
+    int qo[2];
 #pragma unroll
-    for (int b = 0; b < 4; ++b) qo[b] = ((4 * b + g) ^ lat_x(c16)) << 4;
-#pragma unroll
-    for (int b = 0; b < 2; ++b) ro[b] = ((4 * b + g) ^ rope_x(c16)) << 4;
+    for (int p = 0; p < 2; ++p) qo[p] = 16 * ((4 * p + g) ^ swz(c16));
     // V operand of P V for dim block n, keys 32 half + 16 kt + 4g + r: transposing reads, lane
     // (g, i) addressing row 32 half + 16 kt + 4g + i/4, dims 16n + 4(i%4) .. +3, i.e. chunk
-    // 2n + (i%4)/2 (physical (2n + cpart) ^ lat_x(rv) = 8 ((n/4) ^ vq) + 2 ((n%4) ^ (rv%4)) +
-    // cpart), byte 8 (i%2) within it
+    // 2n + (i%4)/2 (group n / 4, slot (2 (n % 4) + (i%4)/2) ^ swz(row)), byte 8 (i%2) in it
     const int rv = 4 * g + (c16 >> 2);
-    const int vq = (rv >> 2) & 1;
-    const int vbase = row_base(rv) + (c16 & 1) * 8;
+    const int vbase = GROW * rv + (c16 & 1) * 8;
     int vo[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) vo[j] = 32 * (j ^ (rv & 3)) + 16 * ((c16 & 3) >> 1);
+    for (int j = 0; j < 4; ++j) vo[j] = 16 * ((2 * j + ((c16 & 3) >> 1)) ^ swz(rv));
 
     v4f O[2][32];                      // O[hq][n]: heads 32 wave + 16 hq + 4g + r, dims 16n + c16
     // m_ref: -inf for the first pass (then fixed by the row's first valid logits); a
@@ -197,15 +231,14 @@ __global__ __launch_bounds__(NW * 64) void sparse_mla_kernel(
     // (the compiler would place them in AGPRs beside O and shuffle part of O out and back
     // around every half).  between(s) runs inside step s's scheduling region.
     auto qk_half = [&](const uint8_t* tb, int half, v4f (&S)[2][2], auto&& between) {
-        const uint8_t* rb = tb + row_base(half * 32 + c16);    // kt adds 16 rows
-        const uint8_t* rr = tb + ROPE_OFF + RROW * (half * 32 + c16);
+        const uint8_t* rb = tb + GROW * (half * 32 + c16);     // kt adds 16 rows
         constexpr int QD = 2;
         u32x4 abuf[QD][2];
 #pragma unroll
         for (int s = 0; s < QD; ++s)
 #pragma unroll
             for (int kt = 0; kt < 2; ++kt)
-                abuf[s][kt] = *reinterpret_cast<const u32x4*>(rb + kt * 16 * LROW + 256 * (s >> 2) + qo[s & 3]);
+                abuf[s][kt] = *reinterpret_cast<const u32x4*>(rb + kt * 16 * GROW + GRP * (s >> 1) + qo[s & 1]);
 #pragma unroll
         for (int s = 0; s < 18; ++s) {
             __builtin_amdgcn_sched_barrier(0);
@@ -215,8 +248,7 @@ __global__ __launch_bounds__(NW * 64) void sparse_mla_kernel(
 #pragma unroll
                 for (int kt = 0; kt < 2; ++kt)
                     abuf[s % QD][kt] = *reinterpret_cast<const u32x4*>(
-                        m < 16 ? rb + kt * 16 * LROW + 256 * (m >> 2) + qo[m & 3]
-                               : rr + kt * 16 * RROW + ro[m & 1]);
+                        rb + kt * 16 * GROW + GRP * (m >> 1) + qo[m & 1]);
             }
 #pragma unroll
             for (int kt = 0; kt < 2; ++kt)
@@ -240,13 +272,13 @@ __global__ __launch_bounds__(NW * 64) void sparse_mla_kernel(
     // O[hq][n] += P[hq] V[:, 16n .. 16n + 15] over one half's 32 keys, the V operands read VD
     // blocks ahead; between(n) runs inside step n's scheduling region
     auto pv_half = [&](const uint8_t* tb, int half, const u32x4 (&pa)[2], auto&& between) {
-        const uint8_t* vb = tb + half * 32 * LROW + vbase;
+        const uint8_t* vb = tb + half * 32 * GROW + vbase;
         constexpr int VD = 4;
         u32x4 vbuf[VD];
         auto vread = [&](int n) -> u32x4 {
-            const int o = 128 * ((n >> 2) ^ vq) + vo[n & 3];
+            const int o = GRP * (n >> 2) + vo[n & 3];
             const u32x2 lo = ds_read_tr(vb + o);
-            const u32x2 hi = ds_read_tr(vb + o + 16 * LROW);
+            const u32x2 hi = ds_read_tr(vb + o + 16 * GROW);
             return u32x4{lo[0], lo[1], hi[0], hi[1]};
         };
 #pragma unroll
@@ -349,14 +381,20 @@ __global__ __launch_bounds__(NW * 64) void sparse_mla_kernel(
             __syncthreads();                           // everyone's part; tile t-1 consumed
             const uint64_t vmask = __ballot(idx_cur >= 0);
             idx_nxt = check_idx(t + 1, idx_nxt);
-            if (t + 1 < ntile) issue((t + 1) & 1, idx_nxt);
+            GatherOps go;
+            if constexpr (KIND == 2)                   // a next tile exists: issued below
+                go = gather_ops((t + 1) & 1, idx_nxt);
+            else if (t + 1 < ntile)
+                issue((t + 1) & 1, idx_nxt);
             idx_cur = idx_nxt;
             idx_nxt = load_idx(t + 2);
             if constexpr (KIND == 2) {
                 v4f S0[2][2], S1[2][2];
                 u32x4 pa0[2], pa1[2];
                 float pb[2], psum[2];
-                qk_half(tb, 0, S0, [](int) {});
+                // the next tile's gather, one instruction per QK step (bunched, the wave's
+                // 18 instructions wait for the address unit, which the other waves' fill too)
+                qk_half(tb, 0, S0, [&](int s) { issue_one(go, s); });
                 qk_half(tb, 1, S1, [&](int s) {
                     if (s < 16) softmax_elem(S0, s, pb, psum, pa0);
                 });
@@ -382,7 +420,7 @@ __global__ __launch_bounds__(NW * 64) void sparse_mla_kernel(
 #pragma unroll 1
         for (; t < ntile && !have_ref; ++t) step(t, s_tile[t & 1], std::integral_constant<int, 0>{});
 #pragma unroll 1
-        for (; t < ntile && __ballot(idx_cur >= 0) == ~0ull; ++t)
+        for (; t + 1 < ntile && __ballot(idx_cur >= 0) == ~0ull; ++t)
             step(t, s_tile[t & 1], std::integral_constant<int, 2>{});
 #pragma unroll 1
         for (; t < ntile; ++t) step(t, s_tile[t & 1], std::integral_constant<int, 1>{});
