@@ -41,7 +41,8 @@ constexpr int T_LROW = 1024;                  // latent bytes per row in a tile
 constexpr int T_RROW = 128;                   // rope bytes per row
 constexpr int T_ROPE = TM * T_LROW;           // rope part of a tile
 constexpr int T_TILE = TM * 1152;             // 73,728 bytes
-// 16-byte chunk swizzles of the tile (conflict-free K-operand reads, as in sparse_mla.hip)
+// 16-byte chunk swizzles of the row-major tile (latent chunk c of row r at slot c ^ 2 (r mod 8),
+// rope chunk b at b ^ ((r >> 1) mod 8)): conflict-free K-operand reads
 __device__ __forceinline__ int t_latx(int r) { return (r & 7) << 1; }
 __device__ __forceinline__ int t_ropex(int r) { return (r >> 1) & 7; }
 
