@@ -63,6 +63,20 @@ constexpr float OVF_SLACK = 64.f;
 // pieces of 8 rows, a 32-byte chunk pair per row).
 __device__ __forceinline__ int swz(int r) { return ((r >> 1) & 3) << 1; }
 
+// s_waitcnt on the LDS counter alone: at most n LDS operations outstanding (n a constant
+// once the caller's loop is unrolled: 0, 2, 4 or 6; anything else waits for all)
+#define DSA_WAIT_LDS(n) __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4) | ((n) << 8))
+__device__ __forceinline__ void wait_lds(int n)
+{
+    switch (n) {
+    case 6: DSA_WAIT_LDS(6); break;
+    case 4: DSA_WAIT_LDS(4); break;
+    case 2: DSA_WAIT_LDS(2); break;
+    default: DSA_WAIT_LDS(0); break;
+    }
+}
+#undef DSA_WAIT_LDS
+
 // The nine gather instructions of rows 8j .. 8j + 7: lane l loads 16 bytes from sbase + voff
 // + 128 G (group G's chunks) into LDS byte lds_rows + GRP G + 16 l.  The instruction's
 // offset applies to the LDS address (M0 + offset + 16 l) as well as to the global one, so
@@ -232,7 +246,7 @@ __global__ __launch_bounds__(NW * 64) void sparse_mla_kernel(
     // around every half).  between(s) runs inside step s's scheduling region.
     auto qk_half = [&](const uint8_t* tb, int half, v4f (&S)[2][2], auto&& between) {
         const uint8_t* rb = tb + GROW * (half * 32 + c16);     // kt adds 16 rows
-        constexpr int QD = 2;
+        constexpr int QD = 4;
         u32x4 abuf[QD][2];
 #pragma unroll
         for (int s = 0; s < QD; ++s)
@@ -242,6 +256,9 @@ __global__ __launch_bounds__(NW * 64) void sparse_mla_kernel(
 #pragma unroll
         for (int s = 0; s < 18; ++s) {
             __builtin_amdgcn_sched_barrier(0);
+            // one wait per two steps: both steps' operands (the reads of later steps may stay
+            // in flight)
+            if ((s & 1) == 0) wait_lds(2 * max(0, min(17, s - 1 + QD) - (s + 1)));
             const u32x4 a[2] = {abuf[s % QD][0], abuf[s % QD][1]};
             if (s + QD < 18) {
                 const int m = s + QD;
@@ -286,6 +303,7 @@ __global__ __launch_bounds__(NW * 64) void sparse_mla_kernel(
 #pragma unroll
         for (int n = 0; n < 32; ++n) {
             __builtin_amdgcn_sched_barrier(0);
+            if ((n & 1) == 0) wait_lds(2 * max(0, min(31, n - 1 + VD) - (n + 1)));
             const u32x4 v = vbuf[n % VD];
             if (n + VD < 32) vbuf[n % VD] = vread(n + VD);
 #pragma unroll
