@@ -64,7 +64,11 @@ constexpr float OVF_SLACK = 64.f;
 __device__ __forceinline__ int swz(int r) { return ((r >> 1) & 3) << 1; }
 
 // s_waitcnt on the LDS counter alone: at most n LDS operations outstanding (n a constant
-// once the caller's loop is unrolled: 0, 2, 4 or 6; anything else waits for all)
+// once the caller's loop is unrolled: 0, 2, 4 or 6; anything else waits for all).  LDS
+// operations complete in order on that counter; no scalar memory load (which shares it and
+// may return out of order) is in flight in the tile loop: the kernel's arguments are loaded
+// and awaited before it.  Further LDS operations issued after the awaited ones only make
+// such a wait stricter.
 #define DSA_WAIT_LDS(n) __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4) | ((n) << 8))
 __device__ __forceinline__ void wait_lds(int n)
 {
