@@ -9,11 +9,11 @@
 // list: four waves (128 head slots), one wave per SIMD with the full 512-register file.  The
 // selected 1152-byte rows are gathered 64 at a time by direct global->LDS loads into a
 // double-buffered tile, so the next tile streams in while the current one is used.  A tile
-// holds the rows' 512 latent dims as [64 rows][1024 B] and their 64 rope dims as
-// [64 rows][128 B], 16-byte chunks XOR-swizzled by row: one gather instruction moves one
-// row's latent part (a wave-uniform scalar base address plus a fixed per-lane chunk offset)
-// or the rope parts of eight rows, so issuing the gather costs a few scalar instructions per
-// row.  Wave w owns 32 heads from end to end:
+// holds nine groups of eight 16-byte chunks (eight groups of 64 latent dims, one of the 64
+// rope dims), each group [64 rows][128 B] with its chunks swizzled by row: one gather
+// instruction fills 1 KB of a group for eight rows from a per-lane row offset and the
+// group's immediate, and a full tile spreads the next tile's gather over its first QK steps.
+// Wave w owns 32 heads from end to end:
 //  * S^T = K Q^T for its heads (A = gathered rows, each 16-byte operand read feeding two
 //    MFMAs; B = Q^T held in registers), then their softmax, whose bf16 probabilities come out
 //    of the accumulators already in the A-operand layout of P V;
