@@ -358,20 +358,27 @@ __global__ __launch_bounds__(NW * 64) void sparse_mla_kernel(
         }
     };
     // Element e of a half's softmax when every key is valid and the references are fixed
-    // (head group e / 8, key group e / 4 % 2, element e % 4): per head the same operations in
-    // the same order as softmax_half, so the results are bitwise those of the unsplit form.
-    auto softmax_elem = [&](const v4f (&S)[2][2], int e, float (&pb)[2], float (&psum)[2],
-                            u32x4 (&pa)[2]) {
+    // (head group e / 8, key group e / 4 % 2, element e % 4), in three stages that the full
+    // tile places in successive MFMA steps, so that no vector instruction of a step waits for
+    // another of the same step: A, the exponent's argument (and the lane's running maximum);
+    // B, the exponential; C, the head's running sum and the bf16 pair.  Per head the same
+    // operations in the same order as softmax_half, so the results are bitwise those of the
+    // unsplit form.
+    auto sm_a = [&](const v4f (&S)[2][2], int e, float (&tv)[16]) {
         const int hq = e >> 3, kt = (e >> 2) & 1, r = e & 3;
         const float x = S[kt][hq][r];
         m_lane[hq] = fmaxf(m_lane[hq], x);
-        const float p = __builtin_amdgcn_exp2f(fmaf(x, scale2, -m_ref[hq]));
-        psum[hq] = (e & 7) == 0 ? p : psum[hq] + p;
+        tv[e] = fmaf(x, scale2, -m_ref[hq]);
+    };
+    auto sm_b = [&](int e, const float (&tv)[16], float (&pv)[16]) {
+        pv[e] = __builtin_amdgcn_exp2f(tv[e]);
+    };
+    auto sm_c = [&](int e, const float (&pv)[16], float (&psum)[2], u32x4 (&pa)[2]) {
+        const int hq = e >> 3, kt = (e >> 2) & 1, r = e & 3;
+        psum[hq] = (e & 7) == 0 ? pv[e] : psum[hq] + pv[e];
         if (r & 1)
             pa[hq][(kt * 4 + r) >> 1] =
-                __builtin_bit_cast(uint32_t, __builtin_convertvector((v2f){pb[hq], p}, v2bf));
-        else
-            pb[hq] = p;
+                __builtin_bit_cast(uint32_t, __builtin_convertvector((v2f){pv[e - 1], pv[e]}, v2bf));
         if ((e & 7) == 7) l_run[hq] += psum[hq];
     };
 
@@ -413,16 +420,28 @@ __global__ __launch_bounds__(NW * 64) void sparse_mla_kernel(
             if constexpr (KIND == 2) {
                 v4f S0[2][2], S1[2][2];
                 u32x4 pa0[2], pa1[2];
-                float pb[2], psum[2];
+                float psum[2];
+                float tv0[16], pv0[16], tv1[16], pv1[16];
                 // the next tile's gather, one instruction per QK step (bunched, the wave's
                 // 18 instructions wait for the address unit, which the other waves' fill too)
                 qk_half(tb, 0, S0, [&](int s) { issue_one(go, s); });
+                // the first half's softmax, stage A of element s, B of s - 1, C of s - 2
                 qk_half(tb, 1, S1, [&](int s) {
-                    if (s < 16) softmax_elem(S0, s, pb, psum, pa0);
+                    if (s < 16) sm_a(S0, s, tv0);
+                    if (s >= 1 && s <= 16) sm_b(s - 1, tv0, pv0);
+                    if (s >= 2) sm_c(s - 2, pv0, psum, pa0);
                 });
+                // the second's, stage A of element n / 2 at even steps, B at odd ones, C a
+                // step later
                 pv_half(tb, 0, pa0, [&](int n) {
-                    if ((n & 1) == 0) softmax_elem(S1, n >> 1, pb, psum, pa1);
+                    if ((n & 1) == 0) {
+                        sm_a(S1, n >> 1, tv1);
+                        if (n >= 2) sm_c((n >> 1) - 1, pv1, psum, pa1);
+                    } else {
+                        sm_b(n >> 1, tv1, pv1);
+                    }
                 });
+                sm_c(15, pv1, psum, pa1);
                 pv_half(tb, 1, pa1, [](int) {});
             } else {
 #pragma unroll 1
