@@ -209,6 +209,10 @@ __global__ __launch_bounds__(IP_WAVES * 64, ip_waves_per_simd<HI>()) void indexe
     // MODE 1: the wave's staged candidates (a wave-uniform count) and its row's threshold
     int nst = 0;
     const uint32_t tau_w = MODE == 1 && wave_active ? ex.tau[tw0] : 0u;
+    // the threshold as a float: score_key(v) >= tau exactly when v >= tau_f for finite v (the
+    // key is monotonic in v with -0 = +0; thresholds at or below the key of -inf keep every key)
+    const float tau_f = tau_w <= 0x007FFFFFu ? -__builtin_huge_valf()
+                        : __uint_as_float((tau_w & 0x80000000u) ? (tau_w & 0x7FFFFFFFu) : ~tau_w);
     auto flush = [&]() {
         int base = 0;
         if (lane == 0) base = atomicAdd(&ex.fill[tw0], nst);
@@ -275,15 +279,15 @@ __global__ __launch_bounds__(IP_WAVES * 64, ip_waves_per_simd<HI>()) void indexe
                         if (vis) srow[sl] = v * s_ks[buf][sl];
                     } else {
                         // lanes hold consecutive keys, so ballot order is position order
-                        const uint32_t key = score_key(v * s_ks[buf][sl]);
-                        const bool take = vis && key >= tau_w;
+                        const float sv = v * s_ks[buf][sl];
+                        const bool take = vis && sv >= tau_f;
                         const uint64_t m = __ballot(take);
                         if (m) {
                             const int nm = __popcll(m);
                             if (nst + nm > IP_CSTAGE) flush();
                             const int rk = __builtin_amdgcn_mbcnt_hi(
                                 (uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
-                            if (take) s_cand[wave][nst + rk] = make_uint2(key, tbase + sl);
+                            if (take) s_cand[wave][nst + rk] = make_uint2(__float_as_uint(sv), tbase + sl);
                             nst += nm;
                         }
                     }

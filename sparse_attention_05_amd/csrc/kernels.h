@@ -16,7 +16,7 @@ struct IdxExtra {
     const int* only = nullptr;       // rows t with only[t] == 0 are not scored
     const uint32_t* tau = nullptr;   // candidates: per-row thresholds (score_key images)
     int* fill = nullptr;             // candidates: per-row counts, 0 before the launch
-    uint2* cand = nullptr;           // candidates: (key, position) arrays of capr per row
+    uint2* cand = nullptr;           // candidates: (score bits, position) arrays of capr per row
     int capr = 0;
 };
 // Scores of T query rows (positions q_pos0 + t) against keys 0..L-1; writes only the
@@ -27,7 +27,8 @@ hipError_t launch_indexer_prefill(const uint8_t* q8, const float* qs, const floa
                                   int q_pos0, float c, float* scores, int64_t ld,
                                   hipStream_t stream, const IdxExtra& ex = IdxExtra{});
 // Candidates instead of scores: row t's visible keys with score_key(score) >= tau[t] are
-// appended to cand + t * capr as (key, position) in no particular order; fill[t] counts all
+// appended to cand + t * capr as (score bits, position) in no particular order (the score
+// compared as a float against tau[t]'s inverse image); fill[t] counts all
 // of them (entries past capr are counted, not stored).
 bool indexer_fused_supports(int H_I);
 hipError_t launch_indexer_candidates(const uint8_t* q8, const float* qs, const float* w,

@@ -842,16 +842,16 @@ __global__ __launch_bounds__(TK_THREADS) void topk_resolve_kernel(
 #pragma unroll
         for (int q = 0; q < SEL_PT / 2; ++q) {
             const u32x4 v = *reinterpret_cast<const u32x4*>(src + 2 * q);
-            kr[2 * q] = v[0];
+            kr[2 * q] = score_key(__uint_as_float(v[0]));
             pr[2 * q] = (int)v[1];
-            kr[2 * q + 1] = v[2];
+            kr[2 * q + 1] = score_key(__uint_as_float(v[2]));
             pr[2 * q + 1] = (int)v[3];
         }
     } else {
 #pragma unroll
         for (int j = 0; j < SEL_PT; ++j) {
             const uint2 e = j < cnt ? src[j] : make_uint2(0u, 0u);
-            kr[j] = e.x;
+            kr[j] = score_key(__uint_as_float(e.x));
             pr[j] = (int)e.y;
         }
     }
